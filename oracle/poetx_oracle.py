@@ -1,0 +1,266 @@
+"""Float64 CPU oracle of the POET-X linear layer y = R W0 P x.
+
+TEST INFRASTRUCTURE. Only tests, the smoke check and the benchmark's CPU
+baseline may import or run this module; the library and its Python binding
+never do. It shares no code with the HIP path.
+
+Sources (all pages carry the title "POET-X: Memory-efficient LLM Training by
+Scaling Orthogonal Transformation"; the technical text is the German summary
+on gist.science, "Technische Zusammenfassung"):
+  [OET]   §1 Problemstellung: a weight is reparameterised as W = R W0 P, with
+          R and P trainable orthogonal matrices; the ICML and arXiv abstracts
+          add that the transform preserves the singular spectrum.
+  [IC]    §2 Methodik, input-centric formulation: instead of rebuilding the
+          weight, the transform is applied to the activations, one operation
+          after another.
+  [BD]    §2 Methodik, batch-parallel block-diagonal matrices: R and P are
+          block-diagonal and their blocks are multiplied as independent
+          matrices.
+  [SKEW]  §2 Methodik, Cayley-Neumann parameterisation: orthogonality comes
+          from a skew-symmetric Q (Q = -Q^T) of which only the upper triangle
+          is stored.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * the orthogonal map is the exact Cayley map R = (I + Q)(I - Q)^-1 (the
+    pages name a truncated-series approximation of it without printing it);
+    the sign convention is the one whose series expansion of (I - Q)^-1 has
+    only positive powers of Q, matching the pages' list of powers Q..Q^4;
+  * Q is built as U - U^T from the strict upper triangle U, no 1/2 factor,
+    packed row-major: idx(i, j) = i(2b - i - 1)/2 + (j - i - 1) for i < j;
+  * R acts on the d_out outputs, P on the d_in inputs; blocks are contiguous
+    and start at feature 0; no permutation;
+  * if b does not divide d, the last block is identity-padded: the generator
+    entries of rows/columns past the end are treated as zero, so the block is
+    diag(Cayley(Q_r), I) and only its leading r x r part acts;
+  * backward outputs are g_x, g_theta_R, g_theta_P (W0 is frozen, no g_W0).
+
+Where "parity unpinned": nothing here. Every function is pinned by
+tests/test_oracle.py against closed forms (b = 2 rotation, b = 3 Rodrigues
+rotation), invariants (orthogonality, det, spectrum), textbook routines
+(dense scipy block_diag products) and central finite differences.
+
+Layouts: activations are token-major, x [N, d_in], y [N, d_out]; W0 is
+[d_out, d_in]; theta is [nblocks, b(b-1)/2].
+"""
+from __future__ import annotations
+
+from typing import List, Tuple
+
+import numpy as np
+
+__all__ = [
+    "packed_upper_index", "skew_from_theta", "theta_from_skew", "cayley",
+    "block_ranges", "orthogonal_blocks", "materialise", "forward",
+    "backward", "cayley_vjp", "forward_input_centric",
+    "backward_input_centric", "LayerOracle",
+]
+
+
+# ---------------------------------------------------------------- [SKEW]
+def packed_upper_index(b: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Row/column indices (i < j) of the packed strict upper triangle, in
+    storage order: row-major, so position p holds Q[i[p], j[p]] with
+    p = i(2b - i - 1)/2 + (j - i - 1). [SKEW]"""
+    rows, cols = [], []
+    for i in range(b):
+        for j in range(i + 1, b):
+            rows.append(i)
+            cols.append(j)
+    return np.asarray(rows, dtype=np.int64), np.asarray(cols, dtype=np.int64)
+
+
+def skew_from_theta(theta: np.ndarray, b: int, d: int | None = None) -> np.ndarray:
+    """Expand packed generators theta [nb, b(b-1)/2] to skew blocks Q [nb, b, b]
+    with Q[i, j] = theta, Q[j, i] = -theta for i < j and a zero diagonal.
+    [SKEW] If `d` is given and b does not divide it, the entries of the last
+    block's rows and columns at or past r = d - (nb-1) b are zeroed
+    (identity padding)."""
+    theta = np.asarray(theta, dtype=np.float64)
+    nb = theta.shape[0]
+    iu, ju = packed_upper_index(b)
+    Q = np.zeros((nb, b, b), dtype=np.float64)
+    Q[:, iu, ju] = theta
+    Q[:, ju, iu] = -theta
+    if d is not None:
+        r = d - (nb - 1) * b
+        if r < b:
+            Q[-1, r:, :] = 0.0
+            Q[-1, :, r:] = 0.0
+    return Q
+
+
+def theta_from_skew(Q: np.ndarray) -> np.ndarray:
+    """Pack the strict upper triangle of each block of Q [nb, b, b]. [SKEW]"""
+    b = Q.shape[-1]
+    iu, ju = packed_upper_index(b)
+    return np.ascontiguousarray(Q[:, iu, ju])
+
+
+# ------------------------------------------------------ exact Cayley map
+def cayley(Q: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact Cayley map of each skew block: B = (I - Q)^-1 by a LAPACK solve
+    (partial pivoting), then R = (I + Q) B. Returns (R, B), each [nb, b, b].
+    [SKEW] names the Cayley-based parameterisation; the exact map is this
+    build's reading (see the module docstring)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    b = Q.shape[-1]
+    I = np.eye(b)
+    B = np.stack([np.linalg.solve(I - q, I) for q in Q]) if len(Q) else np.zeros_like(Q)
+    R = np.stack([(I + q) @ bk for q, bk in zip(Q, B)]) if len(Q) else np.zeros_like(Q)
+    return R, B
+
+
+# ------------------------------------------------------- block structure
+def block_ranges(d: int, b: int) -> List[Tuple[int, int]]:
+    """(start, size) of each contiguous block of features; the last block may
+    be shorter when b does not divide d. [BD]"""
+    return [(s, min(b, d - s)) for s in range(0, d, b)]
+
+
+def orthogonal_blocks(theta: np.ndarray, b: int, d: int) -> Tuple[np.ndarray, np.ndarray]:
+    """theta [nb, b(b-1)/2] -> (R blocks, B blocks) of a block-diagonal
+    orthogonal matrix on d features. [SKEW], [BD]"""
+    return cayley(skew_from_theta(theta, b, d))
+
+
+def materialise(W0: np.ndarray, R: np.ndarray, P: np.ndarray, b_out: int, b_in: int) -> np.ndarray:
+    """W = R W0 P with block-diagonal R (on the d_out rows) and P (on the d_in
+    columns), computed block by block. This is the weight-centric form that
+    the input-centric method avoids on the GPU. [OET], [BD]"""
+    W0 = np.asarray(W0, dtype=np.float64)
+    m, n = W0.shape
+    W = W0.copy()
+    for k, (s, r) in enumerate(block_ranges(m, b_out)):
+        W[s:s + r, :] = R[k, :r, :r] @ W[s:s + r, :]
+    for j, (s, r) in enumerate(block_ranges(n, b_in)):
+        W[:, s:s + r] = W[:, s:s + r] @ P[j, :r, :r]
+    return W
+
+
+# ------------------------------------------------------- forward / backward
+def forward(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """y = W x for every token; token-major Y = X W^T. [OET]"""
+    return np.asarray(x, dtype=np.float64) @ W.T
+
+
+def cayley_vjp(B: np.ndarray, G: np.ndarray) -> np.ndarray:
+    """Gradient of the packed generators given G = dL/dR per block.
+
+    R = 2B - I with B = (I - Q)^-1, so dR = 2 B dQ B and
+    dL/dQ = 2 B^T G B^T; a packed entry theta_(i,j) enters Q at (i, j) with
+    sign + and at (j, i) with sign -, hence
+    dL/dtheta_(i,j) = Mx[i, j] - Mx[j, i] with Mx = 2 B^T G B^T.
+    (The pages never describe the backward; this is the chain rule.)"""
+    b = B.shape[-1]
+    iu, ju = packed_upper_index(b)
+    out = np.empty((B.shape[0], len(iu)), dtype=np.float64)
+    for k in range(B.shape[0]):
+        Mx = 2.0 * B[k].T @ G[k] @ B[k].T
+        out[k] = Mx[iu, ju] - Mx[ju, iu]
+    return out
+
+
+def _pad_grad_zero(g: np.ndarray, b: int, d: int) -> np.ndarray:
+    """Drop (zero) the gradients of padded generator entries."""
+    nb = g.shape[0]
+    r = d - (nb - 1) * b
+    if r < b:
+        iu, ju = packed_upper_index(b)
+        g = g.copy()
+        g[-1, (iu >= r) | (ju >= r)] = 0.0
+    return g
+
+
+def backward(g_y: np.ndarray, x: np.ndarray, W0: np.ndarray,
+             R: np.ndarray, B_R: np.ndarray, P: np.ndarray, B_P: np.ndarray,
+             b_out: int, b_in: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Backward of the layer through the materialised weight.
+
+    G_W = g_Y^T X is the gradient of the full weight. With W = R (W0 P):
+    dL/dR = G_W (W0 P)^T, of which only the diagonal blocks are parameters;
+    with W = (R W0) P: dL/dP = (R W0)^T G_W, again block-diagonal part only.
+    Returns (g_x, g_theta_R, g_theta_P). [OET], [BD]; backward derived by the
+    chain rule."""
+    g_y = np.asarray(g_y, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    W0 = np.asarray(W0, dtype=np.float64)
+    m, n = W0.shape
+    W = materialise(W0, R, P, b_out, b_in)
+    g_x = g_y @ W
+    G_W = g_y.T @ x
+    ident_R = np.broadcast_to(np.eye(b_out), R.shape)
+    ident_P = np.broadcast_to(np.eye(b_in), P.shape)
+    W0P = materialise(W0, ident_R, P, b_out, b_in)
+    RW0 = materialise(W0, R, ident_P, b_out, b_in)
+    G_R = np.zeros_like(R)
+    for k, (s, r) in enumerate(block_ranges(m, b_out)):
+        G_R[k, :r, :r] = G_W[s:s + r, :] @ W0P[s:s + r, :].T
+    G_P = np.zeros_like(P)
+    for j, (s, r) in enumerate(block_ranges(n, b_in)):
+        G_P[j, :r, :r] = RW0[:, s:s + r].T @ G_W[:, s:s + r]
+    g_tR = _pad_grad_zero(cayley_vjp(B_R, G_R), b_out, m)
+    g_tP = _pad_grad_zero(cayley_vjp(B_P, G_P), b_in, n)
+    return g_x, g_tR, g_tP
+
+
+# ----------------------------------------- second route: input-centric [IC]
+def _apply_blocks(a: np.ndarray, blocks: np.ndarray, b: int, transpose: bool) -> np.ndarray:
+    """Token-major block-diagonal product: out[:, blk] = a[:, blk] M^T for
+    M = blocks[k] (transpose=True) or a[:, blk] M (transpose=False)."""
+    out = np.empty_like(a)
+    for k, (s, r) in enumerate(block_ranges(a.shape[1], b)):
+        M = blocks[k, :r, :r]
+        out[:, s:s + r] = a[:, s:s + r] @ (M.T if transpose else M)
+    return out
+
+
+def forward_input_centric(x, W0, R, P, b_out, b_in):
+    """U = X P^T, Z = U W0^T, Y = Z R^T (token-major). Returns (Y, Z, U). [IC]"""
+    x = np.asarray(x, dtype=np.float64)
+    U = _apply_blocks(x, P, b_in, transpose=True)
+    Z = U @ np.asarray(W0, dtype=np.float64).T
+    Y = _apply_blocks(Z, R, b_out, transpose=True)
+    return Y, Z, U
+
+
+def backward_input_centric(g_y, x, W0, R, B_R, P, B_P, b_out, b_in):
+    """Backward along the input-centric dataflow:
+    g_Z = g_Y R, G_R[k] = g_Y[:, k]^T Z[:, k], g_U = g_Z W0,
+    G_P[j] = g_U[:, j]^T X[:, j], g_X = g_U P. [IC], chain rule."""
+    g_y = np.asarray(g_y, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    W0 = np.asarray(W0, dtype=np.float64)
+    m, n = W0.shape
+    _, Z, _ = forward_input_centric(x, W0, R, P, b_out, b_in)
+    g_Z = _apply_blocks(g_y, R, b_out, transpose=False)
+    G_R = np.zeros_like(R)
+    for k, (s, r) in enumerate(block_ranges(m, b_out)):
+        G_R[k, :r, :r] = g_y[:, s:s + r].T @ Z[:, s:s + r]
+    g_U = g_Z @ W0
+    G_P = np.zeros_like(P)
+    for j, (s, r) in enumerate(block_ranges(n, b_in)):
+        G_P[j, :r, :r] = g_U[:, s:s + r].T @ x[:, s:s + r]
+    g_x = _apply_blocks(g_U, P, b_in, transpose=False)
+    g_tR = _pad_grad_zero(cayley_vjp(B_R, G_R), b_out, m)
+    g_tP = _pad_grad_zero(cayley_vjp(B_P, G_P), b_in, n)
+    return g_x, g_tR, g_tP
+
+
+class LayerOracle:
+    """One layer's full oracle result (Cayley build, forward, backward),
+    computed through the materialised weight."""
+
+    def __init__(self, W0, theta_R, theta_P, b_out, b_in):
+        self.W0 = np.asarray(W0, dtype=np.float64)
+        m, n = self.W0.shape
+        self.b_out, self.b_in = b_out, b_in
+        self.R, self.B_R = orthogonal_blocks(theta_R, b_out, m)
+        self.P, self.B_P = orthogonal_blocks(theta_P, b_in, n)
+        self.W = materialise(self.W0, self.R, self.P, b_out, b_in)
+
+    def forward(self, x):
+        return forward(x, self.W)
+
+    def backward(self, g_y, x):
+        return backward(g_y, x, self.W0, self.R, self.B_R, self.P, self.B_P,
+                        self.b_out, self.b_in)

@@ -1,0 +1,68 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail a pin.
+
+Each case rewrites one line of an oracle function (a dropped term, a wrong
+sign or index, a transposed operand), installs the rewritten function in the
+oracle module for the duration of the test, and checks that the named pins
+no longer all pass. This shows the pins constrain every part of the oracle.
+"""
+import inspect
+import textwrap
+
+import pytest
+
+import oracle.poetx_oracle as O
+from tests import oracle_pins as pins
+
+MUTATIONS = [
+    # (function, original text, planted text, pins expected to catch it)
+    ("cayley", "(I + q) @ bk", "(I - q) @ np.linalg.inv(I + q)",
+     [pins.pin_b3_rodrigues, pins.pin_golden_closed_forms]),
+    ("cayley", "(I + q) @ bk", "q @ bk", [pins.pin_b2_rotation]),
+    ("packed_upper_index", "for i in range(b):\n        for j in range(i + 1, b):",
+     "for j in range(b):\n        for i in range(j):", [pins.pin_packing_order, pins.pin_golden_closed_forms]),
+    ("skew_from_theta", "Q[:, ju, iu] = -theta", "Q[:, ju, iu] = theta",
+     [pins.pin_packing_order, pins.pin_orthogonality_det_transpose]),
+    ("cayley_vjp", "Mx = 2.0 * B[k].T @ G[k] @ B[k].T", "Mx = B[k].T @ G[k] @ B[k].T",
+     [pins.pin_finite_differences, pins.pin_theta_zero]),
+    ("cayley_vjp", "Mx = 2.0 * B[k].T @ G[k] @ B[k].T", "Mx = 2.0 * B[k] @ G[k] @ B[k]",
+     [pins.pin_finite_differences, pins.pin_vjp_forms]),
+    ("cayley_vjp", "out[k] = Mx[iu, ju] - Mx[ju, iu]", "out[k] = Mx[ju, iu] - Mx[iu, ju]",
+     [pins.pin_finite_differences, pins.pin_theta_zero]),
+    ("materialise", "W[:, s:s + r] @ P[j, :r, :r]", "W[:, s:s + r] @ P[j, :r, :r].T",
+     [pins.pin_dense_block_diag, pins.pin_input_centric_equals_materialised]),
+    ("materialise", "R[k, :r, :r] @ W[s:s + r, :]", "W[s:s + r, :]",
+     [pins.pin_dense_block_diag, pins.pin_spectrum]),
+    ("backward", "G_W[s:s + r, :] @ W0P[s:s + r, :].T", "W0P[s:s + r, :] @ G_W[s:s + r, :].T",
+     [pins.pin_finite_differences, pins.pin_input_centric_equals_materialised]),
+    ("backward", "g_x = g_y @ W", "g_x = g_y @ W0", [pins.pin_finite_differences, pins.pin_adjoint]),
+    ("backward", "RW0[:, s:s + r].T @ G_W[:, s:s + r]", "RW0[:, s:s + r].T @ G_W[:, s:s + r] * 0.5",
+     [pins.pin_finite_differences]),
+    ("skew_from_theta", "if r < b:\n            Q[-1, r:, :] = 0.0", "if False:\n            Q[-1, r:, :] = 0.0",
+     [pins.pin_dense_block_diag, pins.pin_padding_gradients]),
+]
+
+
+def _install(monkeypatch, fname, old, new):
+    src = textwrap.dedent(inspect.getsource(getattr(O, fname)))
+    assert old in src, (fname, old)
+    ns = {}
+    exec(compile(src.replace(old, new), f"<mutant {fname}>", "exec"), O.__dict__, ns)
+    monkeypatch.setattr(O, fname, ns[fname])
+
+
+@pytest.mark.parametrize("case", MUTATIONS, ids=lambda c: f"{c[0]}:{c[2][:30]}")
+def test_planted_mistake_is_caught(monkeypatch, case):
+    fname, old, new, catchers = case
+    _install(monkeypatch, fname, old, new)
+    caught = []
+    for pin in catchers:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError, np_linalg_error()):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake in {fname} passed every pin {[p.__name__ for p in catchers]}"
+
+
+def np_linalg_error():
+    import numpy as np
+    return np.linalg.LinAlgError
