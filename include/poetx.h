@@ -1,0 +1,201 @@
+/*
+ * poetx.h - C ABI of libpoetx, the POET-X linear layer y = R W0 P x on
+ * MI355X (gfx950).
+ *
+ * Method sources (every page carries the title "POET-X: Memory-efficient LLM
+ * Training by Scaling Orthogonal Transformation"; the technical text is the
+ * German summary on gist.science, "Technische Zusammenfassung"):
+ *   - weight reparameterisation W = R W0 P with trainable orthogonal R, P and
+ *     a frozen W0: section 1 (Problemstellung);
+ *   - input-centric evaluation (transform the activations, never rebuild W):
+ *     section 2 (Methodik), input-centric formulation item;
+ *   - block-diagonal R and P whose blocks are multiplied as independent
+ *     matrices in a batch: section 2, batch-parallel block-diagonal item;
+ *   - skew-symmetric generators Q = -Q^T stored as their upper triangle only:
+ *     section 2, Cayley-Neumann parameterisation item.
+ * The orthogonal map is the exact Cayley map R = (I + Q)(I - Q)^-1. The
+ * backward (to the activations and to the generators) is the chain rule of
+ * that forward; the pages do not spell it out.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The
+ *     library never allocates or frees memory and never synchronises: calls
+ *     validate their arguments on the host, enqueue kernels on `stream` (a
+ *     hipStream_t; NULL is the default stream) and return.
+ *   - Tensors are dense and row-major. Activations are token-major:
+ *     x [tokens, d_in], y and z [tokens, d_out]. W0 is [d_out, d_in].
+ *   - A block size b splits d features into nb = ceil(d / b) contiguous
+ *     blocks starting at feature 0. If b does not divide d the last block
+ *     holds r = d - (nb - 1) b features and is identity-padded: its generator
+ *     entries in rows or columns >= r are ignored (treated as zero) and their
+ *     gradients are written as zero.
+ *   - Generators theta are float32 [nb, b(b-1)/2]: the strict upper triangle
+ *     of each b x b skew block, packed row by row, so entry (i, j), i < j, is
+ *     at i(2b - i - 1)/2 + (j - i - 1). Q[i][j] = theta, Q[j][i] = -theta.
+ *   - Orthogonal blocks are [nb, b, b] row-major. R block k maps output
+ *     features [k b, k b + b); P block j maps input features [j b, j b + b).
+ *     Token-major, the layer is Y = X blockdiag(P)^T W0^T blockdiag(R)^T.
+ *   - `act` selects the storage type (poetx_dtype) of x, W0, y, z, g_y, g_x
+ *     and of the *_act copies of the blocks. theta, the float32 blocks and
+ *     g_theta are float32 in both modes. All accumulation is float32; bf16
+ *     results are rounded to nearest even.
+ *   - Alignment: every tensor pointer is 16-byte aligned; d_in, d_out and b
+ *     are multiples of 8 (bf16) or 4 (float32).
+ *   - Outputs are overwritten (not accumulated into) and must not overlap any
+ *     input. Calls that share a workspace must not run concurrently.
+ *   - Errors: argument faults are detected on the host before any launch and
+ *     returned as a status; nothing is enqueued then. A failed launch returns
+ *     POETX_ERR_HIP. Non-finite inputs are not trapped (NaN in, NaN out).
+ *     Nothing throws across this interface and the library keeps no state
+ *     between calls.
+ */
+#ifndef POETX_H
+#define POETX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define POETX_ABI_VERSION 1
+
+typedef enum poetx_status {
+  POETX_OK = 0,
+  POETX_ERR_NULL = 1,      /* a required pointer is NULL */
+  POETX_ERR_SHAPE = 2,     /* a size is out of range or inconsistent */
+  POETX_ERR_DTYPE = 3,     /* unknown poetx_dtype */
+  POETX_ERR_ALIGN = 4,     /* a pointer or size breaks the alignment rule */
+  POETX_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required */
+  POETX_ERR_HIP = 6,       /* the HIP runtime reported an error */
+  POETX_ERR_ALIAS = 7      /* an output overlaps an input */
+} poetx_status;
+
+typedef enum poetx_dtype { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
+
+/* Shape of one POET-X linear layer. */
+typedef struct poetx_linear_desc {
+  int64_t tokens; /* N >= 1: rows of x, y, z, g_y, g_x */
+  int64_t d_in;   /* n: input features (columns of W0) */
+  int64_t d_out;  /* m: output features (rows of W0) */
+  int32_t b_in;   /* block size of P, 1 <= b_in <= d_in rounded up to a block */
+  int32_t b_out;  /* block size of R */
+  int32_t act;    /* poetx_dtype of the activations, W0 and the *_act blocks */
+  int32_t n_events; /* number of entries in `events` (0 = no stage timing) */
+  /* Optional stage timing: an array of hipEvent_t created by the caller (for
+   * example with poetx_event_create). When n_events >= 2 s + 2, the call
+   * records events[2 s] on `stream` before its stage s and events[2 s + 1]
+   * after it. Forward stages: 0 P-apply, 1 dense W0 GEMM, 2 R-apply.
+   * Backward stages: 0 grad through R, 1 R gram (+ reduction), 2 dense W0
+   * GEMM, 3 P gram (+ reduction), 4 grad to x, 5 Cayley VJP of R,
+   * 6 Cayley VJP of P. May be NULL when n_events is 0. */
+  void* const* events;
+} poetx_linear_desc;
+
+/* Returns POETX_ABI_VERSION. */
+int poetx_abi_version(void);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* poetx_status_string(int status);
+
+/* ceil(d / b); 0 if d < 1 or b < 1. */
+int64_t poetx_num_blocks(int64_t d, int32_t b);
+
+/* Number of float32 generators for d features in blocks of b:
+ * ceil(d / b) * b (b - 1) / 2; 0 if d < 1 or b < 1. */
+int64_t poetx_theta_count(int64_t d, int32_t b);
+
+/* Workspace bytes poetx_build_orthogonal needs for d features, block size b
+ * (0 for invalid sizes). */
+size_t poetx_build_workspace_size(int64_t d, int32_t b);
+
+/*
+ * poetx_build_orthogonal - packed skew generators to orthogonal blocks.
+ * (Cayley-Neumann parameterisation item of section 2: skew generators stored
+ * as the upper triangle; exact Cayley map.)
+ *
+ *   theta       [nb, b(b-1)/2] float32, nb = ceil(d / b). May be NULL only if
+ *               b == 1 (no generators).
+ *   d, b        features covered and block size; 1 <= b <= 4096, d >= 1.
+ *               Several block sets with the same b (for example R and P of
+ *               a layer, or every layer of a model) may be built in one call
+ *               by storing their generators back to back and passing the
+ *               summed feature count, provided b divides each set's d.
+ *   blocks_f32  out [nb, b, b] float32: R_k = (I + Q_k)(I - Q_k)^-1, computed
+ *               as 2 (I - Q_k)^-1 - I by unpivoted blocked Gauss-Jordan
+ *               elimination (I - Q has symmetric part I, so no pivot is ever
+ *               needed).
+ *   blocks_act  out [nb, b, b] copy in `act` type (bf16: round to nearest
+ *               even). Required when act is POETX_BF16; ignored (may be NULL)
+ *               when act is POETX_F32.
+ *   ws          workspace of at least poetx_build_workspace_size(d, b) bytes.
+ */
+int poetx_build_orthogonal(const float* theta, int64_t d, int32_t b,
+                           float* blocks_f32, void* blocks_act, int32_t act,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for poetx_linear_fwd / poetx_linear_bwd (0 if the
+ * descriptor is invalid). */
+size_t poetx_fwd_workspace_size(const poetx_linear_desc* desc);
+size_t poetx_bwd_workspace_size(const poetx_linear_desc* desc);
+
+/*
+ * poetx_linear_fwd - forward of the layer, input-centric (section 2,
+ * input-centric formulation; blocks applied batch-parallel):
+ *   U = X blockdiag(P)^T, Z = U W0^T, Y = Z blockdiag(R)^T.
+ *
+ *   x      [tokens, d_in]  act
+ *   W0     [d_out, d_in]   act (frozen base weight)
+ *   R_act  [nb_out, b_out, b_out] act, from poetx_build_orthogonal
+ *   P_act  [nb_in,  b_in,  b_in ] act
+ *   y      out [tokens, d_out] act
+ *   z_save out [tokens, d_out] act: Z, kept for the backward
+ *   ws     workspace of poetx_fwd_workspace_size(desc) bytes
+ */
+int poetx_linear_fwd(const poetx_linear_desc* desc, const void* x, const void* W0,
+                     const void* R_act, const void* P_act, void* y, void* z_save,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * poetx_linear_bwd - backward of the layer to the activations and to the
+ * generators (chain rule of the forward above; W0 is frozen, so no gradient
+ * for it is formed):
+ *   g_Z = g_Y blockdiag(R)          G_R[k] = g_Y[:, k]^T Z[:, k]
+ *   g_U = g_Z W0                    G_P[j] = g_U[:, j]^T X[:, j]
+ *   g_X = g_U blockdiag(P)
+ *   Cayley VJP per block: M = 1/2 (R^T + I) G (R^T + I),
+ *   g_theta(i, j) = M[i][j] - M[j][i] for i < j.
+ * The token reductions are split over workgroups and summed in a fixed
+ * order, so results are bitwise reproducible.
+ *
+ *   g_y        [tokens, d_out] act
+ *   x          [tokens, d_in]  act
+ *   W0         [d_out, d_in]   act
+ *   R_f32      [nb_out, b_out, b_out] float32, P_f32 [nb_in, b_in, b_in] float32
+ *   R_act, P_act  the act copies of the same blocks
+ *   z_saved    [tokens, d_out] act, z_save of the matching forward
+ *   g_x        out [tokens, d_in] act
+ *   g_theta_R  out [nb_out, b_out(b_out-1)/2] float32
+ *   g_theta_P  out [nb_in,  b_in(b_in-1)/2]   float32
+ *   ws         workspace of poetx_bwd_workspace_size(desc) bytes
+ */
+int poetx_linear_bwd(const poetx_linear_desc* desc, const void* g_y, const void* x,
+                     const void* W0, const float* R_f32, const float* P_f32,
+                     const void* R_act, const void* P_act, const void* z_saved,
+                     void* g_x, float* g_theta_R, float* g_theta_P,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Thin hipEvent helpers so a caller without HIP headers can time stages.
+ * Each returns a poetx_status. */
+int poetx_event_create(void** event);
+int poetx_event_destroy(void* event);
+int poetx_event_record(void* event, void* stream);
+int poetx_event_synchronize(void* event);
+int poetx_event_elapsed_ms(void* start, void* stop, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POETX_H */

@@ -1,0 +1,442 @@
+// C ABI of libpoetx: argument validation, workspace planning and the order
+// of kernel launches for the POET-X linear layer. Declarations and the
+// contract of every entry point are in include/poetx.h.
+//
+// Validation touches no HIP API, so every argument error is reported before
+// anything is enqueued (and can be exercised without a GPU).
+#include "poetx.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "kernels.h"
+
+using poetx::DType;
+using poetx::GemmParams;
+
+namespace {
+
+constexpr int kMaxBlock = 4096;
+constexpr int64_t kMaxBatch = 65535;  // grid.y limit of the batched launches
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t act_size(int act) { return act == POETX_BF16 ? 2 : 4; }
+int act_vec(int act) { return act == POETX_BF16 ? 8 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range_of(const void* p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks shape, dtype and alignment fields of a descriptor.
+int check_desc(const poetx_linear_desc* d) {
+  if (!d) return POETX_ERR_NULL;
+  if (d->act != POETX_F32 && d->act != POETX_BF16) return POETX_ERR_DTYPE;
+  if (d->tokens < 1 || d->d_in < 1 || d->d_out < 1) return POETX_ERR_SHAPE;
+  if (d->tokens > INT32_MAX || d->d_in > INT32_MAX || d->d_out > INT32_MAX) return POETX_ERR_SHAPE;
+  if (d->b_in < 1 || d->b_out < 1 || d->b_in > kMaxBlock || d->b_out > kMaxBlock) return POETX_ERR_SHAPE;
+  if (d->b_in > d->d_in || d->b_out > d->d_out) return POETX_ERR_SHAPE;
+  if (ceil_div(d->d_in, d->b_in) > kMaxBatch || ceil_div(d->d_out, d->b_out) > kMaxBatch) return POETX_ERR_SHAPE;
+  if (d->n_events < 0 || (d->n_events > 0 && !d->events)) return POETX_ERR_NULL;
+  const int v = act_vec(d->act);
+  if (d->d_in % v || d->d_out % v || d->b_in % v || d->b_out % v) return POETX_ERR_ALIGN;
+  return POETX_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+struct FwdPlan {
+  size_t u_off, total;
+};
+FwdPlan plan_fwd(const poetx_linear_desc* d) {
+  FwdPlan p;
+  p.u_off = 0;
+  p.total = align_up((size_t)d->tokens * d->d_in * act_size(d->act));
+  return p;
+}
+
+struct SplitK {
+  int nsplit, kchunk;
+};
+// Splits the token reduction of a gram so the launch has about 1024
+// workgroups, with at least 256 tokens per split.
+SplitK choose_split(int64_t nblocks, int b, int64_t tokens, DType in) {
+  const int mt = in == DType::BF16 ? 128 : 64;
+  const int kt = poetx::gemm_k_tile(in);
+  const int64_t tiles = nblocks * ceil_div(b, mt) * ceil_div(b, mt);
+  int64_t s = std::max<int64_t>(1, ceil_div(1024, tiles));
+  s = std::min<int64_t>(s, std::max<int64_t>(1, tokens / 256));
+  int64_t chunk = ceil_div(ceil_div(tokens, s), kt) * kt;
+  SplitK r;
+  r.kchunk = (int)chunk;
+  r.nsplit = (int)ceil_div(tokens, chunk);
+  return r;
+}
+
+struct BwdPlan {
+  size_t gz, gu, partR, partP, GR, GP, TR, TP, MR, MP, total;
+  SplitK sR, sP;
+};
+BwdPlan plan_bwd(const poetx_linear_desc* d) {
+  BwdPlan p;
+  const DType in = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
+  const int64_t nbR = ceil_div(d->d_out, d->b_out), nbP = ceil_div(d->d_in, d->b_in);
+  const size_t bbR = (size_t)d->b_out * d->b_out * 4, bbP = (size_t)d->b_in * d->b_in * 4;
+  p.sR = choose_split(nbR, d->b_out, d->tokens, in);
+  p.sP = choose_split(nbP, d->b_in, d->tokens, in);
+  size_t off = 0;
+  p.gz = off; off += align_up((size_t)d->tokens * d->d_out * act_size(d->act));
+  p.gu = off; off += align_up((size_t)d->tokens * d->d_in * act_size(d->act));
+  p.partR = off; off += align_up((size_t)p.sR.nsplit * nbR * bbR);
+  p.partP = off; off += align_up((size_t)p.sP.nsplit * nbP * bbP);
+  p.GR = off; off += align_up(nbR * bbR);
+  p.GP = off; off += align_up(nbP * bbP);
+  p.TR = off; off += align_up(nbR * bbR);
+  p.TP = off; off += align_up(nbP * bbP);
+  p.MR = off; off += align_up(nbR * bbR);
+  p.MP = off; off += align_up(nbP * bbP);
+  p.total = off;
+  return p;
+}
+
+// ---------------------------------------------------------------- helpers
+struct Stages {
+  const poetx_linear_desc* d;
+  hipStream_t s;
+  hipError_t begin(int i) const { return mark(2 * i); }
+  hipError_t end(int i) const { return mark(2 * i + 1); }
+  hipError_t mark(int e) const {
+    if (e + 1 > d->n_events) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(d->events[e]), s);
+  }
+};
+
+// Block-diagonal product of token-major activations:
+//   out[:, blk] = in[:, blk] M_blk^T (transpose) or in[:, blk] M_blk
+GemmParams blockdiag_params(const void* in, const void* blocks, void* out, int64_t tokens,
+                            int64_t d, int b, bool transpose_blocks, bool* b_kmajor) {
+  GemmParams g;
+  const int64_t nb = ceil_div(d, b);
+  const int last = (int)(d - (nb - 1) * b);
+  g.A = in; g.lda = d; g.sA = b;
+  g.B = blocks; g.ldb = b; g.sB = (int64_t)b * b;
+  g.C = out; g.ldc = d; g.sC = b;
+  g.M = g.M_last = (int)tokens;
+  g.N = g.K = b;
+  g.N_last = g.K_last = last;
+  g.batch = (int)nb;
+  g.kchunk = b;
+  *b_kmajor = transpose_blocks;  // M^T: B(n, k) = M[n][k]; M: B(n, k) = M[k][n]
+  return g;
+}
+
+// Gram of token-major activations: part[s][blk] = a[:, blk]^T c[:, blk]
+GemmParams gram_params(const void* a, const void* c, float* part, int64_t tokens, int64_t d, int b,
+                       SplitK sk) {
+  GemmParams g;
+  const int64_t nb = ceil_div(d, b);
+  const int last = (int)(d - (nb - 1) * b);
+  g.A = a; g.lda = d; g.sA = b;
+  g.B = c; g.ldb = d; g.sB = b;
+  g.C = part; g.ldc = b; g.sC = (int64_t)b * b;
+  g.M = g.N = b;
+  g.M_last = g.N_last = last;
+  g.K = g.K_last = (int)tokens;
+  g.batch = (int)nb;
+  g.ksplit = sk.nsplit;
+  g.kchunk = sk.kchunk;
+  g.sC_split = nb * (int64_t)b * b;
+  return g;
+}
+
+// Cayley VJP of every block: M = 1/2 (R^T + I) G (R^T + I), packed as
+// g_theta(i, j) = M[i][j] - M[j][i].
+hipError_t cayley_vjp(const float* G, const float* R, float* T, float* M, float* g_theta,
+                      int64_t d, int b, hipStream_t s) {
+  const int64_t nb = ceil_div(d, b);
+  const int last = (int)(d - (nb - 1) * b);
+  GemmParams g;
+  // T = G R^T + G
+  g.A = G; g.lda = b; g.sA = (int64_t)b * b;
+  g.B = R; g.ldb = b; g.sB = (int64_t)b * b;
+  g.C = T; g.ldc = b; g.sC = (int64_t)b * b;
+  g.D = G; g.ldd = b; g.sD = (int64_t)b * b;
+  g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = b;
+  g.batch = (int)nb;
+  g.kchunk = b;
+  g.alpha = 1.0f; g.beta = 1.0f;
+  hipError_t e = poetx::launch_gemm(DType::F32, DType::F32, true, true, g, s);
+  if (e != hipSuccess) return e;
+  // M = 1/2 (R^T T + T): A(m, k) = R[k][m], B(n, k) = T[k][n]
+  g.A = R; g.B = T; g.C = M; g.D = T;
+  g.alpha = 0.5f; g.beta = 0.5f;
+  e = poetx::launch_gemm(DType::F32, DType::F32, false, false, g, s);
+  if (e != hipSuccess) return e;
+  return poetx::launch_pack_skew_grad(M, nb, b, last, g_theta, s);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? POETX_OK : POETX_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int poetx_abi_version(void) { return POETX_ABI_VERSION; }
+
+const char* poetx_status_string(int s) {
+  switch (s) {
+    case POETX_OK: return "ok";
+    case POETX_ERR_NULL: return "null pointer argument";
+    case POETX_ERR_SHAPE: return "invalid or inconsistent shape";
+    case POETX_ERR_DTYPE: return "unknown dtype";
+    case POETX_ERR_ALIGN: return "pointer or size breaks the alignment rule";
+    case POETX_ERR_WORKSPACE: return "workspace missing or too small";
+    case POETX_ERR_HIP: return "HIP runtime error";
+    case POETX_ERR_ALIAS: return "output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+int64_t poetx_num_blocks(int64_t d, int32_t b) { return (d < 1 || b < 1) ? 0 : ceil_div(d, b); }
+
+int64_t poetx_theta_count(int64_t d, int32_t b) {
+  return (d < 1 || b < 1) ? 0 : ceil_div(d, b) * ((int64_t)b * (b - 1) / 2);
+}
+
+size_t poetx_build_workspace_size(int64_t d, int32_t b) {
+  if (d < 1 || b < 1 || b > kMaxBlock || b > d) return 0;
+  return align_up(poetx::cayley_workspace_floats(ceil_div(d, b), b) * sizeof(float));
+}
+
+int poetx_build_orthogonal(const float* theta, int64_t d, int32_t b, float* blocks_f32,
+                           void* blocks_act, int32_t act, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (act != POETX_F32 && act != POETX_BF16) return POETX_ERR_DTYPE;
+  if (d < 1 || b < 1 || b > kMaxBlock || b > d) return POETX_ERR_SHAPE;
+  const int64_t nb = ceil_div(d, b);
+  if (nb > kMaxBatch) return POETX_ERR_SHAPE;
+  if (!blocks_f32 || (b > 1 && !theta) || (act == POETX_BF16 && !blocks_act)) return POETX_ERR_NULL;
+  if (!aligned16(blocks_f32) || (act == POETX_BF16 && !aligned16(blocks_act))) return POETX_ERR_ALIGN;
+  const size_t need = poetx_build_workspace_size(d, b);
+  if (!ws || ws_bytes < need) return POETX_ERR_WORKSPACE;
+  const size_t blocks_bytes = (size_t)nb * b * b * 4;
+  const Range out_f32 = range_of(blocks_f32, blocks_bytes);
+  const Range out_act = range_of(blocks_act, act == POETX_BF16 ? blocks_bytes / 2 : 0);
+  const Range in_theta = range_of(theta, (size_t)poetx_theta_count(d, b) * 4);
+  const Range r_ws = range_of(ws, need);
+  if (overlap(out_f32, in_theta) || overlap(out_f32, r_ws) || overlap(out_act, in_theta) ||
+      overlap(out_act, r_ws) || overlap(out_f32, out_act))
+    return POETX_ERR_ALIAS;
+  const int last = (int)(d - (nb - 1) * b);
+  return hip_status(poetx::launch_cayley_build(theta, nb, b, last, blocks_f32, blocks_act,
+                                               act == POETX_BF16 ? DType::BF16 : DType::F32,
+                                               static_cast<float*>(ws),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+size_t poetx_fwd_workspace_size(const poetx_linear_desc* d) {
+  if (check_desc(d) != POETX_OK) return 0;
+  return plan_fwd(d).total;
+}
+
+size_t poetx_bwd_workspace_size(const poetx_linear_desc* d) {
+  if (check_desc(d) != POETX_OK) return 0;
+  return plan_bwd(d).total;
+}
+
+int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, const void* R_act,
+                     const void* P_act, void* y, void* z_save, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int st = check_desc(d);
+  if (st != POETX_OK) return st;
+  if (!x || !W0 || !R_act || !P_act || !y || !z_save) return POETX_ERR_NULL;
+  const void* ptrs[] = {x, W0, R_act, P_act, y, z_save, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return POETX_ERR_ALIGN;
+  const FwdPlan plan = plan_fwd(d);
+  if (!ws || ws_bytes < plan.total) return POETX_ERR_WORKSPACE;
+
+  const size_t es = act_size(d->act);
+  const int64_t N = d->tokens, n = d->d_in, m = d->d_out;
+  const int64_t nbR = ceil_div(m, d->b_out), nbP = ceil_div(n, d->b_in);
+  const Range r_y = range_of(y, N * m * es), r_z = range_of(z_save, N * m * es);
+  const Range ins[] = {range_of(x, N * n * es), range_of(W0, m * n * es),
+                       range_of(R_act, nbR * d->b_out * d->b_out * es),
+                       range_of(P_act, nbP * d->b_in * d->b_in * es), range_of(ws, plan.total)};
+  for (const Range& r : ins)
+    if (overlap(r, r_y) || overlap(r, r_z)) return POETX_ERR_ALIAS;
+  if (overlap(r_y, r_z)) return POETX_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DType t = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
+  void* U = static_cast<char*>(ws) + plan.u_off;
+  Stages sg{d, s};
+  bool bk;
+  hipError_t e;
+
+  // S2: U = X blockdiag(P)^T
+  if ((e = sg.begin(0)) != hipSuccess) return hip_status(e);
+  GemmParams g = blockdiag_params(x, P_act, U, N, n, d->b_in, true, &bk);
+  if ((e = poetx::launch_gemm(t, t, true, bk, g, s)) != hipSuccess) return hip_status(e);
+  if ((e = sg.end(0)) != hipSuccess) return hip_status(e);
+
+  // S3: Z = U W0^T
+  if ((e = sg.begin(1)) != hipSuccess) return hip_status(e);
+  GemmParams dg;
+  dg.A = U; dg.lda = n;
+  dg.B = W0; dg.ldb = n;
+  dg.C = z_save; dg.ldc = m;
+  dg.M = dg.M_last = (int)N; dg.N = dg.N_last = (int)m; dg.K = dg.K_last = (int)n;
+  dg.kchunk = (int)n;
+  if ((e = poetx::launch_gemm(t, t, true, true, dg, s)) != hipSuccess) return hip_status(e);
+  if ((e = sg.end(1)) != hipSuccess) return hip_status(e);
+
+  // S4: Y = Z blockdiag(R)^T
+  if ((e = sg.begin(2)) != hipSuccess) return hip_status(e);
+  g = blockdiag_params(z_save, R_act, y, N, m, d->b_out, true, &bk);
+  if ((e = poetx::launch_gemm(t, t, true, bk, g, s)) != hipSuccess) return hip_status(e);
+  if ((e = sg.end(2)) != hipSuccess) return hip_status(e);
+  return POETX_OK;
+}
+
+int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x, const void* W0,
+                     const float* R_f32, const float* P_f32, const void* R_act, const void* P_act,
+                     const void* z_saved, void* g_x, float* g_theta_R, float* g_theta_P, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int st = check_desc(d);
+  if (st != POETX_OK) return st;
+  if (!g_y || !x || !W0 || !R_f32 || !P_f32 || !R_act || !P_act || !z_saved || !g_x)
+    return POETX_ERR_NULL;
+  if ((d->b_out > 1 && !g_theta_R) || (d->b_in > 1 && !g_theta_P)) return POETX_ERR_NULL;
+  const void* ptrs[] = {g_y, x, W0, R_f32, P_f32, R_act, P_act, z_saved, g_x, g_theta_R, g_theta_P, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return POETX_ERR_ALIGN;
+  const BwdPlan plan = plan_bwd(d);
+  if (!ws || ws_bytes < plan.total) return POETX_ERR_WORKSPACE;
+
+  const size_t es = act_size(d->act);
+  const int64_t N = d->tokens, n = d->d_in, m = d->d_out;
+  const int bR = d->b_out, bP = d->b_in;
+  const int64_t nbR = ceil_div(m, bR), nbP = ceil_div(n, bP);
+  const Range outs[] = {range_of(g_x, N * n * es),
+                        range_of(g_theta_R, (size_t)poetx_theta_count(m, bR) * 4),
+                        range_of(g_theta_P, (size_t)poetx_theta_count(n, bP) * 4)};
+  const Range ins[] = {range_of(g_y, N * m * es), range_of(x, N * n * es),
+                       range_of(W0, m * n * es), range_of(R_f32, nbR * bR * bR * 4),
+                       range_of(P_f32, nbP * bP * bP * 4), range_of(R_act, nbR * bR * bR * es),
+                       range_of(P_act, nbP * bP * bP * es), range_of(z_saved, N * m * es),
+                       range_of(ws, plan.total)};
+  for (const Range& o : outs) {
+    for (const Range& r : ins)
+      if (overlap(o, r)) return POETX_ERR_ALIAS;
+  }
+  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
+    return POETX_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DType t = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
+  char* w = static_cast<char*>(ws);
+  void* gZ = w + plan.gz;
+  void* gU = w + plan.gu;
+  float* partR = reinterpret_cast<float*>(w + plan.partR);
+  float* partP = reinterpret_cast<float*>(w + plan.partP);
+  float* GR = reinterpret_cast<float*>(w + plan.GR);
+  float* GP = reinterpret_cast<float*>(w + plan.GP);
+  float* TR = reinterpret_cast<float*>(w + plan.TR);
+  float* TP = reinterpret_cast<float*>(w + plan.TP);
+  float* MR = reinterpret_cast<float*>(w + plan.MR);
+  float* MP = reinterpret_cast<float*>(w + plan.MP);
+  const int lastR = (int)(m - (nbR - 1) * bR), lastP = (int)(n - (nbP - 1) * bP);
+  Stages sg{d, s};
+  bool bk;
+  hipError_t e;
+#define POETX_TRY(call)                            \
+  do {                                             \
+    if ((e = (call)) != hipSuccess) return hip_status(e); \
+  } while (0)
+
+  // B1: g_Z = g_Y blockdiag(R)
+  POETX_TRY(sg.begin(0));
+  GemmParams g = blockdiag_params(g_y, R_act, gZ, N, m, bR, false, &bk);
+  POETX_TRY(poetx::launch_gemm(t, t, true, bk, g, s));
+  POETX_TRY(sg.end(0));
+
+  // B2: G_R[k] = g_Y[:, k]^T Z[:, k], split over tokens, then reduced
+  POETX_TRY(sg.begin(1));
+  g = gram_params(g_y, z_saved, partR, N, m, bR, plan.sR);
+  POETX_TRY(poetx::launch_gemm(t, DType::F32, false, false, g, s));
+  POETX_TRY(poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, s));
+  POETX_TRY(sg.end(1));
+
+  // B3: g_U = g_Z W0   (B(n, k) = W0[k][n])
+  POETX_TRY(sg.begin(2));
+  GemmParams dg;
+  dg.A = gZ; dg.lda = m;
+  dg.B = W0; dg.ldb = n;
+  dg.C = gU; dg.ldc = n;
+  dg.M = dg.M_last = (int)N; dg.N = dg.N_last = (int)n; dg.K = dg.K_last = (int)m;
+  dg.kchunk = (int)m;
+  POETX_TRY(poetx::launch_gemm(t, t, true, false, dg, s));
+  POETX_TRY(sg.end(2));
+
+  // B4: G_P[j] = g_U[:, j]^T X[:, j]
+  POETX_TRY(sg.begin(3));
+  g = gram_params(gU, x, partP, N, n, bP, plan.sP);
+  POETX_TRY(poetx::launch_gemm(t, DType::F32, false, false, g, s));
+  POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, s));
+  POETX_TRY(sg.end(3));
+
+  // B5: g_X = g_U blockdiag(P)
+  POETX_TRY(sg.begin(4));
+  g = blockdiag_params(gU, P_act, g_x, N, n, bP, false, &bk);
+  POETX_TRY(poetx::launch_gemm(t, t, true, bk, g, s));
+  POETX_TRY(sg.end(4));
+
+  // B6: Cayley VJP of R and of P
+  POETX_TRY(sg.begin(5));
+  if (bR > 1) POETX_TRY(cayley_vjp(GR, R_f32, TR, MR, g_theta_R, m, bR, s));
+  POETX_TRY(sg.end(5));
+  POETX_TRY(sg.begin(6));
+  if (bP > 1) POETX_TRY(cayley_vjp(GP, P_f32, TP, MP, g_theta_P, n, bP, s));
+  POETX_TRY(sg.end(6));
+#undef POETX_TRY
+  return POETX_OK;
+}
+
+int poetx_event_create(void** ev) {
+  if (!ev) return POETX_ERR_NULL;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return POETX_ERR_HIP;
+  *ev = e;
+  return POETX_OK;
+}
+
+int poetx_event_destroy(void* ev) {
+  if (!ev) return POETX_ERR_NULL;
+  return hip_status(hipEventDestroy(static_cast<hipEvent_t>(ev)));
+}
+
+int poetx_event_record(void* ev, void* stream) {
+  if (!ev) return POETX_ERR_NULL;
+  return hip_status(hipEventRecord(static_cast<hipEvent_t>(ev), static_cast<hipStream_t>(stream)));
+}
+
+int poetx_event_synchronize(void* ev) {
+  if (!ev) return POETX_ERR_NULL;
+  return hip_status(hipEventSynchronize(static_cast<hipEvent_t>(ev)));
+}
+
+int poetx_event_elapsed_ms(void* a, void* b, float* ms) {
+  if (!a || !b || !ms) return POETX_ERR_NULL;
+  return hip_status(hipEventElapsedTime(ms, static_cast<hipEvent_t>(a), static_cast<hipEvent_t>(b)));
+}
+
+}  // extern "C"

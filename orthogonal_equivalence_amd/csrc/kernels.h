@@ -1,0 +1,64 @@
+// Internal launcher interface between the C ABI layer (api.cpp) and the HIP
+// kernels. Host code only; no torch types anywhere.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace poetx {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+// Batched, split-K GEMM on MFMA:
+//   C[s][bt](m, n) = alpha * sum_{k in split s} A[bt](m, k) * B[bt](n, k)
+//                    + beta * D[bt](m, n)          (D optional)
+// with A(m, k) = A[m*lda + k] when a_kmajor, else A[k*lda + m];
+//      B(n, k) = B[n*ldb + k] when b_kmajor, else B[k*ldb + n];
+//      C(m, n) = C[m*ldc + n], D(m, n) = D[m*ldd + n].
+// Every batch uses extents (M, N, K) except the last, which uses
+// (M_last, N_last, K_last) (a ragged, identity-padded last block).
+struct GemmParams {
+  const void* A = nullptr;
+  const void* B = nullptr;
+  void* C = nullptr;
+  const void* D = nullptr;
+  int64_t lda = 0, ldb = 0, ldc = 0, ldd = 0;
+  int64_t sA = 0, sB = 0, sC = 0, sD = 0;  // batch strides (elements)
+  int M = 0, N = 0, K = 0;
+  int M_last = 0, N_last = 0, K_last = 0;
+  int batch = 1;
+  int ksplit = 1;       // grid.z
+  int kchunk = 0;       // K elements per split (multiple of the K tile)
+  int64_t sC_split = 0; // output stride between splits (elements)
+  float alpha = 1.0f, beta = 0.0f;
+};
+
+// Returns hipSuccess or the launch error.
+hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor,
+                       const GemmParams& p, hipStream_t stream);
+
+// K tile of the GEMM configuration used for `in` (split-K chunks are
+// multiples of it).
+int gemm_k_tile(DType in);
+
+// ---- Cayley build (exact Cayley map by blocked Gauss-Jordan) ----
+// Panel width used for block size b.
+int cayley_panel_width(int b);
+// Workspace floats needed by the build for nblocks blocks of size b.
+size_t cayley_workspace_floats(int64_t nblocks, int b);
+hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int last_valid,
+                               float* blocks_f32, void* blocks_act, DType act,
+                               float* ws, hipStream_t stream);
+
+// ---- backward helpers ----
+// G[blk] = sum_s part[s][blk] in split order; entries of the last block at
+// rows or columns >= last_valid are written as zero.
+hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, int b,
+                               int last_valid, float* G, hipStream_t stream);
+// g_theta[blk][idx(i,j)] = M[blk][i][j] - M[blk][j][i] (i < j); zero for
+// entries of the last block at rows or columns >= last_valid.
+hipError_t launch_pack_skew_grad(const float* M, int64_t nblocks, int b, int last_valid,
+                                 float* g_theta, hipStream_t stream);
+
+}  // namespace poetx

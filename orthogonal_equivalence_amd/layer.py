@@ -1,0 +1,113 @@
+"""A POET-X linear layer on top of the libpoetx binding.
+
+Holds the device buffers of one layer (theta, orthogonal blocks, workspaces)
+allocated with torch and drives the three library calls. It allocates and
+calls; every step of the computation runs in libpoetx's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import poetx as P
+
+_DT = {"f32": (torch.float32, P.POETX_F32), "bf16": (torch.bfloat16, P.POETX_BF16)}
+
+
+class PoetxLinear:
+    """y = R W0 P x for token-major x [tokens, d_in]; W0 [d_out, d_in] frozen.
+
+    theta_R [nb_out, b_out(b_out-1)/2] and theta_P [nb_in, b_in(b_in-1)/2]
+    are float32 views into one buffer, so that both block sets are built by a
+    single poetx_build_orthogonal call when b_in == b_out and b divides both
+    d_in and d_out.
+    """
+
+    def __init__(self, W0: torch.Tensor, b_in: int, b_out: int, act: str, device="cuda"):
+        self.torch_dtype, self.act = _DT[act]
+        self.device = torch.device(device)
+        self.W0 = W0.to(self.device, self.torch_dtype).contiguous()
+        self.d_out, self.d_in = self.W0.shape
+        self.b_in, self.b_out = b_in, b_out
+        self.nb_in = P.poetx_num_blocks(self.d_in, b_in)
+        self.nb_out = P.poetx_num_blocks(self.d_out, b_out)
+        tri_in, tri_out = b_in * (b_in - 1) // 2, b_out * (b_out - 1) // 2
+        n_tR, n_tP = self.nb_out * tri_out, self.nb_in * tri_in
+        f32 = dict(device=self.device, dtype=torch.float32)
+        self._theta = torch.zeros(max(n_tR + n_tP, 1), **f32)
+        self.theta_R = self._theta[:n_tR].view(self.nb_out, tri_out)
+        self.theta_P = self._theta[n_tR:n_tR + n_tP].view(self.nb_in, tri_in)
+        self.combined = (b_in == b_out and self.d_in % b_in == 0 and self.d_out % b_out == 0)
+        nR, nP = self.nb_out * b_out * b_out, self.nb_in * b_in * b_in
+        self._blocks_f32 = torch.empty(nR + nP, **f32)
+        self._blocks_act = torch.empty(nR + nP, device=self.device, dtype=self.torch_dtype)
+        self.R_f32 = self._blocks_f32[:nR].view(self.nb_out, b_out, b_out)
+        self.P_f32 = self._blocks_f32[nR:].view(self.nb_in, b_in, b_in)
+        self.R_act = self._blocks_act[:nR].view(self.nb_out, b_out, b_out)
+        self.P_act = self._blocks_act[nR:].view(self.nb_in, b_in, b_in)
+        if self.combined:
+            ws = P.poetx_build_workspace_size(self.d_out + self.d_in, b_out)
+        else:
+            ws = max(P.poetx_build_workspace_size(self.d_out, b_out),
+                     P.poetx_build_workspace_size(self.d_in, b_in))
+        self._build_ws = torch.empty(max(ws, 1), device=self.device, dtype=torch.uint8)
+        self._fwd_ws = {}
+        self._bwd_ws = {}
+
+    # -- parameters ---------------------------------------------------------
+    def set_theta(self, theta_R, theta_P):
+        self.theta_R.copy_(torch.as_tensor(theta_R, dtype=torch.float32))
+        self.theta_P.copy_(torch.as_tensor(theta_P, dtype=torch.float32))
+
+    def desc(self, tokens: int, events=None):
+        return P.make_desc(tokens, self.d_in, self.d_out, self.b_in, self.b_out, self.act, events)
+
+    def _ws(self, cache, size_fn, tokens):
+        if tokens not in cache:
+            n = size_fn(self.desc(tokens))
+            cache[tokens] = torch.empty(max(n, 1), device=self.device, dtype=torch.uint8)
+        return cache[tokens]
+
+    # -- the three calls ----------------------------------------------------
+    def build(self, stream=None):
+        """Cayley build of R and P blocks (one call when the sets combine)."""
+        act_R = self.R_act if self.act == P.POETX_BF16 else None
+        act_P = self.P_act if self.act == P.POETX_BF16 else None
+        if self.combined:
+            P.poetx_build_orthogonal(self._theta, self.d_out + self.d_in, self.b_out,
+                                     self._blocks_f32,
+                                     self._blocks_act if self.act == P.POETX_BF16 else None,
+                                     self.act, self._build_ws, stream)
+        else:
+            P.poetx_build_orthogonal(self.theta_R, self.d_out, self.b_out, self.R_f32, act_R,
+                                     self.act, self._build_ws, stream)
+            P.poetx_build_orthogonal(self.theta_P, self.d_in, self.b_in, self.P_f32, act_P,
+                                     self.act, self._build_ws, stream)
+
+    def blocks_for_act(self):
+        if self.act == P.POETX_BF16:
+            return self.R_act, self.P_act
+        return self.R_f32, self.P_f32
+
+    def forward(self, x, y=None, z=None, stream=None, events=None):
+        N = x.shape[0]
+        y = torch.empty(N, self.d_out, device=self.device, dtype=self.torch_dtype) if y is None else y
+        z = torch.empty(N, self.d_out, device=self.device, dtype=self.torch_dtype) if z is None else z
+        R, Pb = self.blocks_for_act()
+        ws = self._ws(self._fwd_ws, P.poetx_fwd_workspace_size, N)
+        P.poetx_linear_fwd(self.desc(N, events), x, self.W0, R, Pb, y, z, ws, stream)
+        return y, z
+
+    def backward(self, g_y, x, z, g_x=None, g_theta_R=None, g_theta_P=None, stream=None,
+                 events=None):
+        N = x.shape[0]
+        g_x = torch.empty(N, self.d_in, device=self.device, dtype=self.torch_dtype) if g_x is None else g_x
+        if g_theta_R is None:
+            g_theta_R = torch.empty_like(self.theta_R)
+        if g_theta_P is None:
+            g_theta_P = torch.empty_like(self.theta_P)
+        R, Pb = self.blocks_for_act()
+        ws = self._ws(self._bwd_ws, P.poetx_bwd_workspace_size, N)
+        P.poetx_linear_bwd(self.desc(N, events), g_y, x, self.W0, self.R_f32, self.P_f32, R, Pb, z,
+                           g_x, g_theta_R if g_theta_R.numel() else None,
+                           g_theta_P if g_theta_P.numel() else None, ws, stream)
+        return g_x, g_theta_R, g_theta_P

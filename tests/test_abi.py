@@ -1,0 +1,183 @@
+"""The C ABI without a GPU: symbols, sizes and every host-detectable error.
+
+Argument validation runs before any HIP call, so these run on the CPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "poetx.h")
+
+P = pytest.importorskip("orthogonal_equivalence_amd.poetx",
+                        reason="libpoetx.so not built (run the build first)")
+
+ALIGNED = 1 << 20  # a fake 16-byte aligned address; validation never dereferences it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(poetx_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(P.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(P.EXPORTS)
+
+
+def test_version_and_strings():
+    assert P.poetx_abi_version() == 1
+    for s in range(8):
+        assert P.status_string(s) and P.status_string(s) != "unknown status"
+    assert P.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("d,b", [(256, 32), (14336, 256), (4096, 512), (10, 4), (7, 7), (4096, 1)])
+def test_theta_count(d, b):
+    nb = -(-d // b)
+    assert P.poetx_num_blocks(d, b) == nb
+    assert P.poetx_theta_count(d, b) == nb * b * (b - 1) // 2
+
+
+def test_sizes_of_invalid_inputs_are_zero():
+    assert P.poetx_theta_count(0, 4) == 0 and P.poetx_theta_count(4, 0) == 0
+    assert P.poetx_build_workspace_size(4, 8) == 0  # b > d
+    assert P.poetx_build_workspace_size(8192, 8192) == 0  # b > max block
+    assert P.poetx_fwd_workspace_size(P.make_desc(0, 64, 64, 8, 8, P.POETX_BF16)) == 0
+    assert P.poetx_bwd_workspace_size(P.make_desc(16, 64, 64, 8, 8, 5)) == 0
+
+
+def test_workspace_sizes_positive():
+    d = P.make_desc(8192, 4096, 14336, 256, 256, P.POETX_BF16)
+    assert P.poetx_fwd_workspace_size(d) >= 8192 * 4096 * 2
+    assert P.poetx_bwd_workspace_size(d) >= 8192 * (4096 + 14336) * 2
+    assert P.poetx_build_workspace_size(14336 + 4096, 256) > 0
+
+
+def _fwd(desc, **over):
+    args = dict(x=ALIGNED, W0=ALIGNED * 2, R=ALIGNED * 3, P=ALIGNED * 4, y=ALIGNED * 64,
+                z=ALIGNED * 128, ws=ALIGNED * 256, ws_bytes=1 << 40)
+    args.update(over)
+    d = desc
+    return P._lib.poetx_linear_fwd(ctypes.byref(d), args["x"], args["W0"], args["R"], args["P"],
+                                   args["y"], args["z"], args["ws"], args["ws_bytes"], None)
+
+
+def _bwd(desc, **over):
+    a = dict(g_y=ALIGNED, x=ALIGNED * 2, W0=ALIGNED * 3, Rf=ALIGNED * 4, Pf=ALIGNED * 5,
+             Ra=ALIGNED * 6, Pa=ALIGNED * 7, z=ALIGNED * 8, g_x=ALIGNED * 64, gR=ALIGNED * 128,
+             gP=ALIGNED * 192, ws=ALIGNED * 256, ws_bytes=1 << 40)
+    a.update(over)
+    return P._lib.poetx_linear_bwd(ctypes.byref(desc), a["g_y"], a["x"], a["W0"], a["Rf"], a["Pf"],
+                                   a["Ra"], a["Pa"], a["z"], a["g_x"], a["gR"], a["gP"], a["ws"],
+                                   a["ws_bytes"], None)
+
+
+SMALL = dict(tokens=16, d_in=64, d_out=64, b_in=8, b_out=8, act=P.POETX_BF16)
+
+
+def desc(**over):
+    k = dict(SMALL)
+    k.update(over)
+    return P.make_desc(k["tokens"], k["d_in"], k["d_out"], k["b_in"], k["b_out"], k["act"])
+
+
+@pytest.mark.parametrize("call", [_fwd, _bwd])
+def test_null_pointers(call):
+    keys = ["x", "W0", "R", "P", "y", "z"] if call is _fwd else \
+        ["g_y", "x", "W0", "Rf", "Pf", "Ra", "Pa", "z", "g_x", "gR", "gP"]
+    for k in keys:
+        assert call(desc(), **{k: None}) == P.POETX_ERR_NULL, k
+    assert P._lib.poetx_linear_fwd(None, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED,
+                                   ALIGNED, 1, None) == P.POETX_ERR_NULL
+
+
+@pytest.mark.parametrize("call", [_fwd, _bwd])
+@pytest.mark.parametrize("bad", [
+    dict(tokens=0), dict(d_in=0), dict(d_out=-8), dict(b_in=0), dict(b_out=0),
+    dict(b_in=128), dict(b_out=8192, d_out=16384), dict(tokens=1 << 32),
+])
+def test_bad_shapes(call, bad):
+    assert call(desc(**bad)) == P.POETX_ERR_SHAPE
+
+
+@pytest.mark.parametrize("call", [_fwd, _bwd])
+def test_bad_dtype(call):
+    assert call(desc(act=2)) == P.POETX_ERR_DTYPE
+    assert call(desc(act=-1)) == P.POETX_ERR_DTYPE
+
+
+@pytest.mark.parametrize("call", [_fwd, _bwd])
+@pytest.mark.parametrize("bad", [dict(d_in=60), dict(d_out=36), dict(b_in=12, d_in=48),
+                                 dict(b_out=4)])
+def test_alignment_of_sizes(call, bad):
+    assert call(desc(**bad)) == P.POETX_ERR_ALIGN
+
+
+def test_fp32_allows_multiples_of_four():
+    d = desc(act=P.POETX_F32, d_in=60, b_in=12, b_out=4)
+    assert P.poetx_fwd_workspace_size(d) > 0
+
+
+@pytest.mark.parametrize("call", [_fwd, _bwd])
+def test_misaligned_pointers(call):
+    key = "x"
+    assert call(desc(), **{key: ALIGNED + 2}) == P.POETX_ERR_ALIGN
+
+
+@pytest.mark.parametrize("call", [_fwd, _bwd])
+def test_workspace_too_small(call):
+    d = desc()
+    need = (P.poetx_fwd_workspace_size if call is _fwd else P.poetx_bwd_workspace_size)(d)
+    assert call(d, ws_bytes=need - 1) == P.POETX_ERR_WORKSPACE
+    assert call(d, ws=None) == P.POETX_ERR_WORKSPACE
+
+
+def test_aliasing_is_rejected():
+    d = desc()
+    assert _fwd(d, y=ALIGNED) == P.POETX_ERR_ALIAS           # y on top of x
+    assert _fwd(d, z=ALIGNED * 64) == P.POETX_ERR_ALIAS      # z on top of y
+    assert _bwd(d, g_x=ALIGNED * 8) == P.POETX_ERR_ALIAS     # g_x on top of z
+    assert _bwd(d, gR=ALIGNED * 256) == P.POETX_ERR_ALIAS    # g_theta_R inside the workspace
+
+
+def test_events_without_array_rejected():
+    d = desc()
+    d.n_events = 4
+    assert _fwd(d) == P.POETX_ERR_NULL
+
+
+def _build(theta, d, b, f32, act_ptr, act, ws, ws_bytes):
+    return P._lib.poetx_build_orthogonal(theta, d, b, f32, act_ptr, act, ws, ws_bytes, None)
+
+
+def test_build_errors():
+    ok = dict(theta=ALIGNED, d=64, b=8, f32=ALIGNED * 2, act_ptr=ALIGNED * 3, act=P.POETX_BF16,
+              ws=ALIGNED * 4, ws_bytes=1 << 30)
+
+    def call(**over):
+        a = dict(ok)
+        a.update(over)
+        return _build(a["theta"], a["d"], a["b"], a["f32"], a["act_ptr"], a["act"], a["ws"],
+                      a["ws_bytes"])
+
+    assert call(theta=None) == P.POETX_ERR_NULL
+    assert call(f32=None) == P.POETX_ERR_NULL
+    assert call(act_ptr=None) == P.POETX_ERR_NULL
+    assert call(act=7) == P.POETX_ERR_DTYPE
+    assert call(d=0) == P.POETX_ERR_SHAPE
+    assert call(b=0) == P.POETX_ERR_SHAPE
+    assert call(b=128) == P.POETX_ERR_SHAPE               # b > d
+    assert call(d=1 << 20, b=8192) == P.POETX_ERR_SHAPE   # b above the maximum
+    assert call(f32=ALIGNED * 2 + 4) == P.POETX_ERR_ALIGN
+    assert call(ws_bytes=16) == P.POETX_ERR_WORKSPACE
+    assert call(ws=None) == P.POETX_ERR_WORKSPACE
+    assert call(f32=ALIGNED) == P.POETX_ERR_ALIAS          # output on top of theta
+    assert call(act_ptr=ALIGNED * 4) == P.POETX_ERR_ALIAS  # act copy inside the workspace

@@ -1,0 +1,221 @@
+"""GPU parity: libpoetx (through the C ABI) against the float64 oracle on the
+same seeded inputs.
+
+Small cases compare every output element; the full-size workloads compare
+sampled outputs the oracle computes directly (token rows of y and g_x, whole
+generator blocks of g_theta) plus properties that hold at any size.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU too; every test here is gpu-marked
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle.poetx_oracle as O  # noqa: E402
+from orthogonal_equivalence_amd import poetx as P  # noqa: E402
+from orthogonal_equivalence_amd.inputs import CONFIGS, LayerSpec, make_layer, resized  # noqa: E402
+from tests import gpu_util as U  # noqa: E402
+from tests.oracle_pins import load_closed_forms  # noqa: E402
+
+
+def test_single_hip_runtime_loaded():
+    """libpoetx must share torch's HIP runtime (exactly one libamdhip64)."""
+    torch.zeros(1, device="cuda")
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
+    assert any("libpoetx.so" in line for line in maps.splitlines())
+
+
+# ------------------------------------------------------------- Cayley build
+def _build(theta: np.ndarray, d: int, b: int, act=P.POETX_BF16):
+    nb = -(-d // b)
+    th = torch.from_numpy(np.ascontiguousarray(theta, dtype=np.float32)).cuda()
+    f32 = torch.empty(nb, b, b, device="cuda")
+    a = torch.empty(nb, b, b, device="cuda", dtype=torch.bfloat16) if act == P.POETX_BF16 else None
+    ws = torch.empty(max(P.poetx_build_workspace_size(d, b), 1), device="cuda", dtype=torch.uint8)
+    P.poetx_build_orthogonal(th, d, b, f32, a, act, ws)
+    torch.cuda.synchronize()
+    return f32, a
+
+
+def test_build_golden_closed_forms():
+    for name, b, theta, Rref in load_closed_forms():
+        U.log(f"[build golden] {name} b={b}")
+        f32, _ = _build(theta[None, :], b, b, P.POETX_F32)
+        err = np.max(np.abs(U.host(f32)[0] - Rref))
+        assert err <= 2e-7, (name, err)
+
+
+@pytest.mark.parametrize("b,nb,sigma", [
+    (2, 3, 0.5), (3, 2, 0.5), (8, 5, 0.3), (32, 8, 0.02), (48, 3, 0.1), (64, 4, 0.05),
+    (96, 2, 0.05), (128, 3, 0.02), (256, 4, 0.01), (512, 2, 0.01), (1024, 1, 0.01),
+    (256, 2, 0.2),
+])
+def test_build_matches_oracle(b, nb, sigma):
+    U.log(f"[build] b={b} nb={nb} sigma={sigma}")
+    rng = np.random.default_rng(b * 7 + nb)
+    theta = (rng.standard_normal((nb, b * (b - 1) // 2)) * sigma).astype(np.float32).astype(np.float64)
+    R_ref, _ = O.orthogonal_blocks(theta, b, nb * b)
+    f32, act = _build(theta, nb * b, b)
+    R = U.host(f32)
+    err = np.max(np.abs(R - R_ref))
+    U.log(f"    max abs err {err:.2e}")
+    assert err <= 2e-5 * max(1.0, math.sqrt(b) / 8)
+    I = np.eye(b)
+    # float32 elimination: orthogonality defect grows like u b^1.5 (u = 2^-24)
+    orth = max(np.linalg.norm(R[k].T @ R[k] - I) for k in range(nb))
+    U.log(f"    ||R^T R - I||_F {orth:.2e}")
+    assert orth <= 2.0 ** -24 * b ** 1.5 * 4
+    # the bf16 copy is the RNE rounding of the float32 blocks
+    a = act.float()
+    ref = f32.to(torch.bfloat16).float()
+    assert torch.equal(a, ref)
+
+
+def test_build_padded_last_block():
+    """b does not divide d: the last block is diag(Cayley(Q_r), I)."""
+    b, d = 64, 64 * 2 + 24
+    rng = np.random.default_rng(5)
+    theta = (rng.standard_normal((3, b * (b - 1) // 2)) * 0.05).astype(np.float32).astype(np.float64)
+    R_ref, _ = O.orthogonal_blocks(theta, b, d)
+    f32, _ = _build(theta, d, b)
+    R = U.host(f32)
+    assert np.max(np.abs(R - R_ref)) <= 2e-5
+    assert np.array_equal(R[-1, 24:, 24:], np.eye(b - 24))
+    assert np.all(R[-1, :24, 24:] == 0) and np.all(R[-1, 24:, :24] == 0)
+
+
+# ------------------------------------------------------ full layer, small
+SMALL_CASES = [
+    # name, d_in, d_out, b, tokens, dtype, sigma
+    ("f32_tiles", 192, 320, 32, 200, "f32", 0.05),
+    ("f32_b64_ragged_tokens", 256, 128, 64, 77, "f32", 0.05),
+    ("f32_padded_blocks", 200, 136, 48, 130, "f32", 0.05),
+    ("bf16_tiles", 512, 768, 128, 1000, "bf16", 0.02),
+    ("bf16_b256", 512, 1024, 256, 300, "bf16", 0.01),
+    ("bf16_b64_one_token", 256, 384, 64, 1, "bf16", 0.05),
+    ("bf16_padded_blocks", 320, 200, 128, 257, "bf16", 0.02),
+    ("bf16_b512", 1024, 512, 512, 129, "bf16", 0.01),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: c[0])
+def test_layer_small_full_compare(case):
+    name, n, m, b, N, dt, sigma = case
+    spec = LayerSpec(name, n, m, b, N, dt, sigma, seed=len(name))
+    U.log(f"[layer] {name}: d_in={n} d_out={m} b={b} tokens={N} {dt}")
+    L = make_layer(spec)
+    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, b, b)
+    y_ref = ora.forward(L.x)
+    gx_ref, gR_ref, gP_ref = ora.backward(L.g_y, L.x)
+    lay, out = U.run_layer(L)
+    U.check("R", U.host(lay.R_f32), ora.R, "f32")
+    U.check("P", U.host(lay.P_f32), ora.P, "f32")
+    U.check("y", U.host(out["y"]), y_ref, dt)
+    _, z_ref, _ = O.forward_input_centric(L.x, L.W0, ora.R, ora.P, b, b)
+    U.check("z", U.host(out["z"]), z_ref, dt)
+    U.check("g_x", U.host(out["g_x"]), gx_ref, dt)
+    U.check("g_theta_R", U.host(out["g_theta_R"]), gR_ref, dt)
+    U.check("g_theta_P", U.host(out["g_theta_P"]), gP_ref, dt)
+
+
+def test_tiny_config_exact_sizes():
+    """The 256 x 256, b = 32, 64-token float32 workload, every element."""
+    spec = CONFIGS["tiny_f32"][0]
+    L = make_layer(spec)
+    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b)
+    y_ref = ora.forward(L.x)
+    gx_ref, gR_ref, gP_ref = ora.backward(L.g_y, L.x)
+    _, out = U.run_layer(L)
+    U.check("y", U.host(out["y"]), y_ref, "f32")
+    U.check("g_x", U.host(out["g_x"]), gx_ref, "f32")
+    U.check("g_theta_R", U.host(out["g_theta_R"]), gR_ref, "f32")
+    U.check("g_theta_P", U.host(out["g_theta_P"]), gP_ref, "f32")
+
+
+def test_deterministic_bitwise():
+    spec = LayerSpec("det", 512, 768, 128, 1000, "bf16", 0.02, seed=3)
+    L = make_layer(spec)
+    _, a = U.run_layer(L)
+    _, c = U.run_layer(L)
+    for k in ("y", "z", "g_x", "g_theta_R", "g_theta_P"):
+        assert torch.equal(a[k], c[k]), k
+
+
+def test_theta_zero_is_plain_linear():
+    """theta = 0 gives R = P = I: y = x W0^T and g_x = g_y W0 (bf16 path)."""
+    spec = LayerSpec("zero", 256, 512, 64, 130, "bf16", 0.0, seed=9)
+    L = make_layer(spec)
+    lay, out = U.run_layer(L)
+    assert torch.equal(lay.R_f32, torch.eye(64, device="cuda").expand_as(lay.R_f32))
+    U.check("y", U.host(out["y"]), L.x @ L.W0.T, "bf16")
+    U.check("g_x", U.host(out["g_x"]), L.g_y @ L.W0, "bf16")
+
+
+# ------------------------------------------------- full-size workloads
+def _sampled_check(L, lay, out, n_rows=48, rng_seed=0):
+    s = L.spec
+    b = s.b
+    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, b, b)
+    U.check("R", U.host(lay.R_f32), ora.R, "f32")
+    U.check("P", U.host(lay.P_f32), ora.P, "f32")
+    rng = np.random.default_rng(rng_seed)
+    rows = np.sort(rng.choice(s.tokens, size=min(n_rows, s.tokens), replace=False))
+    rows = np.unique(np.concatenate([rows, [0, s.tokens - 1]]))
+    y_gpu = U.host(out["y"][torch.from_numpy(rows).cuda()])
+    U.check("y rows", y_gpu, ora.forward(L.x[rows]), s.dtype)
+    gx_gpu = U.host(out["g_x"][torch.from_numpy(rows).cuda()])
+    U.check("g_x rows", gx_gpu, L.g_y[rows] @ ora.W, s.dtype)
+    # whole generator blocks: first and last R block, last P block
+    W0P = O.materialise(L.W0, np.broadcast_to(np.eye(b), ora.R.shape), ora.P, b, b)
+    RW0 = O.materialise(L.W0, ora.R, np.broadcast_to(np.eye(b), ora.P.shape), b, b)
+    gR = U.host(out["g_theta_R"])
+    gP = U.host(out["g_theta_P"])
+    for k in sorted({0, ora.R.shape[0] - 1}):
+        rk = slice(k * b, (k + 1) * b)
+        G = (L.g_y[:, rk].T @ L.x) @ W0P[rk, :].T
+        ref = O.cayley_vjp(ora.B_R[k:k + 1], G[None])[0]
+        U.check(f"gthR[{k}]", gR[k], ref, s.dtype)
+    j = ora.P.shape[0] - 1
+    cj = slice(j * b, (j + 1) * b)
+    G = RW0[:, cj].T @ (L.g_y.T @ L.x[:, cj])
+    ref = O.cayley_vjp(ora.B_P[j:j + 1], G[None])[0]
+    U.check(f"gthP[{j}]", gP[j], ref, s.dtype)
+    # property at full size: R is orthogonal per block, so ||y_t,k|| = ||z_t,k||
+    y = out["y"].float().view(s.tokens, -1, b)
+    z = out["z"].float().view(s.tokens, -1, b)
+    ny, nz = y.norm(dim=2), z.norm(dim=2)
+    rel = ((ny - nz).norm() / nz.norm()).item()
+    U.log(f"    block-norm preservation rel {rel:.2e}")
+    assert rel <= 2e-2
+
+
+@pytest.mark.parametrize("cfg", ["proj_1b", "mlp_up_8b", "sweep_b64", "sweep_b128", "sweep_b256",
+                                 "sweep_b512", "sweep_b1024"])
+def test_full_size_workload(cfg):
+    for spec in CONFIGS[cfg]:
+        U.log(f"[full] {cfg}/{spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
+        L = make_layer(spec)
+        lay, out = U.run_layer(L)
+        _sampled_check(L, lay, out)
+        del lay, out
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("layer", range(7))
+def test_full_size_layer_set_8b(layer):
+    spec = CONFIGS["layer_set_8b"][layer]
+    U.log(f"[full] layer_set_8b/{spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
+    L = make_layer(spec)
+    lay, out = U.run_layer(L)
+    _sampled_check(L, lay, out)
+    del lay, out
+    torch.cuda.empty_cache()
