@@ -1,0 +1,247 @@
+"""Benchmark of the POET-X linear layer (fwd + bwd) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--gpus 1]
+
+One step = Cayley build of R and P (one launch set for both), forward and
+backward (to x and to the generators, including the Cayley VJP) of every
+layer of the workload, with all inputs resident in HBM. The default workload
+is the 8B-class MLP up-projection: W0 14336 x 4096 (out x in), b = 256,
+8192 tokens, bf16 storage with float32 accumulation.
+
+Prints ONE JSON line: tokens/s of the whole step, the roofline of the
+dominant kernel (the dense W0 GEMM of the forward, timed live with HIP events
+on the launch stream), the layer's algorithmic roofline fraction, a sampled
+parity check against the oracle, and the oracle's own throughput on the
+host's cores on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "POET-X linear fwd+bwd tokens/s at 8B-shaped layer; % bf16 MFMA roofline"
+PEAK_BF16 = 2516.6e12   # MI355X dense bf16 MFMA, FLOP/s
+PEAK_F32 = 157.3e12     # MI355X fp32 (matrix), FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+
+FWD_STAGES = ["p_apply", "dense_fwd", "r_apply"]
+BWD_STAGES = ["grad_r", "gram_r", "dense_bwd", "gram_p", "grad_x", "vjp_r", "vjp_p"]
+
+
+def layer_work(s):
+    """Algorithmic flops and bytes of one layer's step (build + fwd + bwd)."""
+    N, n, m, b = s.tokens, s.d_in, s.d_out, s.b
+    es = 2 if s.dtype == "bf16" else 4
+    flops = 4 * N * m * n + 6 * N * b * (m + n) + 6 * b * b * (m + n)
+    blocks = b * (m + n)          # elements of all R and P blocks
+    theta = (m + n) * (b - 1) // 2
+    fwd = es * (N * n + m * n + blocks + 2 * N * m) + 4 * theta
+    bwd = es * (2 * N * m + N * n + m * n + blocks + N * n) + 4 * blocks + 4 * theta
+    build = 4 * theta + 4 * blocks + es * blocks
+    return flops, fwd + bwd + build
+
+
+def cpu_baseline(spec, sample_tokens):
+    """The float64 oracle (build, materialise, forward, backward) on the first
+    `sample_tokens` tokens of the workload, timed on the host's cores."""
+    import dataclasses
+
+    import oracle.poetx_oracle as O
+    from orthogonal_equivalence_amd.inputs import make_layer
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    L = make_layer(spec)
+    x, g_y = L.x[:sample_tokens], L.g_y[:sample_tokens]
+    t0 = time.perf_counter()
+    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b)
+    ora.forward(x)
+    ora.backward(g_y, x)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 oracle step (exact Cayley solves, block-local materialisation of "
+                      f"R W0 P, forward, backward) on the first {sample_tokens} of {spec.tokens} "
+                      f"tokens of {spec.name} {spec.d_out}x{spec.d_in} b={spec.b}; {dt:.1f} s"}
+
+
+def parity_sample(L, out, lay, rows=32):
+    """Frobenius-relative error of sampled token rows of y and g_x against the
+    oracle's materialised weight (the full-size parity tests do more)."""
+    import oracle.poetx_oracle as O
+    import torch
+    s = L.spec
+    R, _ = O.orthogonal_blocks(L.theta_R, s.b, s.d_out)
+    Pb, _ = O.orthogonal_blocks(L.theta_P, s.b, s.d_in)
+    W = O.materialise(L.W0, R, Pb, s.b, s.b)
+    idx = np.linspace(0, s.tokens - 1, rows).astype(np.int64)
+    ti = torch.from_numpy(idx).cuda()
+    y = out["y"][ti].float().cpu().double().numpy()
+    gx = out["g_x"][ti].float().cpu().double().numpy()
+    y_ref = L.x[idx] @ W.T
+    gx_ref = L.g_y[idx] @ W
+    return {"y_rows_fro_rel": float(np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref)),
+            "g_x_rows_fro_rel": float(np.linalg.norm(gx - gx_ref) / np.linalg.norm(gx_ref)),
+            "rows": rows}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mlp_up_8b")
+    ap.add_argument("--cpu-sample", type=int, default=8192,
+                    help="tokens of the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the token-parallel design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from orthogonal_equivalence_amd import poetx as P
+    from orthogonal_equivalence_amd.inputs import CONFIGS, make_layer
+    from orthogonal_equivalence_amd.layer import PoetxLinear
+
+    specs = CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+    # ---- inputs resident in HBM
+    layers = []
+    for s in specs:
+        L = make_layer(s)
+        lay = PoetxLinear(torch.from_numpy(L.W0).to(tdt[s.dtype]), s.b, s.b, s.dtype, device=dev)
+        lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
+        x = torch.from_numpy(L.x).to(tdt[s.dtype]).to(dev)
+        g_y = torch.from_numpy(L.g_y).to(tdt[s.dtype]).to(dev)
+        out = dict(y=torch.empty(s.tokens, s.d_out, dtype=tdt[s.dtype], device=dev),
+                   z=torch.empty(s.tokens, s.d_out, dtype=tdt[s.dtype], device=dev),
+                   g_x=torch.empty(s.tokens, s.d_in, dtype=tdt[s.dtype], device=dev),
+                   gR=torch.empty_like(lay.theta_R), gP=torch.empty_like(lay.theta_P))
+        layers.append((s, L if len(specs) == 1 else None, lay, x, g_y, out))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for li, (s, _, lay, x, g_y, o) in enumerate(layers):
+            if ev is not None:
+                ev[li]["build"][0].record(stream)
+            lay.build(stream)
+            if ev is not None:
+                ev[li]["build"][1].record(stream)
+            lay.forward(x, o["y"], o["z"], stream=stream,
+                        events=None if ev is None else ev[li]["fwd"])
+            lay.backward(g_y, x, o["z"], o["g_x"], o["gR"], o["gP"], stream=stream,
+                         events=None if ev is None else ev[li]["bwd"])
+
+    def make_events():
+        ev = []
+        for _ in layers:
+            ev.append({"build": (P.Event(), P.Event()),
+                       "fwd": [P.Event() for _ in range(2 * len(FWD_STAGES))],
+                       "bwd": [P.Event() for _ in range(2 * len(BWD_STAGES))]})
+        return ev
+
+    def as_handles(ev):
+        return [{"build": e["build"], "fwd": [x.handle for x in e["fwd"]],
+                 "bwd": [x.handle for x in e["bwd"]]} for e in ev]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps bracketed by synchronize, HIP events per stage
+    step_events = [make_events() for _ in range(args.steps)]
+    handles = [as_handles(e) for e in step_events]
+    t_start, t_stop = P.Event(), P.Event()
+    per_step = [(P.Event(), P.Event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        per_step[k][0].record(stream)
+        step(handles[k])
+        per_step[k][1].record(stream)
+    t_stop.record(stream)
+    t_stop.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = t_start.elapsed_ms(t_stop)
+    ms_per_step = total_ms / args.steps
+    step_ms = [a.elapsed_ms(b) for a, b in per_step]
+    tokens = specs[0].tokens
+    value = tokens / (ms_per_step / 1e3)
+
+    stage_ms = {}
+    for li, (s, _, _, _, _, _) in enumerate(layers):
+        pre = "" if len(layers) == 1 else f"{s.name}."
+        vals = [step_events[k][li]["build"][0].elapsed_ms(step_events[k][li]["build"][1])
+                for k in range(args.steps)]
+        stage_ms[pre + "build"] = statistics.mean(vals)
+        for grp, names in (("fwd", FWD_STAGES), ("bwd", BWD_STAGES)):
+            for si, nm in enumerate(names):
+                vals = [step_events[k][li][grp][2 * si].elapsed_ms(step_events[k][li][grp][2 * si + 1])
+                        for k in range(args.steps)]
+                stage_ms[pre + nm] = statistics.mean(vals)
+
+    # dominant kernel: the forward dense W0 GEMM (Z = U W0^T) of the largest layer
+    big = max(range(len(layers)), key=lambda i: layers[i][0].d_in * layers[i][0].d_out)
+    sb = layers[big][0]
+    dense_ms = stage_ms[("" if len(layers) == 1 else f"{sb.name}.") + "dense_fwd"]
+    dense_flops = 2.0 * sb.tokens * sb.d_in * sb.d_out
+    peak = PEAK_BF16 if sb.dtype == "bf16" else PEAK_F32
+    achieved = dense_flops / (dense_ms / 1e3)
+    roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None,
+                "kernel": "dense_fwd: Z = U W0^T (gemm_kernel bf16, NT)",
+                "flops_per_launch": dense_flops, "avg_launch_ms": dense_ms}
+
+    F = sum(layer_work(s)[0] for s, *_ in layers)
+    B = sum(layer_work(s)[1] for s, *_ in layers)
+    t_roof = max(F / PEAK_BF16, B / PEAK_HBM)
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": specs[0].dtype, "data": "synthetic (seeded N(0,1) activations, N(0,1/d_in) W0, "
+                                          "N(0, sigma^2) generators)",
+        "config": {"workload": args.config,
+                   "layers": [f"{s.name} {s.d_out}x{s.d_in} b={s.b}" for s in specs],
+                   "tokens": tokens, "block": specs[0].b},
+        "roofline": roofline,
+        "layer_roofline": {"flops": F, "bytes": B, "t_roof_ms": t_roof * 1e3,
+                           "frac": t_roof / (ms_per_step / 1e3),
+                           "tflops": F / (ms_per_step / 1e3) / 1e12},
+        "step_ms": {"median": statistics.median(step_ms), "min": min(step_ms), "max": max(step_ms)},
+        "wall_s": wall,
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+    }
+    if not args.no_parity and len(layers) == 1:
+        s, L, lay, x, g_y, o = layers[0]
+        res["parity"] = parity_sample(L, dict(y=o["y"], g_x=o["g_x"]), lay)
+    if args.cpu_sample > 0:
+        res["cpu_baseline"] = cpu_baseline(specs[-1] if len(specs) == 1 else specs[0],
+                                           min(args.cpu_sample, specs[0].tokens))
+    res["gpu"] = torch.cuda.get_device_name(0)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
