@@ -69,7 +69,7 @@ struct SplitK {
 // Splits the token reduction of a gram so the launch has about 1024
 // workgroups, with at least 256 tokens per split.
 SplitK choose_split(int64_t nblocks, int b, int64_t tokens, DType in) {
-  const int mt = in == DType::BF16 ? 128 : 64;
+  const int mt = poetx::gemm_tile_m(in, b, b);
   const int kt = poetx::gemm_k_tile(in);
   const int64_t tiles = nblocks * ceil_div(b, mt) * ceil_div(b, mt);
   int64_t s = std::max<int64_t>(1, ceil_div(1024, tiles));

@@ -4,44 +4,89 @@
 // G_R and G_P (split over tokens), and the Cayley VJP products.
 //
 // One workgroup computes a BM x BN tile of one batch (and one K split). Both
-// operand tiles are staged in LDS K-contiguous ([rows][BK + pad]) in two
-// buffers: the next tile's global loads are issued before the MFMAs on the
-// current one, and one barrier per K step separates the LDS write of the
-// next buffer from the reads of the current one. An operand that is
-// contiguous along M/N in global memory (a transposed access, e.g. the
-// token-major activations of the grams) is loaded as VEC x VEC sub-blocks of
-// 16-byte rows and transposed in registers on the way to LDS.
+// operand tiles are staged in LDS K-contiguous, 128 bytes per row, with the
+// 16-byte chunks of row r XOR-swizzled by f(r) = ((r >> 1) ^ ((r & 1) << 2)) & 7
+// so that the MFMA fragment reads of 8 or 16 consecutive rows hit distinct
+// banks. Two LDS buffers: the next tile's global loads are issued before the
+// MFMAs on the current one, and one barrier per K step separates the LDS
+// write of the next buffer from the reads of the current one. An operand
+// that is contiguous along M/N in global memory (a transposed access, e.g.
+// the token-major activations of the grams, or W0 in the backward) is loaded
+// as VEC x VEC sub-blocks of 16-byte rows and transposed in registers on the
+// way to LDS.
 //
-// bf16 inputs use v_mfma_f32_16x16x32_bf16, float32 inputs
-// v_mfma_f32_16x16x4_f32; accumulation is float32 in both cases.
-#include <type_traits>
-
+// Workgroups are dispatched round-robin over the 8 XCDs; the tile order is
+// remapped so each XCD works on a contiguous range of a grouped (GROUP_M
+// row tiles at a time) ordering, which keeps the A and B panels that
+// concurrently running tiles share in that XCD's L2.
+//
+// Configurations: bf16 256x256x64 tiles, 2x2 waves of 128x128 with
+// v_mfma_f32_32x32x16_bf16 (large shapes); bf16 128x128x64 with
+// v_mfma_f32_16x16x32_bf16 (small shapes); float32 64x64x32 with
+// v_mfma_f32_16x16x4_f32. Accumulation is float32 throughout.
 #include "common.h"
 #include "kernels.h"
 
 namespace poetx {
 namespace {
 
-template <typename T>
-struct Vec16 {  // 16 bytes of T
-  static constexpr int N = ElemTraits<T>::kVec;
-  union {
-    uint4 u;
-    T e[N];
-  };
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
+
+// Transpose of a VEC x VEC block held as VEC 16-byte rows: out[c] holds
+// element c of every input row, in row order.
+template <typename T> struct Transpose;
+template <> struct Transpose<bf16_t> {  // 8 x 8 bf16
+  __device__ static uint4 column(const uint4* v, int c) {
+    // dword d of the output holds rows 2d (low half) and 2d+1 (high half)
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    auto pick = [&](int r) -> uint32_t {
+      const uint4& q = v[r];
+      const int d = c >> 1;
+      return d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
+    };
+    uint4 o;
+    o.x = __builtin_amdgcn_perm(pick(1), pick(0), sel);
+    o.y = __builtin_amdgcn_perm(pick(3), pick(2), sel);
+    o.z = __builtin_amdgcn_perm(pick(5), pick(4), sel);
+    o.w = __builtin_amdgcn_perm(pick(7), pick(6), sel);
+    return o;
+  }
+};
+template <> struct Transpose<float> {  // 4 x 4 float
+  __device__ static uint4 column(const uint4* v, int c) {
+    auto pick = [&](int r) -> uint32_t {
+      const uint4& q = v[r];
+      return c == 0 ? q.x : c == 1 ? q.y : c == 2 ? q.z : q.w;
+    };
+    return make_uint4(pick(0), pick(1), pick(2), pick(3));
+  }
 };
 
+// LDS tile: ROWS rows of BK elements (128 bytes), swizzled chunks.
+template <typename TIn, int BK>
+struct LdsLayout {
+  static constexpr int VEC = ElemTraits<TIn>::kVec;
+  static_assert(BK * sizeof(TIn) == 128, "LDS rows are 128 bytes");
+  __device__ static int chunk_off(int row, int chunk) { return row * BK + ((chunk ^ swz(row)) * VEC); }
+  __device__ static int elem_off(int row, int k) { return chunk_off(row, k / VEC) + (k % VEC); }
+};
+
+// Global -> register -> LDS staging of one operand tile. Only whole 16-byte
+// vectors are moved: the host guarantees that K extents of K-major operands
+// and row extents of MN-major operands are multiples of VEC, so a vector is
+// either entirely inside the operand or entirely outside (then zero).
 template <typename TIn, int ROWS, int BK, int NT, bool KMAJ>
 struct TileLoader {
   static constexpr int VEC = ElemTraits<TIn>::kVec;
-  static constexpr int LDK = BK + VEC;
+  typedef LdsLayout<TIn, BK> L;
   // K-major: one 16-byte chunk (VEC consecutive k of one row) per item.
   // MN-major: one VEC(k) x VEC(row) sub-block per item.
   static constexpr int ITEMS = KMAJ ? ROWS * BK / VEC : (ROWS / VEC) * (BK / VEC);
   static constexpr int PER_THREAD = (ITEMS + NT - 1) / NT;
   static constexpr int REGS = KMAJ ? PER_THREAD : PER_THREAD * VEC;
+  static constexpr bool EXACT = (ITEMS % NT) == 0;
 
-  Vec16<TIn> r[REGS];
+  uint4 r[REGS];
 
   // base points at element (row 0, k 0) of this batch; rows/k are global
   // indices. Rows >= rext or k >= kend read as zero.
@@ -51,34 +96,24 @@ struct TileLoader {
     for (int i = 0; i < PER_THREAD; ++i) {
       const int item = tid + i * NT;
       if (KMAJ) {
-        Vec16<TIn>& v = r[i];
-        v.u = make_uint4(0, 0, 0, 0);
-        if (item < ITEMS) {
-          const int row = item / (BK / VEC);
-          const int kc = (item % (BK / VEC)) * VEC;
-          const int gr = r0 + row, gk = k0 + kc;
-          if (gr < rext && gk < kend) {
-            const TIn* src = base + (int64_t)gr * ld + gk;
-            if (gk + VEC <= kend) {
-              v.u = *reinterpret_cast<const uint4*>(src);
-            } else {
-#pragma unroll
-              for (int e = 0; e < VEC; ++e)
-                if (gk + e < kend) v.e[e] = src[e];
-            }
-          }
-        }
+        const int row = item / (BK / VEC);
+        const int kc = (item % (BK / VEC)) * VEC;
+        const int gr = r0 + row, gk = k0 + kc;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if ((EXACT || item < ITEMS) && gr < rext && gk < kend)
+          v = *reinterpret_cast<const uint4*>(base + (int64_t)gr * ld + gk);
+        r[i] = v;
       } else {
         const int kb = item / (ROWS / VEC);
         const int rb = item % (ROWS / VEC);
         const int gr = r0 + rb * VEC;
+        const bool rows_ok = (EXACT || item < ITEMS) && gr < rext;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          Vec16<TIn>& v = r[i * VEC + e];
-          v.u = make_uint4(0, 0, 0, 0);
           const int gk = k0 + kb * VEC + e;
-          if (item < ITEMS && gr < rext && gk < kend)
-            v.u = *reinterpret_cast<const uint4*>(base + (int64_t)gk * ld + gr);
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (rows_ok && gk < kend) v = *reinterpret_cast<const uint4*>(base + (int64_t)gk * ld + gr);
+          r[i * VEC + e] = v;
         }
       }
     }
@@ -88,61 +123,99 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int item = tid + i * NT;
-      if (item >= ITEMS) continue;
+      if (!EXACT && item >= ITEMS) continue;
       if (KMAJ) {
         const int row = item / (BK / VEC);
-        const int kc = (item % (BK / VEC)) * VEC;
-        *reinterpret_cast<uint4*>(s + row * LDK + kc) = r[i].u;
+        const int kc = item % (BK / VEC);
+        *reinterpret_cast<uint4*>(s + L::chunk_off(row, kc)) = r[i];
       } else {
         const int kb = item / (ROWS / VEC);
         const int rb = item % (ROWS / VEC);
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) {
-          Vec16<TIn> t;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) t.e[e] = r[i * VEC + e].e[c];
-          *reinterpret_cast<uint4*>(s + (rb * VEC + c) * LDK + kb * VEC) = t.u;
-        }
+        for (int c = 0; c < VEC; ++c)
+          *reinterpret_cast<uint4*>(s + L::chunk_off(rb * VEC + c, kb)) =
+              Transpose<TIn>::column(&r[i * VEC], c);
       }
     }
   }
 };
 
-template <typename TIn> struct Mfma;
+// MFMA shapes. `load` reads the fragment of rows [row0, row0 + M) at K
+// offset kk; `out_row` maps accumulator element e of a lane to its row in
+// the M x M output tile (the column is lane % M).
+template <typename TIn, int MI> struct Mfma;
 
-template <> struct Mfma<bf16_t> {
-  static constexpr int KSTEP = 32;
+template <> struct Mfma<bf16_t, 32> {
+  static constexpr int M = 32, KSTEP = 16, NACC = 16;
   typedef bf16x8_t Frag;
-  __device__ static Frag load(const bf16_t* s, int LDK, int row, int kk, int lane) {
-    return *reinterpret_cast<const bf16x8_t*>(s + (row + (lane & 15)) * LDK + kk + 8 * (lane >> 4));
+  typedef floatx16 Acc;
+  template <int BK>
+  __device__ static Frag load(const bf16_t* s, int row0, int kk, int lane) {
+    const int row = row0 + (lane & 31);
+    return *reinterpret_cast<const bf16x8_t*>(s + LdsLayout<bf16_t, BK>::chunk_off(row, (kk >> 3) + (lane >> 5)));
   }
-  __device__ static floatx4 mma(Frag a, Frag b, floatx4 c) {
+  __device__ static Acc mma(Frag a, Frag b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static int out_row(int e, int lane) { return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3); }
+};
+
+template <> struct Mfma<bf16_t, 16> {
+  static constexpr int M = 16, KSTEP = 32, NACC = 4;
+  typedef bf16x8_t Frag;
+  typedef floatx4 Acc;
+  template <int BK>
+  __device__ static Frag load(const bf16_t* s, int row0, int kk, int lane) {
+    const int row = row0 + (lane & 15);
+    return *reinterpret_cast<const bf16x8_t*>(s + LdsLayout<bf16_t, BK>::chunk_off(row, (kk >> 3) + (lane >> 4)));
+  }
+  __device__ static Acc mma(Frag a, Frag b, Acc c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  __device__ static int out_row(int e, int lane) { return 4 * (lane >> 4) + e; }
 };
 
-template <> struct Mfma<float> {
-  static constexpr int KSTEP = 4;
+template <> struct Mfma<float, 16> {
+  static constexpr int M = 16, KSTEP = 4, NACC = 4;
   typedef float Frag;
-  __device__ static Frag load(const float* s, int LDK, int row, int kk, int lane) {
-    return s[(row + (lane & 15)) * LDK + kk + (lane >> 4)];
+  typedef floatx4 Acc;
+  template <int BK>
+  __device__ static Frag load(const float* s, int row0, int kk, int lane) {
+    return s[LdsLayout<float, BK>::elem_off(row0 + (lane & 15), kk + (lane >> 4))];
   }
-  __device__ static floatx4 mma(Frag a, Frag b, floatx4 c) {
+  __device__ static Acc mma(Frag a, Frag b, Acc c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
+  __device__ static int out_row(int e, int lane) { return 4 * (lane >> 4) + e; }
 };
 
-template <typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, int WM, int WN>
+// Logical tile of this workgroup: XCD-contiguous, then grouped by GROUP_M
+// row tiles.
+__device__ __forceinline__ void tile_coords(int num_mt, int num_nt, int& mt, int& nt) {
+  constexpr int GROUP_M = 8;
+  int wg = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
+  const int per_group = GROUP_M * num_nt;
+  const int group = wg / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(num_mt - first_m, GROUP_M);
+  const int in_group = wg - group * per_group;
+  mt = first_m + in_group % gsize;
+  nt = in_group / gsize;
+}
+
+template <typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, int WM,
+          int WN, int MI>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(const GemmParams p) {
+  typedef Mfma<TIn, MI> Op;
   constexpr int NT = 64 * WM * WN;
-  constexpr int VEC = ElemTraits<TIn>::kVec;
-  constexpr int LDK = BK + VEC;
   constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int STAGE = (BM + BN) * LDK;
-  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
-  static_assert(BK % Mfma<TIn>::KSTEP == 0 && BK % VEC == 0, "bad K tile");
+  constexpr int FM = TM / MI, FN = TN / MI;
+  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(TM % MI == 0 && TN % MI == 0, "wave tile must be a multiple of the MFMA tile");
+  static_assert(BK % Op::KSTEP == 0, "bad K tile");
 
   __shared__ __attribute__((aligned(16))) TIn smem[2 * STAGE];
 
@@ -157,8 +230,11 @@ gemm_kernel(const GemmParams p) {
   const int Nx = last ? p.N_last : p.N;
   const int Kx = last ? p.K_last : p.K;
   const int num_mt = (p.M + BM - 1) / BM;
-  const int m0 = (blockIdx.x % num_mt) * BM;
-  const int n0 = (blockIdx.x / num_mt) * BN;
+  const int num_nt = (p.N + BN - 1) / BN;
+  int mt, nt;
+  tile_coords(num_mt, num_nt, mt, nt);
+  const int m0 = mt * BM;
+  const int n0 = nt * BN;
   if (m0 >= Mx || n0 >= Nx) return;  // whole workgroup: tile outside a ragged last batch
 
   const int kbeg = blockIdx.z * p.kchunk;
@@ -171,17 +247,19 @@ gemm_kernel(const GemmParams p) {
   TileLoader<TIn, BM, BK, NT, A_KMAJ> la;
   TileLoader<TIn, BN, BK, NT, B_KMAJ> lb;
 
-  floatx4 acc[FM][FN];
+  typename Op::Acc acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < Op::NACC; ++e) acc[i][j][e] = 0.0f;
 
   if (ntiles > 0) {
     la.load(A, p.lda, m0, Mx, kbeg, kend, tid);
     lb.load(B, p.ldb, n0, Nx, kbeg, kend, tid);
     la.store(smem, tid);
-    lb.store(smem + BM * LDK, tid);
+    lb.store(smem + BM * BK, tid);
     __syncthreads();
   }
 
@@ -194,23 +272,23 @@ gemm_kernel(const GemmParams p) {
       lb.load(B, p.ldb, n0, Nx, k0, kend, tid);
     }
     const TIn* As = smem + cur * STAGE;
-    const TIn* Bs = As + BM * LDK;
+    const TIn* Bs = As + BM * BK;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += Mfma<TIn>::KSTEP) {
-      typename Mfma<TIn>::Frag af[FM], bfr[FN];
+    for (int kk = 0; kk < BK; kk += Op::KSTEP) {
+      typename Op::Frag af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = Mfma<TIn>::load(As, LDK, wm * TM + i * 16, kk, lane);
+      for (int i = 0; i < FM; ++i) af[i] = Op::template load<BK>(As, wm * TM + i * MI, kk, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = Mfma<TIn>::load(Bs, LDK, wn * TN + j * 16, kk, lane);
+      for (int j = 0; j < FN; ++j) bfr[j] = Op::template load<BK>(Bs, wn * TN + j * MI, kk, lane);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = Mfma<TIn>::mma(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = Op::mma(af[i], bfr[j], acc[i][j]);
     }
     if (more) {
       TIn* nxt = smem + (cur ^ 1) * STAGE;
       la.store(nxt, tid);
-      lb.store(nxt + BM * LDK, tid);
+      lb.store(nxt + BM * BK, tid);
     }
     __syncthreads();
   }
@@ -221,10 +299,10 @@ gemm_kernel(const GemmParams p) {
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * TN + j * 16 + (lane & 15);
+      const int n = n0 + wn * TN + j * MI + (lane % MI);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * TM + i * 16 + 4 * (lane >> 4) + e;
+      for (int e = 0; e < Op::NACC; ++e) {
+        const int m = m0 + wm * TM + i * MI + Op::out_row(e, lane);
         if (m < Mx && n < Nx) {
           float v = p.alpha * acc[i][j][e];
           if (D) v += p.beta * ElemTraits<TOut>::to_f32(D[(int64_t)m * p.ldd + n]);
@@ -235,44 +313,52 @@ gemm_kernel(const GemmParams p) {
   }
 }
 
-// Tile shapes: bf16 128 x 128 x 64 with 2 x 2 waves (64 x 64 per wave);
-// float32 64 x 64 x 32 with 2 x 2 waves (32 x 32 per wave).
-template <typename TIn> struct TileCfg;
-template <> struct TileCfg<bf16_t> { static constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2; };
-template <> struct TileCfg<float> { static constexpr int BM = 64, BN = 64, BK = 32, WM = 2, WN = 2; };
+struct Big { static constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, MI = 32; };
+struct SmallBf16 { static constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2, MI = 16; };
+struct SmallF32 { static constexpr int BM = 64, BN = 64, BK = 32, WM = 2, WN = 2, MI = 16; };
 
-template <typename TIn, typename TOut, bool AK, bool BK_>
+template <typename TIn, typename TOut, bool AK, bool BK_, typename C>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {
-  typedef TileCfg<TIn> C;
   const int num_mt = (p.M + C::BM - 1) / C::BM;
   const int num_nt = (p.N + C::BN - 1) / C::BN;
   dim3 grid(num_mt * num_nt, p.batch, p.ksplit);
   dim3 block(64 * C::WM * C::WN);
-  hipLaunchKernelGGL((gemm_kernel<TIn, TOut, AK, BK_, C::BM, C::BN, C::BK, C::WM, C::WN>), grid, block,
-                     0, stream, p);
+  hipLaunchKernelGGL((gemm_kernel<TIn, TOut, AK, BK_, C::BM, C::BN, C::BK, C::WM, C::WN, C::MI>),
+                     grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, typename C>
 hipError_t launch_layout(bool ak, bool bk, const GemmParams& p, hipStream_t stream) {
-  if (ak && bk) return launch_cfg<TIn, TOut, true, true>(p, stream);
-  if (ak && !bk) return launch_cfg<TIn, TOut, true, false>(p, stream);
-  if (!ak && !bk) return launch_cfg<TIn, TOut, false, false>(p, stream);
-  return launch_cfg<TIn, TOut, false, true>(p, stream);
+  if (ak && bk) return launch_cfg<TIn, TOut, true, true, C>(p, stream);
+  if (ak && !bk) return launch_cfg<TIn, TOut, true, false, C>(p, stream);
+  if (!ak && !bk) return launch_cfg<TIn, TOut, false, false, C>(p, stream);
+  return launch_cfg<TIn, TOut, false, true, C>(p, stream);
 }
+
+bool use_big(const GemmParams& p) { return p.M >= 256 && p.N >= 256; }
 
 }  // namespace
 
-int gemm_k_tile(DType in) { return in == DType::BF16 ? TileCfg<bf16_t>::BK : TileCfg<float>::BK; }
+int gemm_k_tile(DType in) { return in == DType::BF16 ? 64 : 32; }
+
+int gemm_tile_m(DType in, int M, int N) {
+  if (in == DType::BF16) return (M >= 256 && N >= 256) ? 256 : 128;
+  return 64;
+}
 
 hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor, const GemmParams& p,
                        hipStream_t stream) {
   if (p.batch <= 0 || p.M <= 0 || p.N <= 0 || p.ksplit <= 0) return hipSuccess;
   if (in == DType::BF16) {
-    if (out == DType::BF16) return launch_layout<bf16_t, bf16_t>(a_kmajor, b_kmajor, p, stream);
-    return launch_layout<bf16_t, float>(a_kmajor, b_kmajor, p, stream);
+    const bool big = use_big(p);
+    if (out == DType::BF16)
+      return big ? launch_layout<bf16_t, bf16_t, Big>(a_kmajor, b_kmajor, p, stream)
+                 : launch_layout<bf16_t, bf16_t, SmallBf16>(a_kmajor, b_kmajor, p, stream);
+    return big ? launch_layout<bf16_t, float, Big>(a_kmajor, b_kmajor, p, stream)
+               : launch_layout<bf16_t, float, SmallBf16>(a_kmajor, b_kmajor, p, stream);
   }
-  if (out == DType::F32) return launch_layout<float, float>(a_kmajor, b_kmajor, p, stream);
+  if (out == DType::F32) return launch_layout<float, float, SmallF32>(a_kmajor, b_kmajor, p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -38,9 +38,10 @@ struct GemmParams {
 hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor,
                        const GemmParams& p, hipStream_t stream);
 
-// K tile of the GEMM configuration used for `in` (split-K chunks are
-// multiples of it).
+// K tile of the GEMM configurations for `in` (split-K chunks are multiples
+// of it) and the M/N tile chosen for an M x N problem.
 int gemm_k_tile(DType in);
+int gemm_tile_m(DType in, int M, int N);
 
 // ---- Cayley build (exact Cayley map by blocked Gauss-Jordan) ----
 // Panel width used for block size b.
