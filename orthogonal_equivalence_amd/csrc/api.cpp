@@ -66,13 +66,15 @@ FwdPlan plan_fwd(const poetx_linear_desc* d) {
 struct SplitK {
   int nsplit, kchunk;
 };
-// Splits the token reduction of a gram so the launch has about 1024
-// workgroups, with at least 256 tokens per split.
+// Splits the token reduction of a gram so the launch fills the chip (about
+// 256 workgroups of the 256 x 256 tile, 1024 of the smaller ones), with at
+// least 256 tokens per split.
 SplitK choose_split(int64_t nblocks, int b, int64_t tokens, DType in) {
   const int mt = poetx::gemm_tile_m(in, b, b);
   const int kt = poetx::gemm_k_tile(in);
   const int64_t tiles = nblocks * ceil_div(b, mt) * ceil_div(b, mt);
-  int64_t s = std::max<int64_t>(1, ceil_div(1024, tiles));
+  const int64_t target = mt >= 256 ? 256 : 1024;
+  int64_t s = std::max<int64_t>(1, ceil_div(target, tiles));
   s = std::min<int64_t>(s, std::max<int64_t>(1, tokens / 256));
   int64_t chunk = ceil_div(ceil_div(tokens, s), kt) * kt;
   SplitK r;
