@@ -140,6 +140,17 @@ GemmParams blockdiag_params(const void* in, const void* blocks, void* out, int64
   return g;
 }
 
+// out[:, blk] = in[:, blk] M_blk^T (transpose) or in[:, blk] M_blk, on the
+// streaming kernel when it supports the shape, else on the batched GEMM.
+hipError_t block_apply(DType t, const void* in, const void* blocks, void* out, int64_t tokens,
+                       int64_t d, int b, bool transpose, hipStream_t s) {
+  if (poetx::blockapply_supported(t, d, b))
+    return poetx::launch_blockapply(in, blocks, out, tokens, d, b, transpose, s);
+  bool bk;
+  GemmParams g = blockdiag_params(in, blocks, out, tokens, d, b, transpose, &bk);
+  return poetx::launch_gemm(t, t, true, bk, g, s);
+}
+
 // Gram of token-major activations: part[s][blk] = a[:, blk]^T c[:, blk]
 GemmParams gram_params(const void* a, const void* c, float* part, int64_t tokens, int64_t d, int b,
                        SplitK sk) {
@@ -286,8 +297,7 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
 
   // S2: U = X blockdiag(P)^T
   if ((e = sg.begin(0)) != hipSuccess) return hip_status(e);
-  GemmParams g = blockdiag_params(x, P_act, U, N, n, d->b_in, true, &bk);
-  if ((e = poetx::launch_gemm(t, t, true, bk, g, s)) != hipSuccess) return hip_status(e);
+  if ((e = block_apply(t, x, P_act, U, N, n, d->b_in, true, s)) != hipSuccess) return hip_status(e);
   if ((e = sg.end(0)) != hipSuccess) return hip_status(e);
 
   // S3: Z = U W0^T
@@ -303,8 +313,8 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
 
   // S4: Y = Z blockdiag(R)^T
   if ((e = sg.begin(2)) != hipSuccess) return hip_status(e);
-  g = blockdiag_params(z_save, R_act, y, N, m, d->b_out, true, &bk);
-  if ((e = poetx::launch_gemm(t, t, true, bk, g, s)) != hipSuccess) return hip_status(e);
+  if ((e = block_apply(t, z_save, R_act, y, N, m, d->b_out, true, s)) != hipSuccess)
+    return hip_status(e);
   if ((e = sg.end(2)) != hipSuccess) return hip_status(e);
   return POETX_OK;
 }
@@ -367,13 +377,12 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B1: g_Z = g_Y blockdiag(R)
   POETX_TRY(sg.begin(0));
-  GemmParams g = blockdiag_params(g_y, R_act, gZ, N, m, bR, false, &bk);
-  POETX_TRY(poetx::launch_gemm(t, t, true, bk, g, s));
+  POETX_TRY(block_apply(t, g_y, R_act, gZ, N, m, bR, false, s));
   POETX_TRY(sg.end(0));
 
   // B2: G_R[k] = g_Y[:, k]^T Z[:, k], split over tokens, then reduced
   POETX_TRY(sg.begin(1));
-  g = gram_params(g_y, z_saved, partR, N, m, bR, plan.sR);
+  GemmParams g = gram_params(g_y, z_saved, partR, N, m, bR, plan.sR);
   POETX_TRY(poetx::launch_gemm(t, DType::F32, false, false, g, s));
   POETX_TRY(poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, s));
   POETX_TRY(sg.end(1));
@@ -398,8 +407,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B5: g_X = g_U blockdiag(P)
   POETX_TRY(sg.begin(4));
-  g = blockdiag_params(gU, P_act, g_x, N, n, bP, false, &bk);
-  POETX_TRY(poetx::launch_gemm(t, t, true, bk, g, s));
+  POETX_TRY(block_apply(t, gU, P_act, g_x, N, n, bP, false, s));
   POETX_TRY(sg.end(4));
 
   // B6: Cayley VJP of R and of P

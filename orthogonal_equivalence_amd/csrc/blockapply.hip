@@ -1,0 +1,279 @@
+// Streaming block-diagonal apply for bf16 activations: for every block k of
+// b features (b = 128 or 256) and every token t,
+//   Y[t, kb + n] = sum_k X[t, kb + k] B(n, k),  B(n, k) = M_k[n][k] (transpose)
+//                                               or      M_k[k][n],
+// i.e. the batch-parallel block products of the POET-X layer (gist.science
+// technical summary of "POET-X: Memory-efficient LLM Training by Scaling
+// Orthogonal Transformation", section 2 Methodik, block-diagonal item):
+// P-apply and R-apply of the forward (transpose) and the gradients through R
+// and P of the backward (no transpose).
+//
+// These products are HBM-bound (about b/2 flop per byte), so the kernel is
+// built to stream: one workgroup owns one block and a contiguous token range
+// (about one workgroup per CU). It loads M_k once (through LDS, using the
+// gfx950 transposing LDS read ds_read_b64_tr_b16 when the fragments need M_k's
+// columns) and keeps it in registers as MFMA B fragments: wave w owns output
+// columns [w b/4, (w+1) b/4). Token tiles of 64 rows are copied from global
+// memory straight into a 4-stage LDS ring (global_load_lds_dwordx4, three
+// tiles in flight), multiplied on v_mfma_f32_32x32x16_bf16, staged back into
+// the consumed ring slot and written with 16-byte stores.
+//
+// Waits on the LDS-bound loads are explicit: before tile t, the wave waits
+// until at most (number of its tile loads issued after tile t) vector memory
+// operations are outstanding. Stores only add to that counter, so the wait is
+// correct whatever order loads and stores complete in.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace poetx {
+namespace {
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kTT = 64;    // tokens per tile
+constexpr int kNT = 256;   // threads
+constexpr int kMaxB = 256;
+constexpr int kStage = kTT * kMaxB;  // bf16 elements per ring slot (sized for b = 256)
+
+// The ring slots are separate arrays so that the compiler can tell which slot
+// an LDS read touches while loads into the other slots are in flight.
+__shared__ __attribute__((aligned(16))) bf16_t g_ring0[kStage];
+__shared__ __attribute__((aligned(16))) bf16_t g_ring1[kStage];
+__shared__ __attribute__((aligned(16))) bf16_t g_ring2[kStage];
+__shared__ __attribute__((aligned(16))) bf16_t g_ring3[kStage];
+
+template <int S> __device__ __forceinline__ bf16_t* ring() {
+  return S == 0 ? g_ring0 : S == 1 ? g_ring1 : S == 2 ? g_ring2 : g_ring3;
+}
+__device__ __forceinline__ bf16_t* ring_rt(int s) {
+  return s == 0 ? g_ring0 : s == 1 ? g_ring1 : s == 2 ? g_ring2 : g_ring3;
+}
+
+// LDS element offset of (row, col) in a row-major tile of width W (bf16) with
+// 16-byte chunks XOR-swizzled by the low 4 row bits.
+template <int W>
+__device__ __forceinline__ int sw(int row, int col) {
+  return row * W + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
+}
+
+// One global_load_lds_dwordx4: every lane copies 16 bytes from gptr into LDS
+// at lds_base + 16 * lane. Issued through inline assembly so that the only
+// waits on it are the explicit s_waitcnt of the pipeline.
+__device__ __forceinline__ void dma16(const void* gptr, const bf16_t* lds_base) {
+  // lds_base is the same for the whole wave; make that explicit for the SGPR
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)lds_base)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(gptr)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding).
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int B, bool TRANS>
+struct BlockApply {
+  static constexpr int CB = B / 128;          // 32-wide column blocks per wave
+  static constexpr int KS = B / 16;           // MFMA K steps
+  static constexpr int STAGE = kTT * B;       // elements of one tile
+  static constexpr int LPW = STAGE * 2 / 1024 / 4;  // 1 KB tile loads per wave
+  static constexpr int CPT = STAGE / 8 / kNT; // 16-byte output chunks per thread
+
+  const bf16_t* X;
+  bf16_t* Y;
+  int64_t d, col0;
+  int t_begin, t_end, ntiles;
+  int tid, lane, wave, nw;
+  bf16x8_t bfr[CB][KS];
+
+  // Issues the LDS-bound loads of token tile `tile` into ring slot `dst`.
+  __device__ __forceinline__ void load_tile(int tile, bf16_t* dst) {
+    const int t0 = t_begin + tile * kTT;
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int Q = wave * LPW + q;            // 1 KB piece of the tile
+      const int e = Q * 512 + lane * 8;        // element this lane lands on
+      const int row = e / B, pch = (e % B) >> 3;
+      const int lch = pch ^ (row & 15);
+      const int grow = min(t0 + row, t_end - 1);  // rows past the end read a valid row
+      dma16(X + (int64_t)grow * d + col0 + lch * 8, dst + Q * 512);
+    }
+  }
+
+  template <int S>
+  __device__ __forceinline__ void tile(int t) {
+    bf16_t* st = ring<S>();
+    // tile t is in LDS once at most (tiles issued after it) x LPW loads are pending
+    if (t + 2 < ntiles) wait_vm<2 * LPW>();
+    else if (t + 1 < ntiles) wait_vm<LPW>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's part of tile t landed; slot of t-1 free
+    if (t + 3 < ntiles) load_tile(t + 3, ring<(S + 3) & 3>());
+
+    floatx16 acc[2][CB];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
+    bf16x8_t af[2][2];
+    auto rd = [&](int ks, bf16x8_t* a) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        a[r] = *reinterpret_cast<const bf16x8_t*>(st + sw<B>(32 * r + (lane & 31), 16 * ks + 8 * (lane >> 5)));
+    };
+    rd(0, af[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) rd(ks + 1, af[(ks + 1) & 1]);
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+          acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][r], bfr[j][ks], acc[r][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_barrier();  // all waves done reading slot S
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        const int n = nw + 32 * j + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = 32 * r + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+          st[sw<B>(m, n)] = f32_to_bf16(acc[r][j][e]);
+        }
+      }
+    __syncthreads();  // output tile staged
+    const int t0 = t_begin + t * kTT;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = tid + q * kNT;
+      const int row = c / (B / 8), ch = c % (B / 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(st + sw<B>(row, ch * 8));
+      if (t0 + row < t_end) *reinterpret_cast<uint4*>(Y + (int64_t)(t0 + row) * d + col0 + ch * 8) = v;
+    }
+  }
+};
+
+template <int B, bool TRANS>
+__global__ void __launch_bounds__(kNT)
+blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
+                  bf16_t* __restrict__ Y, int tokens, int64_t d, int nb, int tok_per_wg) {
+  typedef BlockApply<B, TRANS> K;
+  K k;
+  k.tid = threadIdx.x;
+  k.lane = k.tid & 63;
+  k.wave = k.tid >> 6;
+  const int blk = blockIdx.x % nb;
+  const int split = blockIdx.x / nb;
+  k.t_begin = split * tok_per_wg;
+  k.t_end = min(tokens, k.t_begin + tok_per_wg);
+  if (k.t_begin >= k.t_end) return;
+  k.X = X;
+  k.Y = Y;
+  k.d = d;
+  k.col0 = (int64_t)blk * B;
+  k.nw = k.wave * (B / 4);
+  k.ntiles = (k.t_end - k.t_begin + kTT - 1) / kTT;
+
+  // ---- M_k -> LDS (rows spread over the ring slots) -> register fragments
+  {
+    const bf16_t* Mk = Mb + (int64_t)blk * B * B;
+    constexpr int ROWS_PER_SLOT = kStage / B;
+    for (int c = k.tid; c < B * B / 8; c += kNT) {
+      const int row = c / (B / 8), ch = c % (B / 8);
+      bf16_t* slot = ring_rt(row / ROWS_PER_SLOT);
+      *reinterpret_cast<uint4*>(slot + sw<B>(row % ROWS_PER_SLOT, ch * 8)) =
+          *reinterpret_cast<const uint4*>(Mk + (int64_t)row * B + ch * 8);
+    }
+    __syncthreads();
+    const int lane = k.lane;
+#pragma unroll
+    for (int j = 0; j < K::CB; ++j)
+#pragma unroll
+      for (int ks = 0; ks < K::KS; ++ks) {
+        if (TRANS) {  // B(n, k) = M[n][k]: 8 consecutive k of row n
+          const int n = k.nw + 32 * j + (lane & 31);
+          const int kk = 16 * ks + 8 * (lane >> 5);
+          k.bfr[j][ks] = *reinterpret_cast<const bf16x8_t*>(ring_rt(n / ROWS_PER_SLOT) +
+                                                            sw<B>(n % ROWS_PER_SLOT, kk));
+        } else {      // B(n, k) = M[k][n]: two transposing reads of 4 k each
+          const int g = lane >> 4, i = lane & 15;
+          const int n = k.nw + 32 * j + 16 * (g & 1) + 4 * (i & 3);
+          short4_t h[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int kk = 16 * ks + 8 * (g >> 1) + 4 * hh + (i >> 2);
+            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4*)(ring_rt(kk / ROWS_PER_SLOT) + sw<B>(kk % ROWS_PER_SLOT, n)));
+          }
+          union { short4_t s[2]; bf16x8_t v; } u;
+          u.s[0] = h[0];
+          u.s[1] = h[1];
+          k.bfr[j][ks] = u.v;
+        }
+      }
+    __syncthreads();  // the ring is reused for token tiles from here on
+  }
+
+  const int nt = k.ntiles;
+  k.load_tile(0, ring<0>());
+  if (nt > 1) k.load_tile(1, ring<1>());
+  if (nt > 2) k.load_tile(2, ring<2>());
+  int t = 0;
+  for (; t + 4 <= nt; t += 4) {
+    k.template tile<0>(t);
+    k.template tile<1>(t + 1);
+    k.template tile<2>(t + 2);
+    k.template tile<3>(t + 3);
+  }
+  if (t < nt) k.template tile<0>(t++);
+  if (t < nt) k.template tile<1>(t++);
+  if (t < nt) k.template tile<2>(t++);
+}
+
+template <int B, bool TRANS>
+hipError_t launch_b(const bf16_t* X, const bf16_t* M, bf16_t* Y, int64_t tokens, int64_t d,
+                    hipStream_t s) {
+  const int nb = (int)(d / B);
+  // one round of at most 256 workgroups (one per CU), token ranges in whole tiles
+  int splits = 256 / nb;
+  const int max_splits = (int)((tokens + kTT - 1) / kTT);
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int per = (int)((tokens + splits - 1) / splits);
+  per = (per + kTT - 1) / kTT * kTT;
+  splits = (int)((tokens + per - 1) / per);
+  hipLaunchKernelGGL((blockapply_kernel<B, TRANS>), dim3(nb * splits), dim3(kNT), 0, s, X, M, Y,
+                     (int)tokens, d, nb, per);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool blockapply_supported(DType t, int64_t d, int b) {
+  return t == DType::BF16 && (b == 128 || b == 256) && d % b == 0;
+}
+
+hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,
+                             bool transpose, hipStream_t s) {
+  const bf16_t* x = static_cast<const bf16_t*>(X);
+  const bf16_t* m = static_cast<const bf16_t*>(M);
+  bf16_t* y = static_cast<bf16_t*>(Y);
+  if (b == 256) return transpose ? launch_b<256, true>(x, m, y, tokens, d, s)
+                                 : launch_b<256, false>(x, m, y, tokens, d, s);
+  return transpose ? launch_b<128, true>(x, m, y, tokens, d, s)
+                   : launch_b<128, false>(x, m, y, tokens, d, s);
+}
+
+}  // namespace poetx

@@ -88,31 +88,49 @@ struct TileLoader {
 
   uint4 r[REGS];
 
+  // MN-major items run k-chunk fastest across lanes: the 8 lanes that store
+  // one row's 8 chunks then cover all banks (conflict-free transposed stores),
+  // and each global load instruction still reads whole 128-byte lines.
+  __device__ static void item_pos(int item, int& a, int& b) {
+    if (KMAJ) { a = item / (BK / VEC); b = item % (BK / VEC); }  // row, chunk
+    else { a = item / (BK / VEC); b = item % (BK / VEC); }       // row block, k block
+  }
+
   // base points at element (row 0, k 0) of this batch; rows/k are global
-  // indices. Rows >= rext or k >= kend read as zero.
+  // indices. Rows >= rext or k >= kend read as zero. Tiles that lie wholly
+  // inside the operand take a path without per-vector bounds tests.
   __device__ __forceinline__ void load(const TIn* __restrict__ base, int64_t ld, int r0, int rext,
                                        int k0, int kend, int tid) {
+    const bool full = (r0 + ROWS <= rext) && (k0 + BK <= kend);
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int item = tid + i * NT;
+      int ia, ib;
+      item_pos(item, ia, ib);
+      const bool live = EXACT || item < ITEMS;
       if (KMAJ) {
-        const int row = item / (BK / VEC);
-        const int kc = (item % (BK / VEC)) * VEC;
-        const int gr = r0 + row, gk = k0 + kc;
+        const int gr = r0 + ia, gk = k0 + ib * VEC;
+        const TIn* src = base + (int64_t)gr * ld + gk;
         uint4 v = make_uint4(0, 0, 0, 0);
-        if ((EXACT || item < ITEMS) && gr < rext && gk < kend)
-          v = *reinterpret_cast<const uint4*>(base + (int64_t)gr * ld + gk);
+        if (full) {
+          if (live) v = *reinterpret_cast<const uint4*>(src);
+        } else if (live && gr < rext && gk < kend) {
+          v = *reinterpret_cast<const uint4*>(src);
+        }
         r[i] = v;
       } else {
-        const int kb = item / (ROWS / VEC);
-        const int rb = item % (ROWS / VEC);
-        const int gr = r0 + rb * VEC;
-        const bool rows_ok = (EXACT || item < ITEMS) && gr < rext;
+        const int gr = r0 + ia * VEC;
+        const bool rows_ok = live && gr < rext;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const int gk = k0 + kb * VEC + e;
+          const int gk = k0 + ib * VEC + e;
+          const TIn* src = base + (int64_t)gk * ld + gr;
           uint4 v = make_uint4(0, 0, 0, 0);
-          if (rows_ok && gk < kend) v = *reinterpret_cast<const uint4*>(base + (int64_t)gk * ld + gr);
+          if (full) {
+            if (live) v = *reinterpret_cast<const uint4*>(src);
+          } else if (rows_ok && gk < kend) {
+            v = *reinterpret_cast<const uint4*>(src);
+          }
           r[i * VEC + e] = v;
         }
       }
@@ -124,16 +142,14 @@ struct TileLoader {
     for (int i = 0; i < PER_THREAD; ++i) {
       const int item = tid + i * NT;
       if (!EXACT && item >= ITEMS) continue;
+      int ia, ib;
+      item_pos(item, ia, ib);
       if (KMAJ) {
-        const int row = item / (BK / VEC);
-        const int kc = item % (BK / VEC);
-        *reinterpret_cast<uint4*>(s + L::chunk_off(row, kc)) = r[i];
+        *reinterpret_cast<uint4*>(s + L::chunk_off(ia, ib)) = r[i];
       } else {
-        const int kb = item / (ROWS / VEC);
-        const int rb = item % (ROWS / VEC);
 #pragma unroll
         for (int c = 0; c < VEC; ++c)
-          *reinterpret_cast<uint4*>(s + L::chunk_off(rb * VEC + c, kb)) =
+          *reinterpret_cast<uint4*>(s + L::chunk_off(ia * VEC + c, ib)) =
               Transpose<TIn>::column(&r[i * VEC], c);
       }
     }
@@ -217,7 +233,17 @@ gemm_kernel(const GemmParams p) {
   static_assert(TM % MI == 0 && TN % MI == 0, "wave tile must be a multiple of the MFMA tile");
   static_assert(BK % Op::KSTEP == 0, "bad K tile");
 
-  __shared__ __attribute__((aligned(16))) TIn smem[2 * STAGE];
+  // The output tile is staged through LDS (rows padded by 16 bytes) and
+  // written with 16-byte stores; float32 outputs of the 256 x 256 tile do not
+  // fit and are stored directly from the accumulators.
+  constexpr int CPAD = 16 / sizeof(TOut);
+  constexpr int CLD = BN + CPAD;
+  constexpr size_t RING_BYTES = sizeof(TIn) * 2 * STAGE;
+  constexpr size_t C_BYTES = sizeof(TOut) * BM * CLD;
+  constexpr bool LDS_EPI = C_BYTES <= 144 * 1024;
+  constexpr size_t SMEM_BYTES = (LDS_EPI && C_BYTES > RING_BYTES) ? C_BYTES : RING_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem_raw[SMEM_BYTES];
+  TIn* smem = reinterpret_cast<TIn*>(smem_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -255,58 +281,122 @@ gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int e = 0; e < Op::NACC; ++e) acc[i][j][e] = 0.0f;
 
+  // Software pipeline over K tiles: while the MFMAs consume tile t from one
+  // LDS buffer, the registers holding tile t+1 are written to the other
+  // buffer (free since the previous barrier) and the global loads of tile
+  // t+2 are issued into the same registers. One barrier per tile.
+  constexpr int NK = BK / Op::KSTEP;
+  static_assert(NK >= 2, "the pipeline needs at least two MFMA steps per K tile");
   if (ntiles > 0) {
     la.load(A, p.lda, m0, Mx, kbeg, kend, tid);
     lb.load(B, p.ldb, n0, Nx, kbeg, kend, tid);
     la.store(smem, tid);
     lb.store(smem + BM * BK, tid);
+    if (ntiles > 1) {
+      la.load(A, p.lda, m0, Mx, kbeg + BK, kend, tid);
+      lb.load(B, p.ldb, n0, Nx, kbeg + BK, kend, tid);
+    }
     __syncthreads();
   }
 
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
-    const bool more = (t + 1) < ntiles;
-    if (more) {
-      const int k0 = kbeg + (t + 1) * BK;
-      la.load(A, p.lda, m0, Mx, k0, kend, tid);
-      lb.load(B, p.ldb, n0, Nx, k0, kend, tid);
-    }
     const TIn* As = smem + cur * STAGE;
     const TIn* Bs = As + BM * BK;
+    TIn* nxt = smem + (cur ^ 1) * STAGE;
+    typename Op::Frag af[2][FM], bfr[2][FN];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += Op::KSTEP) {
-      typename Op::Frag af[FM], bfr[FN];
+    for (int i = 0; i < FM; ++i) af[0][i] = Op::template load<BK>(As, wm * TM + i * MI, 0, lane);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = Op::template load<BK>(As, wm * TM + i * MI, kk, lane);
+    for (int j = 0; j < FN; ++j) bfr[0][j] = Op::template load<BK>(Bs, wn * TN + j * MI, 0, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = Op::template load<BK>(Bs, wn * TN + j * MI, kk, lane);
+    for (int s = 0; s < NK; ++s) {
+      const int fb = s & 1;
+      if (s + 1 < NK) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          af[fb ^ 1][i] = Op::template load<BK>(As, wm * TM + i * MI, (s + 1) * Op::KSTEP, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[fb ^ 1][j] = Op::template load<BK>(Bs, wn * TN + j * MI, (s + 1) * Op::KSTEP, lane);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = Op::mma(af[i], bfr[j], acc[i][j]);
-    }
-    if (more) {
-      TIn* nxt = smem + (cur ^ 1) * STAGE;
-      la.store(nxt, tid);
-      lb.store(nxt + BM * BK, tid);
+        for (int j = 0; j < FN; ++j) acc[i][j] = Op::mma(af[fb][i], bfr[fb][j], acc[i][j]);
+      if (s == 0 && t + 1 < ntiles) {
+        la.store(nxt, tid);
+        lb.store(nxt + BM * BK, tid);
+      }
+      if (s == 1 && t + 2 < ntiles) {
+        const int k0 = kbeg + (t + 2) * BK;
+        la.load(A, p.lda, m0, Mx, k0, kend, tid);
+        lb.load(B, p.ldb, n0, Nx, k0, kend, tid);
+      }
     }
     __syncthreads();
   }
 
   TOut* C = static_cast<TOut*>(p.C) + (int64_t)bt * p.sC + (int64_t)blockIdx.z * p.sC_split;
   const TOut* D = p.D ? static_cast<const TOut*>(p.D) + (int64_t)bt * p.sD : nullptr;
+  if constexpr (LDS_EPI) {
+    // accumulators -> LDS tile (row-major, padded) -> 16-byte row segments,
+    // with alpha and beta * D applied on the way out
+    TOut* cs = reinterpret_cast<TOut*>(smem_raw);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * TN + j * MI + (lane % MI);
+      for (int j = 0; j < FN; ++j) {
+        const int n = wn * TN + j * MI + (lane % MI);
 #pragma unroll
-      for (int e = 0; e < Op::NACC; ++e) {
-        const int m = m0 + wm * TM + i * MI + Op::out_row(e, lane);
-        if (m < Mx && n < Nx) {
-          float v = p.alpha * acc[i][j][e];
-          if (D) v += p.beta * ElemTraits<TOut>::to_f32(D[(int64_t)m * p.ldd + n]);
-          store_as<TOut>(C + (int64_t)m * p.ldc + n, v);
+        for (int e = 0; e < Op::NACC; ++e) {
+          const int m = wm * TM + i * MI + Op::out_row(e, lane);
+          cs[m * CLD + n] = ElemTraits<TOut>::from_f32(acc[i][j][e]);
+        }
+      }
+    __syncthreads();
+    constexpr int V = ElemTraits<TOut>::kVec;
+    constexpr int CHUNKS = BM * BN / V;
+    const bool vec_ok = (Nx - n0 >= BN) || ((Nx % V) == 0);
+#pragma unroll 1
+    for (int c = tid; c < CHUNKS; c += NT) {
+      const int ml = c / (BN / V), nl = (c % (BN / V)) * V;
+      const int m = m0 + ml, n = n0 + nl;
+      if (m >= Mx || n >= Nx) continue;
+      union { uint4 u; TOut e[V]; } v;
+      v.u = *reinterpret_cast<const uint4*>(cs + ml * CLD + nl);
+      const bool whole = vec_ok && n + V <= Nx;
+      if (p.alpha != 1.0f || D) {
+#pragma unroll
+        for (int t = 0; t < V; ++t) {
+          float f = p.alpha * ElemTraits<TOut>::to_f32(v.e[t]);
+          if (D && n + t < Nx) f += p.beta * ElemTraits<TOut>::to_f32(D[(int64_t)m * p.ldd + n + t]);
+          v.e[t] = ElemTraits<TOut>::from_f32(f);
+        }
+      }
+      TOut* dst = C + (int64_t)m * p.ldc + n;
+      if (whole) {
+        *reinterpret_cast<uint4*>(dst) = v.u;
+      } else {
+#pragma unroll
+        for (int t = 0; t < V; ++t)
+          if (n + t < Nx) dst[t] = v.e[t];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * TN + j * MI + (lane % MI);
+#pragma unroll
+        for (int e = 0; e < Op::NACC; ++e) {
+          const int m = m0 + wm * TM + i * MI + Op::out_row(e, lane);
+          if (m < Mx && n < Nx) {
+            float v = p.alpha * acc[i][j][e];
+            if (D) v += p.beta * ElemTraits<TOut>::to_f32(D[(int64_t)m * p.ldd + n]);
+            store_as<TOut>(C + (int64_t)m * p.ldc + n, v);
+          }
         }
       }
     }

@@ -43,6 +43,13 @@ hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor,
 int gemm_k_tile(DType in);
 int gemm_tile_m(DType in, int M, int N);
 
+// ---- streaming block-diagonal apply (bf16, b = 128 or 256, b | d) ----
+// Y[:, blk] = X[:, blk] M_blk^T (transpose) or X[:, blk] M_blk, token-major
+// with row stride d.
+bool blockapply_supported(DType t, int64_t d, int b);
+hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,
+                             bool transpose, hipStream_t s);
+
 // ---- Cayley build (exact Cayley map by blocked Gauss-Jordan) ----
 // Panel width used for block size b.
 int cayley_panel_width(int b);
