@@ -69,7 +69,17 @@ struct SplitK {
 // Splits the token reduction of a gram so the launch fills the chip (about
 // 256 workgroups of the 256 x 256 tile, 1024 of the smaller ones), with at
 // least 256 tokens per split.
-SplitK choose_split(int64_t nblocks, int b, int64_t tokens, DType in) {
+SplitK choose_split(int64_t nblocks, int b, int64_t d, int64_t tokens, DType in) {
+  if (poetx::blockgram_supported(in, d, b)) {
+    // streaming gram: one round of about 256 workgroups
+    int64_t s = std::max<int64_t>(1, 256 / nblocks);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, tokens / 256));
+    const int64_t chunk = ceil_div(ceil_div(tokens, s), 64) * 64;
+    SplitK r;
+    r.kchunk = (int)chunk;
+    r.nsplit = (int)ceil_div(tokens, chunk);
+    return r;
+  }
   const int mt = poetx::gemm_tile_m(in, b, b);
   const int kt = poetx::gemm_k_tile(in);
   const int64_t tiles = nblocks * ceil_div(b, mt) * ceil_div(b, mt);
@@ -92,8 +102,8 @@ BwdPlan plan_bwd(const poetx_linear_desc* d) {
   const DType in = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
   const int64_t nbR = ceil_div(d->d_out, d->b_out), nbP = ceil_div(d->d_in, d->b_in);
   const size_t bbR = (size_t)d->b_out * d->b_out * 4, bbP = (size_t)d->b_in * d->b_in * 4;
-  p.sR = choose_split(nbR, d->b_out, d->tokens, in);
-  p.sP = choose_split(nbP, d->b_in, d->tokens, in);
+  p.sR = choose_split(nbR, d->b_out, d->d_out, d->tokens, in);
+  p.sP = choose_split(nbP, d->b_in, d->d_in, d->tokens, in);
   size_t off = 0;
   p.gz = off; off += align_up((size_t)d->tokens * d->d_out * act_size(d->act));
   p.gu = off; off += align_up((size_t)d->tokens * d->d_in * act_size(d->act));
@@ -168,6 +178,16 @@ GemmParams gram_params(const void* a, const void* c, float* part, int64_t tokens
   g.kchunk = sk.kchunk;
   g.sC_split = nb * (int64_t)b * b;
   return g;
+}
+
+// part[s][blk] = a[:, blk]^T c[:, blk] over split s, on the streaming kernel
+// when it supports the shape, else on the batched split-K GEMM.
+hipError_t block_gram(DType t, const void* a, const void* c, float* part, int64_t tokens, int64_t d,
+                      int b, SplitK sk, hipStream_t s) {
+  if (poetx::blockgram_supported(t, d, b))
+    return poetx::launch_blockgram(a, c, part, tokens, d, b, sk.nsplit, sk.kchunk, s);
+  GemmParams g = gram_params(a, c, part, tokens, d, b, sk);
+  return poetx::launch_gemm(t, DType::F32, false, false, g, s);
 }
 
 // Cayley VJP of every block: M = 1/2 (R^T + I) G (R^T + I), packed as
@@ -382,8 +402,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B2: G_R[k] = g_Y[:, k]^T Z[:, k], split over tokens, then reduced
   POETX_TRY(sg.begin(1));
-  GemmParams g = gram_params(g_y, z_saved, partR, N, m, bR, plan.sR);
-  POETX_TRY(poetx::launch_gemm(t, DType::F32, false, false, g, s));
+  POETX_TRY(block_gram(t, g_y, z_saved, partR, N, m, bR, plan.sR, s));
   POETX_TRY(poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, s));
   POETX_TRY(sg.end(1));
 
@@ -400,8 +419,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B4: G_P[j] = g_U[:, j]^T X[:, j]
   POETX_TRY(sg.begin(3));
-  g = gram_params(gU, x, partP, N, n, bP, plan.sP);
-  POETX_TRY(poetx::launch_gemm(t, DType::F32, false, false, g, s));
+  POETX_TRY(block_gram(t, gU, x, partP, N, n, bP, plan.sP, s));
   POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, s));
   POETX_TRY(sg.end(3));
 
