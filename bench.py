@@ -64,16 +64,22 @@ def cpu_baseline(spec, sample_tokens):
         threads = os.cpu_count()
     L = make_layer(spec)
     x, g_y = L.x[:sample_tokens], L.g_y[:sample_tokens]
-    t0 = time.perf_counter()
-    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b)
-    ora.forward(x)
-    ora.backward(g_y, x)
-    dt = time.perf_counter() - t0
-    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(threads),
+    # repeat the whole oracle step until about 10 s of CPU work (at most 6 reps)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b)
+        ora.forward(x)
+        ora.backward(g_y, x)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 6:
+            break
+    return {"value": reps * sample_tokens / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"float64 oracle step (exact Cayley solves, block-local materialisation of "
-                      f"R W0 P, forward, backward) on the first {sample_tokens} of {spec.tokens} "
-                      f"tokens of {spec.name} {spec.d_out}x{spec.d_in} b={spec.b}; {dt:.1f} s"}
+            "sample": f"{reps} float64 oracle steps (exact Cayley solves, block-local "
+                      f"materialisation of R W0 P, forward, backward) on the first "
+                      f"{sample_tokens} of {spec.tokens} tokens of {spec.name} "
+                      f"{spec.d_out}x{spec.d_in} b={spec.b}; {dt:.1f} s"}
 
 
 def parity_sample(L, out, lay, rows=32):
@@ -96,6 +102,47 @@ def parity_sample(L, out, lay, rows=32):
             "rows": rows}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense_fwd_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "orthogonal_equivalence_amd", "csrc", f)
+                  for f in ("gemm.hip", "common.h", "kernels.h")]
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dense forward GEMM from the committed
+    FETCH_SIZE / WRITE_SIZE counter passes, if they were taken on the current
+    kernel sources (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha256") != sources_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_calibration(nbytes=1 << 30):
+    """A plain device copy of known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters: reads nbytes and writes nbytes."""
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,7 +152,12 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=8192,
                     help="tokens of the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -209,7 +261,7 @@ def main():
     peak = PEAK_BF16 if sb.dtype == "bf16" else PEAK_F32
     achieved = dense_flops / (dense_ms / 1e3)
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None,
+                "frac": achieved / peak, "traffic": measured_traffic(),
                 "kernel": "dense_fwd: Z = U W0^T (gemm_kernel bf16, NT)",
                 "flops_per_launch": dense_flops, "avg_launch_ms": dense_ms}
 
