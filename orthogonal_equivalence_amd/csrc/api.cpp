@@ -190,30 +190,66 @@ hipError_t block_gram(DType t, const void* a, const void* c, float* part, int64_
   return poetx::launch_gemm(t, DType::F32, false, false, g, s);
 }
 
-// Cayley VJP of every block: M = 1/2 (R^T + I) G (R^T + I), packed as
-// g_theta(i, j) = M[i][j] - M[j][i].
-hipError_t cayley_vjp(const float* G, const float* R, float* T, float* M, float* g_theta,
-                      int64_t d, int b, hipStream_t s) {
-  const int64_t nb = ceil_div(d, b);
-  const int last = (int)(d - (nb - 1) * b);
+// A dense W0 product C[M][N] = A[M][K] B(n, k) (B(n, k) = B[n][k] when
+// b_kmajor, else B[k][n]): the persistent direct-to-LDS bf16 kernel when the
+// shape allows it, else the general GEMM.
+hipError_t dense(DType t, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                 int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s) {
+  if (t == DType::BF16 && poetx::dense_supported(M, N, K, lda, ldb, ldc))
+    return poetx::launch_dense(A, B, C, M, N, K, lda, ldb, ldc, b_kmajor, s);
   GemmParams g;
-  // T = G R^T + G
-  g.A = G; g.lda = b; g.sA = (int64_t)b * b;
-  g.B = R; g.ldb = b; g.sB = (int64_t)b * b;
-  g.C = T; g.ldc = b; g.sC = (int64_t)b * b;
-  g.D = G; g.ldd = b; g.sD = (int64_t)b * b;
+  g.A = A; g.lda = lda;
+  g.B = B; g.ldb = ldb;
+  g.C = C; g.ldc = ldc;
+  g.M = g.M_last = (int)M; g.N = g.N_last = (int)N; g.K = g.K_last = (int)K;
+  g.kchunk = (int)K;
+  return poetx::launch_gemm(t, t, true, b_kmajor, g, s);
+}
+
+// Cayley VJP of every block: M = 1/2 (R^T + I) G (R^T + I), packed as
+// g_theta(i, j) = M[i][j] - M[j][i]. Computed as S = R G^T + G^T (= T^T for
+// T = G (R^T + I)) and M^T = 1/2 (S R + S), so only one operand of one
+// product is read transposed; the pack then flips the sign. When a second
+// block set of the same size is given (R2/G2 ...), both run in the same
+// launches.
+struct VjpSet {
+  const float* G;
+  const float* R;
+  float* S;
+  float* M;
+  float* g_theta;
+  int64_t d;
+};
+hipError_t cayley_vjp(const VjpSet& a, const VjpSet* b2, int b, hipStream_t s) {
+  const int64_t nb1 = ceil_div(a.d, b);
+  const int64_t nb2 = b2 ? ceil_div(b2->d, b) : 0;
+  const int64_t bb = (int64_t)b * b;
+  GemmParams g;
+  // S = R G^T + G^T: A = R (K-major), B(n, k) = G[n][k], addend G transposed
+  g.A = a.R; g.lda = b; g.sA = bb;
+  g.B = a.G; g.ldb = b; g.sB = bb;
+  g.C = a.S; g.ldc = b; g.sC = bb;
+  g.D = a.G; g.ldd = b; g.sD = bb; g.d_trans = true;
   g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = b;
-  g.batch = (int)nb;
+  g.batch = (int)(nb1 + nb2);
   g.kchunk = b;
   g.alpha = 1.0f; g.beta = 1.0f;
+  if (b2) {
+    g.batch_split = (int)nb1;
+    g.A2 = b2->R; g.B2 = b2->G; g.C2 = b2->S; g.D2 = b2->G;
+  }
   hipError_t e = poetx::launch_gemm(DType::F32, DType::F32, true, true, g, s);
   if (e != hipSuccess) return e;
-  // M = 1/2 (R^T T + T): A(m, k) = R[k][m], B(n, k) = T[k][n]
-  g.A = R; g.B = T; g.C = M; g.D = T;
+  // M^T = 1/2 (S R + S): A = S (K-major), B(n, k) = R[k][n]
+  g.A = a.S; g.B = a.R; g.C = a.M; g.D = a.S; g.d_trans = false;
   g.alpha = 0.5f; g.beta = 0.5f;
-  e = poetx::launch_gemm(DType::F32, DType::F32, false, false, g, s);
+  if (b2) { g.A2 = b2->S; g.B2 = b2->R; g.C2 = b2->M; g.D2 = b2->S; }
+  e = poetx::launch_gemm(DType::F32, DType::F32, true, false, g, s);
   if (e != hipSuccess) return e;
-  return poetx::launch_pack_skew_grad(M, nb, b, last, g_theta, s);
+  e = poetx::launch_pack_skew_grad(a.M, nb1, b, (int)(a.d - (nb1 - 1) * b), -1.0f, a.g_theta, s);
+  if (e != hipSuccess || !b2) return e;
+  return poetx::launch_pack_skew_grad(b2->M, nb2, b, (int)(b2->d - (nb2 - 1) * b), -1.0f,
+                                      b2->g_theta, s);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? POETX_OK : POETX_ERR_HIP; }
@@ -312,7 +348,6 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   const DType t = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
   void* U = static_cast<char*>(ws) + plan.u_off;
   Stages sg{d, s};
-  bool bk;
   hipError_t e;
 
   // S2: U = X blockdiag(P)^T
@@ -322,13 +357,7 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
 
   // S3: Z = U W0^T
   if ((e = sg.begin(1)) != hipSuccess) return hip_status(e);
-  GemmParams dg;
-  dg.A = U; dg.lda = n;
-  dg.B = W0; dg.ldb = n;
-  dg.C = z_save; dg.ldc = m;
-  dg.M = dg.M_last = (int)N; dg.N = dg.N_last = (int)m; dg.K = dg.K_last = (int)n;
-  dg.kchunk = (int)n;
-  if ((e = poetx::launch_gemm(t, t, true, true, dg, s)) != hipSuccess) return hip_status(e);
+  if ((e = dense(t, U, W0, z_save, N, m, n, n, n, m, true, s)) != hipSuccess) return hip_status(e);
   if ((e = sg.end(1)) != hipSuccess) return hip_status(e);
 
   // S4: Y = Z blockdiag(R)^T
@@ -388,7 +417,6 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   float* MP = reinterpret_cast<float*>(w + plan.MP);
   const int lastR = (int)(m - (nbR - 1) * bR), lastP = (int)(n - (nbP - 1) * bP);
   Stages sg{d, s};
-  bool bk;
   hipError_t e;
 #define POETX_TRY(call)                            \
   do {                                             \
@@ -408,13 +436,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B3: g_U = g_Z W0   (B(n, k) = W0[k][n])
   POETX_TRY(sg.begin(2));
-  GemmParams dg;
-  dg.A = gZ; dg.lda = m;
-  dg.B = W0; dg.ldb = n;
-  dg.C = gU; dg.ldc = n;
-  dg.M = dg.M_last = (int)N; dg.N = dg.N_last = (int)n; dg.K = dg.K_last = (int)m;
-  dg.kchunk = (int)m;
-  POETX_TRY(poetx::launch_gemm(t, t, true, false, dg, s));
+  POETX_TRY(dense(t, gZ, W0, gU, N, n, m, m, n, n, false, s));
   POETX_TRY(sg.end(2));
 
   // B4: G_P[j] = g_U[:, j]^T X[:, j]
@@ -428,12 +450,19 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   POETX_TRY(block_apply(t, gU, P_act, g_x, N, n, bP, false, s));
   POETX_TRY(sg.end(4));
 
-  // B6: Cayley VJP of R and of P
+  // B6: Cayley VJP of R and of P (one set of launches when b_in == b_out;
+  // stage 6 is then empty)
+  const VjpSet vR{GR, R_f32, TR, MR, g_theta_R, m};
+  const VjpSet vP{GP, P_f32, TP, MP, g_theta_P, n};
   POETX_TRY(sg.begin(5));
-  if (bR > 1) POETX_TRY(cayley_vjp(GR, R_f32, TR, MR, g_theta_R, m, bR, s));
+  if (bR == bP && bR > 1) {
+    POETX_TRY(cayley_vjp(vR, &vP, bR, s));
+  } else if (bR > 1) {
+    POETX_TRY(cayley_vjp(vR, nullptr, bR, s));
+  }
   POETX_TRY(sg.end(5));
   POETX_TRY(sg.begin(6));
-  if (bP > 1) POETX_TRY(cayley_vjp(GP, P_f32, TP, MP, g_theta_P, n, bP, s));
+  if (bR != bP && bP > 1) POETX_TRY(cayley_vjp(vP, nullptr, bP, s));
   POETX_TRY(sg.end(6));
 #undef POETX_TRY
   return POETX_OK;

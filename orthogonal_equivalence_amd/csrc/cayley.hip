@@ -328,7 +328,7 @@ split_reduce_kernel(const float* __restrict__ part, int nsplit, int nblocks, int
 // grid (ceil(b*b / kNT), nblocks)
 __global__ void __launch_bounds__(kNT)
 pack_skew_grad_kernel(const float* __restrict__ M, int nblocks, int b, int last_valid,
-                      float* __restrict__ g) {
+                      float sign, float* __restrict__ g) {
   const int ij = blockIdx.x * kNT + threadIdx.x;
   if (ij >= b * b) return;
   const int i = ij / b, j = ij - (ij / b) * b;
@@ -336,7 +336,7 @@ pack_skew_grad_kernel(const float* __restrict__ M, int nblocks, int b, int last_
   const int blk = blockIdx.y;
   const int r = (blk == nblocks - 1) ? last_valid : b;
   const float* Mb = M + (int64_t)blk * b * b;
-  const float v = (j < r) ? Mb[(int64_t)i * b + j] - Mb[(int64_t)j * b + i] : 0.0f;
+  const float v = (j < r) ? sign * (Mb[(int64_t)i * b + j] - Mb[(int64_t)j * b + i]) : 0.0f;
   g[(int64_t)blk * (b * (b - 1) / 2) + packed_index(b, i, j)] = v;
 }
 
@@ -387,9 +387,9 @@ hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, i
 }
 
 hipError_t launch_pack_skew_grad(const float* M, int64_t nblocks, int b, int last_valid,
-                                 float* g_theta, hipStream_t stream) {
+                                 float sign, float* g_theta, hipStream_t stream) {
   hipLaunchKernelGGL(pack_skew_grad_kernel, dim3((b * b + kNT - 1) / kNT, (int)nblocks), dim3(kNT),
-                     0, stream, M, (int)nblocks, b, last_valid, g_theta);
+                     0, stream, M, (int)nblocks, b, last_valid, sign, g_theta);
   return hipGetLastError();
 }
 

@@ -34,6 +34,29 @@ template <> struct ElemTraits<bf16_t> {
   __device__ static bf16_t from_f32(float v) { return f32_to_bf16(v); }
 };
 
+// Output tile (mt, nt) of this workgroup in a num_mt x num_nt grid.
+// Workgroups are dispatched round-robin over the 8 XCDs; the order is
+// remapped so each XCD works on a contiguous range of a grouped ordering
+// (GROUP_M row tiles at a time), which keeps the operand panels that
+// concurrently running tiles share in that XCD's L2.
+// The index form maps logical workgroup wg of nwg (a persistent workgroup
+// that walks wg, wg + G, ... with G a multiple of 8 stays on one XCD).
+__device__ __forceinline__ void xcd_grouped_tile_at(int wg, int nwg, int num_mt, int num_nt, int& mt,
+                                                    int& nt) {
+  constexpr int GROUP_M = 8;
+  if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
+  const int per_group = GROUP_M * num_nt;
+  const int group = wg / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(num_mt - first_m, GROUP_M);
+  const int in_group = wg - group * per_group;
+  mt = first_m + in_group % gsize;
+  nt = in_group / gsize;
+}
+__device__ __forceinline__ void xcd_grouped_tile(int num_mt, int num_nt, int& mt, int& nt) {
+  xcd_grouped_tile_at(blockIdx.x, gridDim.x, num_mt, num_nt, mt, nt);
+}
+
 // Store a float32 value as T.
 template <typename T>
 __device__ __forceinline__ void store_as(T* p, float v) { *p = ElemTraits<T>::from_f32(v); }

@@ -22,8 +22,8 @@
 //
 // Configurations: bf16 256x256x64 tiles, 2x2 waves of 128x128 with
 // v_mfma_f32_32x32x16_bf16 (large shapes); bf16 128x128x64 with
-// v_mfma_f32_16x16x32_bf16 (small shapes); float32 64x64x32 with
-// v_mfma_f32_16x16x4_f32. Accumulation is float32 throughout.
+// v_mfma_f32_16x16x32_bf16 (small shapes); float32 128x128x32 or 64x64x32
+// with v_mfma_f32_16x16x4_f32. Accumulation is float32 throughout.
 #include "common.h"
 #include "kernels.h"
 
@@ -205,22 +205,6 @@ template <> struct Mfma<float, 16> {
   __device__ static int out_row(int e, int lane) { return 4 * (lane >> 4) + e; }
 };
 
-// Logical tile of this workgroup: XCD-contiguous, then grouped by GROUP_M
-// row tiles.
-__device__ __forceinline__ void tile_coords(int num_mt, int num_nt, int& mt, int& nt) {
-  constexpr int GROUP_M = 8;
-  int wg = blockIdx.x;
-  const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) wg = (wg & 7) * (nwg >> 3) + (wg >> 3);
-  const int per_group = GROUP_M * num_nt;
-  const int group = wg / per_group;
-  const int first_m = group * GROUP_M;
-  const int gsize = min(num_mt - first_m, GROUP_M);
-  const int in_group = wg - group * per_group;
-  mt = first_m + in_group % gsize;
-  nt = in_group / gsize;
-}
-
 template <typename TIn, typename TOut, bool A_KMAJ, bool B_KMAJ, int BM, int BN, int BK, int WM,
           int WN, int MI>
 __global__ void __launch_bounds__(64 * WM * WN)
@@ -258,7 +242,7 @@ gemm_kernel(const GemmParams p) {
   const int num_mt = (p.M + BM - 1) / BM;
   const int num_nt = (p.N + BN - 1) / BN;
   int mt, nt;
-  tile_coords(num_mt, num_nt, mt, nt);
+  xcd_grouped_tile(num_mt, num_nt, mt, nt);
   const int m0 = mt * BM;
   const int n0 = nt * BN;
   if (m0 >= Mx || n0 >= Nx) return;  // whole workgroup: tile outside a ragged last batch
@@ -267,8 +251,10 @@ gemm_kernel(const GemmParams p) {
   const int kend = min(Kx, kbeg + p.kchunk);
   const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-  const TIn* A = static_cast<const TIn*>(p.A) + (int64_t)bt * p.sA;
-  const TIn* B = static_cast<const TIn*>(p.B) + (int64_t)bt * p.sB;
+  const bool seg2 = bt >= p.batch_split;
+  const int sb = seg2 ? bt - p.batch_split : bt;  // batch index within its segment
+  const TIn* A = static_cast<const TIn*>(seg2 ? p.A2 : p.A) + (int64_t)sb * p.sA;
+  const TIn* B = static_cast<const TIn*>(seg2 ? p.B2 : p.B) + (int64_t)sb * p.sB;
 
   TileLoader<TIn, BM, BK, NT, A_KMAJ> la;
   TileLoader<TIn, BN, BK, NT, B_KMAJ> lb;
@@ -337,8 +323,10 @@ gemm_kernel(const GemmParams p) {
     __syncthreads();
   }
 
-  TOut* C = static_cast<TOut*>(p.C) + (int64_t)bt * p.sC + (int64_t)blockIdx.z * p.sC_split;
-  const TOut* D = p.D ? static_cast<const TOut*>(p.D) + (int64_t)bt * p.sD : nullptr;
+  TOut* C = static_cast<TOut*>(seg2 ? p.C2 : p.C) + (int64_t)sb * p.sC +
+            (int64_t)blockIdx.z * p.sC_split;
+  const void* Dv = seg2 ? p.D2 : p.D;
+  const TOut* D = Dv ? static_cast<const TOut*>(Dv) + (int64_t)sb * p.sD : nullptr;
   if constexpr (LDS_EPI) {
     // accumulators -> LDS tile (row-major, padded) -> 16-byte row segments,
     // with alpha and beta * D applied on the way out
@@ -370,7 +358,10 @@ gemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int t = 0; t < V; ++t) {
           float f = p.alpha * ElemTraits<TOut>::to_f32(v.e[t]);
-          if (D && n + t < Nx) f += p.beta * ElemTraits<TOut>::to_f32(D[(int64_t)m * p.ldd + n + t]);
+          if (D && n + t < Nx) {
+            const int64_t di = p.d_trans ? (int64_t)(n + t) * p.ldd + m : (int64_t)m * p.ldd + n + t;
+            f += p.beta * ElemTraits<TOut>::to_f32(D[di]);
+          }
           v.e[t] = ElemTraits<TOut>::from_f32(f);
         }
       }
@@ -394,7 +385,10 @@ gemm_kernel(const GemmParams p) {
           const int m = m0 + wm * TM + i * MI + Op::out_row(e, lane);
           if (m < Mx && n < Nx) {
             float v = p.alpha * acc[i][j][e];
-            if (D) v += p.beta * ElemTraits<TOut>::to_f32(D[(int64_t)m * p.ldd + n]);
+            if (D) {
+              const int64_t di = p.d_trans ? (int64_t)n * p.ldd + m : (int64_t)m * p.ldd + n;
+              v += p.beta * ElemTraits<TOut>::to_f32(D[di]);
+            }
             store_as<TOut>(C + (int64_t)m * p.ldc + n, v);
           }
         }
@@ -405,6 +399,7 @@ gemm_kernel(const GemmParams p) {
 
 struct Big { static constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, MI = 32; };
 struct SmallBf16 { static constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2, MI = 16; };
+struct MidF32 { static constexpr int BM = 128, BN = 128, BK = 32, WM = 2, WN = 2, MI = 16; };
 struct SmallF32 { static constexpr int BM = 64, BN = 64, BK = 32, WM = 2, WN = 2, MI = 16; };
 
 template <typename TIn, typename TOut, bool AK, bool BK_, typename C>
@@ -427,6 +422,7 @@ hipError_t launch_layout(bool ak, bool bk, const GemmParams& p, hipStream_t stre
 }
 
 bool use_big(const GemmParams& p) { return p.M >= 256 && p.N >= 256; }
+bool use_mid_f32(const GemmParams& p) { return p.M >= 128 && p.N >= 128; }
 
 }  // namespace
 
@@ -434,7 +430,7 @@ int gemm_k_tile(DType in) { return in == DType::BF16 ? 64 : 32; }
 
 int gemm_tile_m(DType in, int M, int N) {
   if (in == DType::BF16) return (M >= 256 && N >= 256) ? 256 : 128;
-  return 64;
+  return (M >= 128 && N >= 128) ? 128 : 64;
 }
 
 hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor, const GemmParams& p,
@@ -448,7 +444,9 @@ hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor, const 
     return big ? launch_layout<bf16_t, float, Big>(a_kmajor, b_kmajor, p, stream)
                : launch_layout<bf16_t, float, SmallBf16>(a_kmajor, b_kmajor, p, stream);
   }
-  if (out == DType::F32) return launch_layout<float, float, SmallF32>(a_kmajor, b_kmajor, p, stream);
+  if (out == DType::F32)
+    return use_mid_f32(p) ? launch_layout<float, float, MidF32>(a_kmajor, b_kmajor, p, stream)
+                          : launch_layout<float, float, SmallF32>(a_kmajor, b_kmajor, p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -32,6 +32,14 @@ struct GemmParams {
   int kchunk = 0;       // K elements per split (multiple of the K tile)
   int64_t sC_split = 0; // output stride between splits (elements)
   float alpha = 1.0f, beta = 0.0f;
+  bool d_trans = false;  // D(m, n) = D[n*ldd + m] instead of D[m*ldd + n]
+  // Optional second segment: batches >= batch_split use A2/B2/C2/D2 (indexed
+  // from batch_split), so two block sets of equal shape share one launch.
+  int batch_split = 1 << 30;
+  const void* A2 = nullptr;
+  const void* B2 = nullptr;
+  void* C2 = nullptr;
+  const void* D2 = nullptr;
 };
 
 // Returns hipSuccess or the launch error.
@@ -42,6 +50,13 @@ hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor,
 // of it) and the M/N tile chosen for an M x N problem.
 int gemm_k_tile(DType in);
 int gemm_tile_m(DType in, int M, int N);
+
+// ---- dense bf16 GEMM with direct-to-LDS loads (the W0 products) ----
+// C[M][N] = A[M][K] B(n, k), B(n, k) = B[n*ldb + k] (b_kmajor) or
+// B[k*ldb + n]; bf16 in and out, float32 accumulation.
+bool dense_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc);
+hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s);
 
 // ---- streaming block-diagonal apply (bf16, b = 128 or 256, b | d) ----
 // Y[:, blk] = X[:, blk] M_blk^T (transpose) or X[:, blk] M_blk, token-major
@@ -71,9 +86,9 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
 // rows or columns >= last_valid are written as zero.
 hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, int b,
                                int last_valid, float* G, hipStream_t stream);
-// g_theta[blk][idx(i,j)] = M[blk][i][j] - M[blk][j][i] (i < j); zero for
-// entries of the last block at rows or columns >= last_valid.
+// g_theta[blk][idx(i,j)] = sign (M[blk][i][j] - M[blk][j][i]) (i < j); zero
+// for entries of the last block at rows or columns >= last_valid.
 hipError_t launch_pack_skew_grad(const float* M, int64_t nblocks, int b, int last_valid,
-                                 float* g_theta, hipStream_t stream);
+                                 float sign, float* g_theta, hipStream_t stream);
 
 }  // namespace poetx
