@@ -103,8 +103,10 @@ def parity_sample(L, out, lay, rows=32):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense_fwd_traffic.json")
+# sources of the dense forward kernel (dense_kernel in dense.hip); the
+# committed counter passes count only while these are unchanged
 KERNEL_SOURCES = [os.path.join(ROOT, "orthogonal_equivalence_amd", "csrc", f)
-                  for f in ("gemm.hip", "common.h", "kernels.h")]
+                  for f in ("dense.hip", "lds_dma.h", "common.h", "kernels.h")]
 
 
 def sources_digest():
@@ -262,7 +264,8 @@ def main():
     achieved = dense_flops / (dense_ms / 1e3)
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": measured_traffic(),
-                "kernel": "dense_fwd: Z = U W0^T (gemm_kernel bf16, NT)",
+                "kernel": "dense_fwd: Z = U W0^T (dense_kernel<true>: bf16, K-major W0, "
+                          "persistent, direct-to-LDS, 16x16x32 MFMA)",
                 "flops_per_launch": dense_flops, "avg_launch_ms": dense_ms}
 
     F = sum(layer_work(s)[0] for s, *_ in layers)

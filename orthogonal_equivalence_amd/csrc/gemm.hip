@@ -22,8 +22,8 @@
 //
 // Configurations: bf16 256x256x64 tiles, 2x2 waves of 128x128 with
 // v_mfma_f32_32x32x16_bf16 (large shapes); bf16 128x128x64 with
-// v_mfma_f32_16x16x32_bf16 (small shapes); float32 128x128x32 or 64x64x32
-// with v_mfma_f32_16x16x4_f32. Accumulation is float32 throughout.
+// v_mfma_f32_16x16x32_bf16 (small shapes); float32 64x64x32 with
+// v_mfma_f32_16x16x4_f32. Accumulation is float32 throughout.
 #include "common.h"
 #include "kernels.h"
 
@@ -399,7 +399,6 @@ gemm_kernel(const GemmParams p) {
 
 struct Big { static constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, MI = 32; };
 struct SmallBf16 { static constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2, MI = 16; };
-struct MidF32 { static constexpr int BM = 128, BN = 128, BK = 32, WM = 2, WN = 2, MI = 16; };
 struct SmallF32 { static constexpr int BM = 64, BN = 64, BK = 32, WM = 2, WN = 2, MI = 16; };
 
 template <typename TIn, typename TOut, bool AK, bool BK_, typename C>
@@ -422,7 +421,6 @@ hipError_t launch_layout(bool ak, bool bk, const GemmParams& p, hipStream_t stre
 }
 
 bool use_big(const GemmParams& p) { return p.M >= 256 && p.N >= 256; }
-bool use_mid_f32(const GemmParams& p) { return p.M >= 128 && p.N >= 128; }
 
 }  // namespace
 
@@ -430,7 +428,7 @@ int gemm_k_tile(DType in) { return in == DType::BF16 ? 64 : 32; }
 
 int gemm_tile_m(DType in, int M, int N) {
   if (in == DType::BF16) return (M >= 256 && N >= 256) ? 256 : 128;
-  return (M >= 128 && N >= 128) ? 128 : 64;
+  return 64;
 }
 
 hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor, const GemmParams& p,
@@ -444,9 +442,7 @@ hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor, const 
     return big ? launch_layout<bf16_t, float, Big>(a_kmajor, b_kmajor, p, stream)
                : launch_layout<bf16_t, float, SmallBf16>(a_kmajor, b_kmajor, p, stream);
   }
-  if (out == DType::F32)
-    return use_mid_f32(p) ? launch_layout<float, float, MidF32>(a_kmajor, b_kmajor, p, stream)
-                          : launch_layout<float, float, SmallF32>(a_kmajor, b_kmajor, p, stream);
+  if (out == DType::F32) return launch_layout<float, float, SmallF32>(a_kmajor, b_kmajor, p, stream);
   return hipErrorInvalidValue;
 }
 
