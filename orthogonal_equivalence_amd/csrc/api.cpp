@@ -210,23 +210,30 @@ hipError_t dense(DType t, const void* A, const void* B, void* C, int64_t M, int6
 // g_theta(i, j) = M[i][j] - M[j][i]. Computed as S = R G^T + G^T (= T^T for
 // T = G (R^T + I)) and M^T = 1/2 (S R + S), so only one operand of one
 // product is read transposed; the pack then flips the sign. When a second
-// block set of the same size is given (R2/G2 ...), both run in the same
-// launches.
+// block set of the same size is given, both run in the same launches.
+//
+// float32 activations: float32 products throughout. bf16 activations: G and
+// S are rounded to bf16 and both products run on bf16 MFMA with float32
+// accumulation (S R in float32; the 1/2 S term is added in float32 by the
+// pack), which adds about 2^-8 relative error to a gradient already formed
+// from bf16 activations.
 struct VjpSet {
-  const float* G;
-  const float* R;
-  float* S;
-  float* M;
+  const void* G;       // float32 or bf16 (the activation type)
+  const float* R;      // float32 blocks
+  const void* R_act;   // activation-type blocks
+  void* S;             // same type as G
+  float* M;            // M^T (float32) or 1/2 S R (bf16 path)
   float* g_theta;
   int64_t d;
 };
-hipError_t cayley_vjp(const VjpSet& a, const VjpSet* b2, int b, hipStream_t s) {
+hipError_t cayley_vjp(DType t, const VjpSet& a, const VjpSet* b2, int b, hipStream_t s) {
   const int64_t nb1 = ceil_div(a.d, b);
   const int64_t nb2 = b2 ? ceil_div(b2->d, b) : 0;
   const int64_t bb = (int64_t)b * b;
+  const bool lowp = t == DType::BF16;
   GemmParams g;
   // S = R G^T + G^T: A = R (K-major), B(n, k) = G[n][k], addend G transposed
-  g.A = a.R; g.lda = b; g.sA = bb;
+  g.A = lowp ? a.R_act : a.R; g.lda = b; g.sA = bb;
   g.B = a.G; g.ldb = b; g.sB = bb;
   g.C = a.S; g.ldc = b; g.sC = bb;
   g.D = a.G; g.ldd = b; g.sD = bb; g.d_trans = true;
@@ -236,20 +243,27 @@ hipError_t cayley_vjp(const VjpSet& a, const VjpSet* b2, int b, hipStream_t s) {
   g.alpha = 1.0f; g.beta = 1.0f;
   if (b2) {
     g.batch_split = (int)nb1;
-    g.A2 = b2->R; g.B2 = b2->G; g.C2 = b2->S; g.D2 = b2->G;
+    g.A2 = lowp ? b2->R_act : b2->R; g.B2 = b2->G; g.C2 = b2->S; g.D2 = b2->G;
   }
-  hipError_t e = poetx::launch_gemm(DType::F32, DType::F32, true, true, g, s);
+  hipError_t e = poetx::launch_gemm(t, t, true, true, g, s);
   if (e != hipSuccess) return e;
-  // M^T = 1/2 (S R + S): A = S (K-major), B(n, k) = R[k][n]
-  g.A = a.S; g.B = a.R; g.C = a.M; g.D = a.S; g.d_trans = false;
-  g.alpha = 0.5f; g.beta = 0.5f;
-  if (b2) { g.A2 = b2->S; g.B2 = b2->R; g.C2 = b2->M; g.D2 = b2->S; }
-  e = poetx::launch_gemm(DType::F32, DType::F32, true, false, g, s);
+  // M^T = 1/2 (S R + S): A = S (K-major), B(n, k) = R[k][n]; in the bf16 path
+  // the GEMM writes 1/2 S R and the pack adds 1/2 S
+  g.A = a.S; g.B = lowp ? a.R_act : a.R; g.C = a.M; g.d_trans = false;
+  g.alpha = 0.5f;
+  g.D = lowp ? nullptr : a.S; g.beta = lowp ? 0.0f : 0.5f;
+  if (b2) {
+    g.A2 = b2->S; g.B2 = lowp ? b2->R_act : b2->R; g.C2 = b2->M; g.D2 = lowp ? nullptr : b2->S;
+  }
+  e = poetx::launch_gemm(t, DType::F32, true, false, g, s);
   if (e != hipSuccess) return e;
-  e = poetx::launch_pack_skew_grad(a.M, nb1, b, (int)(a.d - (nb1 - 1) * b), -1.0f, a.g_theta, s);
+  const void* add1 = lowp ? a.S : nullptr;
+  e = poetx::launch_pack_skew_grad(a.M, add1, 0.5f, nb1, b, (int)(a.d - (nb1 - 1) * b), -1.0f,
+                                   a.g_theta, s);
   if (e != hipSuccess || !b2) return e;
-  return poetx::launch_pack_skew_grad(b2->M, nb2, b, (int)(b2->d - (nb2 - 1) * b), -1.0f,
-                                      b2->g_theta, s);
+  const void* add2 = lowp ? b2->S : nullptr;
+  return poetx::launch_pack_skew_grad(b2->M, add2, 0.5f, nb2, b, (int)(b2->d - (nb2 - 1) * b),
+                                      -1.0f, b2->g_theta, s);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? POETX_OK : POETX_ERR_HIP; }
@@ -431,7 +445,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   // B2: G_R[k] = g_Y[:, k]^T Z[:, k], split over tokens, then reduced
   POETX_TRY(sg.begin(1));
   POETX_TRY(block_gram(t, g_y, z_saved, partR, N, m, bR, plan.sR, s));
-  POETX_TRY(poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, s));
+  POETX_TRY(poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, t, s));
   POETX_TRY(sg.end(1));
 
   // B3: g_U = g_Z W0   (B(n, k) = W0[k][n])
@@ -442,7 +456,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   // B4: G_P[j] = g_U[:, j]^T X[:, j]
   POETX_TRY(sg.begin(3));
   POETX_TRY(block_gram(t, gU, x, partP, N, n, bP, plan.sP, s));
-  POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, s));
+  POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, t, s));
   POETX_TRY(sg.end(3));
 
   // B5: g_X = g_U blockdiag(P)
@@ -452,17 +466,17 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B6: Cayley VJP of R and of P (one set of launches when b_in == b_out;
   // stage 6 is then empty)
-  const VjpSet vR{GR, R_f32, TR, MR, g_theta_R, m};
-  const VjpSet vP{GP, P_f32, TP, MP, g_theta_P, n};
+  const VjpSet vR{GR, R_f32, R_act, TR, MR, g_theta_R, m};
+  const VjpSet vP{GP, P_f32, P_act, TP, MP, g_theta_P, n};
   POETX_TRY(sg.begin(5));
   if (bR == bP && bR > 1) {
-    POETX_TRY(cayley_vjp(vR, &vP, bR, s));
+    POETX_TRY(cayley_vjp(t, vR, &vP, bR, s));
   } else if (bR > 1) {
-    POETX_TRY(cayley_vjp(vR, nullptr, bR, s));
+    POETX_TRY(cayley_vjp(t, vR, nullptr, bR, s));
   }
   POETX_TRY(sg.end(5));
   POETX_TRY(sg.begin(6));
-  if (bR != bP && bP > 1) POETX_TRY(cayley_vjp(vP, nullptr, bP, s));
+  if (bR != bP && bP > 1) POETX_TRY(cayley_vjp(t, vP, nullptr, bP, s));
   POETX_TRY(sg.end(6));
 #undef POETX_TRY
   return POETX_OK;

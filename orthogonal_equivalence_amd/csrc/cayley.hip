@@ -299,9 +299,10 @@ panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
 }
 
 // grid (ceil(b*b / (4 kNT)), nblocks); b*b is a multiple of 4
+template <typename TOut>
 __global__ void __launch_bounds__(kNT)
 split_reduce_kernel(const float* __restrict__ part, int nsplit, int nblocks, int b,
-                    int last_valid, float* __restrict__ G) {
+                    int last_valid, TOut* __restrict__ G) {
   const int q = blockIdx.x * kNT + threadIdx.x;  // float4 index within the block
   const int bb = b * b;
   if (4 * q >= bb) return;
@@ -313,30 +314,37 @@ split_reduce_kernel(const float* __restrict__ part, int nsplit, int nblocks, int
     const float4 t = *reinterpret_cast<const float4*>(part + (int64_t)s * total + off);
     v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
   }
+  float e[4] = {v.x, v.y, v.z, v.w};
   if (blk == nblocks - 1 && last_valid < b) {
-    float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int ij = 4 * q + t, i = ij / b, j = ij - (ij / b) * b;
       if (i >= last_valid || j >= last_valid) e[t] = 0.0f;
     }
-    v = make_float4(e[0], e[1], e[2], e[3]);
   }
-  *reinterpret_cast<float4*>(G + off) = v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) store_as<TOut>(G + off + t, e[t]);
 }
 
 // grid (ceil(b*b / kNT), nblocks)
+// g_theta(i, j) = sign ((M + c S)[i][j] - (M + c S)[j][i]), S optional (bf16)
 __global__ void __launch_bounds__(kNT)
-pack_skew_grad_kernel(const float* __restrict__ M, int nblocks, int b, int last_valid,
-                      float sign, float* __restrict__ g) {
+pack_skew_grad_kernel(const float* __restrict__ M, const bf16_t* __restrict__ S, float c, int nblocks,
+                      int b, int last_valid, float sign, float* __restrict__ g) {
   const int ij = blockIdx.x * kNT + threadIdx.x;
   if (ij >= b * b) return;
   const int i = ij / b, j = ij - (ij / b) * b;
   if (i >= j) return;
   const int blk = blockIdx.y;
   const int r = (blk == nblocks - 1) ? last_valid : b;
-  const float* Mb = M + (int64_t)blk * b * b;
-  const float v = (j < r) ? sign * (Mb[(int64_t)i * b + j] - Mb[(int64_t)j * b + i]) : 0.0f;
+  const int64_t base = (int64_t)blk * b * b;
+  const int64_t a = base + (int64_t)i * b + j, t = base + (int64_t)j * b + i;
+  float v = 0.0f;
+  if (j < r) {
+    v = M[a] - M[t];
+    if (S) v += c * (bf16_to_f32(S[a]) - bf16_to_f32(S[t]));
+    v *= sign;
+  }
   g[(int64_t)blk * (b * (b - 1) / 2) + packed_index(b, i, j)] = v;
 }
 
@@ -380,16 +388,22 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
 }
 
 hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, int b,
-                               int last_valid, float* G, hipStream_t stream) {
-  hipLaunchKernelGGL(split_reduce_kernel, dim3((b * b / 4 + kNT - 1) / kNT, (int)nblocks), dim3(kNT),
-                     0, stream, part, nsplit, (int)nblocks, b, last_valid, G);
+                               int last_valid, void* G, DType out, hipStream_t stream) {
+  const dim3 grid((b * b / 4 + kNT - 1) / kNT, (int)nblocks);
+  if (out == DType::BF16)
+    hipLaunchKernelGGL(split_reduce_kernel<bf16_t>, grid, dim3(kNT), 0, stream, part, nsplit,
+                       (int)nblocks, b, last_valid, static_cast<bf16_t*>(G));
+  else
+    hipLaunchKernelGGL(split_reduce_kernel<float>, grid, dim3(kNT), 0, stream, part, nsplit,
+                       (int)nblocks, b, last_valid, static_cast<float*>(G));
   return hipGetLastError();
 }
 
-hipError_t launch_pack_skew_grad(const float* M, int64_t nblocks, int b, int last_valid,
-                                 float sign, float* g_theta, hipStream_t stream) {
+hipError_t launch_pack_skew_grad(const float* M, const void* S, float c, int64_t nblocks, int b,
+                                 int last_valid, float sign, float* g_theta, hipStream_t stream) {
   hipLaunchKernelGGL(pack_skew_grad_kernel, dim3((b * b + kNT - 1) / kNT, (int)nblocks), dim3(kNT),
-                     0, stream, M, (int)nblocks, b, last_valid, sign, g_theta);
+                     0, stream, M, static_cast<const bf16_t*>(S), c, (int)nblocks, b, last_valid,
+                     sign, g_theta);
   return hipGetLastError();
 }
 

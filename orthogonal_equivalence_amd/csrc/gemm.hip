@@ -420,7 +420,12 @@ hipError_t launch_layout(bool ak, bool bk, const GemmParams& p, hipStream_t stre
   return launch_cfg<TIn, TOut, false, true, C>(p, stream);
 }
 
-bool use_big(const GemmParams& p) { return p.M >= 256 && p.N >= 256; }
+// The 256 x 256 configuration only when it still yields a workgroup per CU;
+// small batched products (the Cayley VJP) go to the 128 x 128 one.
+bool use_big(const GemmParams& p) {
+  const int64_t tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch * p.ksplit;
+  return p.M >= 256 && p.N >= 256 && tiles >= 256;
+}
 
 }  // namespace
 

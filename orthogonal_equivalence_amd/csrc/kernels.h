@@ -82,13 +82,14 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
                                float* ws, hipStream_t stream);
 
 // ---- backward helpers ----
-// G[blk] = sum_s part[s][blk] in split order; entries of the last block at
-// rows or columns >= last_valid are written as zero.
+// G[blk] = sum_s part[s][blk] in split order (float32), stored as `out`;
+// entries of the last block at rows or columns >= last_valid are zero.
 hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, int b,
-                               int last_valid, float* G, hipStream_t stream);
-// g_theta[blk][idx(i,j)] = sign (M[blk][i][j] - M[blk][j][i]) (i < j); zero
-// for entries of the last block at rows or columns >= last_valid.
-hipError_t launch_pack_skew_grad(const float* M, int64_t nblocks, int b, int last_valid,
-                                 float sign, float* g_theta, hipStream_t stream);
+                               int last_valid, void* G, DType out, hipStream_t stream);
+// g_theta[blk][idx(i,j)] = sign ((M + c S)[i][j] - (M + c S)[j][i]) (i < j),
+// S an optional bf16 addend; zero for entries of the last block at rows or
+// columns >= last_valid.
+hipError_t launch_pack_skew_grad(const float* M, const void* S, float c, int64_t nblocks, int b,
+                                 int last_valid, float sign, float* g_theta, hipStream_t stream);
 
 }  // namespace poetx
