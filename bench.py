@@ -106,7 +106,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense_fwd_traffic.json")
 # sources of the dense forward kernel (dense_kernel in dense.hip); the
 # committed counter passes count only while these are unchanged
 KERNEL_SOURCES = [os.path.join(ROOT, "orthogonal_equivalence_amd", "csrc", f)
-                  for f in ("dense.hip", "lds_dma.h", "common.h", "kernels.h")]
+                  for f in ("dense.hip", "lds_dma.h", "common.h")]
 
 
 def sources_digest():

@@ -277,6 +277,18 @@ panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
       *reinterpret_cast<float4*>(&sW[gi * kLdB + gj]) = w;
     }
   }
+  // the tile's current values, all loaded before any store (the stores go to
+  // the same buffer, so the compiler could not move later loads above them)
+  float base[2][2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gi = mma_row(mi, e), gj = mma_col(ni);
+        base[mi][ni][e] = (J != p && gi < pw && gj < pw) ? Ab[(int64_t)(i0 + gi) * b + j0 + gj] : 0.0f;
+      }
   __syncthreads();
   floatx4 acc[2][2];
 #pragma unroll
@@ -291,10 +303,7 @@ panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int gi = mma_row(mi, e), gj = mma_col(ni);
-        if (gi < pw && gj < pw) {
-          const float base = (J == p) ? 0.0f : Ab[(int64_t)(i0 + gi) * b + j0 + gj];
-          emit(gi, gj, base - acc[mi][ni][e]);
-        }
+        if (gi < pw && gj < pw) emit(gi, gj, base[mi][ni][e] - acc[mi][ni][e]);
       }
 }
 
