@@ -13,8 +13,9 @@
 // again has a positive definite symmetric part and is invertible. Each panel
 // of width pw (<= 64) is one pair of launches over all blocks at once:
 //   prep:   D = A[p][p] is inverted in registers (each of 256 threads owns a
-//           4 x 4 piece; the pivot row and column go through LDS, one barrier
-//           per elimination step); the workgroup for column tile J writes
+//           4 x 4 piece; four pivots per step, the pivot row and column
+//           blocks through LDS, one barrier per step); the workgroup for
+//           column tile J writes
 //           W_J = Dinv A[p][J] (Dinv itself for J = p, an fp32 MFMA product
 //           otherwise) to a row-panel buffer and copies A[J][p] to a
 //           column-panel buffer;
@@ -29,8 +30,15 @@ namespace {
 
 constexpr int kPW = 64;   // maximum panel width
 constexpr int kNT = 256;  // threads per workgroup (a 16 x 16 grid of 4 x 4 pieces)
-constexpr int kLdA = 68;  // LDS row stride of a 64 x 64 MFMA A operand ([m][k])
-constexpr int kLdB = 80;  // LDS row stride of a 64 x 64 MFMA B operand ([k][n])
+// 64 x 64 fp32 MFMA operands in LDS: A (A[m][k]) row-major and B (B[k][n])
+// stored transposed, both with the k index permuted inside each group of 16
+// so that the four k values a lane needs for four consecutive
+// v_mfma_f32_16x16x4_f32 steps (k = 16u + 4j + l / 16, j = 0..3) are
+// adjacent: one 16-byte LDS read per operand per four MFMAs.
+constexpr int kLdP = 68;  // row stride (floats)
+__device__ __forceinline__ int kperm(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
+__device__ __forceinline__ int a_off(int m, int k) { return m * kLdP + kperm(k); }
+__device__ __forceinline__ int b_off(int k, int n) { return n * kLdP + kperm(k); }
 
 __device__ __forceinline__ int packed_index(int b, int i, int j) {
   // position of (i, j), i < j, in the row-major strict upper triangle
@@ -79,72 +87,118 @@ __device__ __forceinline__ float recip(float x) {
   return fmaf(r, fmaf(-x, r, 1.0f), r);
 }
 
-// One elimination step k = 4 k4 + KK of gj_invert_regs (KK compile-time, so
-// every register index is static).
-template <int KK>
-__device__ __forceinline__ void gj_step(float a[4][4], int k4, float* rowb, float* colb) {
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int k = 4 * k4 + KK;
-  const bool own_row = ty == k4, own_col = tx == k4;
-  if (own_row)
-    *reinterpret_cast<float4*>(&rowb[4 * tx]) = make_float4(a[KK][0], a[KK][1], a[KK][2], a[KK][3]);
-  if (own_col)
-    *reinterpret_cast<float4*>(&colb[4 * ty]) = make_float4(a[0][KK], a[1][KK], a[2][KK], a[3][KK]);
-  __syncthreads();
-  const float pinv = recip(rowb[k]);
-  const float4 r = *reinterpret_cast<const float4*>(&rowb[4 * tx]);
-  const float4 c = *reinterpret_cast<const float4*>(&colb[4 * ty]);
-  const float rs[4] = {r.x * pinv, r.y * pinv, r.z * pinv, r.w * pinv};
-  const float cv[4] = {c.x, c.y, c.z, c.w};
+// In-place Gauss-Jordan inverse of a 4 x 4 matrix held in registers.
+__device__ __forceinline__ void inv4(float m[4][4]) {
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
+  for (int k = 0; k < 4; ++k) {
+    const float piv = recip(m[k][k]);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) a[ii][jj] = fmaf(-cv[ii], rs[jj], a[ii][jj]);
-  if (own_col) {
+    for (int j = 0; j < 4; ++j)
+      if (j != k) m[k][j] *= piv;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) a[ii][KK] = -cv[ii] * pinv;
-  }
-  if (own_row) {
+    for (int i = 0; i < 4; ++i) {
+      if (i == k) continue;
+      const float f = m[i][k];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) a[KK][jj] = rs[jj];
-    if (own_col) a[KK][KK] = pinv;
+      for (int j = 0; j < 4; ++j)
+        if (j != k) m[i][j] = fmaf(-f, m[k][j], m[i][j]);
+      m[i][k] = -f * piv;
+    }
+    m[k][k] = piv;
   }
 }
 
 // In-place Gauss-Jordan inverse of the leading pw x pw part of a 64 x 64
 // matrix distributed as 4 x 4 register pieces (thread (ty, tx) owns rows
 // 4ty.., columns 4tx..); entries outside pw x pw must hold the identity.
-// Step k: the owners of row k and column k publish them through LDS (double
-// buffered, so one barrier per step); every thread applies the rank-1 update
-// a -= c r / a_kk to its piece, then the owners of row k and column k
-// overwrite them with r / a_kk and -c / a_kk (and a_kk with 1 / a_kk).
-__device__ __forceinline__ void gj_invert_regs(float a[4][4], int pw, float (*rowb)[kPW],
-                                               float (*colb)[kPW]) {
-  for (int k4 = 0; 4 * k4 < pw; ++k4) {
-    gj_step<0>(a, k4, rowb[0], colb[0]);
-    if (4 * k4 + 1 < pw) gj_step<1>(a, k4, rowb[1], colb[1]);
-    if (4 * k4 + 2 < pw) gj_step<2>(a, k4, rowb[0], colb[0]);
-    if (4 * k4 + 3 < pw) gj_step<3>(a, k4, rowb[1], colb[1]);
+// Eliminated four pivots at a time: at block step k the pieces of row block
+// k and column block k go through LDS (double buffered: one barrier per
+// step), every thread inverts the 4 x 4 pivot block D itself and applies
+//   a <- base - C' (D^-1 R'),
+// with C' = A[i][k] (-I in row block k), R' = A[k][j] (I in column block
+// k) and base = a (0 in row or column block k): the row panel becomes
+// D^-1 A[k][j], the column panel -A[i][k] D^-1, the pivot block D^-1 and
+// every other piece A[i][j] - A[i][k] D^-1 A[k][j].
+// buf: 1024 floats of LDS.
+__device__ __forceinline__ void gj_invert_regs(float a[4][4], int pw, float* buf) {
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  for (int k = 0; 4 * k < pw; ++k) {
+    float* rb = buf + (k & 1) * 512;  // row-block pieces, by tx
+    float* cb = rb + 256;             // column-block pieces, by ty
+    if (ty == k) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        *reinterpret_cast<float4*>(rb + 16 * tx + 4 * ii) = make_float4(a[ii][0], a[ii][1], a[ii][2], a[ii][3]);
+    }
+    if (tx == k) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        *reinterpret_cast<float4*>(cb + 16 * ty + 4 * ii) = make_float4(a[ii][0], a[ii][1], a[ii][2], a[ii][3]);
+    }
+    __syncthreads();
+    float d[4][4], r[4][4], c[4][4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const float4 dv = *reinterpret_cast<const float4*>(rb + 16 * k + 4 * ii);
+      const float4 rv = *reinterpret_cast<const float4*>(rb + 16 * tx + 4 * ii);
+      const float4 cv = *reinterpret_cast<const float4*>(cb + 16 * ty + 4 * ii);
+      d[ii][0] = dv.x; d[ii][1] = dv.y; d[ii][2] = dv.z; d[ii][3] = dv.w;
+      r[ii][0] = rv.x; r[ii][1] = rv.y; r[ii][2] = rv.z; r[ii][3] = rv.w;
+      c[ii][0] = cv.x; c[ii][1] = cv.y; c[ii][2] = cv.z; c[ii][3] = cv.w;
+    }
+    inv4(d);
+    const bool in_row = ty == k, in_col = tx == k;
+    // W = D^-1 R'
+    float w[4][4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float v = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float rq = in_col ? (q == jj ? 1.0f : 0.0f) : r[q][jj];
+          v = fmaf(d[ii][q], rq, v);
+        }
+        w[ii][jj] = v;
+      }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float v = (in_row || in_col) ? 0.0f : a[ii][jj];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float cq = in_row ? (ii == q ? -1.0f : 0.0f) : c[ii][q];
+          v = fmaf(-cq, w[q][jj], v);
+        }
+        a[ii][jj] = v;
+      }
   }
   __syncthreads();
 }
 
-// acc (this wave's 32 x 32 quadrant of a 64 x 64 product) += sA sB, with sA
-// [64][kLdA] (A[m][k]) and sB [64][kLdB] (B[k][n]) in LDS; fp32 MFMA.
+// acc (this wave's 32 x 32 quadrant of a 64 x 64 product) += A B with both
+// operands in the permuted LDS layouts above; fp32 MFMA.
 __device__ __forceinline__ void mma64(const float* sA, const float* sB, floatx4 acc[2][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = (wave >> 1) * 32, c0 = (wave & 1) * 32;
-#pragma unroll 4
-  for (int k0 = 0; k0 < kPW; k0 += 4) {
-    const int k = k0 + (lane >> 4);
-    const float a0 = sA[(r0 + (lane & 15)) * kLdA + k];
-    const float a1 = sA[(r0 + 16 + (lane & 15)) * kLdA + k];
-    const float b0 = sB[k * kLdB + c0 + (lane & 15)];
-    const float b1 = sB[k * kLdB + c0 + 16 + (lane & 15)];
-    acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-    acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-    acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-    acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+  const int q = 4 * (lane >> 4);
+#pragma unroll
+  for (int u = 0; u < kPW / 16; ++u) {
+    const float4 a0 = *reinterpret_cast<const float4*>(sA + (r0 + (lane & 15)) * kLdP + 16 * u + q);
+    const float4 a1 = *reinterpret_cast<const float4*>(sA + (r0 + 16 + (lane & 15)) * kLdP + 16 * u + q);
+    const float4 b0 = *reinterpret_cast<const float4*>(sB + (c0 + (lane & 15)) * kLdP + 16 * u + q);
+    const float4 b1 = *reinterpret_cast<const float4*>(sB + (c0 + 16 + (lane & 15)) * kLdP + 16 * u + q);
+    const float av0[4] = {a0.x, a0.y, a0.z, a0.w}, av1[4] = {a1.x, a1.y, a1.z, a1.w};
+    const float bv0[4] = {b0.x, b0.y, b0.z, b0.w}, bv1[4] = {b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[j], bv0[j], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av0[j], bv1[j], acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[j], bv0[j], acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av1[j], bv1[j], acc[1][1], 0, 0, 0);
+    }
   }
 }
 
@@ -162,16 +216,27 @@ __device__ __forceinline__ int mma_col(int ni) {
 __global__ void __launch_bounds__(kNT)
 panel_prep_kernel(const float* __restrict__ A, int b, int pw, int p,
                   float* __restrict__ rowbuf, float* __restrict__ colbuf) {
-  __shared__ __attribute__((aligned(16))) float sD[kPW * kLdA];
-  __shared__ __attribute__((aligned(16))) float sX[kPW * kLdB];
-  __shared__ __attribute__((aligned(16))) float rowb[2][kPW];
-  __shared__ __attribute__((aligned(16))) float colb[2][kPW];
+  __shared__ __attribute__((aligned(16))) float sD[kPW * kLdP];
+  __shared__ __attribute__((aligned(16))) float sX[kPW * kLdP];
+  __shared__ __attribute__((aligned(16))) float gjbuf[1024];
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int J = blockIdx.x;
   const int64_t blk = blockIdx.y;
   const float* Ab = A + blk * (int64_t)b * b;
   const int p0 = p * pw, j0 = J * pw;
 
+  // all loads first, from clamped (always valid) addresses, then the selects
+  // and stores: no load waits behind a store or a branch
+  float av[4][4], cv[4][4], xv[4][4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int gi = min(4 * ty + ii, pw - 1), gj = min(4 * tx + jj, pw - 1);
+      av[ii][jj] = Ab[(int64_t)(p0 + gi) * b + p0 + gj];
+      cv[ii][jj] = Ab[(int64_t)(j0 + gi) * b + p0 + gj];
+      xv[ii][jj] = Ab[(int64_t)(p0 + gi) * b + j0 + gj];
+    }
   float a[4][4];
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
@@ -179,11 +244,11 @@ panel_prep_kernel(const float* __restrict__ A, int b, int pw, int p,
     for (int jj = 0; jj < 4; ++jj) {
       const int gi = 4 * ty + ii, gj = 4 * tx + jj;
       const bool in = gi < pw && gj < pw;
-      a[ii][jj] = in ? Ab[(int64_t)(p0 + gi) * b + p0 + gj] : (gi == gj ? 1.0f : 0.0f);
-      if (in) colbuf[(blk * b + j0 + gi) * pw + gj] = Ab[(int64_t)(j0 + gi) * b + p0 + gj];
-      if (J != p) sX[gi * kLdB + gj] = in ? Ab[(int64_t)(p0 + gi) * b + j0 + gj] : 0.0f;
+      a[ii][jj] = in ? av[ii][jj] : (gi == gj ? 1.0f : 0.0f);
+      if (in) colbuf[(blk * b + j0 + gi) * pw + gj] = cv[ii][jj];
+      if (J != p) sX[b_off(gi, gj)] = in ? xv[ii][jj] : 0.0f;
     }
-  gj_invert_regs(a, pw, rowb, colb);
+  gj_invert_regs(a, pw, gjbuf);
 
   float* rb = rowbuf + blk * (int64_t)pw * b;
   if (J == p) {
@@ -199,7 +264,7 @@ panel_prep_kernel(const float* __restrict__ A, int b, int pw, int p,
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) sD[(4 * ty + ii) * kLdA + 4 * tx + jj] = a[ii][jj];
+    for (int jj = 0; jj < 4; ++jj) sD[a_off(4 * ty + ii, 4 * tx + jj)] = a[ii][jj];
   __syncthreads();
   floatx4 acc[2][2];
 #pragma unroll
@@ -224,8 +289,8 @@ __global__ void __launch_bounds__(kNT)
 panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
                     const float* __restrict__ rowbuf, const float* __restrict__ colbuf,
                     int final, bf16_t* __restrict__ act_out) {
-  __shared__ __attribute__((aligned(16))) float sC[kPW * kLdA];
-  __shared__ __attribute__((aligned(16))) float sW[kPW * kLdB];
+  __shared__ __attribute__((aligned(16))) float sC[kPW * kLdP];
+  __shared__ __attribute__((aligned(16))) float sW[kPW * kLdP];
   const int tid = threadIdx.x;
   const int nt = b / pw;
   const int I = blockIdx.x / nt, J = blockIdx.x - (blockIdx.x / nt) * nt;
@@ -245,37 +310,42 @@ panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
   };
 
   if (I == p) {
-    for (int e = tid; e < pw * pw; e += kNT) {
-      const int gi = e / pw, gj = e - (e / pw) * pw;
-      emit(gi, gj, rb[(int64_t)gi * b + j0 + gj]);
+    float v[kPW * kPW / kNT];  // all loads before the stores
+#pragma unroll
+    for (int t = 0; t < kPW * kPW / kNT; ++t) {
+      const int e = tid + t * kNT, gi = min(e >> 6, pw - 1), gj = min(e & 63, pw - 1);
+      v[t] = rb[(int64_t)gi * b + j0 + gj];
+    }
+#pragma unroll
+    for (int t = 0; t < kPW * kPW / kNT; ++t) {
+      const int e = tid + t * kNT, gi = e >> 6, gj = e & 63;
+      if (gi < pw && gj < pw) emit(gi, gj, v[t]);
     }
     return;
   }
   {
-    // each thread stages a 4 x 4 piece of C (colpanel rows I) and W (rowpanel
-    // columns J); pw is a power of two >= 4 here or the whole block (b <= 64)
+    // each thread stages a 4 x 4 piece of C (column panel rows I) and W (row
+    // panel columns J): all loads first, from clamped (always valid)
+    // addresses, then the LDS stores
     const int ty = tid >> 4, tx = tid & 15;
+    float cv[4][4], wv[4][4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int gi = 4 * ty + ii, gj = 4 * tx;
-      float4 c = make_float4(0.f, 0.f, 0.f, 0.f), w = c;
-      if (gi < pw && gj < pw) {
-        if ((pw & 3) == 0) {
-          c = *reinterpret_cast<const float4*>(cb + (int64_t)(i0 + gi) * pw + gj);
-          w = *reinterpret_cast<const float4*>(rb + (int64_t)gi * b + j0 + gj);
-        } else {
-          float ce[4] = {0.f, 0.f, 0.f, 0.f}, we[4] = {0.f, 0.f, 0.f, 0.f};
-          for (int t = 0; t < 4 && gj + t < pw; ++t) {
-            ce[t] = cb[(int64_t)(i0 + gi) * pw + gj + t];
-            we[t] = rb[(int64_t)gi * b + j0 + gj + t];
-          }
-          c = make_float4(ce[0], ce[1], ce[2], ce[3]);
-          w = make_float4(we[0], we[1], we[2], we[3]);
-        }
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int gi = min(4 * ty + ii, pw - 1), gj = min(4 * tx + jj, pw - 1);
+        cv[ii][jj] = cb[(int64_t)(i0 + gi) * pw + gj];
+        wv[ii][jj] = rb[(int64_t)gi * b + j0 + gj];
       }
-      *reinterpret_cast<float4*>(&sC[gi * kLdA + gj]) = c;
-      *reinterpret_cast<float4*>(&sW[gi * kLdB + gj]) = w;
-    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int gi = 4 * ty + ii, gj = 4 * tx + jj;
+        const bool in = gi < pw && gj < pw;
+        sC[a_off(gi, gj)] = in ? cv[ii][jj] : 0.0f;
+        sW[b_off(gi, gj)] = in ? wv[ii][jj] : 0.0f;
+      }
   }
   // the tile's current values, all loaded before any store (the stores go to
   // the same buffer, so the compiler could not move later loads above them)
