@@ -154,6 +154,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=8192,
                     help="tokens of the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--recompute-z", action="store_true",
+                    help="POET-Xmem variant: the forward keeps no Z, the backward recomputes it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -181,16 +183,19 @@ def main():
     layers = []
     for s in specs:
         L = make_layer(s)
-        lay = PoetxLinear(torch.from_numpy(L.W0).to(tdt[s.dtype]), s.b, s.b, s.dtype, device=dev)
+        lay = PoetxLinear(torch.from_numpy(L.W0).to(tdt[s.dtype]), s.b, s.b, s.dtype, device=dev,
+                          recompute_z=args.recompute_z)
         lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
         x = torch.from_numpy(L.x).to(tdt[s.dtype]).to(dev)
         g_y = torch.from_numpy(L.g_y).to(tdt[s.dtype]).to(dev)
         out = dict(y=torch.empty(s.tokens, s.d_out, dtype=tdt[s.dtype], device=dev),
-                   z=torch.empty(s.tokens, s.d_out, dtype=tdt[s.dtype], device=dev),
+                   z=None if args.recompute_z else
+                   torch.empty(s.tokens, s.d_out, dtype=tdt[s.dtype], device=dev),
                    g_x=torch.empty(s.tokens, s.d_in, dtype=tdt[s.dtype], device=dev),
                    gR=torch.empty_like(lay.theta_R), gP=torch.empty_like(lay.theta_P))
         layers.append((s, L if len(specs) == 1 else None, lay, x, g_y, out))
     stream = torch.cuda.current_stream()
+    bwd_stages = BWD_STAGES + (["recompute_z"] if args.recompute_z else [])
 
     def step(ev=None):
         for li, (s, _, lay, x, g_y, o) in enumerate(layers):
@@ -209,7 +214,7 @@ def main():
         for _ in layers:
             ev.append({"build": (P.Event(), P.Event()),
                        "fwd": [P.Event() for _ in range(2 * len(FWD_STAGES))],
-                       "bwd": [P.Event() for _ in range(2 * len(BWD_STAGES))]})
+                       "bwd": [P.Event() for _ in range(2 * len(bwd_stages))]})
         return ev
 
     def as_handles(ev):
@@ -249,7 +254,7 @@ def main():
         vals = [step_events[k][li]["build"][0].elapsed_ms(step_events[k][li]["build"][1])
                 for k in range(args.steps)]
         stage_ms[pre + "build"] = statistics.mean(vals)
-        for grp, names in (("fwd", FWD_STAGES), ("bwd", BWD_STAGES)):
+        for grp, names in (("fwd", FWD_STAGES), ("bwd", bwd_stages)):
             for si, nm in enumerate(names):
                 vals = [step_events[k][li][grp][2 * si].elapsed_ms(step_events[k][li][grp][2 * si + 1])
                         for k in range(args.steps)]
@@ -279,7 +284,9 @@ def main():
                                           "N(0, sigma^2) generators)",
         "config": {"workload": args.config,
                    "layers": [f"{s.name} {s.d_out}x{s.d_in} b={s.b}" for s in specs],
-                   "tokens": tokens, "block": specs[0].b},
+                   "tokens": tokens, "block": specs[0].b,
+                   "variant": "POET-Xmem (Z recomputed in the backward)" if args.recompute_z
+                   else "POET-X (Z kept for the backward)"},
         "roofline": roofline,
         "layer_roofline": {"flops": F, "bytes": B, "t_roof_ms": t_roof * 1e3,
                            "frac": t_roof / (ms_per_step / 1e3),

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define POETX_ABI_VERSION 1
+#define POETX_ABI_VERSION 2
 
 typedef enum poetx_status {
   POETX_OK = 0,
@@ -74,6 +74,16 @@ typedef enum poetx_status {
 
 typedef enum poetx_dtype { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
 
+/* poetx_linear_desc.flags */
+/* Recompute Z in the backward instead of keeping it (POET-Xmem: section 2
+ * Methodik, gradient-checkpointing item; some forward intermediates are not
+ * stored but recomputed in the backward). With this flag the
+ * forward takes z_save == NULL and keeps Z in its workspace only, and the
+ * backward takes z_saved == NULL and recomputes U = X P^T and Z = U W0^T in
+ * its own workspace (one extra dense product). Results are those of the
+ * stored-Z path. */
+#define POETX_RECOMPUTE_Z 1
+
 /* Shape of one POET-X linear layer. */
 typedef struct poetx_linear_desc {
   int64_t tokens; /* N >= 1: rows of x, y, z, g_y, g_x */
@@ -83,13 +93,17 @@ typedef struct poetx_linear_desc {
   int32_t b_out;  /* block size of R */
   int32_t act;    /* poetx_dtype of the activations, W0 and the *_act blocks */
   int32_t n_events; /* number of entries in `events` (0 = no stage timing) */
+  int32_t flags;    /* 0 or POETX_RECOMPUTE_Z */
+  int32_t reserved; /* must be 0 */
   /* Optional stage timing: an array of hipEvent_t created by the caller (for
    * example with poetx_event_create). When n_events >= 2 s + 2, the call
    * records events[2 s] on `stream` before its stage s and events[2 s + 1]
    * after it. Forward stages: 0 P-apply, 1 dense W0 GEMM, 2 R-apply.
    * Backward stages: 0 grad through R, 1 R gram (+ reduction), 2 dense W0
    * GEMM, 3 P gram (+ reduction), 4 grad to x, 5 Cayley VJP of R,
-   * 6 Cayley VJP of P. May be NULL when n_events is 0. */
+   * 6 Cayley VJP of P, 7 recompute of Z (POETX_RECOMPUTE_Z only; it runs
+   * first, and stage 1 then runs before stage 0). May be NULL when n_events
+   * is 0. */
   void* const* events;
 } poetx_linear_desc;
 
@@ -136,7 +150,7 @@ int poetx_build_orthogonal(const float* theta, int64_t d, int32_t b,
                            void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for poetx_linear_fwd / poetx_linear_bwd (0 if the
- * descriptor is invalid). */
+ * descriptor is invalid). With POETX_RECOMPUTE_Z the forward's includes Z. */
 size_t poetx_fwd_workspace_size(const poetx_linear_desc* desc);
 size_t poetx_bwd_workspace_size(const poetx_linear_desc* desc);
 
@@ -150,7 +164,8 @@ size_t poetx_bwd_workspace_size(const poetx_linear_desc* desc);
  *   R_act  [nb_out, b_out, b_out] act, from poetx_build_orthogonal
  *   P_act  [nb_in,  b_in,  b_in ] act
  *   y      out [tokens, d_out] act
- *   z_save out [tokens, d_out] act: Z, kept for the backward
+ *   z_save out [tokens, d_out] act: Z, kept for the backward; NULL (and
+ *          only NULL) when desc->flags has POETX_RECOMPUTE_Z
  *   ws     workspace of poetx_fwd_workspace_size(desc) bytes
  */
 int poetx_linear_fwd(const poetx_linear_desc* desc, const void* x, const void* W0,
@@ -165,7 +180,9 @@ int poetx_linear_fwd(const poetx_linear_desc* desc, const void* x, const void* W
  *   g_U = g_Z W0                    G_P[j] = g_U[:, j]^T X[:, j]
  *   g_X = g_U blockdiag(P)
  *   Cayley VJP per block: M = 1/2 (R^T + I) G (R^T + I),
- *   g_theta(i, j) = M[i][j] - M[j][i] for i < j.
+ *   g_theta(i, j) = M[i][j] - M[j][i] for i < j
+ *   (bf16 mode: G and S = R G^T + G^T are rounded to bf16 for the two VJP
+ *   products, which accumulate in float32).
  * The token reductions are split over workgroups and summed in a fixed
  * order, so results are bitwise reproducible.
  *
@@ -174,7 +191,8 @@ int poetx_linear_fwd(const poetx_linear_desc* desc, const void* x, const void* W
  *   W0         [d_out, d_in]   act
  *   R_f32      [nb_out, b_out, b_out] float32, P_f32 [nb_in, b_in, b_in] float32
  *   R_act, P_act  the act copies of the same blocks
- *   z_saved    [tokens, d_out] act, z_save of the matching forward
+ *   z_saved    [tokens, d_out] act, z_save of the matching forward; NULL
+ *              (and only NULL) when desc->flags has POETX_RECOMPUTE_Z
  *   g_x        out [tokens, d_in] act
  *   g_theta_R  out [nb_out, b_out(b_out-1)/2] float32
  *   g_theta_P  out [nb_in,  b_in(b_in-1)/2]   float32

@@ -47,19 +47,25 @@ int check_desc(const poetx_linear_desc* d) {
   if (d->b_in > d->d_in || d->b_out > d->d_out) return POETX_ERR_SHAPE;
   if (ceil_div(d->d_in, d->b_in) > kMaxBatch || ceil_div(d->d_out, d->b_out) > kMaxBatch) return POETX_ERR_SHAPE;
   if (d->n_events < 0 || (d->n_events > 0 && !d->events)) return POETX_ERR_NULL;
+  if ((d->flags & ~POETX_RECOMPUTE_Z) != 0 || d->reserved != 0) return POETX_ERR_SHAPE;
   const int v = act_vec(d->act);
   if (d->d_in % v || d->d_out % v || d->b_in % v || d->b_out % v) return POETX_ERR_ALIGN;
   return POETX_OK;
 }
 
 // ---------------------------------------------------------------- workspace
+bool recompute_z(const poetx_linear_desc* d) { return (d->flags & POETX_RECOMPUTE_Z) != 0; }
+
 struct FwdPlan {
-  size_t u_off, total;
+  size_t u_off, z_off, total;
 };
 FwdPlan plan_fwd(const poetx_linear_desc* d) {
   FwdPlan p;
   p.u_off = 0;
-  p.total = align_up((size_t)d->tokens * d->d_in * act_size(d->act));
+  size_t off = align_up((size_t)d->tokens * d->d_in * act_size(d->act));
+  p.z_off = off;  // Z lives here only when it is not kept
+  if (recompute_z(d)) off += align_up((size_t)d->tokens * d->d_out * act_size(d->act));
+  p.total = off;
   return p;
 }
 
@@ -340,7 +346,8 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
                      void* stream) {
   int st = check_desc(d);
   if (st != POETX_OK) return st;
-  if (!x || !W0 || !R_act || !P_act || !y || !z_save) return POETX_ERR_NULL;
+  if (!x || !W0 || !R_act || !P_act || !y) return POETX_ERR_NULL;
+  if (recompute_z(d) ? z_save != nullptr : z_save == nullptr) return POETX_ERR_NULL;
   const void* ptrs[] = {x, W0, R_act, P_act, y, z_save, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return POETX_ERR_ALIGN;
@@ -350,7 +357,8 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   const size_t es = act_size(d->act);
   const int64_t N = d->tokens, n = d->d_in, m = d->d_out;
   const int64_t nbR = ceil_div(m, d->b_out), nbP = ceil_div(n, d->b_in);
-  const Range r_y = range_of(y, N * m * es), r_z = range_of(z_save, N * m * es);
+  const Range r_y = range_of(y, N * m * es);
+  const Range r_z = z_save ? range_of(z_save, N * m * es) : Range{0, 0};
   const Range ins[] = {range_of(x, N * n * es), range_of(W0, m * n * es),
                        range_of(R_act, nbR * d->b_out * d->b_out * es),
                        range_of(P_act, nbP * d->b_in * d->b_in * es), range_of(ws, plan.total)};
@@ -361,6 +369,7 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const DType t = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
   void* U = static_cast<char*>(ws) + plan.u_off;
+  void* Z = z_save ? z_save : static_cast<char*>(ws) + plan.z_off;
   Stages sg{d, s};
   hipError_t e;
 
@@ -371,12 +380,12 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
 
   // S3: Z = U W0^T
   if ((e = sg.begin(1)) != hipSuccess) return hip_status(e);
-  if ((e = dense(t, U, W0, z_save, N, m, n, n, n, m, true, s)) != hipSuccess) return hip_status(e);
+  if ((e = dense(t, U, W0, Z, N, m, n, n, n, m, true, s)) != hipSuccess) return hip_status(e);
   if ((e = sg.end(1)) != hipSuccess) return hip_status(e);
 
   // S4: Y = Z blockdiag(R)^T
   if ((e = sg.begin(2)) != hipSuccess) return hip_status(e);
-  if ((e = block_apply(t, z_save, R_act, y, N, m, d->b_out, true, s)) != hipSuccess)
+  if ((e = block_apply(t, Z, R_act, y, N, m, d->b_out, true, s)) != hipSuccess)
     return hip_status(e);
   if ((e = sg.end(2)) != hipSuccess) return hip_status(e);
   return POETX_OK;
@@ -388,8 +397,8 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
                      size_t ws_bytes, void* stream) {
   int st = check_desc(d);
   if (st != POETX_OK) return st;
-  if (!g_y || !x || !W0 || !R_f32 || !P_f32 || !R_act || !P_act || !z_saved || !g_x)
-    return POETX_ERR_NULL;
+  if (!g_y || !x || !W0 || !R_f32 || !P_f32 || !R_act || !P_act || !g_x) return POETX_ERR_NULL;
+  if (recompute_z(d) ? z_saved != nullptr : z_saved == nullptr) return POETX_ERR_NULL;
   if ((d->b_out > 1 && !g_theta_R) || (d->b_in > 1 && !g_theta_P)) return POETX_ERR_NULL;
   const void* ptrs[] = {g_y, x, W0, R_f32, P_f32, R_act, P_act, z_saved, g_x, g_theta_R, g_theta_P, ws};
   for (const void* p : ptrs)
@@ -407,7 +416,8 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   const Range ins[] = {range_of(g_y, N * m * es), range_of(x, N * n * es),
                        range_of(W0, m * n * es), range_of(R_f32, nbR * bR * bR * 4),
                        range_of(P_f32, nbP * bP * bP * 4), range_of(R_act, nbR * bR * bR * es),
-                       range_of(P_act, nbP * bP * bP * es), range_of(z_saved, N * m * es),
+                       range_of(P_act, nbP * bP * bP * es),
+                       z_saved ? range_of(z_saved, N * m * es) : Range{0, 0},
                        range_of(ws, plan.total)};
   for (const Range& o : outs) {
     for (const Range& r : ins)
@@ -437,16 +447,35 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     if ((e = (call)) != hipSuccess) return hip_status(e); \
   } while (0)
 
-  // B1: g_Z = g_Y blockdiag(R)
-  POETX_TRY(sg.begin(0));
-  POETX_TRY(block_apply(t, g_y, R_act, gZ, N, m, bR, false, s));
-  POETX_TRY(sg.end(0));
-
-  // B2: G_R[k] = g_Y[:, k]^T Z[:, k], split over tokens, then reduced
-  POETX_TRY(sg.begin(1));
-  POETX_TRY(block_gram(t, g_y, z_saved, partR, N, m, bR, plan.sR, s));
-  POETX_TRY(poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, t, s));
-  POETX_TRY(sg.end(1));
+  auto grad_r = [&]() -> hipError_t {  // B1: g_Z = g_Y blockdiag(R)
+    hipError_t r;
+    if ((r = sg.begin(0)) != hipSuccess) return r;
+    if ((r = block_apply(t, g_y, R_act, gZ, N, m, bR, false, s)) != hipSuccess) return r;
+    return sg.end(0);
+  };
+  auto gram_r = [&](const void* Z) -> hipError_t {
+    // B2: G_R[k] = g_Y[:, k]^T Z[:, k], split over tokens, then reduced
+    hipError_t r;
+    if ((r = sg.begin(1)) != hipSuccess) return r;
+    if ((r = block_gram(t, g_y, Z, partR, N, m, bR, plan.sR, s)) != hipSuccess) return r;
+    if ((r = poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, t, s)) !=
+        hipSuccess)
+      return r;
+    return sg.end(1);
+  };
+  if (z_saved) {
+    POETX_TRY(grad_r());
+    POETX_TRY(gram_r(z_saved));
+  } else {
+    // POET-Xmem: U = X P^T into the g_U buffer and Z = U W0^T into the g_Z
+    // buffer (both overwritten later), the R gram on Z, then g_Z over Z
+    POETX_TRY(sg.begin(7));
+    POETX_TRY(block_apply(t, x, P_act, gU, N, n, bP, true, s));
+    POETX_TRY(dense(t, gU, W0, gZ, N, m, n, n, n, m, true, s));
+    POETX_TRY(sg.end(7));
+    POETX_TRY(gram_r(gZ));
+    POETX_TRY(grad_r());
+  }
 
   // B3: g_U = g_Z W0   (B(n, k) = W0[k][n])
   POETX_TRY(sg.begin(2));

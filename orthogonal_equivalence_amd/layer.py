@@ -20,10 +20,15 @@ class PoetxLinear:
     are float32 views into one buffer, so that both block sets are built by a
     single poetx_build_orthogonal call when b_in == b_out and b divides both
     d_in and d_out.
+
+    recompute_z=True is the memory-saving variant: the forward keeps no
+    Z = W0 P x for the backward, which recomputes it (POETX_RECOMPUTE_Z).
     """
 
-    def __init__(self, W0: torch.Tensor, b_in: int, b_out: int, act: str, device="cuda"):
+    def __init__(self, W0: torch.Tensor, b_in: int, b_out: int, act: str, device="cuda",
+                 recompute_z: bool = False):
         self.torch_dtype, self.act = _DT[act]
+        self.flags = P.POETX_RECOMPUTE_Z if recompute_z else 0
         self.device = torch.device(device)
         self.W0 = W0.to(self.device, self.torch_dtype).contiguous()
         self.d_out, self.d_in = self.W0.shape
@@ -59,7 +64,8 @@ class PoetxLinear:
         self.theta_P.copy_(torch.as_tensor(theta_P, dtype=torch.float32))
 
     def desc(self, tokens: int, events=None):
-        return P.make_desc(tokens, self.d_in, self.d_out, self.b_in, self.b_out, self.act, events)
+        return P.make_desc(tokens, self.d_in, self.d_out, self.b_in, self.b_out, self.act, events,
+                           self.flags)
 
     def _ws(self, cache, size_fn, tokens):
         if tokens not in cache:
@@ -91,13 +97,16 @@ class PoetxLinear:
     def forward(self, x, y=None, z=None, stream=None, events=None):
         N = x.shape[0]
         y = torch.empty(N, self.d_out, device=self.device, dtype=self.torch_dtype) if y is None else y
-        z = torch.empty(N, self.d_out, device=self.device, dtype=self.torch_dtype) if z is None else z
+        if self.flags & P.POETX_RECOMPUTE_Z:
+            z = None
+        elif z is None:
+            z = torch.empty(N, self.d_out, device=self.device, dtype=self.torch_dtype)
         R, Pb = self.blocks_for_act()
         ws = self._ws(self._fwd_ws, P.poetx_fwd_workspace_size, N)
         P.poetx_linear_fwd(self.desc(N, events), x, self.W0, R, Pb, y, z, ws, stream)
         return y, z
 
-    def backward(self, g_y, x, z, g_x=None, g_theta_R=None, g_theta_P=None, stream=None,
+    def backward(self, g_y, x, z=None, g_x=None, g_theta_R=None, g_theta_P=None, stream=None,
                  events=None):
         N = x.shape[0]
         g_x = torch.empty(N, self.d_in, device=self.device, dtype=self.torch_dtype) if g_x is None else g_x

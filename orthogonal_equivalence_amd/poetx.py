@@ -27,6 +27,9 @@ POETX_ERR_ALIAS = 7
 POETX_F32 = 0
 POETX_BF16 = 1
 
+POETX_ABI_VERSION = 2
+POETX_RECOMPUTE_Z = 1
+
 EXPORTS = (
     "poetx_abi_version", "poetx_status_string", "poetx_num_blocks", "poetx_theta_count",
     "poetx_build_workspace_size", "poetx_build_orthogonal", "poetx_fwd_workspace_size",
@@ -51,6 +54,8 @@ class LinearDesc(ctypes.Structure):
         ("b_out", ctypes.c_int32),
         ("act", ctypes.c_int32),
         ("n_events", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("events", ctypes.POINTER(ctypes.c_void_p)),
     ]
 
@@ -138,8 +143,8 @@ def poetx_build_workspace_size(d: int, b: int) -> int:
     return _lib.poetx_build_workspace_size(d, b)
 
 
-def make_desc(tokens, d_in, d_out, b_in, b_out, act, events=None) -> LinearDesc:
-    desc = LinearDesc(tokens, d_in, d_out, b_in, b_out, act, 0, None)
+def make_desc(tokens, d_in, d_out, b_in, b_out, act, events=None, flags=0) -> LinearDesc:
+    desc = LinearDesc(tokens, d_in, d_out, b_in, b_out, act, 0, flags, 0, None)
     if events:
         arr = (ctypes.c_void_p * len(events))(*events)
         desc.n_events = len(events)

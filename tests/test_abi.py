@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert P.poetx_abi_version() == 1
+    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 2
     for s in range(8):
         assert P.status_string(s) and P.status_string(s) != "unknown status"
     assert P.status_string(99) == "unknown status"
@@ -86,7 +86,8 @@ SMALL = dict(tokens=16, d_in=64, d_out=64, b_in=8, b_out=8, act=P.POETX_BF16)
 def desc(**over):
     k = dict(SMALL)
     k.update(over)
-    return P.make_desc(k["tokens"], k["d_in"], k["d_out"], k["b_in"], k["b_out"], k["act"])
+    return P.make_desc(k["tokens"], k["d_in"], k["d_out"], k["b_in"], k["b_out"], k["act"],
+                       flags=k.get("flags", 0))
 
 
 @pytest.mark.parametrize("call", [_fwd, _bwd])
@@ -181,3 +182,48 @@ def test_build_errors():
     assert call(ws=None) == P.POETX_ERR_WORKSPACE
     assert call(f32=ALIGNED) == P.POETX_ERR_ALIAS          # output on top of theta
     assert call(act_ptr=ALIGNED * 4) == P.POETX_ERR_ALIAS  # act copy inside the workspace
+
+
+# -- POETX_RECOMPUTE_Z (POET-Xmem: Z is not kept by the forward) --------------
+
+def test_unknown_flags_and_reserved_rejected():
+    for call in (_fwd, _bwd):
+        assert call(desc(flags=2)) == P.POETX_ERR_SHAPE
+        assert call(desc(flags=-1)) == P.POETX_ERR_SHAPE
+        d = desc()
+        d.reserved = 1
+        assert call(d) == P.POETX_ERR_SHAPE
+    d = desc()
+    d.reserved = 3
+    assert P.poetx_fwd_workspace_size(d) == 0 and P.poetx_bwd_workspace_size(d) == 0
+
+
+def test_recompute_z_takes_null_z_and_only_null():
+    d = desc(flags=P.POETX_RECOMPUTE_Z)
+    assert _fwd(d) == P.POETX_ERR_NULL          # a z_save buffer is not taken
+    assert _bwd(d) == P.POETX_ERR_NULL          # nor a z_saved one
+    assert _fwd(desc(), z=None) == P.POETX_ERR_NULL   # without the flag Z is required
+    # with the flag and z NULL, only the (fake) workspace size stands between the
+    # call and a launch: check it with a workspace that is one byte short
+    need = P.poetx_fwd_workspace_size(d)
+    assert _fwd(d, z=None, ws_bytes=need - 1) == P.POETX_ERR_WORKSPACE
+    need = P.poetx_bwd_workspace_size(d)
+    assert _bwd(d, z=None, ws_bytes=need - 1) == P.POETX_ERR_WORKSPACE
+
+
+def test_recompute_z_forward_workspace_holds_z():
+    for act, es in ((P.POETX_BF16, 2), (P.POETX_F32, 4)):
+        keep = P.poetx_fwd_workspace_size(desc(act=act, tokens=1000, d_out=4096))
+        mem = P.poetx_fwd_workspace_size(desc(act=act, tokens=1000, d_out=4096,
+                                              flags=P.POETX_RECOMPUTE_Z))
+        assert mem - keep >= 1000 * 4096 * es
+        # the backward recomputes into buffers it already has
+        assert P.poetx_bwd_workspace_size(desc(act=act, tokens=1000, d_out=4096)) == \
+            P.poetx_bwd_workspace_size(desc(act=act, tokens=1000, d_out=4096,
+                                            flags=P.POETX_RECOMPUTE_Z))
+
+
+def test_recompute_z_alias_checks_skip_null_z():
+    d = desc(flags=P.POETX_RECOMPUTE_Z)
+    assert _fwd(d, z=None, y=ALIGNED) == P.POETX_ERR_ALIAS
+    assert _bwd(d, z=None, g_x=ALIGNED) == P.POETX_ERR_ALIAS

@@ -219,3 +219,41 @@ def test_full_size_layer_set_8b(layer):
     _sampled_check(L, lay, out)
     del lay, out
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------- POET-Xmem: Z recomputed
+@pytest.mark.parametrize("case", [SMALL_CASES[i] for i in (0, 2, 3, 5, 6)], ids=lambda c: c[0])
+def test_recompute_z_small(case):
+    """POETX_RECOMPUTE_Z: the oracle's results, and bit for bit those of the
+    path that keeps Z (the same kernels recompute the same Z)."""
+    name, n, m, b, N, dt, sigma = case
+    spec = LayerSpec(name, n, m, b, N, dt, sigma, seed=len(name))
+    U.log(f"[recompute-z] {name}: d_in={n} d_out={m} b={b} tokens={N} {dt}")
+    L = make_layer(spec)
+    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, b, b)
+    y_ref = ora.forward(L.x)
+    gx_ref, gR_ref, gP_ref = ora.backward(L.g_y, L.x)
+    _, mem = U.run_layer(L, recompute_z=True)
+    assert mem["z"] is None
+    U.check("y", U.host(mem["y"]), y_ref, dt)
+    U.check("g_x", U.host(mem["g_x"]), gx_ref, dt)
+    U.check("g_theta_R", U.host(mem["g_theta_R"]), gR_ref, dt)
+    U.check("g_theta_P", U.host(mem["g_theta_P"]), gP_ref, dt)
+    _, keep = U.run_layer(L)
+    for k in ("y", "g_x", "g_theta_R", "g_theta_P"):
+        assert torch.equal(mem[k], keep[k]), k
+
+
+def test_recompute_z_full_size_mlp_up_8b():
+    """The 8B MLP up-projection (14336 x 4096, b = 256, 8192 tokens) with Z
+    recomputed: sampled oracle checks, and equal to the stored-Z path."""
+    spec = CONFIGS["mlp_up_8b"][0]
+    U.log(f"[recompute-z full] {spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
+    L = make_layer(spec)
+    lay, mem = U.run_layer(L, recompute_z=True)
+    _, keep = U.run_layer(L)
+    for k in ("y", "g_x", "g_theta_R", "g_theta_P"):
+        assert torch.equal(mem[k], keep[k]), k
+    _sampled_check(L, lay, keep)
+    del lay, mem, keep
+    torch.cuda.empty_cache()
