@@ -19,6 +19,8 @@ on gist.science, "Technische Zusammenfassung"):
   [SKEW]  §2 Methodik, Cayley-Neumann parameterisation: orthogonality comes
           from a skew-symmetric Q (Q = -Q^T) of which only the upper triangle
           is stored.
+  [CNP]   same item: the Cayley map is approximated by a truncated Neumann
+          series whose higher-order terms are Q^2, Q^3 and Q^4.
 
 Readings taken where the pages are silent (each is listed in the design doc):
   * the orthogonal map is the exact Cayley map R = (I + Q)(I - Q)^-1 (the
@@ -32,12 +34,20 @@ Readings taken where the pages are silent (each is listed in the design doc):
   * if b does not divide d, the last block is identity-padded: the generator
     entries of rows/columns past the end are treated as zero, so the block is
     diag(Cayley(Q_r), I) and only its leading r x r part acts;
-  * backward outputs are g_x, g_theta_R, g_theta_P (W0 is frozen, no g_W0).
+  * backward outputs are g_x, g_theta_R, g_theta_P (W0 is frozen, no g_W0);
+  * the Cayley-Neumann variant (selected explicitly; the exact map is the
+    default) truncates (I - Q)^-1 = I + Q + Q^2 + ... after Q^4 inside
+    R = 2 (I - Q)^-1 - I, so R = I + 2 (Q + Q^2 + Q^3 + Q^4): only the
+    powers the pages list occur. (Truncating inside (I + Q)(I - Q)^-1 would
+    add a Q^5 term; that reading is not taken.)
 
 Where "parity unpinned": nothing here. Every function is pinned by
 tests/test_oracle.py against closed forms (b = 2 rotation, b = 3 Rodrigues
-rotation), invariants (orthogonality, det, spectrum), textbook routines
-(dense scipy block_diag products) and central finite differences.
+rotation, the b = 2 Cayley-Neumann block and its derivative), invariants
+(orthogonality, det, spectrum, the series tail 2 Q^5 (I - Q)^-1 between the
+exact and truncated maps), textbook routines (dense scipy block_diag
+products), the block-triangular Frechet identity and central finite
+differences.
 
 Layouts: activations are token-major, x [N, d_in], y [N, d_out]; W0 is
 [d_out, d_in]; theta is [nblocks, b(b-1)/2].
@@ -52,7 +62,8 @@ __all__ = [
     "packed_upper_index", "skew_from_theta", "theta_from_skew", "cayley",
     "block_ranges", "orthogonal_blocks", "materialise", "forward",
     "backward", "cayley_vjp", "forward_input_centric",
-    "backward_input_centric", "LayerOracle",
+    "backward_input_centric", "LayerOracle", "CNP_ORDER", "cayley_neumann",
+    "cayley_neumann_vjp", "orthogonal_blocks_cnp",
 ]
 
 
@@ -110,6 +121,55 @@ def cayley(Q: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return R, B
 
 
+# ----------------------------------------- Cayley-Neumann series [CNP]
+CNP_ORDER = 4  # highest power of Q kept: the pages list Q^2, Q^3, Q^4
+
+
+def cayley_neumann(Q: np.ndarray) -> np.ndarray:
+    """Truncated Cayley map of each skew block: (I - Q)^-1 is replaced by its
+    Neumann series up to Q^4 in R = 2 (I - Q)^-1 - I, so
+    R = I + 2 (Q + Q^2 + Q^3 + Q^4). [CNP] Powers are formed one after the
+    other, Q^k = Q^(k-1) Q. Returns R [nb, b, b]; orthogonal only up to
+    O(|Q|^6)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    b = Q.shape[-1]
+    I = np.eye(b)
+    out = np.empty_like(Q)
+    for k, q in enumerate(Q):
+        series = np.zeros((b, b))
+        power = I
+        for _ in range(CNP_ORDER):
+            power = power @ q
+            series = series + power
+        out[k] = I + 2.0 * series
+    return out
+
+
+def cayley_neumann_vjp(Q: np.ndarray, G: np.ndarray) -> np.ndarray:
+    """Gradient of the packed generators given G = dL/dR per block, for
+    R = I + 2 sum_{k=1..4} Q^k.
+
+    d(Q^k) = sum_{i+j=k-1} Q^i dQ Q^j, so
+    dL/dQ = 2 sum_{k=1..4} sum_{i+j=k-1} (Q^T)^i G (Q^T)^j, and, as for the
+    exact map, dL/dtheta_(i,j) = D[i, j] - D[j, i] with D = dL/dQ.
+    (The chain rule of the series; the pages describe no backward.)"""
+    b = Q.shape[-1]
+    iu, ju = packed_upper_index(b)
+    out = np.empty((Q.shape[0], len(iu)), dtype=np.float64)
+    for n in range(Q.shape[0]):
+        Qt = Q[n].T
+        pw = [np.eye(b)]
+        for _ in range(CNP_ORDER - 1):
+            pw.append(pw[-1] @ Qt)
+        D = np.zeros((b, b))
+        for k in range(1, CNP_ORDER + 1):
+            for i in range(k):
+                D += pw[i] @ G[n] @ pw[k - 1 - i]
+        D *= 2.0
+        out[n] = D[iu, ju] - D[ju, iu]
+    return out
+
+
 # ------------------------------------------------------- block structure
 def block_ranges(d: int, b: int) -> List[Tuple[int, int]]:
     """(start, size) of each contiguous block of features; the last block may
@@ -121,6 +181,12 @@ def orthogonal_blocks(theta: np.ndarray, b: int, d: int) -> Tuple[np.ndarray, np
     """theta [nb, b(b-1)/2] -> (R blocks, B blocks) of a block-diagonal
     orthogonal matrix on d features. [SKEW], [BD]"""
     return cayley(skew_from_theta(theta, b, d))
+
+
+def orthogonal_blocks_cnp(theta: np.ndarray, b: int, d: int) -> Tuple[np.ndarray, np.ndarray]:
+    """theta -> (R blocks by the truncated series, Q blocks). [CNP], [BD]"""
+    Q = skew_from_theta(theta, b, d)
+    return cayley_neumann(Q), Q
 
 
 def materialise(W0: np.ndarray, R: np.ndarray, P: np.ndarray, b_out: int, b_in: int) -> np.ndarray:
@@ -173,14 +239,17 @@ def _pad_grad_zero(g: np.ndarray, b: int, d: int) -> np.ndarray:
 
 def backward(g_y: np.ndarray, x: np.ndarray, W0: np.ndarray,
              R: np.ndarray, B_R: np.ndarray, P: np.ndarray, B_P: np.ndarray,
-             b_out: int, b_in: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+             b_out: int, b_in: int, vjp=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Backward of the layer through the materialised weight.
 
     G_W = g_Y^T X is the gradient of the full weight. With W = R (W0 P):
     dL/dR = G_W (W0 P)^T, of which only the diagonal blocks are parameters;
     with W = (R W0) P: dL/dP = (R W0)^T G_W, again block-diagonal part only.
     Returns (g_x, g_theta_R, g_theta_P). [OET], [BD]; backward derived by the
-    chain rule."""
+    chain rule. `vjp(B, G)` maps the block gradients to generator gradients
+    (cayley_vjp with B = (I - Q)^-1 by default; cayley_neumann_vjp with
+    B = Q for the truncated series)."""
+    vjp = cayley_vjp if vjp is None else vjp
     g_y = np.asarray(g_y, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     W0 = np.asarray(W0, dtype=np.float64)
@@ -198,8 +267,8 @@ def backward(g_y: np.ndarray, x: np.ndarray, W0: np.ndarray,
     G_P = np.zeros_like(P)
     for j, (s, r) in enumerate(block_ranges(n, b_in)):
         G_P[j, :r, :r] = RW0[:, s:s + r].T @ G_W[:, s:s + r]
-    g_tR = _pad_grad_zero(cayley_vjp(B_R, G_R), b_out, m)
-    g_tP = _pad_grad_zero(cayley_vjp(B_P, G_P), b_in, n)
+    g_tR = _pad_grad_zero(vjp(B_R, G_R), b_out, m)
+    g_tP = _pad_grad_zero(vjp(B_P, G_P), b_in, n)
     return g_x, g_tR, g_tP
 
 
@@ -223,10 +292,11 @@ def forward_input_centric(x, W0, R, P, b_out, b_in):
     return Y, Z, U
 
 
-def backward_input_centric(g_y, x, W0, R, B_R, P, B_P, b_out, b_in):
+def backward_input_centric(g_y, x, W0, R, B_R, P, B_P, b_out, b_in, vjp=None):
     """Backward along the input-centric dataflow:
     g_Z = g_Y R, G_R[k] = g_Y[:, k]^T Z[:, k], g_U = g_Z W0,
     G_P[j] = g_U[:, j]^T X[:, j], g_X = g_U P. [IC], chain rule."""
+    vjp = cayley_vjp if vjp is None else vjp
     g_y = np.asarray(g_y, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     W0 = np.asarray(W0, dtype=np.float64)
@@ -241,21 +311,27 @@ def backward_input_centric(g_y, x, W0, R, B_R, P, B_P, b_out, b_in):
     for j, (s, r) in enumerate(block_ranges(n, b_in)):
         G_P[j, :r, :r] = g_U[:, s:s + r].T @ x[:, s:s + r]
     g_x = _apply_blocks(g_U, P, b_in, transpose=False)
-    g_tR = _pad_grad_zero(cayley_vjp(B_R, G_R), b_out, m)
-    g_tP = _pad_grad_zero(cayley_vjp(B_P, G_P), b_in, n)
+    g_tR = _pad_grad_zero(vjp(B_R, G_R), b_out, m)
+    g_tP = _pad_grad_zero(vjp(B_P, G_P), b_in, n)
     return g_x, g_tR, g_tP
 
 
 class LayerOracle:
-    """One layer's full oracle result (Cayley build, forward, backward),
-    computed through the materialised weight."""
+    """One layer's full oracle result (orthogonal build, forward, backward),
+    computed through the materialised weight. map: "cayley" (exact) or "cnp"
+    (truncated Cayley-Neumann series); B_R / B_P hold what that map's VJP
+    needs ((I - Q)^-1 or Q)."""
 
-    def __init__(self, W0, theta_R, theta_P, b_out, b_in):
+    def __init__(self, W0, theta_R, theta_P, b_out, b_in, map="cayley"):
         self.W0 = np.asarray(W0, dtype=np.float64)
         m, n = self.W0.shape
         self.b_out, self.b_in = b_out, b_in
-        self.R, self.B_R = orthogonal_blocks(theta_R, b_out, m)
-        self.P, self.B_P = orthogonal_blocks(theta_P, b_in, n)
+        if map not in ("cayley", "cnp"):
+            raise ValueError(f"unknown orthogonal map {map!r}")
+        build = orthogonal_blocks if map == "cayley" else orthogonal_blocks_cnp
+        self.vjp = cayley_vjp if map == "cayley" else cayley_neumann_vjp
+        self.R, self.B_R = build(theta_R, b_out, m)
+        self.P, self.B_P = build(theta_P, b_in, n)
         self.W = materialise(self.W0, self.R, self.P, b_out, b_in)
 
     def forward(self, x):
@@ -263,4 +339,4 @@ class LayerOracle:
 
     def backward(self, g_y, x):
         return backward(g_y, x, self.W0, self.R, self.B_R, self.P, self.B_P,
-                        self.b_out, self.b_in)
+                        self.b_out, self.b_in, self.vjp)

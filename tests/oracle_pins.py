@@ -293,9 +293,149 @@ def pin_padding_gradients():
     assert np.all(gR[-1, pad_R] == 0.0) and np.any(pad_R)
 
 
+# ------------------------------------------ Cayley-Neumann series (CNP)
+def load_cnp_closed_forms():
+    """(kind, name, b, theta, values, grad) rows of the hand-derived CNP file."""
+    rows = []
+    with open(os.path.join(GOLDEN, "cnp_closed_forms.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = [c.strip() for c in line.split("|")]
+            kind, name, b, th = parts[0], parts[1], int(parts[2]), parts[3]
+            theta = np.array([float(v) for v in th.split(",")])
+            vals = np.array([float(v) for v in parts[4].split(",")]).reshape(b, b)
+            grad = float(parts[5]) if kind == "G" else None
+            rows.append((kind, name, b, theta, vals, grad))
+    return rows
+
+
+def pin_cnp_golden(tol=1e-15):
+    """The truncated series and its derivative on the hand-derived b = 2 and
+    b = 4 cases (values exact in binary or within a few ulps)."""
+    rows = load_cnp_closed_forms()
+    assert sum(r[0] == "R" for r in rows) >= 6 and sum(r[0] == "G" for r in rows) >= 4
+    for kind, name, b, theta, vals, grad in rows:
+        Q = O.skew_from_theta(theta[None, :], b)
+        if kind == "R":
+            R = O.cayley_neumann(Q)[0]
+            scale = max(1.0, np.abs(vals).max())
+            assert np.max(np.abs(R - vals)) <= 8 * tol * scale, (name, R, vals)
+        else:
+            g = O.cayley_neumann_vjp(Q, vals[None])[0]
+            assert g.shape == (1,) and abs(g[0] - grad) <= 1e-14, (name, g, grad)
+
+
+def pin_cnp_b3_closed_form():
+    """b = 3: Q = [w]_x has Q^3 = -|w|^2 Q and Q^4 = -|w|^2 Q^2, so the series
+    is R = I + 2 (1 - |w|^2)(Q + Q^2), with Q^2 = w w^T - |w|^2 I."""
+    rng = np.random.default_rng(41)
+    for _ in range(20):
+        w = rng.standard_normal(3) * rng.uniform(0.05, 1.5)
+        # theta order (0,1), (0,2), (1,2) holds Q entries -w2, w1, -w0
+        theta = np.array([[-w[2], w[1], -w[0]]])
+        K = _cross(w)
+        n2 = float(w @ w)
+        K2 = np.outer(w, w) - n2 * np.eye(3)
+        ref = np.eye(3) + 2.0 * (1.0 - n2) * (K + K2)
+        R = O.cayley_neumann(O.skew_from_theta(theta, 3))[0]
+        assert np.max(np.abs(R - ref)) <= 1e-13 * max(1.0, np.abs(ref).max()), (w, R, ref)
+
+
+def pin_cnp_series_tail():
+    """Exact map minus truncated series is the tail 2 sum_{k>=5} Q^k =
+    2 Q^5 (I - Q)^-1, computed from the (separately pinned) exact map and an
+    independent solve; at small |Q| the two maps agree to O(|Q|^5)."""
+    rng = np.random.default_rng(43)
+    for b, sigma in ((5, 0.3), (16, 0.05), (32, 0.02), (7, 0.6)):
+        th = rng.standard_normal((3, b * (b - 1) // 2)) * sigma
+        Q = O.skew_from_theta(th, b)
+        R_exact, _ = O.cayley(Q)
+        R_cnp = O.cayley_neumann(Q)
+        for k in range(3):
+            tail = 2.0 * np.linalg.matrix_power(Q[k], 5) @ np.linalg.solve(np.eye(b) - Q[k], np.eye(b))
+            diff = R_exact[k] - R_cnp[k]
+            assert np.max(np.abs(diff - tail)) <= 1e-13 * max(1.0, np.abs(tail).max()), (b, sigma)
+            assert np.abs(tail).max() > 0.0
+
+
+def pin_cnp_vjp_frechet():
+    """The VJP of a real matrix polynomial p at Q is the Frechet derivative of
+    p at Q^T in the direction G: the upper-right block of p applied to the
+    block-triangular [[Q^T, G], [0, Q^T]]. Evaluated with the series itself
+    (independently of the VJP's double sum), then packed."""
+    rng = np.random.default_rng(47)
+    for b, sigma in ((4, 0.5), (9, 0.2), (16, 0.1)):
+        th = rng.standard_normal((2, b * (b - 1) // 2)) * sigma
+        Q = O.skew_from_theta(th, b)
+        G = rng.standard_normal((2, b, b))
+        got = O.cayley_neumann_vjp(Q, G)
+        iu, ju = O.packed_upper_index(b)
+        for k in range(2):
+            M = np.zeros((2 * b, 2 * b))
+            M[:b, :b] = Q[k].T
+            M[b:, b:] = Q[k].T
+            M[:b, b:] = G[k]
+            D = O.cayley_neumann(M[None])[0][:b, b:]
+            ref = D[iu, ju] - D[ju, iu]
+            assert np.max(np.abs(got[k] - ref)) <= 1e-13 * np.abs(ref).max(), (b, k)
+
+
+def pin_cnp_theta_zero():
+    """theta = 0: the series gives R = I and the same generator gradient as
+    the exact map, 2 (G - G^T) packed."""
+    rng = np.random.default_rng(53)
+    b = 8
+    Q = np.zeros((3, b, b))
+    G = rng.standard_normal((3, b, b))
+    assert np.array_equal(O.cayley_neumann(Q), np.broadcast_to(np.eye(b), Q.shape))
+    iu, ju = O.packed_upper_index(b)
+    ref = 2.0 * (G[:, iu, ju] - G[:, ju, iu])
+    assert np.max(np.abs(O.cayley_neumann_vjp(Q, G) - ref)) <= 1e-14
+
+
+def pin_cnp_finite_differences(h=1e-6, rtol=1e-6):
+    """Central differences of L = <g_y, y> for the layer built with the
+    series, against the oracle's backward, for every generator and x entry;
+    with b dividing d and (second case) with a padded last block, whose
+    padded entries must have zero gradient."""
+    for (m, n, b, N, seed) in ((8, 8, 4, 5, 59), (10, 6, 4, 3, 61)):
+        W0, thR, thP, x, g_y = _layer(m, n, b, b, N, 0.3, seed)
+
+        def loss(thR_, thP_, x_):
+            return float(np.sum(g_y * O.LayerOracle(W0, thR_, thP_, b, b, map="cnp").forward(x_)))
+
+        g_x, gR, gP = O.LayerOracle(W0, thR, thP, b, b, map="cnp").backward(g_y, x)
+
+        def fd(arr, fn):
+            out = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                a1 = arr.copy(); a1[idx] += h
+                a2 = arr.copy(); a2[idx] -= h
+                out[idx] = (fn(a1) - fn(a2)) / (2 * h)
+            return out
+
+        fR = fd(thR, lambda a: loss(a, thP, x))
+        fP = fd(thP, lambda a: loss(thR, a, x))
+        fx = fd(x, lambda a: loss(thR, thP, a))
+        for got, ref in ((gR, fR), (gP, fP), (g_x, fx)):
+            scale = np.abs(ref).max()
+            assert np.max(np.abs(got - ref)) <= rtol * scale, (np.max(np.abs(got - ref)), scale)
+        if m % b:
+            iu, ju = O.packed_upper_index(b)
+            r = m - (gR.shape[0] - 1) * b
+            pad = (iu >= r) | (ju >= r)
+            assert np.all(gR[-1, pad] == 0.0) and np.any(pad)
+            R = O.LayerOracle(W0, thR, thP, b, b, map="cnp").R
+            assert np.array_equal(R[-1, r:, r:], np.eye(b - r))
+
+
 ALL_PINS = [
     pin_packing_order, pin_golden_closed_forms, pin_b2_rotation, pin_b3_rodrigues,
     pin_eigenvalue_map, pin_orthogonality_det_transpose, pin_spectrum,
     pin_dense_block_diag, pin_input_centric_equals_materialised, pin_theta_zero,
     pin_vjp_forms, pin_adjoint, pin_finite_differences, pin_padding_gradients,
+    pin_cnp_golden, pin_cnp_b3_closed_form, pin_cnp_series_tail, pin_cnp_vjp_frechet,
+    pin_cnp_theta_zero, pin_cnp_finite_differences,
 ]

@@ -39,6 +39,20 @@ MUTATIONS = [
      [pins.pin_finite_differences]),
     ("skew_from_theta", "if r < b:\n            Q[-1, r:, :] = 0.0", "if False:\n            Q[-1, r:, :] = 0.0",
      [pins.pin_dense_block_diag, pins.pin_padding_gradients]),
+    # Cayley-Neumann series and its VJP
+    ("cayley_neumann", "for _ in range(CNP_ORDER):", "for _ in range(CNP_ORDER - 1):",
+     [pins.pin_cnp_golden, pins.pin_cnp_series_tail]),
+    ("cayley_neumann", "out[k] = I + 2.0 * series", "out[k] = I + series",
+     [pins.pin_cnp_golden, pins.pin_cnp_b3_closed_form]),
+    ("cayley_neumann", "power = power @ q", "power = power @ q.T",
+     [pins.pin_cnp_golden, pins.pin_cnp_series_tail]),
+    ("cayley_neumann_vjp", "D += pw[i] @ G[n] @ pw[k - 1 - i]", "D += pw[i] @ G[n].T @ pw[k - 1 - i]",
+     [pins.pin_cnp_finite_differences, pins.pin_cnp_vjp_frechet]),
+    ("cayley_neumann_vjp", "Qt = Q[n].T", "Qt = Q[n]",
+     [pins.pin_cnp_golden, pins.pin_cnp_vjp_frechet]),
+    ("cayley_neumann_vjp", "D += pw[i] @ G[n] @ pw[k - 1 - i]", "D += pw[i] @ G[n] @ pw[i]",
+     [pins.pin_cnp_finite_differences, pins.pin_cnp_vjp_frechet]),
+    ("cayley_neumann_vjp", "D *= 2.0", "D *= 1.0", [pins.pin_cnp_golden, pins.pin_cnp_theta_zero]),
 ]
 
 
