@@ -50,7 +50,7 @@ def layer_work(s):
     return flops, fwd + bwd + build
 
 
-def cpu_baseline(spec, sample_tokens):
+def cpu_baseline(spec, sample_tokens, map="cayley"):
     """The float64 oracle (build, materialise, forward, backward) on the first
     `sample_tokens` tokens of the workload, timed on the host's cores."""
     import dataclasses
@@ -67,7 +67,7 @@ def cpu_baseline(spec, sample_tokens):
     # repeat the whole oracle step until about 10 s of CPU work (at most 6 reps)
     reps, t0 = 0, time.perf_counter()
     while True:
-        ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b)
+        ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b, map=map)
         ora.forward(x)
         ora.backward(g_y, x)
         reps += 1
@@ -82,14 +82,15 @@ def cpu_baseline(spec, sample_tokens):
                       f"{spec.d_out}x{spec.d_in} b={spec.b}; {dt:.1f} s"}
 
 
-def parity_sample(L, out, lay, rows=32):
+def parity_sample(L, out, lay, rows=32, map="cayley"):
     """Frobenius-relative error of sampled token rows of y and g_x against the
     oracle's materialised weight (the full-size parity tests do more)."""
     import oracle.poetx_oracle as O
     import torch
     s = L.spec
-    R, _ = O.orthogonal_blocks(L.theta_R, s.b, s.d_out)
-    Pb, _ = O.orthogonal_blocks(L.theta_P, s.b, s.d_in)
+    build = O.orthogonal_blocks if map == "cayley" else O.orthogonal_blocks_cnp
+    R, _ = build(L.theta_R, s.b, s.d_out)
+    Pb, _ = build(L.theta_P, s.b, s.d_in)
     W = O.materialise(L.W0, R, Pb, s.b, s.b)
     idx = np.linspace(0, s.tokens - 1, rows).astype(np.int64)
     ti = torch.from_numpy(idx).cuda()
@@ -156,6 +157,9 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--recompute-z", action="store_true",
                     help="POET-Xmem variant: the forward keeps no Z, the backward recomputes it")
+    ap.add_argument("--map", choices=("cayley", "cnp"), default="cayley",
+                    help="orthogonal map: exact Cayley (default) or the truncated "
+                         "Cayley-Neumann series")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -184,7 +188,7 @@ def main():
     for s in specs:
         L = make_layer(s)
         lay = PoetxLinear(torch.from_numpy(L.W0).to(tdt[s.dtype]), s.b, s.b, s.dtype, device=dev,
-                          recompute_z=args.recompute_z)
+                          recompute_z=args.recompute_z, map=args.map)
         lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
         x = torch.from_numpy(L.x).to(tdt[s.dtype]).to(dev)
         g_y = torch.from_numpy(L.g_y).to(tdt[s.dtype]).to(dev)
@@ -285,8 +289,10 @@ def main():
         "config": {"workload": args.config,
                    "layers": [f"{s.name} {s.d_out}x{s.d_in} b={s.b}" for s in specs],
                    "tokens": tokens, "block": specs[0].b,
-                   "variant": "POET-Xmem (Z recomputed in the backward)" if args.recompute_z
-                   else "POET-X (Z kept for the backward)"},
+                   "variant": ("POET-Xmem (Z recomputed in the backward)" if args.recompute_z
+                               else "POET-X (Z kept for the backward)"),
+                   "orthogonal_map": ("exact Cayley" if args.map == "cayley"
+                                      else "Cayley-Neumann series to Q^4")},
         "roofline": roofline,
         "layer_roofline": {"flops": F, "bytes": B, "t_roof_ms": t_roof * 1e3,
                            "frac": t_roof / (ms_per_step / 1e3),
@@ -297,10 +303,10 @@ def main():
     }
     if not args.no_parity and len(layers) == 1:
         s, L, lay, x, g_y, o = layers[0]
-        res["parity"] = parity_sample(L, dict(y=o["y"], g_x=o["g_x"]), lay)
+        res["parity"] = parity_sample(L, dict(y=o["y"], g_x=o["g_x"]), lay, map=args.map)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(specs[-1] if len(specs) == 1 else specs[0],
-                                           min(args.cpu_sample, specs[0].tokens))
+                                           min(args.cpu_sample, specs[0].tokens), map=args.map)
     res["gpu"] = torch.cuda.get_device_name(0)
     print(json.dumps(res), flush=True)
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define POETX_ABI_VERSION 2
+#define POETX_ABI_VERSION 3
 
 typedef enum poetx_status {
   POETX_OK = 0,
@@ -83,6 +83,11 @@ typedef enum poetx_dtype { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
  * its own workspace (one extra dense product). Results are those of the
  * stored-Z path. */
 #define POETX_RECOMPUTE_Z 1
+/* The blocks were built by the truncated Cayley-Neumann series
+ * (poetx_build_cnp) rather than the exact Cayley map: the backward then takes
+ * the skew blocks Q in place of the float32 orthogonal blocks and applies the
+ * series' VJP (section 2 Methodik, Cayley-Neumann parameterisation item). */
+#define POETX_CAYLEY_NEUMANN 2
 
 /* Shape of one POET-X linear layer. */
 typedef struct poetx_linear_desc {
@@ -93,7 +98,7 @@ typedef struct poetx_linear_desc {
   int32_t b_out;  /* block size of R */
   int32_t act;    /* poetx_dtype of the activations, W0 and the *_act blocks */
   int32_t n_events; /* number of entries in `events` (0 = no stage timing) */
-  int32_t flags;    /* 0 or POETX_RECOMPUTE_Z */
+  int32_t flags;    /* 0 or POETX_RECOMPUTE_Z | POETX_CAYLEY_NEUMANN */
   int32_t reserved; /* must be 0 */
   /* Optional stage timing: an array of hipEvent_t created by the caller (for
    * example with poetx_event_create). When n_events >= 2 s + 2, the call
@@ -149,6 +154,32 @@ int poetx_build_orthogonal(const float* theta, int64_t d, int32_t b,
                            float* blocks_f32, void* blocks_act, int32_t act,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes poetx_build_cnp needs for d features, block size b (0 for
+ * invalid sizes, including b not a multiple of 4). */
+size_t poetx_build_cnp_workspace_size(int64_t d, int32_t b);
+
+/*
+ * poetx_build_cnp - packed skew generators to blocks by the truncated
+ * Cayley-Neumann series (section 2 Methodik, Cayley-Neumann parameterisation
+ * item: the Cayley map approximated by a Neumann series whose higher terms
+ * are Q^2, Q^3, Q^4). The series truncates (I - Q)^-1 inside
+ * R = 2 (I - Q)^-1 - I:
+ *   R_k = I + 2 (Q_k + Q_k^2 + Q_k^3 + Q_k^4),
+ * orthogonal only up to O(|Q|^6) and divergent from the exact map for
+ * |Q| >= 1. Products in float32 on MFMA.
+ *
+ *   theta, d, act, blocks_act, ws  as for poetx_build_orthogonal, with
+ *               ws of poetx_build_cnp_workspace_size(d, b) bytes.
+ *   b           block size, 4 <= b <= 4096, b % 4 == 0 (else POETX_ERR_ALIGN).
+ *   q_f32       out [nb, b, b] float32: the skew blocks Q_k (generators of a
+ *               padded last block's rows/columns past d are zero). Pass them
+ *               as R_f32 / P_f32 to poetx_linear_bwd with POETX_CAYLEY_NEUMANN.
+ *   blocks_f32  out [nb, b, b] float32: R_k.
+ * Errors as poetx_build_orthogonal; q_f32 must overlap no other argument.
+ */
+int poetx_build_cnp(const float* theta, int64_t d, int32_t b, float* q_f32, float* blocks_f32,
+                    void* blocks_act, int32_t act, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for poetx_linear_fwd / poetx_linear_bwd (0 if the
  * descriptor is invalid). With POETX_RECOMPUTE_Z the forward's includes Z. */
 size_t poetx_fwd_workspace_size(const poetx_linear_desc* desc);
@@ -183,14 +214,19 @@ int poetx_linear_fwd(const poetx_linear_desc* desc, const void* x, const void* W
  *   g_theta(i, j) = M[i][j] - M[j][i] for i < j
  *   (bf16 mode: G and S = R G^T + G^T are rounded to bf16 for the two VJP
  *   products, which accumulate in float32).
+ *   With POETX_CAYLEY_NEUMANN, the series' VJP instead:
+ *   D = 2 sum_{k=1..4} sum_{i+j=k-1} (Q^T)^i G (Q^T)^j,
+ *   g_theta(i, j) = D[i][j] - D[j][i], all in float32.
  * The token reductions are split over workgroups and summed in a fixed
  * order, so results are bitwise reproducible.
  *
  *   g_y        [tokens, d_out] act
  *   x          [tokens, d_in]  act
  *   W0         [d_out, d_in]   act
- *   R_f32      [nb_out, b_out, b_out] float32, P_f32 [nb_in, b_in, b_in] float32
- *   R_act, P_act  the act copies of the same blocks
+ *   R_f32      [nb_out, b_out, b_out] float32, P_f32 [nb_in, b_in, b_in] float32:
+ *              the orthogonal blocks, or with POETX_CAYLEY_NEUMANN the skew
+ *              blocks q_f32 of poetx_build_cnp
+ *   R_act, P_act  the act copies of the orthogonal blocks
  *   z_saved    [tokens, d_out] act, z_save of the matching forward; NULL
  *              (and only NULL) when desc->flags has POETX_RECOMPUTE_Z
  *   g_x        out [tokens, d_in] act

@@ -47,7 +47,8 @@ int check_desc(const poetx_linear_desc* d) {
   if (d->b_in > d->d_in || d->b_out > d->d_out) return POETX_ERR_SHAPE;
   if (ceil_div(d->d_in, d->b_in) > kMaxBatch || ceil_div(d->d_out, d->b_out) > kMaxBatch) return POETX_ERR_SHAPE;
   if (d->n_events < 0 || (d->n_events > 0 && !d->events)) return POETX_ERR_NULL;
-  if ((d->flags & ~POETX_RECOMPUTE_Z) != 0 || d->reserved != 0) return POETX_ERR_SHAPE;
+  if ((d->flags & ~(POETX_RECOMPUTE_Z | POETX_CAYLEY_NEUMANN)) != 0 || d->reserved != 0)
+    return POETX_ERR_SHAPE;
   const int v = act_vec(d->act);
   if (d->d_in % v || d->d_out % v || d->b_in % v || d->b_out % v) return POETX_ERR_ALIGN;
   return POETX_OK;
@@ -55,6 +56,7 @@ int check_desc(const poetx_linear_desc* d) {
 
 // ---------------------------------------------------------------- workspace
 bool recompute_z(const poetx_linear_desc* d) { return (d->flags & POETX_RECOMPUTE_Z) != 0; }
+bool neumann(const poetx_linear_desc* d) { return (d->flags & POETX_CAYLEY_NEUMANN) != 0; }
 
 struct FwdPlan {
   size_t u_off, z_off, total;
@@ -272,6 +274,61 @@ hipError_t cayley_vjp(DType t, const VjpSet& a, const VjpSet* b2, int b, hipStre
                                       -1.0f, b2->g_theta, s);
 }
 
+// VJP of the truncated Cayley-Neumann series R = I + 2 (Q + Q^2 + Q^3 + Q^4)
+// for every block, float32 throughout (the factored form is derived in
+// cnp.hip):
+//   Q2 = Q Q -> w1;  Tt = Q2 - Q -> w2;  Tbar = 2 G Q2 + 2 G -> w3;
+//   Nbar = 2 Tt G -> w1;  Ws = (Tbar + Nbar) + (Tbar + Nbar)^T -> w2;
+//   X = Tbar - Ws Q -> w1;  g_theta(i, j) = X[i][j] - X[j][i].
+// w1..w3 are b x b float32 scratch sets; G and Q are only read. A second
+// block set of the same size shares the GEMM launches.
+struct CnpVjpSet {
+  const float* G;  // float32 gram (dL/dR per block)
+  const float* Q;  // float32 skew blocks
+  float* w1;
+  float* w2;
+  float* w3;
+  float* g_theta;
+  int64_t d;
+};
+hipError_t cnp_vjp(const CnpVjpSet& a, const CnpVjpSet* b2, int b, hipStream_t s) {
+  const int64_t nb1 = ceil_div(a.d, b);
+  const int64_t nb2 = b2 ? ceil_div(b2->d, b) : 0;
+  const int64_t bb = (int64_t)b * b;
+  GemmParams g;
+  g.lda = g.ldb = g.ldc = g.ldd = b;
+  g.sA = g.sB = g.sC = g.sD = bb;
+  g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = b;
+  g.kchunk = b;
+  g.batch = (int)(nb1 + nb2);
+  if (b2) g.batch_split = (int)nb1;
+  // C = alpha A B + beta D per block (A, B row-major b x b)
+  auto mm = [&](const float* A1, const float* B1, float* C1, const float* D1, const float* A2,
+                const float* B2, float* C2, const float* D2, float alpha, float beta) {
+    g.A = A1; g.B = B1; g.C = C1; g.D = D1;
+    g.A2 = A2; g.B2 = B2; g.C2 = C2; g.D2 = D2;
+    g.alpha = alpha; g.beta = beta;
+    return poetx::launch_gemm(DType::F32, DType::F32, true, false, g, s);
+  };
+  const CnpVjpSet z{};
+  const CnpVjpSet& c = b2 ? *b2 : z;
+  hipError_t e;
+  if ((e = mm(a.Q, a.Q, a.w1, nullptr, c.Q, c.Q, c.w1, nullptr, 1.0f, 0.0f)) != hipSuccess) return e;
+  if ((e = poetx::launch_sub(a.w1, a.Q, a.w2, nb1 * bb, s)) != hipSuccess) return e;
+  if (b2 && (e = poetx::launch_sub(c.w1, c.Q, c.w2, nb2 * bb, s)) != hipSuccess) return e;
+  if ((e = mm(a.G, a.w1, a.w3, a.G, c.G, c.w1, c.w3, c.G, 2.0f, 2.0f)) != hipSuccess) return e;
+  if ((e = mm(a.w2, a.G, a.w1, nullptr, c.w2, c.G, c.w1, nullptr, 2.0f, 0.0f)) != hipSuccess) return e;
+  if ((e = poetx::launch_sym_sum(a.w3, a.w1, a.w2, nb1, b, s)) != hipSuccess) return e;
+  if (b2 && (e = poetx::launch_sym_sum(c.w3, c.w1, c.w2, nb2, b, s)) != hipSuccess) return e;
+  if ((e = mm(a.w2, a.Q, a.w1, a.w3, c.w2, c.Q, c.w1, c.w3, -1.0f, 1.0f)) != hipSuccess) return e;
+  if ((e = poetx::launch_pack_skew_grad(a.w1, nullptr, 0.0f, nb1, b, (int)(a.d - (nb1 - 1) * b),
+                                        1.0f, a.g_theta, s)) != hipSuccess)
+    return e;
+  if (!b2) return hipSuccess;
+  return poetx::launch_pack_skew_grad(c.w1, nullptr, 0.0f, nb2, b, (int)(c.d - (nb2 - 1) * b),
+                                      1.0f, c.g_theta, s);
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? POETX_OK : POETX_ERR_HIP; }
 
 }  // namespace
@@ -329,6 +386,79 @@ int poetx_build_orthogonal(const float* theta, int64_t d, int32_t b, float* bloc
                                                act == POETX_BF16 ? DType::BF16 : DType::F32,
                                                static_cast<float*>(ws),
                                                static_cast<hipStream_t>(stream)));
+}
+
+size_t poetx_build_cnp_workspace_size(int64_t d, int32_t b) {
+  if (d < 1 || b < 4 || b > kMaxBlock || b > d || b % 4) return 0;
+  const int64_t nb = ceil_div(d, b);
+  if (nb > kMaxBatch) return 0;
+  return 2 * align_up((size_t)nb * b * b * sizeof(float));
+}
+
+int poetx_build_cnp(const float* theta, int64_t d, int32_t b, float* q_f32, float* blocks_f32,
+                    void* blocks_act, int32_t act, void* ws, size_t ws_bytes, void* stream) {
+  if (act != POETX_F32 && act != POETX_BF16) return POETX_ERR_DTYPE;
+  if (d < 1 || b < 1 || b > kMaxBlock || b > d) return POETX_ERR_SHAPE;
+  const int64_t nb = ceil_div(d, b);
+  if (nb > kMaxBatch) return POETX_ERR_SHAPE;
+  if (b % 4) return POETX_ERR_ALIGN;
+  if (!theta || !q_f32 || !blocks_f32 || (act == POETX_BF16 && !blocks_act)) return POETX_ERR_NULL;
+  if (!aligned16(q_f32) || !aligned16(blocks_f32) || (act == POETX_BF16 && !aligned16(blocks_act)))
+    return POETX_ERR_ALIGN;
+  const size_t need = poetx_build_cnp_workspace_size(d, b);
+  if (!ws || ws_bytes < need) return POETX_ERR_WORKSPACE;
+  if (!aligned16(ws)) return POETX_ERR_ALIGN;
+  const size_t blocks_bytes = (size_t)nb * b * b * 4;
+  const Range out_q = range_of(q_f32, blocks_bytes);
+  const Range out_f32 = range_of(blocks_f32, blocks_bytes);
+  const Range out_act = range_of(blocks_act, act == POETX_BF16 ? blocks_bytes / 2 : 0);
+  const Range in_theta = range_of(theta, (size_t)poetx_theta_count(d, b) * 4);
+  const Range r_ws = range_of(ws, need);
+  const Range outs[] = {out_q, out_f32, out_act};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], in_theta) || overlap(outs[i], r_ws)) return POETX_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return POETX_ERR_ALIAS;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int last = (int)(d - (nb - 1) * b);
+  const int64_t bb = (int64_t)b * b;
+  float* Q2 = static_cast<float*>(ws);
+  float* E = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(blocks_bytes));
+  hipError_t e;
+  // Q (generators past d taken as zero, so a padded block's R is identity there)
+  if ((e = poetx::launch_expand_skew(theta, nb, b, last, 0.0f, 1.0f, q_f32, s)) != hipSuccess)
+    return hip_status(e);
+  GemmParams g;
+  g.lda = g.ldb = g.ldc = g.ldd = b;
+  g.sA = g.sB = g.sC = g.sD = bb;
+  g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = b;
+  g.kchunk = b;
+  g.batch = (int)nb;
+  // Q2 = Q Q
+  g.A = q_f32; g.B = q_f32; g.C = Q2;
+  if ((e = poetx::launch_gemm(DType::F32, DType::F32, true, false, g, s)) != hipSuccess)
+    return hip_status(e);
+  // E = Q2 Q2 + Q2 and F = Q Q2 + Q (F into blocks_f32), one launch when the
+  // two segments fit the grid
+  g.beta = 1.0f;
+  g.A = Q2; g.B = Q2; g.C = E; g.D = Q2;
+  if (2 * nb <= kMaxBatch) {
+    g.batch = (int)(2 * nb);
+    g.batch_split = (int)nb;
+    g.A2 = q_f32; g.B2 = Q2; g.C2 = blocks_f32; g.D2 = q_f32;
+    if ((e = poetx::launch_gemm(DType::F32, DType::F32, true, false, g, s)) != hipSuccess)
+      return hip_status(e);
+  } else {
+    if ((e = poetx::launch_gemm(DType::F32, DType::F32, true, false, g, s)) != hipSuccess)
+      return hip_status(e);
+    g.A = q_f32; g.B = Q2; g.C = blocks_f32; g.D = q_f32;
+    if ((e = poetx::launch_gemm(DType::F32, DType::F32, true, false, g, s)) != hipSuccess)
+      return hip_status(e);
+  }
+  // R = I + 2 (E + F), in place, and the bf16 copy
+  return hip_status(poetx::launch_cnp_finish(E, blocks_f32, act == POETX_BF16 ? blocks_act : nullptr,
+                                             nb, b, s));
 }
 
 size_t poetx_fwd_workspace_size(const poetx_linear_desc* d) {
@@ -440,6 +570,8 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   float* MR = reinterpret_cast<float*>(w + plan.MR);
   float* MP = reinterpret_cast<float*>(w + plan.MP);
   const int lastR = (int)(m - (nbR - 1) * bR), lastP = (int)(n - (nbP - 1) * bP);
+  // the reduced grams: activation type for the Cayley VJP, float32 for the series
+  const DType gt = neumann(d) ? DType::F32 : t;
   Stages sg{d, s};
   hipError_t e;
 #define POETX_TRY(call)                            \
@@ -458,7 +590,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     hipError_t r;
     if ((r = sg.begin(1)) != hipSuccess) return r;
     if ((r = block_gram(t, g_y, Z, partR, N, m, bR, plan.sR, s)) != hipSuccess) return r;
-    if ((r = poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, t, s)) !=
+    if ((r = poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, gt, s)) !=
         hipSuccess)
       return r;
     return sg.end(1);
@@ -485,7 +617,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   // B4: G_P[j] = g_U[:, j]^T X[:, j]
   POETX_TRY(sg.begin(3));
   POETX_TRY(block_gram(t, gU, x, partP, N, n, bP, plan.sP, s));
-  POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, t, s));
+  POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, gt, s));
   POETX_TRY(sg.end(3));
 
   // B5: g_X = g_U blockdiag(P)
@@ -493,20 +625,34 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   POETX_TRY(block_apply(t, gU, P_act, g_x, N, n, bP, false, s));
   POETX_TRY(sg.end(4));
 
-  // B6: Cayley VJP of R and of P (one set of launches when b_in == b_out;
-  // stage 6 is then empty)
-  const VjpSet vR{GR, R_f32, R_act, TR, MR, g_theta_R, m};
-  const VjpSet vP{GP, P_f32, P_act, TP, MP, g_theta_P, n};
-  POETX_TRY(sg.begin(5));
-  if (bR == bP && bR > 1) {
-    POETX_TRY(cayley_vjp(t, vR, &vP, bR, s));
-  } else if (bR > 1) {
-    POETX_TRY(cayley_vjp(t, vR, nullptr, bR, s));
+  // B6: VJP of the orthogonal map for R and for P (one set of launches when
+  // b_in == b_out and both sets fit one grid; stage 6 is then empty)
+  const bool merged = bR == bP && nbR + nbP <= kMaxBatch;
+  if (neumann(d)) {
+    // R_f32 / P_f32 hold the skew blocks Q; the partial-gram, T and M
+    // buffers are free once the grams are reduced
+    const CnpVjpSet cR{GR, R_f32, partR, TR, MR, g_theta_R, m};
+    const CnpVjpSet cP{GP, P_f32, partP, TP, MP, g_theta_P, n};
+    POETX_TRY(sg.begin(5));
+    POETX_TRY(cnp_vjp(cR, merged ? &cP : nullptr, bR, s));
+    POETX_TRY(sg.end(5));
+    POETX_TRY(sg.begin(6));
+    if (!merged) POETX_TRY(cnp_vjp(cP, nullptr, bP, s));
+    POETX_TRY(sg.end(6));
+  } else {
+    const VjpSet vR{GR, R_f32, R_act, TR, MR, g_theta_R, m};
+    const VjpSet vP{GP, P_f32, P_act, TP, MP, g_theta_P, n};
+    POETX_TRY(sg.begin(5));
+    if (merged && bR > 1) {
+      POETX_TRY(cayley_vjp(t, vR, &vP, bR, s));
+    } else if (bR > 1) {
+      POETX_TRY(cayley_vjp(t, vR, nullptr, bR, s));
+    }
+    POETX_TRY(sg.end(5));
+    POETX_TRY(sg.begin(6));
+    if (!merged && bP > 1) POETX_TRY(cayley_vjp(t, vP, nullptr, bP, s));
+    POETX_TRY(sg.end(6));
   }
-  POETX_TRY(sg.end(5));
-  POETX_TRY(sg.begin(6));
-  if (bR != bP && bP > 1) POETX_TRY(cayley_vjp(t, vP, nullptr, bP, s));
-  POETX_TRY(sg.end(6));
 #undef POETX_TRY
   return POETX_OK;
 }

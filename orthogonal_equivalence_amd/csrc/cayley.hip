@@ -45,13 +45,14 @@ __device__ __forceinline__ int packed_index(int b, int i, int j) {
   return i * (2 * b - i - 1) / 2 + (j - i - 1);
 }
 
-// A = I - Q for every block; the last block's rows/columns >= last_valid
-// are identity. grid (tiles of 32 x 32, nblocks). A tile below the diagonal
-// reads its generators from the mirrored tile above it (coalesced along the
-// packed rows) and transposes through LDS.
+// A = diag I + sign Q for every block (I - Q for the exact map, Q itself for
+// the series); the generators of the last block's rows/columns >= last_valid
+// are taken as zero. grid (tiles of 32 x 32, nblocks). A tile below the
+// diagonal reads its generators from the mirrored tile above it (coalesced
+// along the packed rows) and transposes through LDS.
 __global__ void __launch_bounds__(kNT)
-expand_kernel(const float* __restrict__ theta, int nblocks, int b, int last_valid,
-              float* __restrict__ A) {
+expand_kernel(const float* __restrict__ theta, int nblocks, int b, int last_valid, float diag,
+              float sign, float* __restrict__ A) {
   __shared__ float t[32][33];
   const int ntile = (b + 31) / 32;
   const int TI = blockIdx.x / ntile, TJ = blockIdx.x - (blockIdx.x / ntile) * ntile;
@@ -74,9 +75,9 @@ expand_kernel(const float* __restrict__ theta, int nblocks, int b, int last_vali
     const int i = TI * 32 + ty, j = TJ * 32 + tx;
     if (i >= b || j >= b) continue;
     float v;
-    if (i == j) v = 1.0f;
-    else if (i > j) v = t[tx][ty];  // A[i][j] = -Q[i][j] = Q[j][i]
-    else v = -t[ty][tx];
+    if (i == j) v = diag;
+    else if (i > j) v = -sign * t[tx][ty];  // Q[i][j] = -Q[j][i]
+    else v = sign * t[ty][tx];
     Ab[(int64_t)i * b + j] = v;
   }
 }
@@ -452,7 +453,7 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
   bf16_t* act_out = (act == DType::BF16) ? static_cast<bf16_t*>(blocks_act) : nullptr;
   const int et = (b + 31) / 32;
   hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb), dim3(kNT), 0, stream, theta, nb, b,
-                     last_valid, blocks_f32);
+                     last_valid, 1.0f, -1.0f, blocks_f32);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   for (int p = 0; p < nt; ++p) {
@@ -464,6 +465,14 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_expand_skew(const float* theta, int64_t nblocks, int b, int last_valid,
+                              float diag, float sign, float* out, hipStream_t stream) {
+  const int et = (b + 31) / 32;
+  hipLaunchKernelGGL(expand_kernel, dim3(et * et, (int)nblocks), dim3(kNT), 0, stream, theta,
+                     (int)nblocks, b, last_valid, diag, sign, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, int b,

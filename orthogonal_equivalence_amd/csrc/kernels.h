@@ -81,6 +81,23 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
                                float* blocks_f32, void* blocks_act, DType act,
                                float* ws, hipStream_t stream);
 
+// A = diag I + sign Q per block from packed generators (generators of the
+// last block's rows/columns >= last_valid taken as zero): I - Q with
+// (1, -1), Q itself with (0, 1).
+hipError_t launch_expand_skew(const float* theta, int64_t nblocks, int b, int last_valid,
+                              float diag, float sign, float* out, hipStream_t stream);
+
+// ---- Cayley-Neumann series (cnp.hip); b % 4 == 0 ----
+// RF = I + 2 (E + RF) per block (float32, in place), plus a bf16 copy when
+// act_bf16 is not null.
+hipError_t launch_cnp_finish(const float* E, float* RF, void* act_bf16, int64_t nblocks, int b,
+                             hipStream_t stream);
+// C = A - B over n floats (n % 4 == 0, 16-byte aligned pointers).
+hipError_t launch_sub(const float* A, const float* B, float* C, int64_t n, hipStream_t stream);
+// W = S + S^T per b x b block, S = A + B.
+hipError_t launch_sym_sum(const float* A, const float* B, float* W, int64_t nblocks, int b,
+                          hipStream_t stream);
+
 // ---- backward helpers ----
 // G[blk] = sum_s part[s][blk] in split order (float32), stored as `out`;
 // entries of the last block at rows or columns >= last_valid are zero.

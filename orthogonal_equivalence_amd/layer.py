@@ -23,12 +23,19 @@ class PoetxLinear:
 
     recompute_z=True is the memory-saving variant: the forward keeps no
     Z = W0 P x for the backward, which recomputes it (POETX_RECOMPUTE_Z).
+    map="cnp" builds the blocks by the truncated Cayley-Neumann series
+    (poetx_build_cnp) and keeps the skew blocks Q for its VJP
+    (POETX_CAYLEY_NEUMANN); map="cayley" (default) is the exact map.
     """
 
     def __init__(self, W0: torch.Tensor, b_in: int, b_out: int, act: str, device="cuda",
-                 recompute_z: bool = False):
+                 recompute_z: bool = False, map: str = "cayley"):
+        if map not in ("cayley", "cnp"):
+            raise ValueError(f"unknown orthogonal map {map!r}")
         self.torch_dtype, self.act = _DT[act]
-        self.flags = P.POETX_RECOMPUTE_Z if recompute_z else 0
+        self.map = map
+        self.flags = (P.POETX_RECOMPUTE_Z if recompute_z else 0) | \
+            (P.POETX_CAYLEY_NEUMANN if map == "cnp" else 0)
         self.device = torch.device(device)
         self.W0 = W0.to(self.device, self.torch_dtype).contiguous()
         self.d_out, self.d_in = self.W0.shape
@@ -49,11 +56,15 @@ class PoetxLinear:
         self.P_f32 = self._blocks_f32[nR:].view(self.nb_in, b_in, b_in)
         self.R_act = self._blocks_act[:nR].view(self.nb_out, b_out, b_out)
         self.P_act = self._blocks_act[nR:].view(self.nb_in, b_in, b_in)
+        if map == "cnp":
+            self._q = torch.empty(nR + nP, **f32)
+            self.Q_R = self._q[:nR].view(self.nb_out, b_out, b_out)
+            self.Q_P = self._q[nR:].view(self.nb_in, b_in, b_in)
+        wsz = P.poetx_build_cnp_workspace_size if map == "cnp" else P.poetx_build_workspace_size
         if self.combined:
-            ws = P.poetx_build_workspace_size(self.d_out + self.d_in, b_out)
+            ws = wsz(self.d_out + self.d_in, b_out)
         else:
-            ws = max(P.poetx_build_workspace_size(self.d_out, b_out),
-                     P.poetx_build_workspace_size(self.d_in, b_in))
+            ws = max(wsz(self.d_out, b_out), wsz(self.d_in, b_in))
         self._build_ws = torch.empty(max(ws, 1), device=self.device, dtype=torch.uint8)
         self._fwd_ws = {}
         self._bwd_ws = {}
@@ -75,9 +86,20 @@ class PoetxLinear:
 
     # -- the three calls ----------------------------------------------------
     def build(self, stream=None):
-        """Cayley build of R and P blocks (one call when the sets combine)."""
+        """Build of the R and P blocks (one call when the sets combine)."""
         act_R = self.R_act if self.act == P.POETX_BF16 else None
         act_P = self.P_act if self.act == P.POETX_BF16 else None
+        if self.map == "cnp":
+            act_all = self._blocks_act if self.act == P.POETX_BF16 else None
+            if self.combined:
+                P.poetx_build_cnp(self._theta, self.d_out + self.d_in, self.b_out, self._q,
+                                  self._blocks_f32, act_all, self.act, self._build_ws, stream)
+            else:
+                P.poetx_build_cnp(self.theta_R, self.d_out, self.b_out, self.Q_R, self.R_f32,
+                                  act_R, self.act, self._build_ws, stream)
+                P.poetx_build_cnp(self.theta_P, self.d_in, self.b_in, self.Q_P, self.P_f32,
+                                  act_P, self.act, self._build_ws, stream)
+            return
         if self.combined:
             P.poetx_build_orthogonal(self._theta, self.d_out + self.d_in, self.b_out,
                                      self._blocks_f32,
@@ -116,7 +138,8 @@ class PoetxLinear:
             g_theta_P = torch.empty_like(self.theta_P)
         R, Pb = self.blocks_for_act()
         ws = self._ws(self._bwd_ws, P.poetx_bwd_workspace_size, N)
-        P.poetx_linear_bwd(self.desc(N, events), g_y, x, self.W0, self.R_f32, self.P_f32, R, Pb, z,
+        vR, vP = (self.Q_R, self.Q_P) if self.map == "cnp" else (self.R_f32, self.P_f32)
+        P.poetx_linear_bwd(self.desc(N, events), g_y, x, self.W0, vR, vP, R, Pb, z,
                            g_x, g_theta_R if g_theta_R.numel() else None,
                            g_theta_P if g_theta_P.numel() else None, ws, stream)
         return g_x, g_theta_R, g_theta_P

@@ -27,12 +27,14 @@ POETX_ERR_ALIAS = 7
 POETX_F32 = 0
 POETX_BF16 = 1
 
-POETX_ABI_VERSION = 2
+POETX_ABI_VERSION = 3
 POETX_RECOMPUTE_Z = 1
+POETX_CAYLEY_NEUMANN = 2
 
 EXPORTS = (
     "poetx_abi_version", "poetx_status_string", "poetx_num_blocks", "poetx_theta_count",
-    "poetx_build_workspace_size", "poetx_build_orthogonal", "poetx_fwd_workspace_size",
+    "poetx_build_workspace_size", "poetx_build_orthogonal", "poetx_build_cnp_workspace_size",
+    "poetx_build_cnp", "poetx_fwd_workspace_size",
     "poetx_bwd_workspace_size", "poetx_linear_fwd", "poetx_linear_bwd",
     "poetx_event_create", "poetx_event_destroy", "poetx_event_record",
     "poetx_event_synchronize", "poetx_event_elapsed_ms",
@@ -75,6 +77,8 @@ def _load() -> ctypes.CDLL:
         "poetx_theta_count": (i64, [i64, i32]),
         "poetx_build_workspace_size": (sz, [i64, i32]),
         "poetx_build_orthogonal": (ctypes.c_int, [vp, i64, i32, vp, vp, i32, vp, sz, vp]),
+        "poetx_build_cnp_workspace_size": (sz, [i64, i32]),
+        "poetx_build_cnp": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, i32, vp, sz, vp]),
         "poetx_fwd_workspace_size": (sz, [dp]),
         "poetx_bwd_workspace_size": (sz, [dp]),
         "poetx_linear_fwd": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -143,6 +147,10 @@ def poetx_build_workspace_size(d: int, b: int) -> int:
     return _lib.poetx_build_workspace_size(d, b)
 
 
+def poetx_build_cnp_workspace_size(d: int, b: int) -> int:
+    return _lib.poetx_build_cnp_workspace_size(d, b)
+
+
 def make_desc(tokens, d_in, d_out, b_in, b_out, act, events=None, flags=0) -> LinearDesc:
     desc = LinearDesc(tokens, d_in, d_out, b_in, b_out, act, 0, flags, 0, None)
     if events:
@@ -167,6 +175,14 @@ def poetx_build_orthogonal(theta, d, b, blocks_f32, blocks_act, act, ws, stream=
     if raw:
         return st
     _check(st, "poetx_build_orthogonal")
+
+
+def poetx_build_cnp(theta, d, b, q_f32, blocks_f32, blocks_act, act, ws, stream=None, raw=False):
+    st = _lib.poetx_build_cnp(_ptr(theta), d, b, _ptr(q_f32), _ptr(blocks_f32), _ptr(blocks_act),
+                              act, _ptr(ws), _nbytes(ws), _stream(stream))
+    if raw:
+        return st
+    _check(st, "poetx_build_cnp")
 
 
 def poetx_linear_fwd(desc, x, W0, R_act, P_act, y, z_save, ws, stream=None, raw=False):

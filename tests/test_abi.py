@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 2
+    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 3
     for s in range(8):
         assert P.status_string(s) and P.status_string(s) != "unknown status"
     assert P.status_string(99) == "unknown status"
@@ -188,7 +188,8 @@ def test_build_errors():
 
 def test_unknown_flags_and_reserved_rejected():
     for call in (_fwd, _bwd):
-        assert call(desc(flags=2)) == P.POETX_ERR_SHAPE
+        assert call(desc(flags=4)) == P.POETX_ERR_SHAPE
+        assert call(desc(flags=8 | P.POETX_CAYLEY_NEUMANN)) == P.POETX_ERR_SHAPE
         assert call(desc(flags=-1)) == P.POETX_ERR_SHAPE
         d = desc()
         d.reserved = 1
@@ -227,3 +228,58 @@ def test_recompute_z_alias_checks_skip_null_z():
     d = desc(flags=P.POETX_RECOMPUTE_Z)
     assert _fwd(d, z=None, y=ALIGNED) == P.POETX_ERR_ALIAS
     assert _bwd(d, z=None, g_x=ALIGNED) == P.POETX_ERR_ALIAS
+
+
+# -- POETX_CAYLEY_NEUMANN and poetx_build_cnp (truncated series map) ---------
+
+def test_cnp_flag_is_valid_alone_and_with_recompute():
+    for f in (P.POETX_CAYLEY_NEUMANN, P.POETX_CAYLEY_NEUMANN | P.POETX_RECOMPUTE_Z):
+        d = desc(flags=f)
+        assert P.poetx_fwd_workspace_size(d) > 0 and P.poetx_bwd_workspace_size(d) > 0
+        # validation passes up to the workspace check
+        z = None if f & P.POETX_RECOMPUTE_Z else ALIGNED * 8
+        assert _bwd(d, z=z, ws_bytes=P.poetx_bwd_workspace_size(d) - 1) == P.POETX_ERR_WORKSPACE
+    # the series needs no extra backward workspace
+    assert P.poetx_bwd_workspace_size(desc(flags=P.POETX_CAYLEY_NEUMANN)) == \
+        P.poetx_bwd_workspace_size(desc())
+
+
+def test_cnp_workspace_size():
+    assert P.poetx_build_cnp_workspace_size(64, 8) >= 2 * 8 * 8 * 8 * 4
+    assert P.poetx_build_cnp_workspace_size(100, 12) >= 2 * 9 * 12 * 12 * 4   # padded last block
+    for d, b in ((64, 6), (64, 2), (0, 8), (8, 16), (1 << 20, 8192), (64, 0)):
+        assert P.poetx_build_cnp_workspace_size(d, b) == 0, (d, b)
+
+
+def _cnp(theta, d, b, q, f32, act_ptr, act, ws, ws_bytes):
+    return P._lib.poetx_build_cnp(theta, d, b, q, f32, act_ptr, act, ws, ws_bytes, None)
+
+
+def test_build_cnp_errors():
+    ok = dict(theta=ALIGNED, d=64, b=8, q=ALIGNED * 2, f32=ALIGNED * 3, act_ptr=ALIGNED * 4,
+              act=P.POETX_BF16, ws=ALIGNED * 5, ws_bytes=1 << 30)
+
+    def call(**over):
+        a = dict(ok)
+        a.update(over)
+        return _cnp(a["theta"], a["d"], a["b"], a["q"], a["f32"], a["act_ptr"], a["act"], a["ws"],
+                    a["ws_bytes"])
+
+    assert call(act=7) == P.POETX_ERR_DTYPE
+    assert call(d=0) == P.POETX_ERR_SHAPE
+    assert call(b=0) == P.POETX_ERR_SHAPE
+    assert call(b=128) == P.POETX_ERR_SHAPE                 # b > d
+    assert call(d=1 << 20, b=8192) == P.POETX_ERR_SHAPE     # b above the maximum
+    assert call(b=6) == P.POETX_ERR_ALIGN                   # b not a multiple of 4
+    assert call(b=2) == P.POETX_ERR_ALIGN
+    assert call(theta=None) == P.POETX_ERR_NULL
+    assert call(q=None) == P.POETX_ERR_NULL
+    assert call(f32=None) == P.POETX_ERR_NULL
+    assert call(act_ptr=None) == P.POETX_ERR_NULL
+    assert call(q=ALIGNED * 2 + 4) == P.POETX_ERR_ALIGN
+    assert call(f32=ALIGNED * 3 + 8) == P.POETX_ERR_ALIGN
+    assert call(ws_bytes=16) == P.POETX_ERR_WORKSPACE
+    assert call(ws=None) == P.POETX_ERR_WORKSPACE
+    assert call(q=ALIGNED) == P.POETX_ERR_ALIAS             # Q on top of theta
+    assert call(f32=ALIGNED * 2) == P.POETX_ERR_ALIAS       # R on top of Q
+    assert call(act_ptr=ALIGNED * 5) == P.POETX_ERR_ALIAS   # act copy inside the workspace
