@@ -21,6 +21,10 @@ on gist.science, "Technische Zusammenfassung"):
           is stored.
   [CNP]   same item: the Cayley map is approximated by a truncated Neumann
           series whose higher-order terms are Q^2, Q^3 and Q^4.
+  [PERM]  §2 Methodik, permutation item: permutation matrices mix the blocks
+          of the orthogonal matrices; they are applied as index maps
+          (bijections) on the data, and two of the four permutations of the
+          forward pass are folded into the weight in advance.
 
 Readings taken where the pages are silent (each is listed in the design doc):
   * the orthogonal map is the exact Cayley map R = (I + Q)(I - Q)^-1 (the
@@ -40,6 +44,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
     R = 2 (I - Q)^-1 - I, so R = I + 2 (Q + Q^2 + Q^3 + Q^4): only the
     powers the pages list occur. (Truncating inside (I + Q)(I - Q)^-1 would
     add a Q^5 term; that reading is not taken.)
+  * with block-mixing permutations (optional; none by default) the
+    orthogonal factors are R = Pi_R^T blockdiag(R_k) Pi_R and
+    P = Pi_P^T blockdiag(P_j) Pi_P, where (Pi v)_i = v[pi(i)] for an index
+    map pi; these are the four permutations of the forward, and the inner
+    two fold into W0' = Pi_R W0 Pi_P^T, W0'[i][j] = W0[pi_R(i)][pi_P(j)].
 
 Where "parity unpinned": nothing here. Every function is pinned by
 tests/test_oracle.py against closed forms (b = 2 rotation, b = 3 Rodrigues
@@ -63,7 +72,8 @@ __all__ = [
     "block_ranges", "orthogonal_blocks", "materialise", "forward",
     "backward", "cayley_vjp", "forward_input_centric",
     "backward_input_centric", "LayerOracle", "CNP_ORDER", "cayley_neumann",
-    "cayley_neumann_vjp", "orthogonal_blocks_cnp",
+    "cayley_neumann_vjp", "orthogonal_blocks_cnp", "permutation_matrix",
+    "fold_permutations", "materialise_permuted",
 ]
 
 
@@ -203,6 +213,36 @@ def materialise(W0: np.ndarray, R: np.ndarray, P: np.ndarray, b_out: int, b_in: 
     return W
 
 
+# ------------------------------------------- block-mixing permutations [PERM]
+def permutation_matrix(pi: np.ndarray) -> np.ndarray:
+    """The matrix Pi of an index map: (Pi v)_i = v[pi[i]], so row i of Pi is
+    the unit row e_pi[i]. [PERM]"""
+    pi = np.asarray(pi, dtype=np.int64)
+    d = len(pi)
+    if sorted(pi.tolist()) != list(range(d)):
+        raise ValueError("not a permutation")
+    M = np.zeros((d, d))
+    M[np.arange(d), pi] = 1.0
+    return M
+
+
+def fold_permutations(W0: np.ndarray, perm_out: np.ndarray, perm_in: np.ndarray) -> np.ndarray:
+    """W0' = Pi_out W0 Pi_in^T, i.e. W0'[i][j] = W0[perm_out[i]][perm_in[j]]:
+    the two inner permutations of the forward folded into the weight once.
+    [PERM] (reduction)"""
+    return np.asarray(W0, dtype=np.float64)[np.ix_(np.asarray(perm_out), np.asarray(perm_in))]
+
+
+def materialise_permuted(W0, R, P, b_out, b_in, perm_out, perm_in):
+    """W = Pi_out^T blockdiag(R) Pi_out W0 Pi_in^T blockdiag(P) Pi_in, formed
+    as M = blockdiag(R) W0' blockdiag(P) with the folded W0', then
+    W[perm_out[i]][perm_in[j]] = M[i][j] (W = Pi_out^T M Pi_in). [PERM], [OET]"""
+    M = materialise(fold_permutations(W0, perm_out, perm_in), R, P, b_out, b_in)
+    W = np.empty_like(M)
+    W[np.ix_(np.asarray(perm_out), np.asarray(perm_in))] = M
+    return W
+
+
 # ------------------------------------------------------- forward / backward
 def forward(x: np.ndarray, W: np.ndarray) -> np.ndarray:
     """y = W x for every token; token-major Y = X W^T. [OET]"""
@@ -239,7 +279,8 @@ def _pad_grad_zero(g: np.ndarray, b: int, d: int) -> np.ndarray:
 
 def backward(g_y: np.ndarray, x: np.ndarray, W0: np.ndarray,
              R: np.ndarray, B_R: np.ndarray, P: np.ndarray, B_P: np.ndarray,
-             b_out: int, b_in: int, vjp=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+             b_out: int, b_in: int, vjp=None, perm_out=None,
+             perm_in=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Backward of the layer through the materialised weight.
 
     G_W = g_Y^T X is the gradient of the full weight. With W = R (W0 P):
@@ -248,15 +289,27 @@ def backward(g_y: np.ndarray, x: np.ndarray, W0: np.ndarray,
     Returns (g_x, g_theta_R, g_theta_P). [OET], [BD]; backward derived by the
     chain rule. `vjp(B, G)` maps the block gradients to generator gradients
     (cayley_vjp with B = (I - Q)^-1 by default; cayley_neumann_vjp with
-    B = Q for the truncated series)."""
+    B = Q for the truncated series).
+
+    With permutations, W = Pi_out^T M Pi_in for M = blockdiag(R) W0'
+    blockdiag(P): the gradient of M is G_M = Pi_out G_W Pi_in^T
+    (G_M[i][j] = G_W[perm_out[i]][perm_in[j]]) and the blocks see W0' in
+    place of W0. [PERM]"""
     vjp = cayley_vjp if vjp is None else vjp
     g_y = np.asarray(g_y, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     W0 = np.asarray(W0, dtype=np.float64)
     m, n = W0.shape
-    W = materialise(W0, R, P, b_out, b_in)
+    permuted = perm_out is not None
+    if permuted:
+        W = materialise_permuted(W0, R, P, b_out, b_in, perm_out, perm_in)
+    else:
+        W = materialise(W0, R, P, b_out, b_in)
     g_x = g_y @ W
     G_W = g_y.T @ x
+    if permuted:
+        G_W = G_W[np.ix_(np.asarray(perm_out), np.asarray(perm_in))]
+        W0 = fold_permutations(W0, perm_out, perm_in)
     ident_R = np.broadcast_to(np.eye(b_out), R.shape)
     ident_P = np.broadcast_to(np.eye(b_in), P.shape)
     W0P = materialise(W0, ident_R, P, b_out, b_in)
@@ -283,24 +336,40 @@ def _apply_blocks(a: np.ndarray, blocks: np.ndarray, b: int, transpose: bool) ->
     return out
 
 
-def forward_input_centric(x, W0, R, P, b_out, b_in):
-    """U = X P^T, Z = U W0^T, Y = Z R^T (token-major). Returns (Y, Z, U). [IC]"""
+def forward_input_centric(x, W0, R, P, b_out, b_in, perm_out=None, perm_in=None):
+    """U = X P^T, Z = U W0^T, Y = Z R^T (token-major). Returns (Y, Z, U). [IC]
+    With permutations (W0 is then the folded W0'): X_p = X[:, perm_in]
+    (gather), U = X_p blockdiag(P)^T, Z = U W0'^T, Y_p = Z blockdiag(R)^T and
+    Y[:, perm_out] = Y_p (scatter). [PERM]"""
     x = np.asarray(x, dtype=np.float64)
+    if perm_in is not None:
+        x = x[:, np.asarray(perm_in)]
     U = _apply_blocks(x, P, b_in, transpose=True)
     Z = U @ np.asarray(W0, dtype=np.float64).T
     Y = _apply_blocks(Z, R, b_out, transpose=True)
+    if perm_out is not None:
+        Yp = Y
+        Y = np.empty_like(Yp)
+        Y[:, np.asarray(perm_out)] = Yp
     return Y, Z, U
 
 
-def backward_input_centric(g_y, x, W0, R, B_R, P, B_P, b_out, b_in, vjp=None):
+def backward_input_centric(g_y, x, W0, R, B_R, P, B_P, b_out, b_in, vjp=None,
+                           perm_out=None, perm_in=None):
     """Backward along the input-centric dataflow:
     g_Z = g_Y R, G_R[k] = g_Y[:, k]^T Z[:, k], g_U = g_Z W0,
-    G_P[j] = g_U[:, j]^T X[:, j], g_X = g_U P. [IC], chain rule."""
+    G_P[j] = g_U[:, j]^T X[:, j], g_X = g_U P. [IC], chain rule.
+    With permutations (W0 folded): g_Y and X are gathered by perm_out and
+    perm_in first and g_X is scattered by perm_in at the end. [PERM]"""
     vjp = cayley_vjp if vjp is None else vjp
     g_y = np.asarray(g_y, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     W0 = np.asarray(W0, dtype=np.float64)
     m, n = W0.shape
+    if perm_out is not None:
+        g_y = g_y[:, np.asarray(perm_out)]
+    if perm_in is not None:
+        x = x[:, np.asarray(perm_in)]
     _, Z, _ = forward_input_centric(x, W0, R, P, b_out, b_in)
     g_Z = _apply_blocks(g_y, R, b_out, transpose=False)
     G_R = np.zeros_like(R)
@@ -311,6 +380,10 @@ def backward_input_centric(g_y, x, W0, R, B_R, P, B_P, b_out, b_in, vjp=None):
     for j, (s, r) in enumerate(block_ranges(n, b_in)):
         G_P[j, :r, :r] = g_U[:, s:s + r].T @ x[:, s:s + r]
     g_x = _apply_blocks(g_U, P, b_in, transpose=False)
+    if perm_in is not None:
+        g_xp = g_x
+        g_x = np.empty_like(g_xp)
+        g_x[:, np.asarray(perm_in)] = g_xp
     g_tR = _pad_grad_zero(vjp(B_R, G_R), b_out, m)
     g_tP = _pad_grad_zero(vjp(B_P, G_P), b_in, n)
     return g_x, g_tR, g_tP
@@ -320,9 +393,11 @@ class LayerOracle:
     """One layer's full oracle result (orthogonal build, forward, backward),
     computed through the materialised weight. map: "cayley" (exact) or "cnp"
     (truncated Cayley-Neumann series); B_R / B_P hold what that map's VJP
-    needs ((I - Q)^-1 or Q)."""
+    needs ((I - Q)^-1 or Q). perm_out / perm_in: optional block-mixing index
+    maps of R and P (both or neither); W0 is the unfolded weight."""
 
-    def __init__(self, W0, theta_R, theta_P, b_out, b_in, map="cayley"):
+    def __init__(self, W0, theta_R, theta_P, b_out, b_in, map="cayley", perm_out=None,
+                 perm_in=None):
         self.W0 = np.asarray(W0, dtype=np.float64)
         m, n = self.W0.shape
         self.b_out, self.b_in = b_out, b_in
@@ -332,11 +407,17 @@ class LayerOracle:
         self.vjp = cayley_vjp if map == "cayley" else cayley_neumann_vjp
         self.R, self.B_R = build(theta_R, b_out, m)
         self.P, self.B_P = build(theta_P, b_in, n)
-        self.W = materialise(self.W0, self.R, self.P, b_out, b_in)
+        if (perm_out is None) != (perm_in is None):
+            raise ValueError("give both permutations or neither")
+        self.perm_out, self.perm_in = perm_out, perm_in
+        if perm_out is None:
+            self.W = materialise(self.W0, self.R, self.P, b_out, b_in)
+        else:
+            self.W = materialise_permuted(self.W0, self.R, self.P, b_out, b_in, perm_out, perm_in)
 
     def forward(self, x):
         return forward(x, self.W)
 
     def backward(self, g_y, x):
         return backward(g_y, x, self.W0, self.R, self.B_R, self.P, self.B_P,
-                        self.b_out, self.b_in, self.vjp)
+                        self.b_out, self.b_in, self.vjp, self.perm_out, self.perm_in)

@@ -431,11 +431,107 @@ def pin_cnp_finite_differences(h=1e-6, rtol=1e-6):
             assert np.array_equal(R[-1, r:, r:], np.eye(b - r))
 
 
+# ------------------------------------------- block-mixing permutations
+def _perm_layer(m, n, b, N, sigma, seed):
+    W0, thR, thP, x, g_y = _layer(m, n, b, b, N, sigma, seed)
+    rng = np.random.default_rng(seed + 1000)
+    return W0, thR, thP, x, g_y, rng.permutation(m), rng.permutation(n)
+
+
+def pin_permutation_convention():
+    """(Pi v)_i = v[pi(i)] on a hand example, and non-permutations refused."""
+    Pi = O.permutation_matrix(np.array([2, 0, 1]))
+    assert np.array_equal(Pi @ np.array([10.0, 20.0, 30.0]), np.array([30.0, 10.0, 20.0]))
+    assert np.array_equal(Pi @ Pi.T, np.eye(3))
+    for bad in ([0, 0, 1], [0, 1, 3]):
+        try:
+            O.permutation_matrix(np.array(bad))
+        except ValueError:
+            continue
+        raise AssertionError(f"accepted {bad}")
+
+
+def pin_perm_explicit_matrices():
+    """The permuted layer equals the explicit product with permutation and
+    block-diagonal matrices (scipy block_diag), and the fold equals
+    Pi_R W0 Pi_P^T as a matrix product."""
+    for (m, n, b, seed) in ((24, 16, 8, 71), (20, 12, 8, 73)):   # second: padded blocks
+        W0, thR, thP, x, _, po, pi = _perm_layer(m, n, b, 4, 0.3, seed)
+        ora = O.LayerOracle(W0, thR, thP, b, b, perm_out=po, perm_in=pi)
+        PiR, PiP = O.permutation_matrix(po), O.permutation_matrix(pi)
+        DR = scipy.linalg.block_diag(*[ora.R[k, :r, :r] for k, (_, r) in enumerate(O.block_ranges(m, b))])
+        DP = scipy.linalg.block_diag(*[ora.P[j, :r, :r] for j, (_, r) in enumerate(O.block_ranges(n, b))])
+        W = PiR.T @ DR @ PiR @ W0 @ PiP.T @ DP @ PiP
+        assert np.max(np.abs(ora.W - W)) <= 1e-13
+        assert np.max(np.abs(ora.forward(x) - x @ W.T)) <= 1e-12
+        assert np.max(np.abs(O.fold_permutations(W0, po, pi) - PiR @ W0 @ PiP.T)) == 0.0
+
+
+def pin_perm_identity_reduces():
+    """Identity index maps give exactly the unpermuted layer."""
+    m, n, b = 32, 24, 8
+    W0, thR, thP, x, g_y = _layer(m, n, b, b, 5, 0.3, 79)
+    a = O.LayerOracle(W0, thR, thP, b, b)
+    c = O.LayerOracle(W0, thR, thP, b, b, perm_out=np.arange(m), perm_in=np.arange(n))
+    assert np.array_equal(a.W, c.W)
+    for u, v in zip(a.backward(g_y, x), c.backward(g_y, x)):
+        assert np.array_equal(u, v)
+
+
+def pin_perm_spectrum_and_routes():
+    """With permutations R and P stay orthogonal, so W keeps W0's singular
+    values; the input-centric route (gather, blocks, folded W0, blocks,
+    scatter) equals the materialised one, forward and backward."""
+    m, n, b, N = 48, 40, 8, 7
+    W0, thR, thP, x, g_y, po, pi = _perm_layer(m, n, b, N, 0.4, 83)
+    ora = O.LayerOracle(W0, thR, thP, b, b, perm_out=po, perm_in=pi)
+    s0 = np.linalg.svd(W0, compute_uv=False)
+    s1 = np.linalg.svd(ora.W, compute_uv=False)
+    assert np.max(np.abs(s0 - s1)) <= 1e-12 * s0.max()
+    W0f = O.fold_permutations(W0, po, pi)
+    y2, _, _ = O.forward_input_centric(x, W0f, ora.R, ora.P, b, b, po, pi)
+    assert np.max(np.abs(ora.forward(x) - y2)) <= 1e-12
+    g1 = ora.backward(g_y, x)
+    g2 = O.backward_input_centric(g_y, x, W0f, ora.R, ora.B_R, ora.P, ora.B_P, b, b, None, po, pi)
+    for u, v in zip(g1, g2):
+        assert np.max(np.abs(u - v)) <= 1e-12 * max(np.abs(u).max(), 1e-300)
+
+
+def pin_perm_finite_differences(h=1e-6, rtol=1e-6):
+    """Central differences of L = <g_y, y> for the permuted layer (exact map
+    and series) against the oracle's backward, every generator and x entry."""
+    for map_ in ("cayley", "cnp"):
+        m, n, b, N = 8, 12, 4, 4
+        W0, thR, thP, x, g_y, po, pi = _perm_layer(m, n, b, N, 0.3, 89)
+
+        def loss(thR_, thP_, x_):
+            o = O.LayerOracle(W0, thR_, thP_, b, b, map=map_, perm_out=po, perm_in=pi)
+            return float(np.sum(g_y * o.forward(x_)))
+
+        g_x, gR, gP = O.LayerOracle(W0, thR, thP, b, b, map=map_, perm_out=po,
+                                    perm_in=pi).backward(g_y, x)
+
+        def fd(arr, fn):
+            out = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                a1 = arr.copy(); a1[idx] += h
+                a2 = arr.copy(); a2[idx] -= h
+                out[idx] = (fn(a1) - fn(a2)) / (2 * h)
+            return out
+
+        for got, ref in ((gR, fd(thR, lambda a: loss(a, thP, x))),
+                         (gP, fd(thP, lambda a: loss(thR, a, x))),
+                         (g_x, fd(x, lambda a: loss(thR, thP, a)))):
+            assert np.max(np.abs(got - ref)) <= rtol * np.abs(ref).max(), map_
+
+
 ALL_PINS = [
     pin_packing_order, pin_golden_closed_forms, pin_b2_rotation, pin_b3_rodrigues,
     pin_eigenvalue_map, pin_orthogonality_det_transpose, pin_spectrum,
     pin_dense_block_diag, pin_input_centric_equals_materialised, pin_theta_zero,
     pin_vjp_forms, pin_adjoint, pin_finite_differences, pin_padding_gradients,
     pin_cnp_golden, pin_cnp_b3_closed_form, pin_cnp_series_tail, pin_cnp_vjp_frechet,
-    pin_cnp_theta_zero, pin_cnp_finite_differences,
+    pin_cnp_theta_zero, pin_cnp_finite_differences, pin_permutation_convention,
+    pin_perm_explicit_matrices, pin_perm_identity_reduces, pin_perm_spectrum_and_routes,
+    pin_perm_finite_differences,
 ]

@@ -53,6 +53,19 @@ MUTATIONS = [
     ("cayley_neumann_vjp", "D += pw[i] @ G[n] @ pw[k - 1 - i]", "D += pw[i] @ G[n] @ pw[i]",
      [pins.pin_cnp_finite_differences, pins.pin_cnp_vjp_frechet]),
     ("cayley_neumann_vjp", "D *= 2.0", "D *= 1.0", [pins.pin_cnp_golden, pins.pin_cnp_theta_zero]),
+    # block-mixing permutations
+    ("materialise_permuted", "W[np.ix_(np.asarray(perm_out), np.asarray(perm_in))] = M",
+     "W = M[np.ix_(np.asarray(perm_out), np.asarray(perm_in))]",
+     [pins.pin_perm_explicit_matrices]),
+    ("fold_permutations", "np.ix_(np.asarray(perm_out), np.asarray(perm_in))",
+     "np.ix_(np.argsort(perm_out), np.asarray(perm_in))",
+     [pins.pin_perm_explicit_matrices, pins.pin_perm_finite_differences]),
+    ("backward", "G_W = G_W[np.ix_(np.asarray(perm_out), np.asarray(perm_in))]", "G_W = G_W",
+     [pins.pin_perm_finite_differences, pins.pin_perm_spectrum_and_routes]),
+    ("forward_input_centric", "x = x[:, np.asarray(perm_in)]", "x = x[:, np.argsort(perm_in)]",
+     [pins.pin_perm_spectrum_and_routes]),
+    ("permutation_matrix", "M[np.arange(d), pi] = 1.0", "M[pi, np.arange(d)] = 1.0",
+     [pins.pin_permutation_convention, pins.pin_perm_explicit_matrices]),
 ]
 
 
