@@ -33,8 +33,11 @@ PEAK_BF16 = 2516.6e12   # MI355X dense bf16 MFMA, FLOP/s
 PEAK_F32 = 157.3e12     # MI355X fp32 (matrix), FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
 
+# stage names by the library's stage index (None: a stage that does not run)
 FWD_STAGES = ["p_apply", "dense_fwd", "r_apply"]
+FWD_PERM_STAGES = ["gather_x", "scatter_y"]
 BWD_STAGES = ["grad_r", "gram_r", "dense_bwd", "gram_p", "grad_x", "vjp_r", "vjp_p"]
+BWD_PERM_STAGES = ["gather_gy_x", "scatter_gx"]
 
 
 def layer_work(s):
@@ -50,13 +53,13 @@ def layer_work(s):
     return flops, fwd + bwd + build
 
 
-def cpu_baseline(spec, sample_tokens, map="cayley"):
+def cpu_baseline(spec, sample_tokens, map="cayley", permute=False):
     """The float64 oracle (build, materialise, forward, backward) on the first
     `sample_tokens` tokens of the workload, timed on the host's cores."""
     import dataclasses
 
     import oracle.poetx_oracle as O
-    from orthogonal_equivalence_amd.inputs import make_layer
+    from orthogonal_equivalence_amd.inputs import make_layer, make_permutations
     try:
         from threadpoolctl import threadpool_info
         threads = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
@@ -67,7 +70,9 @@ def cpu_baseline(spec, sample_tokens, map="cayley"):
     # repeat the whole oracle step until about 10 s of CPU work (at most 6 reps)
     reps, t0 = 0, time.perf_counter()
     while True:
-        ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b, map=map)
+        po, pi = make_permutations(spec) if permute else (None, None)
+        ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b, map=map, perm_out=po,
+                            perm_in=pi)
         ora.forward(x)
         ora.backward(g_y, x)
         reps += 1
@@ -82,7 +87,7 @@ def cpu_baseline(spec, sample_tokens, map="cayley"):
                       f"{spec.d_out}x{spec.d_in} b={spec.b}; {dt:.1f} s"}
 
 
-def parity_sample(L, out, lay, rows=32, map="cayley"):
+def parity_sample(L, out, lay, rows=32, map="cayley", perms=None):
     """Frobenius-relative error of sampled token rows of y and g_x against the
     oracle's materialised weight (the full-size parity tests do more)."""
     import oracle.poetx_oracle as O
@@ -91,7 +96,10 @@ def parity_sample(L, out, lay, rows=32, map="cayley"):
     build = O.orthogonal_blocks if map == "cayley" else O.orthogonal_blocks_cnp
     R, _ = build(L.theta_R, s.b, s.d_out)
     Pb, _ = build(L.theta_P, s.b, s.d_in)
-    W = O.materialise(L.W0, R, Pb, s.b, s.b)
+    if perms is None:
+        W = O.materialise(L.W0, R, Pb, s.b, s.b)
+    else:
+        W = O.materialise_permuted(L.W0, R, Pb, s.b, s.b, perms[0], perms[1])
     idx = np.linspace(0, s.tokens - 1, rows).astype(np.int64)
     ti = torch.from_numpy(idx).cuda()
     y = out["y"][ti].float().cpu().double().numpy()
@@ -157,6 +165,8 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--recompute-z", action="store_true",
                     help="POET-Xmem variant: the forward keeps no Z, the backward recomputes it")
+    ap.add_argument("--permute", action="store_true",
+                    help="random block-mixing permutations of R and P (W0 folded once)")
     ap.add_argument("--map", choices=("cayley", "cnp"), default="cayley",
                     help="orthogonal map: exact Cayley (default) or the truncated "
                          "Cayley-Neumann series")
@@ -175,7 +185,7 @@ def main():
     import torch
 
     from orthogonal_equivalence_amd import poetx as P
-    from orthogonal_equivalence_amd.inputs import CONFIGS, make_layer
+    from orthogonal_equivalence_amd.inputs import CONFIGS, make_layer, make_permutations
     from orthogonal_equivalence_amd.layer import PoetxLinear
 
     specs = CONFIGS[args.config]
@@ -187,8 +197,9 @@ def main():
     layers = []
     for s in specs:
         L = make_layer(s)
+        po, pi = make_permutations(s) if args.permute else (None, None)
         lay = PoetxLinear(torch.from_numpy(L.W0).to(tdt[s.dtype]), s.b, s.b, s.dtype, device=dev,
-                          recompute_z=args.recompute_z, map=args.map)
+                          recompute_z=args.recompute_z, map=args.map, perm_out=po, perm_in=pi)
         lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
         x = torch.from_numpy(L.x).to(tdt[s.dtype]).to(dev)
         g_y = torch.from_numpy(L.g_y).to(tdt[s.dtype]).to(dev)
@@ -199,7 +210,11 @@ def main():
                    gR=torch.empty_like(lay.theta_R), gP=torch.empty_like(lay.theta_P))
         layers.append((s, L if len(specs) == 1 else None, lay, x, g_y, out))
     stream = torch.cuda.current_stream()
-    bwd_stages = BWD_STAGES + (["recompute_z"] if args.recompute_z else [])
+    fwd_stages = FWD_STAGES + (FWD_PERM_STAGES if args.permute else [])
+    bwd_stages = BWD_STAGES + (["recompute_z" if args.recompute_z else None] +
+                               (BWD_PERM_STAGES if args.permute else []))
+    if bwd_stages[-1] is None:
+        bwd_stages.pop()
 
     def step(ev=None):
         for li, (s, _, lay, x, g_y, o) in enumerate(layers):
@@ -217,7 +232,7 @@ def main():
         ev = []
         for _ in layers:
             ev.append({"build": (P.Event(), P.Event()),
-                       "fwd": [P.Event() for _ in range(2 * len(FWD_STAGES))],
+                       "fwd": [P.Event() for _ in range(2 * len(fwd_stages))],
                        "bwd": [P.Event() for _ in range(2 * len(bwd_stages))]})
         return ev
 
@@ -258,8 +273,10 @@ def main():
         vals = [step_events[k][li]["build"][0].elapsed_ms(step_events[k][li]["build"][1])
                 for k in range(args.steps)]
         stage_ms[pre + "build"] = statistics.mean(vals)
-        for grp, names in (("fwd", FWD_STAGES), ("bwd", bwd_stages)):
+        for grp, names in (("fwd", fwd_stages), ("bwd", bwd_stages)):
             for si, nm in enumerate(names):
+                if nm is None:
+                    continue
                 vals = [step_events[k][li][grp][2 * si].elapsed_ms(step_events[k][li][grp][2 * si + 1])
                         for k in range(args.steps)]
                 stage_ms[pre + nm] = statistics.mean(vals)
@@ -292,7 +309,8 @@ def main():
                    "variant": ("POET-Xmem (Z recomputed in the backward)" if args.recompute_z
                                else "POET-X (Z kept for the backward)"),
                    "orthogonal_map": ("exact Cayley" if args.map == "cayley"
-                                      else "Cayley-Neumann series to Q^4")},
+                                      else "Cayley-Neumann series to Q^4"),
+                   "permutations": bool(args.permute)},
         "roofline": roofline,
         "layer_roofline": {"flops": F, "bytes": B, "t_roof_ms": t_roof * 1e3,
                            "frac": t_roof / (ms_per_step / 1e3),
@@ -303,10 +321,12 @@ def main():
     }
     if not args.no_parity and len(layers) == 1:
         s, L, lay, x, g_y, o = layers[0]
-        res["parity"] = parity_sample(L, dict(y=o["y"], g_x=o["g_x"]), lay, map=args.map)
+        res["parity"] = parity_sample(L, dict(y=o["y"], g_x=o["g_x"]), lay, map=args.map,
+                                      perms=make_permutations(s) if args.permute else None)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(specs[-1] if len(specs) == 1 else specs[0],
-                                           min(args.cpu_sample, specs[0].tokens), map=args.map)
+                                           min(args.cpu_sample, specs[0].tokens), map=args.map,
+                                           permute=args.permute)
     res["gpu"] = torch.cuda.get_device_name(0)
     print(json.dumps(res), flush=True)
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define POETX_ABI_VERSION 3
+#define POETX_ABI_VERSION 4
 
 typedef enum poetx_status {
   POETX_OK = 0,
@@ -107,9 +107,24 @@ typedef struct poetx_linear_desc {
    * Backward stages: 0 grad through R, 1 R gram (+ reduction), 2 dense W0
    * GEMM, 3 P gram (+ reduction), 4 grad to x, 5 Cayley VJP of R,
    * 6 Cayley VJP of P, 7 recompute of Z (POETX_RECOMPUTE_Z only; it runs
-   * first, and stage 1 then runs before stage 0). May be NULL when n_events
-   * is 0. */
+   * first, and stage 1 then runs before stage 0). With permutations, forward
+   * stage 3 gathers x and stage 4 scatters y; backward stage 8 gathers g_y
+   * and x and stage 9 scatters g_x. May be NULL when n_events is 0. */
   void* const* events;
+  /* Optional block-mixing permutations (section 2 Methodik, permutation
+   * item): index maps perm_in [d_in] and perm_out [d_out], int32 device
+   * arrays (4-byte aligned), both or neither (NULL: no permutation). With
+   * them the layer is
+   *   y = Pi_out^T blockdiag(R) Pi_out W0 Pi_in^T blockdiag(P) Pi_in x,
+   * (Pi v)_i = v[perm[i]], and the W0 argument of the forward and backward
+   * is the folded weight W0' = Pi_out W0 Pi_in^T (poetx_fold_weight), so
+   * only the two outer permutations run per call: x's columns are gathered by
+   * perm_in, y's scattered by perm_out (the backward mirrors this). Each map
+   * must be a permutation of 0..d-1; an entry outside that range reads as
+   * zero (never an out-of-bounds access), a repeated entry leaves the result
+   * unspecified. */
+  const int32_t* perm_in;
+  const int32_t* perm_out;
 } poetx_linear_desc;
 
 /* Returns POETX_ABI_VERSION. */
@@ -179,6 +194,21 @@ size_t poetx_build_cnp_workspace_size(int64_t d, int32_t b);
  */
 int poetx_build_cnp(const float* theta, int64_t d, int32_t b, float* q_f32, float* blocks_f32,
                     void* blocks_act, int32_t act, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * poetx_fold_weight - the two inner permutations of the forward folded into
+ * the frozen weight once (section 2 Methodik, permutation item, reduction):
+ *   W0_folded[i][j] = W0[perm_out[i]][perm_in[j]]   (W0' = Pi_out W0 Pi_in^T)
+ *
+ *   W0, W0_folded  [d_out, d_in] in `act` type, 16-byte aligned, no overlap
+ *   perm_out       [d_out] int32, perm_in [d_in] int32 (device, 4-byte aligned);
+ *                  out-of-range entries read as zero
+ * Errors: POETX_ERR_DTYPE, POETX_ERR_SHAPE (d < 1), POETX_ERR_NULL,
+ * POETX_ERR_ALIGN (d_in not a multiple of 8 for bf16 / 4 for float32, or a
+ * pointer), POETX_ERR_ALIAS, POETX_ERR_HIP.
+ */
+int poetx_fold_weight(const void* W0, int64_t d_out, int64_t d_in, const int32_t* perm_out,
+                      const int32_t* perm_in, int32_t act, void* W0_folded, void* stream);
 
 /* Workspace bytes for poetx_linear_fwd / poetx_linear_bwd (0 if the
  * descriptor is invalid). With POETX_RECOMPUTE_Z the forward's includes Z. */

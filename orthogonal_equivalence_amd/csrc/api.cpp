@@ -49,6 +49,9 @@ int check_desc(const poetx_linear_desc* d) {
   if (d->n_events < 0 || (d->n_events > 0 && !d->events)) return POETX_ERR_NULL;
   if ((d->flags & ~(POETX_RECOMPUTE_Z | POETX_CAYLEY_NEUMANN)) != 0 || d->reserved != 0)
     return POETX_ERR_SHAPE;
+  if ((d->perm_in == nullptr) != (d->perm_out == nullptr)) return POETX_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(d->perm_in) & 3) || (reinterpret_cast<uintptr_t>(d->perm_out) & 3))
+    return POETX_ERR_ALIGN;
   const int v = act_vec(d->act);
   if (d->d_in % v || d->d_out % v || d->b_in % v || d->b_out % v) return POETX_ERR_ALIGN;
   return POETX_OK;
@@ -57,16 +60,25 @@ int check_desc(const poetx_linear_desc* d) {
 // ---------------------------------------------------------------- workspace
 bool recompute_z(const poetx_linear_desc* d) { return (d->flags & POETX_RECOMPUTE_Z) != 0; }
 bool neumann(const poetx_linear_desc* d) { return (d->flags & POETX_CAYLEY_NEUMANN) != 0; }
+bool permuted(const poetx_linear_desc* d) { return d->perm_in != nullptr; }
 
 struct FwdPlan {
-  size_t u_off, z_off, total;
+  size_t u_off, z_off, xp_off, yp_off, inv_off, total;
 };
 FwdPlan plan_fwd(const poetx_linear_desc* d) {
   FwdPlan p;
+  const size_t es = act_size(d->act);
   p.u_off = 0;
-  size_t off = align_up((size_t)d->tokens * d->d_in * act_size(d->act));
+  size_t off = align_up((size_t)d->tokens * d->d_in * es);
   p.z_off = off;  // Z lives here only when it is not kept
-  if (recompute_z(d)) off += align_up((size_t)d->tokens * d->d_out * act_size(d->act));
+  if (recompute_z(d)) off += align_up((size_t)d->tokens * d->d_out * es);
+  // with permutations: the gathered x, Y before its scatter, the inverse map
+  p.xp_off = p.yp_off = p.inv_off = off;
+  if (permuted(d)) {
+    p.xp_off = off; off += align_up((size_t)d->tokens * d->d_in * es);
+    p.yp_off = off; off += align_up((size_t)d->tokens * d->d_out * es);
+    p.inv_off = off; off += align_up((size_t)d->d_out * 4);
+  }
   p.total = off;
   return p;
 }
@@ -102,7 +114,7 @@ SplitK choose_split(int64_t nblocks, int b, int64_t d, int64_t tokens, DType in)
 }
 
 struct BwdPlan {
-  size_t gz, gu, partR, partP, GR, GP, TR, TP, MR, MP, total;
+  size_t gz, gu, partR, partP, GR, GP, TR, TP, MR, MP, gyp, xp, inv, total;
   SplitK sR, sP;
 };
 BwdPlan plan_bwd(const poetx_linear_desc* d) {
@@ -123,6 +135,14 @@ BwdPlan plan_bwd(const poetx_linear_desc* d) {
   p.TP = off; off += align_up(nbP * bbP);
   p.MR = off; off += align_up(nbR * bbR);
   p.MP = off; off += align_up(nbP * bbP);
+  // with permutations: gathered g_y, gathered x (then g_X before its
+  // scatter), the inverse map of perm_in
+  p.gyp = p.xp = p.inv = off;
+  if (permuted(d)) {
+    p.gyp = off; off += align_up((size_t)d->tokens * d->d_out * act_size(d->act));
+    p.xp = off; off += align_up((size_t)d->tokens * d->d_in * act_size(d->act));
+    p.inv = off; off += align_up((size_t)d->d_in * 4);
+  }
   p.total = off;
   return p;
 }
@@ -461,6 +481,25 @@ int poetx_build_cnp(const float* theta, int64_t d, int32_t b, float* q_f32, floa
                                              nb, b, s));
 }
 
+int poetx_fold_weight(const void* W0, int64_t d_out, int64_t d_in, const int32_t* perm_out,
+                      const int32_t* perm_in, int32_t act, void* W0_folded, void* stream) {
+  if (act != POETX_F32 && act != POETX_BF16) return POETX_ERR_DTYPE;
+  if (d_out < 1 || d_in < 1 || d_out > INT32_MAX || d_in > INT32_MAX) return POETX_ERR_SHAPE;
+  if (!W0 || !perm_out || !perm_in || !W0_folded) return POETX_ERR_NULL;
+  if (d_in % act_vec(act) || !aligned16(W0) || !aligned16(W0_folded) ||
+      (reinterpret_cast<uintptr_t>(perm_out) & 3) || (reinterpret_cast<uintptr_t>(perm_in) & 3))
+    return POETX_ERR_ALIGN;
+  const size_t bytes = (size_t)d_out * d_in * act_size(act);
+  const Range out = range_of(W0_folded, bytes);
+  if (overlap(out, range_of(W0, bytes)) || overlap(out, range_of(perm_out, d_out * 4)) ||
+      overlap(out, range_of(perm_in, d_in * 4)))
+    return POETX_ERR_ALIAS;
+  const DType t = act == POETX_BF16 ? DType::BF16 : DType::F32;
+  return hip_status(poetx::launch_gather_columns(t, W0, d_in, perm_out, d_out, d_out, (int)d_in,
+                                                 perm_in, W0_folded, d_in,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 size_t poetx_fwd_workspace_size(const poetx_linear_desc* d) {
   if (check_desc(d) != POETX_OK) return 0;
   return plan_fwd(d).total;
@@ -491,21 +530,39 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   const Range r_z = z_save ? range_of(z_save, N * m * es) : Range{0, 0};
   const Range ins[] = {range_of(x, N * n * es), range_of(W0, m * n * es),
                        range_of(R_act, nbR * d->b_out * d->b_out * es),
-                       range_of(P_act, nbP * d->b_in * d->b_in * es), range_of(ws, plan.total)};
+                       range_of(P_act, nbP * d->b_in * d->b_in * es), range_of(ws, plan.total),
+                       range_of(d->perm_in, permuted(d) ? n * 4 : 0),
+                       range_of(d->perm_out, permuted(d) ? m * 4 : 0)};
   for (const Range& r : ins)
     if (overlap(r, r_y) || overlap(r, r_z)) return POETX_ERR_ALIAS;
   if (overlap(r_y, r_z)) return POETX_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const DType t = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
-  void* U = static_cast<char*>(ws) + plan.u_off;
-  void* Z = z_save ? z_save : static_cast<char*>(ws) + plan.z_off;
+  char* w = static_cast<char*>(ws);
+  void* U = w + plan.u_off;
+  void* Z = z_save ? z_save : w + plan.z_off;
+  const bool perm = permuted(d);
+  void* Xp = w + plan.xp_off;
+  void* Yp = w + plan.yp_off;
+  int32_t* inv = reinterpret_cast<int32_t*>(w + plan.inv_off);
   Stages sg{d, s};
   hipError_t e;
 
+  // stage 3 (permutations only): X_p = X[:, perm_in], the outer P permutation
+  const void* X = x;
+  if (perm) {
+    if ((e = sg.begin(3)) != hipSuccess) return hip_status(e);
+    if ((e = poetx::launch_gather_columns(t, x, n, nullptr, N, N, (int)n, d->perm_in, Xp, n, s)) !=
+        hipSuccess)
+      return hip_status(e);
+    if ((e = sg.end(3)) != hipSuccess) return hip_status(e);
+    X = Xp;
+  }
+
   // S2: U = X blockdiag(P)^T
   if ((e = sg.begin(0)) != hipSuccess) return hip_status(e);
-  if ((e = block_apply(t, x, P_act, U, N, n, d->b_in, true, s)) != hipSuccess) return hip_status(e);
+  if ((e = block_apply(t, X, P_act, U, N, n, d->b_in, true, s)) != hipSuccess) return hip_status(e);
   if ((e = sg.end(0)) != hipSuccess) return hip_status(e);
 
   // S3: Z = U W0^T
@@ -515,9 +572,21 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
 
   // S4: Y = Z blockdiag(R)^T
   if ((e = sg.begin(2)) != hipSuccess) return hip_status(e);
-  if ((e = block_apply(t, Z, R_act, y, N, m, d->b_out, true, s)) != hipSuccess)
+  if ((e = block_apply(t, Z, R_act, perm ? Yp : y, N, m, d->b_out, true, s)) != hipSuccess)
     return hip_status(e);
   if ((e = sg.end(2)) != hipSuccess) return hip_status(e);
+
+  // stage 4 (permutations only): y[:, perm_out[i]] = Y_p[:, i], as a gather
+  // by the inverse map
+  if (perm) {
+    if ((e = sg.begin(4)) != hipSuccess) return hip_status(e);
+    if ((e = poetx::launch_invert_permutation(d->perm_out, (int)m, inv, s)) != hipSuccess)
+      return hip_status(e);
+    if ((e = poetx::launch_gather_columns(t, Yp, m, nullptr, N, N, (int)m, inv, y, m, s)) !=
+        hipSuccess)
+      return hip_status(e);
+    if ((e = sg.end(4)) != hipSuccess) return hip_status(e);
+  }
   return POETX_OK;
 }
 
@@ -548,7 +617,9 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
                        range_of(P_f32, nbP * bP * bP * 4), range_of(R_act, nbR * bR * bR * es),
                        range_of(P_act, nbP * bP * bP * es),
                        z_saved ? range_of(z_saved, N * m * es) : Range{0, 0},
-                       range_of(ws, plan.total)};
+                       range_of(ws, plan.total),
+                       range_of(d->perm_in, permuted(d) ? n * 4 : 0),
+                       range_of(d->perm_out, permuted(d) ? m * 4 : 0)};
   for (const Range& o : outs) {
     for (const Range& r : ins)
       if (overlap(o, r)) return POETX_ERR_ALIAS;
@@ -579,17 +650,37 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     if ((e = (call)) != hipSuccess) return hip_status(e); \
   } while (0)
 
+  // stage 8 (permutations only): g_Y and X gathered by perm_out and perm_in;
+  // g_X is formed in the gathered-X buffer (free after the P gram) and
+  // scattered into g_x at the end
+  const bool perm = permuted(d);
+  const void* gY = g_y;
+  const void* X = x;
+  void* gX = g_x;
+  int32_t* inv = reinterpret_cast<int32_t*>(w + plan.inv);
+  if (perm) {
+    void* gyp = w + plan.gyp;
+    void* xp = w + plan.xp;
+    POETX_TRY(sg.begin(8));
+    POETX_TRY(poetx::launch_gather_columns(t, g_y, m, nullptr, N, N, (int)m, d->perm_out, gyp, m, s));
+    POETX_TRY(poetx::launch_gather_columns(t, x, n, nullptr, N, N, (int)n, d->perm_in, xp, n, s));
+    POETX_TRY(sg.end(8));
+    gY = gyp;
+    X = xp;
+    gX = xp;
+  }
+
   auto grad_r = [&]() -> hipError_t {  // B1: g_Z = g_Y blockdiag(R)
     hipError_t r;
     if ((r = sg.begin(0)) != hipSuccess) return r;
-    if ((r = block_apply(t, g_y, R_act, gZ, N, m, bR, false, s)) != hipSuccess) return r;
+    if ((r = block_apply(t, gY, R_act, gZ, N, m, bR, false, s)) != hipSuccess) return r;
     return sg.end(0);
   };
   auto gram_r = [&](const void* Z) -> hipError_t {
     // B2: G_R[k] = g_Y[:, k]^T Z[:, k], split over tokens, then reduced
     hipError_t r;
     if ((r = sg.begin(1)) != hipSuccess) return r;
-    if ((r = block_gram(t, g_y, Z, partR, N, m, bR, plan.sR, s)) != hipSuccess) return r;
+    if ((r = block_gram(t, gY, Z, partR, N, m, bR, plan.sR, s)) != hipSuccess) return r;
     if ((r = poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, gt, s)) !=
         hipSuccess)
       return r;
@@ -602,7 +693,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     // POET-Xmem: U = X P^T into the g_U buffer and Z = U W0^T into the g_Z
     // buffer (both overwritten later), the R gram on Z, then g_Z over Z
     POETX_TRY(sg.begin(7));
-    POETX_TRY(block_apply(t, x, P_act, gU, N, n, bP, true, s));
+    POETX_TRY(block_apply(t, X, P_act, gU, N, n, bP, true, s));
     POETX_TRY(dense(t, gU, W0, gZ, N, m, n, n, n, m, true, s));
     POETX_TRY(sg.end(7));
     POETX_TRY(gram_r(gZ));
@@ -616,14 +707,22 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B4: G_P[j] = g_U[:, j]^T X[:, j]
   POETX_TRY(sg.begin(3));
-  POETX_TRY(block_gram(t, gU, x, partP, N, n, bP, plan.sP, s));
+  POETX_TRY(block_gram(t, gU, X, partP, N, n, bP, plan.sP, s));
   POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, gt, s));
   POETX_TRY(sg.end(3));
 
   // B5: g_X = g_U blockdiag(P)
   POETX_TRY(sg.begin(4));
-  POETX_TRY(block_apply(t, gU, P_act, g_x, N, n, bP, false, s));
+  POETX_TRY(block_apply(t, gU, P_act, gX, N, n, bP, false, s));
   POETX_TRY(sg.end(4));
+
+  // stage 9 (permutations only): g_x[:, perm_in[j]] = g_X[:, j]
+  if (perm) {
+    POETX_TRY(sg.begin(9));
+    POETX_TRY(poetx::launch_invert_permutation(d->perm_in, (int)n, inv, s));
+    POETX_TRY(poetx::launch_gather_columns(t, gX, n, nullptr, N, N, (int)n, inv, g_x, n, s));
+    POETX_TRY(sg.end(9));
+  }
 
   // B6: VJP of the orthogonal map for R and for P (one set of launches when
   // b_in == b_out and both sets fit one grid; stage 6 is then empty)

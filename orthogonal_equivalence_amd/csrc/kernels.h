@@ -98,6 +98,16 @@ hipError_t launch_sub(const float* A, const float* B, float* C, int64_t n, hipSt
 hipError_t launch_sym_sum(const float* A, const float* B, float* W, int64_t nblocks, int b,
                           hipStream_t stream);
 
+// ---- block-mixing permutations (permute.hip) ----
+// out[r][j] = in[src][perm[j]] for r < rows, j < d, src = rowmap ? rowmap[r] : r;
+// indices outside [0, d) (or a src outside [0, in_rows)) read as zero.
+// d, ld_in, ld_out multiples of 16 bytes / element size; out must not overlap in.
+hipError_t launch_gather_columns(DType t, const void* in, int64_t ld_in, const int32_t* rowmap,
+                                 int64_t in_rows, int64_t rows, int d, const int32_t* perm,
+                                 void* out, int64_t ld_out, hipStream_t s);
+// inv[perm[i]] = i for in-range entries, -1 elsewhere (two small launches).
+hipError_t launch_invert_permutation(const int32_t* perm, int d, int32_t* inv, hipStream_t s);
+
 // ---- backward helpers ----
 // G[blk] = sum_s part[s][blk] in split order (float32), stored as `out`;
 // entries of the last block at rows or columns >= last_valid are zero.

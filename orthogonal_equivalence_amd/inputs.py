@@ -23,6 +23,10 @@ Recipe (one layer):
   bfloat16 RNE).
 The arrays returned are float64 arrays holding exactly the rounded values, so
 the oracle consumes the very numbers the GPU path is given.
+
+Block-mixing permutations (when a test or the benchmark uses them) are drawn
+from their own generator, numpy.random.default_rng(seed + 7919):
+perm_out = permutation(d_out), then perm_in = permutation(d_in), int32.
 """
 from __future__ import annotations
 
@@ -35,6 +39,7 @@ import numpy as np
 __all__ = [
     "LayerSpec", "LayerInputs", "CONFIGS", "config_layers", "make_layer",
     "round_to_dtype", "bf16_bits", "num_blocks", "theta_count", "resized",
+    "make_permutations",
 ]
 
 
@@ -126,6 +131,14 @@ def make_layer(spec: LayerSpec) -> LayerInputs:
         x=round_to_dtype(x, act),
         g_y=round_to_dtype(g_y, act),
     )
+
+
+def make_permutations(spec: LayerSpec):
+    """Seeded random index maps (perm_out [d_out], perm_in [d_in]), int32."""
+    rng = np.random.default_rng(spec.seed + 7919)
+    perm_out = rng.permutation(spec.d_out).astype(np.int32)
+    perm_in = rng.permutation(spec.d_in).astype(np.int32)
+    return perm_out, perm_in
 
 
 def resized(spec: LayerSpec, **changes) -> LayerSpec:

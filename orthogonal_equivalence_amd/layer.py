@@ -26,10 +26,13 @@ class PoetxLinear:
     map="cnp" builds the blocks by the truncated Cayley-Neumann series
     (poetx_build_cnp) and keeps the skew blocks Q for its VJP
     (POETX_CAYLEY_NEUMANN); map="cayley" (default) is the exact map.
+    perm_out / perm_in (both or neither): block-mixing index maps of R and P;
+    W0 is folded with them once here (poetx_fold_weight) and the calls then
+    gather and scatter the activations' columns.
     """
 
     def __init__(self, W0: torch.Tensor, b_in: int, b_out: int, act: str, device="cuda",
-                 recompute_z: bool = False, map: str = "cayley"):
+                 recompute_z: bool = False, map: str = "cayley", perm_out=None, perm_in=None):
         if map not in ("cayley", "cnp"):
             raise ValueError(f"unknown orthogonal map {map!r}")
         self.torch_dtype, self.act = _DT[act]
@@ -39,6 +42,17 @@ class PoetxLinear:
         self.device = torch.device(device)
         self.W0 = W0.to(self.device, self.torch_dtype).contiguous()
         self.d_out, self.d_in = self.W0.shape
+        if (perm_out is None) != (perm_in is None):
+            raise ValueError("give both permutations or neither")
+        self.perm_out = self.perm_in = None
+        if perm_out is not None:
+            i32 = dict(device=self.device, dtype=torch.int32)
+            self.perm_out = torch.as_tensor(perm_out).to(**i32).contiguous()
+            self.perm_in = torch.as_tensor(perm_in).to(**i32).contiguous()
+            folded = torch.empty_like(self.W0)
+            P.poetx_fold_weight(self.W0, self.d_out, self.d_in, self.perm_out, self.perm_in,
+                                self.act, folded)
+            self.W0 = folded
         self.b_in, self.b_out = b_in, b_out
         self.nb_in = P.poetx_num_blocks(self.d_in, b_in)
         self.nb_out = P.poetx_num_blocks(self.d_out, b_out)
@@ -76,7 +90,7 @@ class PoetxLinear:
 
     def desc(self, tokens: int, events=None):
         return P.make_desc(tokens, self.d_in, self.d_out, self.b_in, self.b_out, self.act, events,
-                           self.flags)
+                           self.flags, self.perm_in, self.perm_out)
 
     def _ws(self, cache, size_fn, tokens):
         if tokens not in cache:

@@ -48,13 +48,15 @@ def check(name: str, got, ref, dtype: str) -> float:
     return err
 
 
-def run_layer(L, stream=None, recompute_z=False, map="cayley"):
+def run_layer(L, stream=None, recompute_z=False, map="cayley", perms=None):
     """Build, forward and backward one layer on the GPU (the bench's path).
     Returns the PoetxLinear and a dict of device results (z is None when the
-    layer recomputes Z in the backward)."""
+    layer recomputes Z in the backward). perms: (perm_out, perm_in) or None."""
     from orthogonal_equivalence_amd.layer import PoetxLinear
     s = L.spec
-    lay = PoetxLinear(dev(L.W0, s.dtype), s.b, s.b, s.dtype, recompute_z=recompute_z, map=map)
+    po, pi = perms if perms is not None else (None, None)
+    lay = PoetxLinear(dev(L.W0, s.dtype), s.b, s.b, s.dtype, recompute_z=recompute_z, map=map,
+                      perm_out=po, perm_in=pi)
     lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
     x = dev(L.x, s.dtype)
     g_y = dev(L.g_y, s.dtype)

@@ -17,6 +17,16 @@ P = pytest.importorskip("orthogonal_equivalence_amd.poetx",
 ALIGNED = 1 << 20  # a fake 16-byte aligned address; validation never dereferences it
 
 
+@pytest.fixture(autouse=True)
+def _cpu_only():
+    """Every call here is meant to stop in host validation; on a machine with a
+    visible GPU a call that got past it would launch on fake addresses, so
+    these tests run only where no GPU is visible."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-validation tests use fake device addresses; run them without a GPU")
+
+
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -33,7 +43,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 3
+    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 4
     for s in range(8):
         assert P.status_string(s) and P.status_string(s) != "unknown status"
     assert P.status_string(99) == "unknown status"
@@ -87,7 +97,8 @@ def desc(**over):
     k = dict(SMALL)
     k.update(over)
     return P.make_desc(k["tokens"], k["d_in"], k["d_out"], k["b_in"], k["b_out"], k["act"],
-                       flags=k.get("flags", 0))
+                       flags=k.get("flags", 0), perm_in=k.get("perm_in"),
+                       perm_out=k.get("perm_out"))
 
 
 @pytest.mark.parametrize("call", [_fwd, _bwd])
@@ -283,3 +294,61 @@ def test_build_cnp_errors():
     assert call(q=ALIGNED) == P.POETX_ERR_ALIAS             # Q on top of theta
     assert call(f32=ALIGNED * 2) == P.POETX_ERR_ALIAS       # R on top of Q
     assert call(act_ptr=ALIGNED * 5) == P.POETX_ERR_ALIAS   # act copy inside the workspace
+
+
+# -- block-mixing permutations: descriptor maps and poetx_fold_weight --------
+
+PERMS = dict(perm_in=ALIGNED * 300, perm_out=ALIGNED * 301)
+
+
+def test_permutations_both_or_neither():
+    for call in (_fwd, _bwd):
+        assert call(desc(perm_in=ALIGNED * 300)) == P.POETX_ERR_NULL
+        assert call(desc(perm_out=ALIGNED * 301)) == P.POETX_ERR_NULL
+        assert call(desc(perm_in=ALIGNED * 300 + 2, perm_out=ALIGNED * 301)) == P.POETX_ERR_ALIGN
+        d = desc(**PERMS)
+        need = (P.poetx_fwd_workspace_size if call is _fwd else P.poetx_bwd_workspace_size)(d)
+        assert call(d, ws_bytes=need - 1) == P.POETX_ERR_WORKSPACE
+    assert P.poetx_fwd_workspace_size(desc(perm_in=ALIGNED)) == 0
+
+
+def test_permutation_workspace_sizes():
+    es = 2
+    base = desc(tokens=1000, d_in=512, d_out=768)
+    perm = desc(tokens=1000, d_in=512, d_out=768, **PERMS)
+    N, n, m = 1000, 512, 768
+    assert P.poetx_fwd_workspace_size(perm) - P.poetx_fwd_workspace_size(base) >= N * (n + m) * es + m * 4
+    assert P.poetx_bwd_workspace_size(perm) - P.poetx_bwd_workspace_size(base) >= N * (n + m) * es + n * 4
+
+
+def test_permutation_maps_are_inputs_for_alias_checks():
+    d = desc(**PERMS)
+    assert _fwd(d, y=ALIGNED * 300) == P.POETX_ERR_ALIAS       # y on top of perm_in
+    assert _bwd(d, g_x=ALIGNED * 301) == P.POETX_ERR_ALIAS     # g_x on top of perm_out
+
+
+def _fold(W0, d_out, d_in, po, pi, act, out):
+    return P._lib.poetx_fold_weight(W0, d_out, d_in, po, pi, act, out, None)
+
+
+def test_fold_weight_errors():
+    ok = dict(W0=ALIGNED, d_out=64, d_in=32, po=ALIGNED * 2, pi=ALIGNED * 3, act=P.POETX_BF16,
+              out=ALIGNED * 4)
+
+    def call(**over):
+        a = dict(ok)
+        a.update(over)
+        return _fold(a["W0"], a["d_out"], a["d_in"], a["po"], a["pi"], a["act"], a["out"])
+
+    assert call(act=3) == P.POETX_ERR_DTYPE
+    assert call(d_out=0) == P.POETX_ERR_SHAPE
+    assert call(d_in=-4) == P.POETX_ERR_SHAPE
+    assert call(W0=None) == P.POETX_ERR_NULL
+    assert call(po=None) == P.POETX_ERR_NULL
+    assert call(pi=None) == P.POETX_ERR_NULL
+    assert call(out=None) == P.POETX_ERR_NULL
+    assert call(d_in=36) == P.POETX_ERR_ALIGN                # bf16 rows of 72 bytes
+    assert call(out=ALIGNED * 4 + 8) == P.POETX_ERR_ALIGN
+    assert call(po=ALIGNED * 2 + 2) == P.POETX_ERR_ALIGN
+    assert call(out=ALIGNED) == P.POETX_ERR_ALIAS            # in place
+    assert call(out=ALIGNED * 3) == P.POETX_ERR_ALIAS        # on top of perm_in

@@ -20,7 +20,8 @@ if not torch.cuda.is_available():  # collected on CPU too; every test here is gp
 
 import oracle.poetx_oracle as O  # noqa: E402
 from orthogonal_equivalence_amd import poetx as P  # noqa: E402
-from orthogonal_equivalence_amd.inputs import CONFIGS, LayerSpec, make_layer, resized  # noqa: E402
+from orthogonal_equivalence_amd.inputs import (CONFIGS, LayerSpec, make_layer,  # noqa: E402
+                                               make_permutations, resized, round_to_dtype)
 from tests import gpu_util as U  # noqa: E402
 from tests.oracle_pins import load_closed_forms, load_cnp_closed_forms  # noqa: E402
 
@@ -161,10 +162,11 @@ def test_theta_zero_is_plain_linear():
 
 
 # ------------------------------------------------- full-size workloads
-def _sampled_check(L, lay, out, n_rows=48, rng_seed=0, map="cayley"):
+def _sampled_check(L, lay, out, n_rows=48, rng_seed=0, map="cayley", perms=None):
     s = L.spec
     b = s.b
-    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, b, b, map=map)
+    po, pi = perms if perms is not None else (None, None)
+    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, b, b, map=map, perm_out=po, perm_in=pi)
     U.check("R", U.host(lay.R_f32), ora.R, "f32")
     U.check("P", U.host(lay.P_f32), ora.P, "f32")
     rng = np.random.default_rng(rng_seed)
@@ -174,24 +176,28 @@ def _sampled_check(L, lay, out, n_rows=48, rng_seed=0, map="cayley"):
     U.check("y rows", y_gpu, ora.forward(L.x[rows]), s.dtype)
     gx_gpu = U.host(out["g_x"][torch.from_numpy(rows).cuda()])
     U.check("g_x rows", gx_gpu, L.g_y[rows] @ ora.W, s.dtype)
-    # whole generator blocks: first and last R block, last P block
-    W0P = O.materialise(L.W0, np.broadcast_to(np.eye(b), ora.R.shape), ora.P, b, b)
-    RW0 = O.materialise(L.W0, ora.R, np.broadcast_to(np.eye(b), ora.P.shape), b, b)
+    # whole generator blocks: first and last R block, last P block (with
+    # permutations the blocks see the folded W0 and the gathered g_y and x)
+    W0f, gy, xx = L.W0, L.g_y, L.x
+    if perms is not None:
+        W0f, gy, xx = O.fold_permutations(L.W0, po, pi), L.g_y[:, po], L.x[:, pi]
+    W0P = O.materialise(W0f, np.broadcast_to(np.eye(b), ora.R.shape), ora.P, b, b)
+    RW0 = O.materialise(W0f, ora.R, np.broadcast_to(np.eye(b), ora.P.shape), b, b)
     gR = U.host(out["g_theta_R"])
     gP = U.host(out["g_theta_P"])
     for k in sorted({0, ora.R.shape[0] - 1}):
         rk = slice(k * b, (k + 1) * b)
-        G = (L.g_y[:, rk].T @ L.x) @ W0P[rk, :].T
+        G = (gy[:, rk].T @ xx) @ W0P[rk, :].T
         ref = ora.vjp(ora.B_R[k:k + 1], G[None])[0]
         U.check(f"gthR[{k}]", gR[k], ref, s.dtype)
     j = ora.P.shape[0] - 1
     cj = slice(j * b, (j + 1) * b)
-    G = RW0[:, cj].T @ (L.g_y.T @ L.x[:, cj])
+    G = RW0[:, cj].T @ (gy.T @ xx[:, cj])
     ref = ora.vjp(ora.B_P[j:j + 1], G[None])[0]
     U.check(f"gthP[{j}]", gP[j], ref, s.dtype)
     # property at full size: R is orthogonal per block, so ||y_t,k|| = ||z_t,k||
     # (the series is orthogonal to O(|Q|^6), far below bf16 at these sizes)
-    if out.get("z") is not None:
+    if out.get("z") is not None and perms is None:
         y = out["y"].float().view(s.tokens, -1, b)
         z = out["z"].float().view(s.tokens, -1, b)
         ny, nz = y.norm(dim=2), z.norm(dim=2)
@@ -367,5 +373,103 @@ def test_cnp_full_size_mlp_up_8b():
     L = make_layer(spec)
     lay, out = U.run_layer(L, map="cnp")
     _sampled_check(L, lay, out, map="cnp")
+    del lay, out
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------- block-mixing permutations
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+@pytest.mark.parametrize("dt,d_out,d_in", [
+    ("bf16", 48, 4096), ("f32", 40, 1024), ("bf16", 9, 14336),
+    ("bf16", 5, 40000), ("f32", 3, 20000),   # rows over 64 KB: the global-memory gather
+])
+def test_fold_weight_bit_exact(dt, d_out, d_in):
+    U.log(f"[fold] {dt} {d_out}x{d_in}")
+    rng = np.random.default_rng(d_out * 31 + d_in)
+    W0 = round_to_dtype(rng.standard_normal((d_out, d_in)), dt)
+    po, pi = rng.permutation(d_out), rng.permutation(d_in)
+    act = P.POETX_BF16 if dt == "bf16" else P.POETX_F32
+    Wd = U.dev(W0, dt)
+    out = torch.empty_like(Wd)
+    P.poetx_fold_weight(Wd, d_out, d_in, _i32(po), _i32(pi), act, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(U.host(out), W0[np.ix_(po, pi)])
+
+
+def test_fold_weight_out_of_range_entries_read_zero():
+    """Entries outside [0, d) are bounds-checked in the kernel and read as zero."""
+    rng = np.random.default_rng(3)
+    d_out, d_in = 6, 64
+    W0 = round_to_dtype(rng.standard_normal((d_out, d_in)), "bf16")
+    po = np.array([5, 4, -1, 2, 6, 0])
+    pi = rng.permutation(d_in)
+    pi[[3, 17]] = [-7, d_in]
+    out = torch.empty(d_out, d_in, device="cuda", dtype=torch.bfloat16)
+    P.poetx_fold_weight(U.dev(W0, "bf16"), d_out, d_in, _i32(po), _i32(pi), P.POETX_BF16, out)
+    torch.cuda.synchronize()
+    got = U.host(out)
+    ref = np.zeros((d_out, d_in))
+    for i in range(d_out):
+        for j in range(d_in):
+            if 0 <= po[i] < d_out and 0 <= pi[j] < d_in:
+                ref[i, j] = W0[po[i], pi[j]]
+    assert np.array_equal(got, ref)
+
+
+PERM_CASES = [
+    # name, d_in, d_out, b, tokens, dtype, sigma, map
+    ("perm_f32_tiles", 192, 320, 32, 200, "f32", 0.05, "cayley"),
+    ("perm_f32_padded_cnp", 200, 136, 48, 130, "f32", 0.05, "cnp"),
+    ("perm_bf16_b128", 512, 768, 128, 1000, "bf16", 0.02, "cayley"),
+    ("perm_bf16_b256_cnp", 512, 1024, 256, 300, "bf16", 0.01, "cnp"),
+    ("perm_bf16_padded", 320, 200, 128, 257, "bf16", 0.02, "cayley"),
+]
+
+
+@pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: c[0])
+def test_perm_layer_small_full_compare(case):
+    name, n, m, b, N, dt, sigma, map_ = case
+    spec = LayerSpec(name, n, m, b, N, dt, sigma, seed=len(name) + 200)
+    U.log(f"[perm layer] {name}: d_in={n} d_out={m} b={b} tokens={N} {dt} {map_}")
+    L = make_layer(spec)
+    po, pi = make_permutations(spec)
+    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, b, b, map=map_, perm_out=po, perm_in=pi)
+    y_ref = ora.forward(L.x)
+    gx_ref, gR_ref, gP_ref = ora.backward(L.g_y, L.x)
+    lay, out = U.run_layer(L, map=map_, perms=(po, pi))
+    assert np.array_equal(U.host(lay.W0), L.W0[np.ix_(po, pi)])
+    U.check("y", U.host(out["y"]), y_ref, dt)
+    U.check("g_x", U.host(out["g_x"]), gx_ref, dt)
+    U.check("g_theta_R", U.host(out["g_theta_R"]), gR_ref, dt)
+    U.check("g_theta_P", U.host(out["g_theta_P"]), gP_ref, dt)
+    # Z recomputed from the gathered x: the same bits
+    _, mem = U.run_layer(L, map=map_, perms=(po, pi), recompute_z=True)
+    for k in ("y", "g_x", "g_theta_R", "g_theta_P"):
+        assert torch.equal(mem[k], out[k]), k
+
+
+def test_perm_identity_maps_bitwise():
+    """Identity index maps: every output bit for bit that of the layer
+    without permutations (gathers by the identity copy exactly)."""
+    spec = LayerSpec("perm_id", 512, 768, 128, 1000, "bf16", 0.02, seed=21)
+    L = make_layer(spec)
+    _, a = U.run_layer(L)
+    _, c = U.run_layer(L, perms=(np.arange(768), np.arange(512)))
+    for k in ("y", "z", "g_x", "g_theta_R", "g_theta_P"):
+        assert torch.equal(a[k], c[k]), k
+
+
+def test_perm_full_size_mlp_up_8b():
+    """The 8B MLP up-projection (14336 x 4096, b = 256, 8192 tokens) with
+    random block-mixing permutations: sampled oracle checks."""
+    spec = CONFIGS["mlp_up_8b"][0]
+    U.log(f"[perm full] {spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
+    L = make_layer(spec)
+    po, pi = make_permutations(spec)
+    lay, out = U.run_layer(L, perms=(po, pi))
+    _sampled_check(L, lay, out, perms=(po, pi))
     del lay, out
     torch.cuda.empty_cache()
