@@ -25,6 +25,10 @@ on gist.science, "Technische Zusammenfassung"):
           of the orthogonal matrices; they are applied as index maps
           (bijections) on the data, and two of the four permutations of the
           forward pass are folded into the weight in advance.
+  [XQ]    §2 Methodik, quantised-support item (POET-XQ): since the transform
+          acts on the activations and no high-precision copy of the weight
+          has to be kept, the frozen weight may be a quantised (e.g. INT8)
+          model.
 
 Readings taken where the pages are silent (each is listed in the design doc):
   * the orthogonal map is the exact Cayley map R = (I + Q)(I - Q)^-1 (the
@@ -48,7 +52,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
     orthogonal factors are R = Pi_R^T blockdiag(R_k) Pi_R and
     P = Pi_P^T blockdiag(P_j) Pi_P, where (Pi v)_i = v[pi(i)] for an index
     map pi; these are the four permutations of the forward, and the inner
-    two fold into W0' = Pi_R W0 Pi_P^T, W0'[i][j] = W0[pi_R(i)][pi_P(j)].
+    two fold into W0' = Pi_R W0 Pi_P^T, W0'[i][j] = W0[pi_R(i)][pi_P(j)];
+  * INT8 weights (optional) are symmetric with one float32 scale per output
+    row: s_i = amax_i / 127 and q_ij = clamp(rint(w_ij / s_i), -127, 127),
+    both divisions in float32 (round to nearest even), s_i = 0 and q = 0 for
+    an all-zero row; the layer then uses W0 = diag(s) q exactly.
 
 Where "parity unpinned": nothing here. Every function is pinned by
 tests/test_oracle.py against closed forms (b = 2 rotation, b = 3 Rodrigues
@@ -73,7 +81,7 @@ __all__ = [
     "backward", "cayley_vjp", "forward_input_centric",
     "backward_input_centric", "LayerOracle", "CNP_ORDER", "cayley_neumann",
     "cayley_neumann_vjp", "orthogonal_blocks_cnp", "permutation_matrix",
-    "fold_permutations", "materialise_permuted",
+    "fold_permutations", "materialise_permuted", "quantize_rows", "dequantize_rows",
 ]
 
 
@@ -241,6 +249,28 @@ def materialise_permuted(W0, R, P, b_out, b_in, perm_out, perm_in):
     W = np.empty_like(M)
     W[np.ix_(np.asarray(perm_out), np.asarray(perm_in))] = M
     return W
+
+
+# --------------------------------------------------- INT8 base weight [XQ]
+def quantize_rows(W0: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric per-output-row INT8 codes of W0 [d_out, d_in]:
+    s_i = amax_i / 127 and q_ij = clamp(rint(w_ij / s_i), -127, 127), every
+    operation in float32 (so the codes are decided in the precision the GPU
+    uses); a zero row gets s = 0, q = 0. Returns (q int8, s float32). [XQ]"""
+    W = np.asarray(W0, dtype=np.float32)
+    amax = np.max(np.abs(W), axis=1).astype(np.float32)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    q = np.zeros(W.shape, dtype=np.int8)
+    for i in range(W.shape[0]):
+        if s[i] > 0:
+            r = np.rint((W[i] / s[i]).astype(np.float32))
+            q[i] = np.clip(r, -127, 127).astype(np.int8)
+    return q, s
+
+
+def dequantize_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """W0 = diag(s) q in float64 (exact: an int8 code times a float32). [XQ]"""
+    return np.asarray(s, dtype=np.float64)[:, None] * np.asarray(q, dtype=np.float64)
 
 
 # ------------------------------------------------------- forward / backward

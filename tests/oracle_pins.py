@@ -525,6 +525,41 @@ def pin_perm_finite_differences(h=1e-6, rtol=1e-6):
             assert np.max(np.abs(got - ref)) <= rtol * np.abs(ref).max(), map_
 
 
+# ------------------------------------------------------------ INT8 weights
+def pin_quantize_closed_forms():
+    """Rows built as 2^-7 times integers with amax 127 * 2^-7 quantise to
+    exactly those integers with s = 2^-7; ties w / s = k + 1/2 round to even;
+    a zero row gives s = 0, q = 0; rows are scaled independently."""
+    u = 2.0 ** -7
+    W = np.zeros((4, 8))
+    W[0] = u * np.array([127, -3, 64, 0, 1, -127, 5, 100])
+    W[1] = u * np.array([2.5, 3.5, -2.5, -3.5, 0.5, 1.5, 127, 0])   # ties
+    W[3] = 0.5 * u * np.array([127, 1, 2, 3, -4, 5, 6, 7])          # s = 2^-8
+    q, s = O.quantize_rows(W)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert s[0] == u and s[1] == u and s[2] == 0.0 and s[3] == u / 2
+    assert np.array_equal(q[0], [127, -3, 64, 0, 1, -127, 5, 100])
+    assert np.array_equal(q[1], [2, 4, -2, -4, 0, 2, 127, 0])
+    assert np.array_equal(q[2], np.zeros(8))
+    assert np.array_equal(q[3], [127, 1, 2, 3, -4, 5, 6, 7])
+    D = O.dequantize_rows(q, s)
+    assert np.array_equal(D[0], W[0]) and np.array_equal(D[3], W[3])
+    assert np.array_equal(D[1], u * np.array([2, 4, -2, -4, 0, 2, 127, 0]))
+    assert np.array_equal(D[2], np.zeros(8))
+
+
+def pin_quantize_error_bound():
+    """Random rows: |q| <= 127 with 127 reached in every nonzero row, and
+    |w - s q| <= s / 2 up to float32 rounding of w / s."""
+    rng = np.random.default_rng(97)
+    W = (rng.standard_normal((64, 300)) * rng.uniform(0.01, 3.0, (64, 1))).astype(np.float32)
+    q, s = O.quantize_rows(W)
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    assert np.all(np.max(np.abs(q.astype(int)), axis=1) == 127)
+    err = np.abs(W.astype(np.float64) - O.dequantize_rows(q, s))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 1e-5)), err.max()
+
+
 ALL_PINS = [
     pin_packing_order, pin_golden_closed_forms, pin_b2_rotation, pin_b3_rodrigues,
     pin_eigenvalue_map, pin_orthogonality_det_transpose, pin_spectrum,
@@ -533,5 +568,5 @@ ALL_PINS = [
     pin_cnp_golden, pin_cnp_b3_closed_form, pin_cnp_series_tail, pin_cnp_vjp_frechet,
     pin_cnp_theta_zero, pin_cnp_finite_differences, pin_permutation_convention,
     pin_perm_explicit_matrices, pin_perm_identity_reduces, pin_perm_spectrum_and_routes,
-    pin_perm_finite_differences,
+    pin_perm_finite_differences, pin_quantize_closed_forms, pin_quantize_error_bound,
 ]

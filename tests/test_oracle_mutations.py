@@ -66,6 +66,19 @@ MUTATIONS = [
      [pins.pin_perm_spectrum_and_routes]),
     ("permutation_matrix", "M[np.arange(d), pi] = 1.0", "M[pi, np.arange(d)] = 1.0",
      [pins.pin_permutation_convention, pins.pin_perm_explicit_matrices]),
+    # INT8 weights
+    ("quantize_rows", "r = np.rint((W[i] / s[i]).astype(np.float32))",
+     "r = np.floor((W[i] / s[i]).astype(np.float32) + 0.5)",
+     [pins.pin_quantize_closed_forms]),
+    ("quantize_rows", "s = (amax / np.float32(127.0)).astype(np.float32)",
+     "s = (amax / np.float32(128.0)).astype(np.float32)",
+     [pins.pin_quantize_closed_forms, pins.pin_quantize_error_bound]),
+    ("quantize_rows", "amax = np.max(np.abs(W), axis=1).astype(np.float32)",
+     "amax = np.full(W.shape[0], np.max(np.abs(W)), dtype=np.float32)",
+     [pins.pin_quantize_closed_forms, pins.pin_quantize_error_bound]),
+    ("dequantize_rows", "np.asarray(s, dtype=np.float64)[:, None] * np.asarray(q, dtype=np.float64)",
+     "np.asarray(s, dtype=np.float64)[None, :1] * np.asarray(q, dtype=np.float64)",
+     [pins.pin_quantize_closed_forms]),
 ]
 
 
