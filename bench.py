@@ -36,6 +36,8 @@ PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
 # stage names by the library's stage index (None: a stage that does not run)
 FWD_STAGES = ["p_apply", "dense_fwd", "r_apply"]
 FWD_PERM_STAGES = ["gather_x", "scatter_y"]
+FWD_INT8_STAGE = 5       # widen the INT8 codes, scale R's block columns
+BWD_INT8_STAGE = 10
 BWD_STAGES = ["grad_r", "gram_r", "dense_bwd", "gram_p", "grad_x", "vjp_r", "vjp_p"]
 BWD_PERM_STAGES = ["gather_gy_x", "scatter_gx"]
 
@@ -53,7 +55,7 @@ def layer_work(s):
     return flops, fwd + bwd + build
 
 
-def cpu_baseline(spec, sample_tokens, map="cayley", permute=False):
+def cpu_baseline(spec, sample_tokens, map="cayley", permute=False, int8=False):
     """The float64 oracle (build, materialise, forward, backward) on the first
     `sample_tokens` tokens of the workload, timed on the host's cores."""
     import dataclasses
@@ -71,7 +73,8 @@ def cpu_baseline(spec, sample_tokens, map="cayley", permute=False):
     reps, t0 = 0, time.perf_counter()
     while True:
         po, pi = make_permutations(spec) if permute else (None, None)
-        ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b, map=map, perm_out=po,
+        W0 = O.dequantize_rows(*O.quantize_rows(L.W0)) if int8 else L.W0
+        ora = O.LayerOracle(W0, L.theta_R, L.theta_P, spec.b, spec.b, map=map, perm_out=po,
                             perm_in=pi)
         ora.forward(x)
         ora.backward(g_y, x)
@@ -87,7 +90,7 @@ def cpu_baseline(spec, sample_tokens, map="cayley", permute=False):
                       f"{spec.d_out}x{spec.d_in} b={spec.b}; {dt:.1f} s"}
 
 
-def parity_sample(L, out, lay, rows=32, map="cayley", perms=None):
+def parity_sample(L, out, lay, rows=32, map="cayley", perms=None, int8=False):
     """Frobenius-relative error of sampled token rows of y and g_x against the
     oracle's materialised weight (the full-size parity tests do more)."""
     import oracle.poetx_oracle as O
@@ -96,10 +99,11 @@ def parity_sample(L, out, lay, rows=32, map="cayley", perms=None):
     build = O.orthogonal_blocks if map == "cayley" else O.orthogonal_blocks_cnp
     R, _ = build(L.theta_R, s.b, s.d_out)
     Pb, _ = build(L.theta_P, s.b, s.d_in)
+    W0 = O.dequantize_rows(*O.quantize_rows(L.W0)) if int8 else L.W0
     if perms is None:
-        W = O.materialise(L.W0, R, Pb, s.b, s.b)
+        W = O.materialise(W0, R, Pb, s.b, s.b)
     else:
-        W = O.materialise_permuted(L.W0, R, Pb, s.b, s.b, perms[0], perms[1])
+        W = O.materialise_permuted(W0, R, Pb, s.b, s.b, perms[0], perms[1])
     idx = np.linspace(0, s.tokens - 1, rows).astype(np.int64)
     ti = torch.from_numpy(idx).cuda()
     y = out["y"][ti].float().cpu().double().numpy()
@@ -167,6 +171,8 @@ def main():
                     help="POET-Xmem variant: the forward keeps no Z, the backward recomputes it")
     ap.add_argument("--permute", action="store_true",
                     help="random block-mixing permutations of R and P (W0 folded once)")
+    ap.add_argument("--int8", action="store_true",
+                    help="POET-XQ: the frozen weight stored as INT8 codes with per-row scales")
     ap.add_argument("--map", choices=("cayley", "cnp"), default="cayley",
                     help="orthogonal map: exact Cayley (default) or the truncated "
                          "Cayley-Neumann series")
@@ -199,7 +205,8 @@ def main():
         L = make_layer(s)
         po, pi = make_permutations(s) if args.permute else (None, None)
         lay = PoetxLinear(torch.from_numpy(L.W0).to(tdt[s.dtype]), s.b, s.b, s.dtype, device=dev,
-                          recompute_z=args.recompute_z, map=args.map, perm_out=po, perm_in=pi)
+                          recompute_z=args.recompute_z, map=args.map, perm_out=po, perm_in=pi,
+                          int8=args.int8)
         lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
         x = torch.from_numpy(L.x).to(tdt[s.dtype]).to(dev)
         g_y = torch.from_numpy(L.g_y).to(tdt[s.dtype]).to(dev)
@@ -210,10 +217,15 @@ def main():
                    gR=torch.empty_like(lay.theta_R), gP=torch.empty_like(lay.theta_P))
         layers.append((s, L if len(specs) == 1 else None, lay, x, g_y, out))
     stream = torch.cuda.current_stream()
-    fwd_stages = FWD_STAGES + (FWD_PERM_STAGES if args.permute else [])
+    fwd_stages = FWD_STAGES + (FWD_PERM_STAGES if args.permute else [None, None])
     bwd_stages = BWD_STAGES + (["recompute_z" if args.recompute_z else None] +
-                               (BWD_PERM_STAGES if args.permute else []))
-    if bwd_stages[-1] is None:
+                               (BWD_PERM_STAGES if args.permute else [None, None]))
+    if args.int8:
+        fwd_stages += [None] * (FWD_INT8_STAGE - len(fwd_stages)) + ["int8_widen_fwd"]
+        bwd_stages += [None] * (BWD_INT8_STAGE - len(bwd_stages)) + ["int8_widen_bwd"]
+    while fwd_stages[-1] is None:
+        fwd_stages.pop()
+    while bwd_stages[-1] is None:
         bwd_stages.pop()
 
     def step(ev=None):
@@ -310,7 +322,8 @@ def main():
                                else "POET-X (Z kept for the backward)"),
                    "orthogonal_map": ("exact Cayley" if args.map == "cayley"
                                       else "Cayley-Neumann series to Q^4"),
-                   "permutations": bool(args.permute)},
+                   "permutations": bool(args.permute),
+                   "weight": "int8 codes + per-row float32 scales" if args.int8 else specs[0].dtype},
         "roofline": roofline,
         "layer_roofline": {"flops": F, "bytes": B, "t_roof_ms": t_roof * 1e3,
                            "frac": t_roof / (ms_per_step / 1e3),
@@ -322,11 +335,12 @@ def main():
     if not args.no_parity and len(layers) == 1:
         s, L, lay, x, g_y, o = layers[0]
         res["parity"] = parity_sample(L, dict(y=o["y"], g_x=o["g_x"]), lay, map=args.map,
-                                      perms=make_permutations(s) if args.permute else None)
+                                      perms=make_permutations(s) if args.permute else None,
+                                      int8=args.int8)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(specs[-1] if len(specs) == 1 else specs[0],
                                            min(args.cpu_sample, specs[0].tokens), map=args.map,
-                                           permute=args.permute)
+                                           permute=args.permute, int8=args.int8)
     res["gpu"] = torch.cuda.get_device_name(0)
     print(json.dumps(res), flush=True)
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define POETX_ABI_VERSION 4
+#define POETX_ABI_VERSION 5
 
 typedef enum poetx_status {
   POETX_OK = 0,
@@ -109,7 +109,9 @@ typedef struct poetx_linear_desc {
    * 6 Cayley VJP of P, 7 recompute of Z (POETX_RECOMPUTE_Z only; it runs
    * first, and stage 1 then runs before stage 0). With permutations, forward
    * stage 3 gathers x and stage 4 scatters y; backward stage 8 gathers g_y
-   * and x and stage 9 scatters g_x. May be NULL when n_events is 0. */
+   * and x and stage 9 scatters g_x. With an INT8 weight, forward stage 5 and
+   * backward stage 10 widen the codes and scale R's block columns. May be
+   * NULL when n_events is 0. */
   void* const* events;
   /* Optional block-mixing permutations (section 2 Methodik, permutation
    * item): index maps perm_in [d_in] and perm_out [d_out], int32 device
@@ -125,6 +127,16 @@ typedef struct poetx_linear_desc {
    * unspecified. */
   const int32_t* perm_in;
   const int32_t* perm_out;
+  /* Optional INT8 frozen weight (section 2 Methodik, quantised-support item,
+   * POET-XQ). NULL: W0 is in the act type. Otherwise W0 holds int8 codes
+   * q [d_out, d_in] and w_scale [d_out] float32 row scales
+   * (poetx_quantize_weight), the layer's weight being diag(w_scale) q
+   * exactly; d_in must be a multiple of 8. The codes are widened to the act
+   * type without rounding and the scales enter through R: the forward
+   * computes Z_q = U q^T and Y = Z_q (blockdiag(R) diag(s))^T and keeps Z_q as
+   * z_save; the backward uses g_Z' = g_Y blockdiag(R) diag(s),
+   * g_U = g_Z' q and G_R = (g_Y^T Z_q) diag(s). */
+  const float* w_scale;
 } poetx_linear_desc;
 
 /* Returns POETX_ABI_VERSION. */
@@ -210,6 +222,25 @@ int poetx_build_cnp(const float* theta, int64_t d, int32_t b, float* q_f32, floa
 int poetx_fold_weight(const void* W0, int64_t d_out, int64_t d_in, const int32_t* perm_out,
                       const int32_t* perm_in, int32_t act, void* W0_folded, void* stream);
 
+/*
+ * poetx_quantize_weight - symmetric per-row INT8 codes of a weight (the
+ * scheme is not given on the pages; this one is):
+ *   scale[i] = amax_j |W0[i][j]| / 127,
+ *   q[i][j]  = clamp(rint(W0[i][j] / scale[i]), -127, 127)
+ * with both divisions correctly rounded in float32 and rint rounding half to
+ * even; an all-zero row gets scale 0 and codes 0. Weights must be finite.
+ *
+ *   W0     [d_out, d_in] in `act` type, 16-byte aligned
+ *   q      out [d_out, d_in] int8, 16-byte aligned
+ *   scale  out [d_out] float32, 4-byte aligned
+ * Errors: POETX_ERR_DTYPE, POETX_ERR_SHAPE (d < 1), POETX_ERR_NULL,
+ * POETX_ERR_ALIGN (d_in not a multiple of 8, or a pointer), POETX_ERR_ALIAS,
+ * POETX_ERR_HIP. Folding permutations first and then quantising gives the
+ * same codes as quantising first and folding (the row maxima are unchanged).
+ */
+int poetx_quantize_weight(const void* W0, int64_t d_out, int64_t d_in, int32_t act, int8_t* q,
+                          float* scale, void* stream);
+
 /* Workspace bytes for poetx_linear_fwd / poetx_linear_bwd (0 if the
  * descriptor is invalid). With POETX_RECOMPUTE_Z the forward's includes Z. */
 size_t poetx_fwd_workspace_size(const poetx_linear_desc* desc);
@@ -221,7 +252,8 @@ size_t poetx_bwd_workspace_size(const poetx_linear_desc* desc);
  *   U = X blockdiag(P)^T, Z = U W0^T, Y = Z blockdiag(R)^T.
  *
  *   x      [tokens, d_in]  act
- *   W0     [d_out, d_in]   act (frozen base weight)
+ *   W0     [d_out, d_in]   act (frozen base weight), or int8 codes when
+ *          desc->w_scale is set
  *   R_act  [nb_out, b_out, b_out] act, from poetx_build_orthogonal
  *   P_act  [nb_in,  b_in,  b_in ] act
  *   y      out [tokens, d_out] act

@@ -52,6 +52,9 @@ int check_desc(const poetx_linear_desc* d) {
   if ((d->perm_in == nullptr) != (d->perm_out == nullptr)) return POETX_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(d->perm_in) & 3) || (reinterpret_cast<uintptr_t>(d->perm_out) & 3))
     return POETX_ERR_ALIGN;
+  // INT8 weight codes are widened 8 at a time
+  if (d->w_scale && ((reinterpret_cast<uintptr_t>(d->w_scale) & 3) || d->d_in % 8))
+    return POETX_ERR_ALIGN;
   const int v = act_vec(d->act);
   if (d->d_in % v || d->d_out % v || d->b_in % v || d->b_out % v) return POETX_ERR_ALIGN;
   return POETX_OK;
@@ -61,9 +64,13 @@ int check_desc(const poetx_linear_desc* d) {
 bool recompute_z(const poetx_linear_desc* d) { return (d->flags & POETX_RECOMPUTE_Z) != 0; }
 bool neumann(const poetx_linear_desc* d) { return (d->flags & POETX_CAYLEY_NEUMANN) != 0; }
 bool permuted(const poetx_linear_desc* d) { return d->perm_in != nullptr; }
+bool int8_weight(const poetx_linear_desc* d) { return d->w_scale != nullptr; }
+size_t weight_bytes(const poetx_linear_desc* d) {
+  return (size_t)d->d_out * d->d_in * (int8_weight(d) ? 1 : act_size(d->act));
+}
 
 struct FwdPlan {
-  size_t u_off, z_off, xp_off, yp_off, inv_off, total;
+  size_t u_off, z_off, xp_off, yp_off, inv_off, wq_off, rs_off, total;
 };
 FwdPlan plan_fwd(const poetx_linear_desc* d) {
   FwdPlan p;
@@ -78,6 +85,12 @@ FwdPlan plan_fwd(const poetx_linear_desc* d) {
     p.xp_off = off; off += align_up((size_t)d->tokens * d->d_in * es);
     p.yp_off = off; off += align_up((size_t)d->tokens * d->d_out * es);
     p.inv_off = off; off += align_up((size_t)d->d_out * 4);
+  }
+  // INT8 weight: the widened codes and the column-scaled R blocks
+  p.wq_off = p.rs_off = off;
+  if (int8_weight(d)) {
+    p.wq_off = off; off += align_up((size_t)d->d_out * d->d_in * es);
+    p.rs_off = off; off += align_up((size_t)ceil_div(d->d_out, d->b_out) * d->b_out * d->b_out * es);
   }
   p.total = off;
   return p;
@@ -114,7 +127,7 @@ SplitK choose_split(int64_t nblocks, int b, int64_t d, int64_t tokens, DType in)
 }
 
 struct BwdPlan {
-  size_t gz, gu, partR, partP, GR, GP, TR, TP, MR, MP, gyp, xp, inv, total;
+  size_t gz, gu, partR, partP, GR, GP, TR, TP, MR, MP, gyp, xp, inv, wq, rs, total;
   SplitK sR, sP;
 };
 BwdPlan plan_bwd(const poetx_linear_desc* d) {
@@ -142,6 +155,12 @@ BwdPlan plan_bwd(const poetx_linear_desc* d) {
     p.gyp = off; off += align_up((size_t)d->tokens * d->d_out * act_size(d->act));
     p.xp = off; off += align_up((size_t)d->tokens * d->d_in * act_size(d->act));
     p.inv = off; off += align_up((size_t)d->d_in * 4);
+  }
+  p.wq = p.rs = off;
+  if (int8_weight(d)) {
+    const size_t es = act_size(d->act);
+    p.wq = off; off += align_up((size_t)d->d_out * d->d_in * es);
+    p.rs = off; off += align_up((size_t)nbR * d->b_out * d->b_out * es);
   }
   p.total = off;
   return p;
@@ -500,6 +519,21 @@ int poetx_fold_weight(const void* W0, int64_t d_out, int64_t d_in, const int32_t
                                                  static_cast<hipStream_t>(stream)));
 }
 
+int poetx_quantize_weight(const void* W0, int64_t d_out, int64_t d_in, int32_t act, int8_t* q,
+                          float* scale, void* stream) {
+  if (act != POETX_F32 && act != POETX_BF16) return POETX_ERR_DTYPE;
+  if (d_out < 1 || d_in < 1 || d_out > INT32_MAX || d_in > INT32_MAX) return POETX_ERR_SHAPE;
+  if (!W0 || !q || !scale) return POETX_ERR_NULL;
+  if (d_in % 8 || !aligned16(W0) || !aligned16(q) || (reinterpret_cast<uintptr_t>(scale) & 3))
+    return POETX_ERR_ALIGN;
+  const Range in = range_of(W0, (size_t)d_out * d_in * act_size(act));
+  const Range rq = range_of(q, (size_t)d_out * d_in), rs = range_of(scale, (size_t)d_out * 4);
+  if (overlap(in, rq) || overlap(in, rs) || overlap(rq, rs)) return POETX_ERR_ALIAS;
+  const DType t = act == POETX_BF16 ? DType::BF16 : DType::F32;
+  return hip_status(poetx::launch_quantize_rows(t, W0, d_out, (int)d_in, q, scale,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 size_t poetx_fwd_workspace_size(const poetx_linear_desc* d) {
   if (check_desc(d) != POETX_OK) return 0;
   return plan_fwd(d).total;
@@ -528,11 +562,12 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   const int64_t nbR = ceil_div(m, d->b_out), nbP = ceil_div(n, d->b_in);
   const Range r_y = range_of(y, N * m * es);
   const Range r_z = z_save ? range_of(z_save, N * m * es) : Range{0, 0};
-  const Range ins[] = {range_of(x, N * n * es), range_of(W0, m * n * es),
+  const Range ins[] = {range_of(x, N * n * es), range_of(W0, weight_bytes(d)),
                        range_of(R_act, nbR * d->b_out * d->b_out * es),
                        range_of(P_act, nbP * d->b_in * d->b_in * es), range_of(ws, plan.total),
                        range_of(d->perm_in, permuted(d) ? n * 4 : 0),
-                       range_of(d->perm_out, permuted(d) ? m * 4 : 0)};
+                       range_of(d->perm_out, permuted(d) ? m * 4 : 0),
+                       range_of(d->w_scale, int8_weight(d) ? m * 4 : 0)};
   for (const Range& r : ins)
     if (overlap(r, r_y) || overlap(r, r_z)) return POETX_ERR_ALIAS;
   if (overlap(r_y, r_z)) return POETX_ERR_ALIAS;
@@ -548,6 +583,26 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   int32_t* inv = reinterpret_cast<int32_t*>(w + plan.inv_off);
   Stages sg{d, s};
   hipError_t e;
+
+  // stage 5 (INT8 weight only): the codes widened exactly to the activation
+  // type, and R's blocks with column j scaled by the row scale s_j, so that
+  // Y = (U q^T) (R diag(s))^T
+  const void* Wmat = W0;
+  const void* Rb = R_act;
+  if (int8_weight(d)) {
+    void* Wq = w + plan.wq_off;
+    void* Rs = w + plan.rs_off;
+    if ((e = sg.begin(5)) != hipSuccess) return hip_status(e);
+    if ((e = poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0), m * n, Wq, s)) !=
+        hipSuccess)
+      return hip_status(e);
+    if ((e = poetx::launch_scale_block_columns(t, R_act, d->w_scale, nbR, d->b_out, m, Rs, s)) !=
+        hipSuccess)
+      return hip_status(e);
+    if ((e = sg.end(5)) != hipSuccess) return hip_status(e);
+    Wmat = Wq;
+    Rb = Rs;
+  }
 
   // stage 3 (permutations only): X_p = X[:, perm_in], the outer P permutation
   const void* X = x;
@@ -567,12 +622,12 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
 
   // S3: Z = U W0^T
   if ((e = sg.begin(1)) != hipSuccess) return hip_status(e);
-  if ((e = dense(t, U, W0, Z, N, m, n, n, n, m, true, s)) != hipSuccess) return hip_status(e);
+  if ((e = dense(t, U, Wmat, Z, N, m, n, n, n, m, true, s)) != hipSuccess) return hip_status(e);
   if ((e = sg.end(1)) != hipSuccess) return hip_status(e);
 
   // S4: Y = Z blockdiag(R)^T
   if ((e = sg.begin(2)) != hipSuccess) return hip_status(e);
-  if ((e = block_apply(t, Z, R_act, perm ? Yp : y, N, m, d->b_out, true, s)) != hipSuccess)
+  if ((e = block_apply(t, Z, Rb, perm ? Yp : y, N, m, d->b_out, true, s)) != hipSuccess)
     return hip_status(e);
   if ((e = sg.end(2)) != hipSuccess) return hip_status(e);
 
@@ -613,13 +668,14 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
                         range_of(g_theta_R, (size_t)poetx_theta_count(m, bR) * 4),
                         range_of(g_theta_P, (size_t)poetx_theta_count(n, bP) * 4)};
   const Range ins[] = {range_of(g_y, N * m * es), range_of(x, N * n * es),
-                       range_of(W0, m * n * es), range_of(R_f32, nbR * bR * bR * 4),
+                       range_of(W0, weight_bytes(d)), range_of(R_f32, nbR * bR * bR * 4),
                        range_of(P_f32, nbP * bP * bP * 4), range_of(R_act, nbR * bR * bR * es),
                        range_of(P_act, nbP * bP * bP * es),
                        z_saved ? range_of(z_saved, N * m * es) : Range{0, 0},
                        range_of(ws, plan.total),
                        range_of(d->perm_in, permuted(d) ? n * 4 : 0),
-                       range_of(d->perm_out, permuted(d) ? m * 4 : 0)};
+                       range_of(d->perm_out, permuted(d) ? m * 4 : 0),
+                       range_of(d->w_scale, int8_weight(d) ? m * 4 : 0)};
   for (const Range& o : outs) {
     for (const Range& r : ins)
       if (overlap(o, r)) return POETX_ERR_ALIAS;
@@ -670,10 +726,26 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     gX = xp;
   }
 
+  // stage 10 (INT8 weight only): widened codes and R blocks with scaled
+  // columns: g_Z' = g_Y R diag(s), g_U = g_Z' q, G_R = (g_Y^T Z_q) diag(s)
+  // with Z_q = U q^T the forward's saved product
+  const void* Wmat = W0;
+  const void* Rb = R_act;
+  if (int8_weight(d)) {
+    void* Wq = w + plan.wq;
+    void* Rs = w + plan.rs;
+    POETX_TRY(sg.begin(10));
+    POETX_TRY(poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0), m * n, Wq, s));
+    POETX_TRY(poetx::launch_scale_block_columns(t, R_act, d->w_scale, nbR, bR, m, Rs, s));
+    POETX_TRY(sg.end(10));
+    Wmat = Wq;
+    Rb = Rs;
+  }
+
   auto grad_r = [&]() -> hipError_t {  // B1: g_Z = g_Y blockdiag(R)
     hipError_t r;
     if ((r = sg.begin(0)) != hipSuccess) return r;
-    if ((r = block_apply(t, gY, R_act, gZ, N, m, bR, false, s)) != hipSuccess) return r;
+    if ((r = block_apply(t, gY, Rb, gZ, N, m, bR, false, s)) != hipSuccess) return r;
     return sg.end(0);
   };
   auto gram_r = [&](const void* Z) -> hipError_t {
@@ -681,8 +753,8 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     hipError_t r;
     if ((r = sg.begin(1)) != hipSuccess) return r;
     if ((r = block_gram(t, gY, Z, partR, N, m, bR, plan.sR, s)) != hipSuccess) return r;
-    if ((r = poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, gt, s)) !=
-        hipSuccess)
+    if ((r = poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, gt, s,
+                                        d->w_scale)) != hipSuccess)
       return r;
     return sg.end(1);
   };
@@ -694,7 +766,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     // buffer (both overwritten later), the R gram on Z, then g_Z over Z
     POETX_TRY(sg.begin(7));
     POETX_TRY(block_apply(t, X, P_act, gU, N, n, bP, true, s));
-    POETX_TRY(dense(t, gU, W0, gZ, N, m, n, n, n, m, true, s));
+    POETX_TRY(dense(t, gU, Wmat, gZ, N, m, n, n, n, m, true, s));
     POETX_TRY(sg.end(7));
     POETX_TRY(gram_r(gZ));
     POETX_TRY(grad_r());
@@ -702,7 +774,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B3: g_U = g_Z W0   (B(n, k) = W0[k][n])
   POETX_TRY(sg.begin(2));
-  POETX_TRY(dense(t, gZ, W0, gU, N, n, m, m, n, n, false, s));
+  POETX_TRY(dense(t, gZ, Wmat, gU, N, n, m, m, n, n, false, s));
   POETX_TRY(sg.end(2));
 
   // B4: G_P[j] = g_U[:, j]^T X[:, j]

@@ -378,11 +378,12 @@ panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
       }
 }
 
-// grid (ceil(b*b / (4 kNT)), nblocks); b*b is a multiple of 4
+// grid (ceil(b*b / (4 kNT)), nblocks); b*b is a multiple of 4. col_scale
+// (optional) multiplies column j of block blk by col_scale[blk b + j].
 template <typename TOut>
 __global__ void __launch_bounds__(kNT)
 split_reduce_kernel(const float* __restrict__ part, int nsplit, int nblocks, int b,
-                    int last_valid, TOut* __restrict__ G) {
+                    int last_valid, const float* __restrict__ col_scale, TOut* __restrict__ G) {
   const int q = blockIdx.x * kNT + threadIdx.x;  // float4 index within the block
   const int bb = b * b;
   if (4 * q >= bb) return;
@@ -395,6 +396,14 @@ split_reduce_kernel(const float* __restrict__ part, int nsplit, int nblocks, int
     v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
   }
   float e[4] = {v.x, v.y, v.z, v.w};
+  if (col_scale) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = (4 * q + t) % b;
+      const int valid = (blk == nblocks - 1) ? last_valid : b;
+      e[t] *= (j < valid) ? col_scale[(int64_t)blk * b + j] : 0.0f;
+    }
+  }
   if (blk == nblocks - 1 && last_valid < b) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -476,14 +485,15 @@ hipError_t launch_expand_skew(const float* theta, int64_t nblocks, int b, int la
 }
 
 hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, int b,
-                               int last_valid, void* G, DType out, hipStream_t stream) {
+                               int last_valid, void* G, DType out, hipStream_t stream,
+                               const float* col_scale) {
   const dim3 grid((b * b / 4 + kNT - 1) / kNT, (int)nblocks);
   if (out == DType::BF16)
     hipLaunchKernelGGL(split_reduce_kernel<bf16_t>, grid, dim3(kNT), 0, stream, part, nsplit,
-                       (int)nblocks, b, last_valid, static_cast<bf16_t*>(G));
+                       (int)nblocks, b, last_valid, col_scale, static_cast<bf16_t*>(G));
   else
     hipLaunchKernelGGL(split_reduce_kernel<float>, grid, dim3(kNT), 0, stream, part, nsplit,
-                       (int)nblocks, b, last_valid, static_cast<float*>(G));
+                       (int)nblocks, b, last_valid, col_scale, static_cast<float*>(G));
   return hipGetLastError();
 }
 

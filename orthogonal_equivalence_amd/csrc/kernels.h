@@ -108,11 +108,24 @@ hipError_t launch_gather_columns(DType t, const void* in, int64_t ld_in, const i
 // inv[perm[i]] = i for in-range entries, -1 elsewhere (two small launches).
 hipError_t launch_invert_permutation(const int32_t* perm, int d, int32_t* inv, hipStream_t s);
 
+// ---- INT8 frozen weight (quant.hip) ----
+// Per-row symmetric codes: scale[r] = amax / 127, q = clamp(rint(w / scale)),
+// float32 correctly rounded divisions; d % 8 == 0.
+hipError_t launch_quantize_rows(DType t, const void* W, int64_t rows, int d, int8_t* q,
+                                float* scale, hipStream_t s);
+// out = q in the activation type (exact); n % 8 == 0.
+hipError_t launch_widen_codes(DType t, const int8_t* q, int64_t n, void* out, hipStream_t s);
+// out[k][i][j] = M[k][i][j] * scale[k b + j] (0 past d), activation type.
+hipError_t launch_scale_block_columns(DType t, const void* M, const float* scale, int64_t nblocks,
+                                      int b, int64_t d, void* out, hipStream_t s);
+
 // ---- backward helpers ----
 // G[blk] = sum_s part[s][blk] in split order (float32), stored as `out`;
-// entries of the last block at rows or columns >= last_valid are zero.
+// entries of the last block at rows or columns >= last_valid are zero. With
+// col_scale, column j of block blk is multiplied by col_scale[blk b + j].
 hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, int b,
-                               int last_valid, void* G, DType out, hipStream_t stream);
+                               int last_valid, void* G, DType out, hipStream_t stream,
+                               const float* col_scale = nullptr);
 // g_theta[blk][idx(i,j)] = sign ((M + c S)[i][j] - (M + c S)[j][i]) (i < j),
 // S an optional bf16 addend; zero for entries of the last block at rows or
 // columns >= last_valid.

@@ -29,10 +29,13 @@ class PoetxLinear:
     perm_out / perm_in (both or neither): block-mixing index maps of R and P;
     W0 is folded with them once here (poetx_fold_weight) and the calls then
     gather and scatter the activations' columns.
+    int8=True stores the frozen weight as INT8 codes with per-row scales
+    (poetx_quantize_weight, after any folding); the act-type copy is dropped.
     """
 
     def __init__(self, W0: torch.Tensor, b_in: int, b_out: int, act: str, device="cuda",
-                 recompute_z: bool = False, map: str = "cayley", perm_out=None, perm_in=None):
+                 recompute_z: bool = False, map: str = "cayley", perm_out=None, perm_in=None,
+                 int8: bool = False):
         if map not in ("cayley", "cnp"):
             raise ValueError(f"unknown orthogonal map {map!r}")
         self.torch_dtype, self.act = _DT[act]
@@ -53,6 +56,12 @@ class PoetxLinear:
             P.poetx_fold_weight(self.W0, self.d_out, self.d_in, self.perm_out, self.perm_in,
                                 self.act, folded)
             self.W0 = folded
+        self.w_scale = None
+        if int8:
+            q = torch.empty(self.d_out, self.d_in, device=self.device, dtype=torch.int8)
+            self.w_scale = torch.empty(self.d_out, device=self.device, dtype=torch.float32)
+            P.poetx_quantize_weight(self.W0, self.d_out, self.d_in, self.act, q, self.w_scale)
+            self.W0 = q
         self.b_in, self.b_out = b_in, b_out
         self.nb_in = P.poetx_num_blocks(self.d_in, b_in)
         self.nb_out = P.poetx_num_blocks(self.d_out, b_out)
@@ -90,7 +99,7 @@ class PoetxLinear:
 
     def desc(self, tokens: int, events=None):
         return P.make_desc(tokens, self.d_in, self.d_out, self.b_in, self.b_out, self.act, events,
-                           self.flags, self.perm_in, self.perm_out)
+                           self.flags, self.perm_in, self.perm_out, self.w_scale)
 
     def _ws(self, cache, size_fn, tokens):
         if tokens not in cache:

@@ -27,14 +27,14 @@ POETX_ERR_ALIAS = 7
 POETX_F32 = 0
 POETX_BF16 = 1
 
-POETX_ABI_VERSION = 4
+POETX_ABI_VERSION = 5
 POETX_RECOMPUTE_Z = 1
 POETX_CAYLEY_NEUMANN = 2
 
 EXPORTS = (
     "poetx_abi_version", "poetx_status_string", "poetx_num_blocks", "poetx_theta_count",
     "poetx_build_workspace_size", "poetx_build_orthogonal", "poetx_build_cnp_workspace_size",
-    "poetx_build_cnp", "poetx_fold_weight", "poetx_fwd_workspace_size",
+    "poetx_build_cnp", "poetx_fold_weight", "poetx_quantize_weight", "poetx_fwd_workspace_size",
     "poetx_bwd_workspace_size", "poetx_linear_fwd", "poetx_linear_bwd",
     "poetx_event_create", "poetx_event_destroy", "poetx_event_record",
     "poetx_event_synchronize", "poetx_event_elapsed_ms",
@@ -61,6 +61,7 @@ class LinearDesc(ctypes.Structure):
         ("events", ctypes.POINTER(ctypes.c_void_p)),
         ("perm_in", ctypes.c_void_p),
         ("perm_out", ctypes.c_void_p),
+        ("w_scale", ctypes.c_void_p),
     ]
 
 
@@ -82,6 +83,7 @@ def _load() -> ctypes.CDLL:
         "poetx_build_cnp_workspace_size": (sz, [i64, i32]),
         "poetx_build_cnp": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, i32, vp, sz, vp]),
         "poetx_fold_weight": (ctypes.c_int, [vp, i64, i64, vp, vp, i32, vp, vp]),
+        "poetx_quantize_weight": (ctypes.c_int, [vp, i64, i64, i32, vp, vp, vp]),
         "poetx_fwd_workspace_size": (sz, [dp]),
         "poetx_bwd_workspace_size": (sz, [dp]),
         "poetx_linear_fwd": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -155,9 +157,9 @@ def poetx_build_cnp_workspace_size(d: int, b: int) -> int:
 
 
 def make_desc(tokens, d_in, d_out, b_in, b_out, act, events=None, flags=0, perm_in=None,
-              perm_out=None) -> LinearDesc:
+              perm_out=None, w_scale=None) -> LinearDesc:
     desc = LinearDesc(tokens, d_in, d_out, b_in, b_out, act, 0, flags, 0, None,
-                      _ptr(perm_in), _ptr(perm_out))
+                      _ptr(perm_in), _ptr(perm_out), _ptr(w_scale))
     if events:
         arr = (ctypes.c_void_p * len(events))(*events)
         desc.n_events = len(events)
@@ -196,6 +198,14 @@ def poetx_fold_weight(W0, d_out, d_in, perm_out, perm_in, act, W0_folded, stream
     if raw:
         return st
     _check(st, "poetx_fold_weight")
+
+
+def poetx_quantize_weight(W0, d_out, d_in, act, q, scale, stream=None, raw=False):
+    st = _lib.poetx_quantize_weight(_ptr(W0), d_out, d_in, act, _ptr(q), _ptr(scale),
+                                    _stream(stream))
+    if raw:
+        return st
+    _check(st, "poetx_quantize_weight")
 
 
 def poetx_linear_fwd(desc, x, W0, R_act, P_act, y, z_save, ws, stream=None, raw=False):

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 4
+    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 5
     for s in range(8):
         assert P.status_string(s) and P.status_string(s) != "unknown status"
     assert P.status_string(99) == "unknown status"
@@ -98,7 +98,7 @@ def desc(**over):
     k.update(over)
     return P.make_desc(k["tokens"], k["d_in"], k["d_out"], k["b_in"], k["b_out"], k["act"],
                        flags=k.get("flags", 0), perm_in=k.get("perm_in"),
-                       perm_out=k.get("perm_out"))
+                       perm_out=k.get("perm_out"), w_scale=k.get("w_scale"))
 
 
 @pytest.mark.parametrize("call", [_fwd, _bwd])
@@ -352,3 +352,47 @@ def test_fold_weight_errors():
     assert call(po=ALIGNED * 2 + 2) == P.POETX_ERR_ALIGN
     assert call(out=ALIGNED) == P.POETX_ERR_ALIAS            # in place
     assert call(out=ALIGNED * 3) == P.POETX_ERR_ALIAS        # on top of perm_in
+
+
+# -- INT8 frozen weight: descriptor w_scale and poetx_quantize_weight ---------
+
+def test_int8_weight_descriptor_checks():
+    for call in (_fwd, _bwd):
+        assert call(desc(w_scale=ALIGNED * 310 + 2)) == P.POETX_ERR_ALIGN
+        d = desc(w_scale=ALIGNED * 310, act=P.POETX_F32, d_in=60, b_in=12, b_out=4)
+        assert call(d) == P.POETX_ERR_ALIGN                      # d_in not a multiple of 8
+        d = desc(w_scale=ALIGNED * 310)
+        need = (P.poetx_fwd_workspace_size if call is _fwd else P.poetx_bwd_workspace_size)(d)
+        assert call(d, ws_bytes=need - 1) == P.POETX_ERR_WORKSPACE
+    assert _fwd(desc(w_scale=ALIGNED * 64)) == P.POETX_ERR_ALIAS  # scales on top of y
+
+
+def test_int8_workspace_holds_codes_and_scaled_blocks():
+    N, n, m, b, es = 100, 512, 768, 128, 2
+    base = desc(tokens=N, d_in=n, d_out=m, b_in=b, b_out=b)
+    q8 = desc(tokens=N, d_in=n, d_out=m, b_in=b, b_out=b, w_scale=ALIGNED * 310)
+    extra = m * n * es + (m // b) * b * b * es
+    assert P.poetx_fwd_workspace_size(q8) - P.poetx_fwd_workspace_size(base) >= extra
+    assert P.poetx_bwd_workspace_size(q8) - P.poetx_bwd_workspace_size(base) >= extra
+
+
+def test_quantize_weight_errors():
+    ok = dict(W0=ALIGNED, d_out=64, d_in=32, act=P.POETX_BF16, q=ALIGNED * 2, sc=ALIGNED * 3)
+
+    def call(**over):
+        a = dict(ok)
+        a.update(over)
+        return P._lib.poetx_quantize_weight(a["W0"], a["d_out"], a["d_in"], a["act"], a["q"],
+                                            a["sc"], None)
+
+    assert call(act=5) == P.POETX_ERR_DTYPE
+    assert call(d_out=0) == P.POETX_ERR_SHAPE
+    assert call(d_in=0) == P.POETX_ERR_SHAPE
+    assert call(W0=None) == P.POETX_ERR_NULL
+    assert call(q=None) == P.POETX_ERR_NULL
+    assert call(sc=None) == P.POETX_ERR_NULL
+    assert call(d_in=36, act=P.POETX_F32) == P.POETX_ERR_ALIGN
+    assert call(q=ALIGNED * 2 + 8) == P.POETX_ERR_ALIGN
+    assert call(sc=ALIGNED * 3 + 2) == P.POETX_ERR_ALIGN
+    assert call(q=ALIGNED) == P.POETX_ERR_ALIAS                 # codes on top of W0
+    assert call(sc=ALIGNED * 2 + 64) == P.POETX_ERR_ALIAS       # scales inside the codes

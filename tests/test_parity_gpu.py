@@ -473,3 +473,89 @@ def test_perm_full_size_mlp_up_8b():
     _sampled_check(L, lay, out, perms=(po, pi))
     del lay, out
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------- INT8 frozen weight (POET-XQ)
+@pytest.mark.parametrize("dt,d_out,d_in", [("bf16", 200, 512), ("f32", 64, 136), ("bf16", 14336, 4096)])
+def test_quantize_weight_bit_exact(dt, d_out, d_in):
+    """Codes and scales equal the oracle's (decided in float32 on both sides),
+    including a zero row and rows with exact ties."""
+    U.log(f"[quantize] {dt} {d_out}x{d_in}")
+    rng = np.random.default_rng(d_out + d_in)
+    W = rng.standard_normal((d_out, d_in)) * rng.uniform(0.01, 2.0, (d_out, 1))
+    W[1] = 0.0
+    u = 2.0 ** -7
+    W[2] = u * np.resize(np.array([2.5, 3.5, -2.5, -0.5, 127.0, 1.5]), d_in)
+    W = round_to_dtype(W, dt)
+    act = P.POETX_BF16 if dt == "bf16" else P.POETX_F32
+    q = torch.empty(d_out, d_in, device="cuda", dtype=torch.int8)
+    sc = torch.empty(d_out, device="cuda", dtype=torch.float32)
+    P.poetx_quantize_weight(U.dev(W, dt), d_out, d_in, act, q, sc)
+    torch.cuda.synchronize()
+    q_ref, s_ref = O.quantize_rows(W)
+    assert np.array_equal(sc.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def _int8_reference_inputs(L):
+    """The layer inputs with W0 replaced by diag(s) q of the oracle's codes."""
+    import dataclasses
+    q, s = O.quantize_rows(L.W0)
+    return dataclasses.replace(L, W0=O.dequantize_rows(q, s))
+
+
+INT8_CASES = [
+    # name, d_in, d_out, b, tokens, dtype, sigma, map, permute, recompute
+    ("q8_f32_tiles", 192, 320, 32, 200, "f32", 0.05, "cayley", False, False),
+    ("q8_bf16_b128", 512, 768, 128, 1000, "bf16", 0.02, "cayley", False, False),
+    ("q8_bf16_padded_cnp", 320, 200, 128, 257, "bf16", 0.02, "cnp", False, False),
+    ("q8_bf16_b256_perm_mem", 512, 1024, 256, 300, "bf16", 0.01, "cayley", True, True),
+]
+
+
+@pytest.mark.parametrize("case", INT8_CASES, ids=lambda c: c[0])
+def test_int8_layer_small_full_compare(case):
+    name, n, m, b, N, dt, sigma, map_, permute, mem = case
+    spec = LayerSpec(name, n, m, b, N, dt, sigma, seed=len(name) + 300)
+    U.log(f"[int8 layer] {name}: d_in={n} d_out={m} b={b} tokens={N} {dt} {map_} "
+          f"perm={permute} recompute={mem}")
+    L = make_layer(spec)
+    po, pi = make_permutations(spec) if permute else (None, None)
+    Lq = _int8_reference_inputs(L)
+    ora = O.LayerOracle(Lq.W0, L.theta_R, L.theta_P, b, b, map=map_, perm_out=po, perm_in=pi)
+    y_ref = ora.forward(L.x)
+    gx_ref, gR_ref, gP_ref = ora.backward(L.g_y, L.x)
+    from orthogonal_equivalence_amd.layer import PoetxLinear
+    lay = PoetxLinear(U.dev(L.W0, dt), b, b, dt, map=map_, perm_out=po, perm_in=pi, int8=True,
+                      recompute_z=mem)
+    assert lay.W0.dtype == torch.int8
+    lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
+    x, g_y = U.dev(L.x, dt), U.dev(L.g_y, dt)
+    lay.build()
+    y, z = lay.forward(x)
+    g_x, gR, gP = lay.backward(g_y, x, z)
+    torch.cuda.synchronize()
+    U.check("y", U.host(y), y_ref, dt)
+    U.check("g_x", U.host(g_x), gx_ref, dt)
+    U.check("g_theta_R", U.host(gR), gR_ref, dt)
+    U.check("g_theta_P", U.host(gP), gP_ref, dt)
+
+
+def test_int8_full_size_mlp_up_8b():
+    """The 8B MLP up-projection with an INT8 weight: sampled oracle checks
+    against the dequantised weight."""
+    spec = CONFIGS["mlp_up_8b"][0]
+    U.log(f"[int8 full] {spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
+    L = make_layer(spec)
+    from orthogonal_equivalence_amd.layer import PoetxLinear
+    lay = PoetxLinear(U.dev(L.W0, spec.dtype), spec.b, spec.b, spec.dtype, int8=True)
+    lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
+    x, g_y = U.dev(L.x, spec.dtype), U.dev(L.g_y, spec.dtype)
+    lay.build()
+    y, z = lay.forward(x)
+    g_x, gR, gP = lay.backward(g_y, x, z)
+    torch.cuda.synchronize()
+    out = dict(y=y, z=None, g_x=g_x, g_theta_R=gR, g_theta_P=gP)
+    _sampled_check(_int8_reference_inputs(L), lay, out)
+    del lay, out, y, z, g_x
+    torch.cuda.empty_cache()
