@@ -32,6 +32,29 @@ namespace {
 
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
 
+// (batch, tile) of this workgroup for a grid of (tiles, batch, splits).
+// Workgroups are dispatched to the 8 XCDs round-robin by linear index, so
+// the linear index is remapped to give each XCD a contiguous run of the
+// batch-major tile order: all tiles of a batch entry (a b x b block) then
+// run on one XCD and share its L2, instead of every XCD streaming every
+// block's operands. Inside a batch entry, tiles go in groups of 8 tile rows.
+__device__ __forceinline__ void batched_tile(int num_mt, int num_nt, int& bt, int& mt, int& nt) {
+  const int T = num_mt * num_nt;  // == gridDim.x
+  const int nwg = (int)(gridDim.x * gridDim.y);
+  int w = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  if ((nwg & 7) == 0) w = (w & 7) * (nwg >> 3) + (w >> 3);
+  bt = w / T;
+  const int t = w - bt * T;
+  constexpr int GROUP_M = 8;
+  const int per_group = GROUP_M * num_nt;
+  const int group = t / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(num_mt - first_m, GROUP_M);
+  const int in_group = t - group * per_group;
+  mt = first_m + in_group % gsize;
+  nt = in_group / gsize;
+}
+
 // Transpose of a VEC x VEC block held as VEC 16-byte rows: out[c] holds
 // element c of every input row, in row order.
 template <typename T> struct Transpose;
@@ -234,15 +257,14 @@ gemm_kernel(const GemmParams p) {
   const int wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
 
-  const int bt = blockIdx.y;
+  const int num_mt = (p.M + BM - 1) / BM;
+  const int num_nt = (p.N + BN - 1) / BN;
+  int bt, mt, nt;
+  batched_tile(num_mt, num_nt, bt, mt, nt);
   const bool last = (bt == p.batch - 1);
   const int Mx = last ? p.M_last : p.M;
   const int Nx = last ? p.N_last : p.N;
   const int Kx = last ? p.K_last : p.K;
-  const int num_mt = (p.M + BM - 1) / BM;
-  const int num_nt = (p.N + BN - 1) / BN;
-  int mt, nt;
-  xcd_grouped_tile(num_mt, num_nt, mt, nt);
   const int m0 = mt * BM;
   const int n0 = nt * BN;
   if (m0 >= Mx || n0 >= Nx) return;  // whole workgroup: tile outside a ragged last batch
@@ -400,6 +422,9 @@ gemm_kernel(const GemmParams p) {
 struct Big { static constexpr int BM = 256, BN = 256, BK = 64, WM = 2, WN = 2, MI = 32; };
 struct SmallBf16 { static constexpr int BM = 128, BN = 128, BK = 64, WM = 2, WN = 2, MI = 16; };
 struct SmallF32 { static constexpr int BM = 64, BN = 64, BK = 32, WM = 2, WN = 2, MI = 16; };
+// float32 products with M >= 128: each wave 64 x 32, eight MFMAs per six
+// fragment reads per k step (the 64 x 64 tile does four per four)
+struct MidF32 { static constexpr int BM = 128, BN = 64, BK = 32, WM = 2, WN = 2, MI = 16; };
 
 template <typename TIn, typename TOut, bool AK, bool BK_, typename C>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t stream) {
@@ -433,7 +458,7 @@ int gemm_k_tile(DType in) { return in == DType::BF16 ? 64 : 32; }
 
 int gemm_tile_m(DType in, int M, int N) {
   if (in == DType::BF16) return (M >= 256 && N >= 256) ? 256 : 128;
-  return 64;
+  return M >= 128 ? 128 : 64;
 }
 
 hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor, const GemmParams& p,
@@ -447,7 +472,9 @@ hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor, const 
     return big ? launch_layout<bf16_t, float, Big>(a_kmajor, b_kmajor, p, stream)
                : launch_layout<bf16_t, float, SmallBf16>(a_kmajor, b_kmajor, p, stream);
   }
-  if (out == DType::F32) return launch_layout<float, float, SmallF32>(a_kmajor, b_kmajor, p, stream);
+  if (out == DType::F32)
+    return p.M >= 128 ? launch_layout<float, float, MidF32>(a_kmajor, b_kmajor, p, stream)
+                      : launch_layout<float, float, SmallF32>(a_kmajor, b_kmajor, p, stream);
   return hipErrorInvalidValue;
 }
 
