@@ -184,8 +184,9 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the token-parallel design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path (the layer would "
+              "shard over tokens, with one all-reduce of the packed generator gradients)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

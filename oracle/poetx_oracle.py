@@ -30,7 +30,7 @@ on gist.science, "Technische Zusammenfassung"):
           has to be kept, the frozen weight may be a quantised (e.g. INT8)
           model.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * the orthogonal map is the exact Cayley map R = (I + Q)(I - Q)^-1 (the
     pages name a truncated-series approximation of it without printing it);
     the sign convention is the one whose series expansion of (I - Q)^-1 has
