@@ -415,26 +415,51 @@ split_reduce_kernel(const float* __restrict__ part, int nsplit, int nblocks, int
   for (int t = 0; t < 4; ++t) store_as<TOut>(G + off + t, e[t]);
 }
 
-// grid (ceil(b*b / kNT), nblocks)
-// g_theta(i, j) = sign ((M + c S)[i][j] - (M + c S)[j][i]), S optional (bf16)
+// g_theta(i, j) = sign ((M + c S)[i][j] - (M + c S)[j][i]), S optional (bf16).
+// grid (nt (nt + 1) / 2 tile pairs, nblocks), nt = ceil(b / 32): the workgroup
+// for the upper tile (TI, TJ), TI <= TJ, reads it and its mirror (TJ, TI)
+// row by row (coalesced) into LDS and writes the packed entries of (TI, TJ),
+// which are contiguous along j for each row i.
 __global__ void __launch_bounds__(kNT)
 pack_skew_grad_kernel(const float* __restrict__ M, const bf16_t* __restrict__ S, float c, int nblocks,
                       int b, int last_valid, float sign, float* __restrict__ g) {
-  const int ij = blockIdx.x * kNT + threadIdx.x;
-  if (ij >= b * b) return;
-  const int i = ij / b, j = ij - (ij / b) * b;
-  if (i >= j) return;
+  __shared__ float up[32][33], lo[32][33];
+  const int nt = (b + 31) / 32;
+  int p = blockIdx.x, TI = 0;
+  while (p >= nt - TI) {  // tile pair p -> (TI, TJ), row by row of the upper triangle
+    p -= nt - TI;
+    ++TI;
+  }
+  const int TJ = TI + p;
   const int blk = blockIdx.y;
   const int r = (blk == nblocks - 1) ? last_valid : b;
   const int64_t base = (int64_t)blk * b * b;
-  const int64_t a = base + (int64_t)i * b + j, t = base + (int64_t)j * b + i;
-  float v = 0.0f;
-  if (j < r) {
-    v = M[a] - M[t];
-    if (S) v += c * (bf16_to_f32(S[a]) - bf16_to_f32(S[t]));
-    v *= sign;
+  const int tx = threadIdx.x & 31, ty0 = threadIdx.x >> 5;
+  for (int ty = ty0; ty < 32; ty += 8) {
+    const int i = TI * 32 + ty, j = TJ * 32 + tx;      // (TI, TJ)
+    const int i2 = TJ * 32 + ty, j2 = TI * 32 + tx;    // (TJ, TI)
+    float u = 0.0f, l = 0.0f;
+    if (i < b && j < b) {
+      const int64_t a = base + (int64_t)i * b + j;
+      u = M[a];
+      if (S) u += c * bf16_to_f32(S[a]);
+    }
+    if (i2 < b && j2 < b) {
+      const int64_t a = base + (int64_t)i2 * b + j2;
+      l = M[a];
+      if (S) l += c * bf16_to_f32(S[a]);
+    }
+    up[ty][tx] = u;
+    lo[ty][tx] = l;
   }
-  g[(int64_t)blk * (b * (b - 1) / 2) + packed_index(b, i, j)] = v;
+  __syncthreads();
+  float* gb = g + (int64_t)blk * (b * (b - 1) / 2);
+  for (int ty = ty0; ty < 32; ty += 8) {
+    const int i = TI * 32 + ty, j = TJ * 32 + tx;
+    if (i >= j || j >= b) continue;
+    // (M + c S)[j][i] = lo[j - 32 TJ][i - 32 TI]
+    gb[packed_index(b, i, j)] = (j < r) ? sign * (up[ty][tx] - lo[tx][ty]) : 0.0f;
+  }
 }
 
 }  // namespace
@@ -499,9 +524,10 @@ hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, i
 
 hipError_t launch_pack_skew_grad(const float* M, const void* S, float c, int64_t nblocks, int b,
                                  int last_valid, float sign, float* g_theta, hipStream_t stream) {
-  hipLaunchKernelGGL(pack_skew_grad_kernel, dim3((b * b + kNT - 1) / kNT, (int)nblocks), dim3(kNT),
-                     0, stream, M, static_cast<const bf16_t*>(S), c, (int)nblocks, b, last_valid,
-                     sign, g_theta);
+  const int nt = (b + 31) / 32;
+  hipLaunchKernelGGL(pack_skew_grad_kernel, dim3(nt * (nt + 1) / 2, (int)nblocks), dim3(kNT), 0,
+                     stream, M, static_cast<const bf16_t*>(S), c, (int)nblocks, b, last_valid, sign,
+                     g_theta);
   return hipGetLastError();
 }
 
