@@ -120,23 +120,27 @@ __device__ __forceinline__ void inv4(float m[4][4]) {
 // k) and base = a (0 in row or column block k): the row panel becomes
 // D^-1 A[k][j], the column panel -A[i][k] D^-1, the pivot block D^-1 and
 // every other piece A[i][j] - A[i][k] D^-1 A[k][j].
-// buf: 1024 floats of LDS.
-__device__ __forceinline__ void gj_invert_regs(float a[4][4], int pw, float* buf) {
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+// buf: 1024 floats of LDS. In a workgroup of more than 256 threads, the
+// threads with tid < 256 pass active = true and hold the pieces; every thread
+// of the workgroup must call it (it contains workgroup barriers).
+__device__ __forceinline__ void gj_invert_regs(float a[4][4], int pw, float* buf,
+                                               int tid = (int)threadIdx.x, bool active = true) {
+  const int ty = (tid >> 4) & 15, tx = tid & 15;
   for (int k = 0; 4 * k < pw; ++k) {
     float* rb = buf + (k & 1) * 512;  // row-block pieces, by tx
     float* cb = rb + 256;             // column-block pieces, by ty
-    if (ty == k) {
+    if (active && ty == k) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
         *reinterpret_cast<float4*>(rb + 16 * tx + 4 * ii) = make_float4(a[ii][0], a[ii][1], a[ii][2], a[ii][3]);
     }
-    if (tx == k) {
+    if (active && tx == k) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
         *reinterpret_cast<float4*>(cb + 16 * ty + 4 * ii) = make_float4(a[ii][0], a[ii][1], a[ii][2], a[ii][3]);
     }
     __syncthreads();
+    if (!active) continue;
     float d[4][4], r[4][4], c[4][4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -378,6 +382,271 @@ panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
       }
 }
 
+// ---- whole block per workgroup: b = 64 NT, NT = 2 or 4 ----
+// The block stays on one CU from the generators to R. Each wave owns TPW of
+// the NT x NT 64 x 64 tiles in registers, in the layout of the fp32 MFMA
+// accumulators (tile element (16 mi + 4 (lane / 16) + e, 16 ni + lane % 16)
+// is acc[mi][ni][e]); the blocked Gauss-Jordan elimination runs panel by
+// panel with the pivot block inverted by the first 256 threads in 4 x 4
+// register pieces (gj_invert_regs) and every 64 x 64 x 64 product on MFMA:
+//   pivot      D = A[p][p]          -> D^-1
+//   row        A[p][J]              -> W_J = D^-1 A[p][J]
+//   column     A[I][p] (= C_I)      -> -C_I D^-1
+//   the rest   A[I][J]              -> A[I][J] - C_I W_J
+// LDS holds D^-1 in both operand layouts, the row panel (B layout) and the
+// negated column panel (A layout).
+
+// acc[mi][ni] += A B for one wave's full 64 x 64 tile, K = 64, operands in
+// the permuted LDS layouts of a_off / b_off.
+__device__ __forceinline__ void wave_mma64(const float* sA, const float* sB, floatx4 acc[4][4],
+                                           int lane) {
+  const int q = 4 * (lane >> 4);
+#pragma unroll
+  for (int u = 0; u < kPW / 16; ++u) {
+    float4 av[4], bv[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      av[mi] = *reinterpret_cast<const float4*>(sA + (16 * mi + (lane & 15)) * kLdP + 16 * u + q);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      bv[ni] = *reinterpret_cast<const float4*>(sB + (16 * ni + (lane & 15)) * kLdP + 16 * u + q);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const float a = j == 0 ? av[mi].x : j == 1 ? av[mi].y : j == 2 ? av[mi].z : av[mi].w;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const float bb = j == 0 ? bv[ni].x : j == 1 ? bv[ni].y : j == 2 ? bv[ni].z : bv[ni].w;
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc[mi][ni], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int tile_row(int mi, int e, int lane) { return 16 * mi + 4 * (lane >> 4) + e; }
+__device__ __forceinline__ int tile_col(int ni, int lane) { return 16 * ni + (lane & 15); }
+
+template <int NT> struct BlockShape {
+  static constexpr int B = 64 * NT;
+  static constexpr int WAVES = NT * NT / 2 > 4 ? NT * NT / 2 : 4;
+  static constexpr int TPW = NT * NT / WAVES;  // tiles per wave
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int TILE = kPW * kLdP;      // floats of one 64 x 64 operand tile
+  // D^-1 twice, the row and column panels, the pivot-inversion buffer
+  static constexpr int LDS = (2 + 2 * (NT - 1)) * TILE + 1024;
+  static_assert(WAVES * TILE <= LDS, "per-wave staging tiles must fit");
+};
+
+// Tile (I, J) held in slot s of a wave. Waves go to the four SIMDs round
+// robin; for NT = 4 the SIMD of tile (I, J) is (I + J) mod 4, so every SIMD
+// owns one tile of each tile row and column and a panel's trailing update
+// (the tiles outside row and column p) puts at most three tiles on a SIMD.
+template <int NT>
+__device__ __forceinline__ void tile_of(int wave, int s, int& I, int& J) {
+  if constexpr (NT == 4) {
+    I = 2 * (wave >> 2) + s;
+    J = ((wave & 3) - I) & 3;
+  } else {
+    const int q = wave * BlockShape<NT>::TPW + s;
+    I = q / NT;
+    J = q % NT;
+  }
+}
+
+// grid (nblocks); R (float32) to out and, when act is given, its bf16 copy.
+template <int NT>
+__global__ void __launch_bounds__(BlockShape<NT>::THREADS)
+cayley_block_kernel(const float* __restrict__ theta, int nblocks, int last_valid,
+                    float* __restrict__ out, bf16_t* __restrict__ act) {
+  typedef BlockShape<NT> S;
+  constexpr int B = S::B, TPW = S::TPW, TILE = S::TILE;
+  __shared__ __attribute__((aligned(16))) float lds[S::LDS];
+  float* const sDa = lds;                    // D^-1, A-operand layout (and D, row-major)
+  float* const sDb = lds + TILE;             // D^-1, B-operand layout
+  float* const sW = lds + 2 * TILE;          // row panel, B layout, NT - 1 tiles
+  float* const sC = sW + (NT - 1) * TILE;    // negated column panel, A layout
+  float* const gjbuf = sC + (NT - 1) * TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* const stage = lds + wave * TILE;    // this wave's 64 x 68 staging tile (start, end)
+  const int blk = blockIdx.x;
+  const int r = (blk == nblocks - 1) ? last_valid : B;
+  const float* th = theta + (int64_t)blk * (B * (B - 1) / 2);
+
+  // A = I - Q from the packed generators (those of rows / columns >= r read
+  // as 0). Every tile stages the upper-triangle tile of its position,
+  // (min(I, J), max(I, J)), one row per load instruction: lane l reads
+  // column l, so a row is 64 consecutive generators (its packed index is
+  // rowbase(i) + j with rowbase uniform across the wave). The tile then takes
+  // -theta(i, j) above the diagonal and +theta(j, i) (the staged transpose)
+  // below it: (I - Q)[i][j] = theta(j, i) for i > j.
+  floatx4 t[TPW][4][4];
+#pragma unroll
+  for (int s = 0; s < TPW; ++s) {
+    int I, J;
+    tile_of<NT>(wave, s, I, J);
+    const int R0 = 64 * (I < J ? I : J), C0 = 64 * (I < J ? J : I);
+    const int j = C0 + lane;
+    float g[64];  // all 64 row loads in flight before the first LDS store
+#pragma unroll
+    for (int row = 0; row < 64; ++row) {
+      const int i = R0 + row;
+      const int rowbase = i * (2 * B - i - 1) / 2 - i - 1;
+      g[row] = (i < j && j < r) ? th[rowbase + j] : 0.0f;
+    }
+#pragma unroll
+    for (int row = 0; row < 64; ++row) stage[row * kLdP + lane] = g[row];
+    const bool diag = I == J, lower = I > J;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = tile_row(mi, e, lane), cc = tile_col(ni, lane);
+          float v;
+          if (diag) v = rr == cc ? 1.0f : rr < cc ? -stage[rr * kLdP + cc] : stage[cc * kLdP + rr];
+          else if (lower) v = stage[cc * kLdP + rr];
+          else v = -stage[rr * kLdP + cc];
+          t[s][mi][ni][e] = v;
+        }
+  }
+  __syncthreads();  // the staging tiles overlap the panel buffers
+
+  for (int p = 0; p < NT; ++p) {
+    // publish the pivot block (row-major), the row panel (B layout) and the
+    // negated column panel (A layout)
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) {
+      int I, J;
+      tile_of<NT>(wave, s, I, J);
+      if (I != p && J != p) continue;
+      float* dst = (I == p && J == p) ? sDa
+                 : (I == p) ? sW + (J < p ? J : J - 1) * TILE
+                            : sC + (I < p ? I : I - 1) * TILE;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rr = tile_row(mi, e, lane), cc = tile_col(ni, lane);
+            const float v = t[s][mi][ni][e];
+            if (I == p && J == p) dst[rr * kLdP + cc] = v;
+            else if (I == p) dst[b_off(rr, cc)] = v;
+            else dst[a_off(rr, cc)] = -v;
+          }
+    }
+    __syncthreads();
+
+    // D^-1 by the first 256 threads, written in both operand layouts
+    {
+      const bool active = tid < 256;
+      const int ty = (tid >> 4) & 15, tx = tid & 15;
+      float a[4][4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) a[ii][jj] = active ? sDa[(4 * ty + ii) * kLdP + 4 * tx + jj] : 0.0f;
+      gj_invert_regs(a, kPW, gjbuf, tid, active);
+      if (active) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            sDa[a_off(4 * ty + ii, 4 * tx + jj)] = a[ii][jj];
+            sDb[b_off(4 * ty + ii, 4 * tx + jj)] = a[ii][jj];
+          }
+      }
+    }
+    __syncthreads();
+
+    // pivot, row and column panels
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) {
+      int I, J;
+      tile_of<NT>(wave, s, I, J);
+      if (I != p && J != p) continue;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) t[s][mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (I == p && J == p) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              t[s][mi][ni][e] = sDa[a_off(tile_row(mi, e, lane), tile_col(ni, lane))];
+      } else if (I == p) {
+        wave_mma64(sDa, sW + (J < p ? J : J - 1) * TILE, t[s], lane);
+      } else {
+        wave_mma64(sC + (I < p ? I : I - 1) * TILE, sDb, t[s], lane);
+      }
+    }
+    __syncthreads();  // the old row panel is no longer read
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) {
+      int I, J;
+      tile_of<NT>(wave, s, I, J);
+      if (I != p || J == p) continue;
+      float* dst = sW + (J < p ? J : J - 1) * TILE;
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dst[b_off(tile_row(mi, e, lane), tile_col(ni, lane))] = t[s][mi][ni][e];
+    }
+    __syncthreads();
+
+    // trailing update A[I][J] += (-C_I) W_J
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) {
+      int I, J;
+      tile_of<NT>(wave, s, I, J);
+      if (I == p || J == p) continue;
+      wave_mma64(sC + (I < p ? I : I - 1) * TILE, sW + (J < p ? J : J - 1) * TILE, t[s], lane);
+    }
+    __syncthreads();  // panels are rewritten by the next step (and by the staging below)
+  }
+
+  // R = 2 (I - Q)^-1 - I, staged row-major so that rows leave as 16-byte
+  // (float32) and 8-byte (bf16) vectors
+  float* ob = out + (int64_t)blk * B * B;
+  bf16_t* ab = act ? act + (int64_t)blk * B * B : nullptr;
+#pragma unroll
+  for (int s = 0; s < TPW; ++s) {
+    int I, J;
+    tile_of<NT>(wave, s, I, J);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = tile_row(mi, e, lane), cc = tile_col(ni, lane);
+          stage[rr * kLdP + cc] = 2.0f * t[s][mi][ni][e] - (64 * I + rr == 64 * J + cc ? 1.0f : 0.0f);
+        }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int rr = 4 * q + (lane >> 4), c4 = 4 * (lane & 15);
+      const float4 v = *reinterpret_cast<const float4*>(stage + rr * kLdP + c4);
+      const int64_t off = (int64_t)(64 * I + rr) * B + 64 * J + c4;
+      *reinterpret_cast<float4*>(ob + off) = v;
+      if (ab) {
+        union { uint2 u; bf16_t h[4]; } o;
+        o.h[0] = f32_to_bf16(v.x); o.h[1] = f32_to_bf16(v.y);
+        o.h[2] = f32_to_bf16(v.z); o.h[3] = f32_to_bf16(v.w);
+        *reinterpret_cast<uint2*>(ab + off) = o.u;
+      }
+    }
+  }
+}
+
 // grid (ceil(b*b / (4 kNT)), nblocks); b*b is a multiple of 4. col_scale
 // (optional) multiplies column j of block blk by col_scale[blk b + j].
 template <typename TOut>
@@ -479,6 +748,16 @@ size_t cayley_workspace_floats(int64_t nblocks, int b) {
 hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int last_valid,
                                float* blocks_f32, void* blocks_act, DType act, float* ws,
                                hipStream_t stream) {
+  bf16_t* act_bf16 = (act == DType::BF16) ? static_cast<bf16_t*>(blocks_act) : nullptr;
+  if (b == 128 || b == 256) {  // the whole block on one CU
+    if (b == 256)
+      hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nblocks), dim3(BlockShape<4>::THREADS),
+                         0, stream, theta, (int)nblocks, last_valid, blocks_f32, act_bf16);
+    else
+      hipLaunchKernelGGL(cayley_block_kernel<2>, dim3((unsigned)nblocks), dim3(BlockShape<2>::THREADS),
+                         0, stream, theta, (int)nblocks, last_valid, blocks_f32, act_bf16);
+    return hipGetLastError();
+  }
   const int pw = cayley_panel_width(b);
   const int nt = b / pw;
   const int nb = (int)nblocks;

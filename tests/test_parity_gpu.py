@@ -81,17 +81,23 @@ def test_build_matches_oracle(b, nb, sigma):
     assert torch.equal(a, ref)
 
 
-def test_build_padded_last_block():
-    """b does not divide d: the last block is diag(Cayley(Q_r), I)."""
-    b, d = 64, 64 * 2 + 24
-    rng = np.random.default_rng(5)
-    theta = (rng.standard_normal((3, b * (b - 1) // 2)) * 0.05).astype(np.float32).astype(np.float64)
+@pytest.mark.parametrize("b,r", [(64, 24), (128, 77), (256, 24), (256, 193)])
+def test_build_padded_last_block(b, r):
+    """b does not divide d: the last block is diag(Cayley(Q_r), I) (b = 64 on
+    the panel kernels, b = 128 and 256 on the whole-block kernel, with the
+    valid part ending inside a 64-wide tile or at its first column)."""
+    d = b * 2 + r
+    U.log(f"[build padded] b={b} d={d}")
+    rng = np.random.default_rng(5 + b + r)
+    sigma = 0.05 if b == 64 else 0.01
+    theta = (rng.standard_normal((3, b * (b - 1) // 2)) * sigma).astype(np.float32).astype(np.float64)
     R_ref, _ = O.orthogonal_blocks(theta, b, d)
-    f32, _ = _build(theta, d, b)
+    f32, act = _build(theta, d, b)
     R = U.host(f32)
     assert np.max(np.abs(R - R_ref)) <= 2e-5
-    assert np.array_equal(R[-1, 24:, 24:], np.eye(b - 24))
-    assert np.all(R[-1, :24, 24:] == 0) and np.all(R[-1, 24:, :24] == 0)
+    assert np.array_equal(R[-1, r:, r:], np.eye(b - r))
+    assert np.all(R[-1, :r, r:] == 0) and np.all(R[-1, r:, :r] == 0)
+    assert torch.equal(act.float(), f32.to(torch.bfloat16).float())
 
 
 # ------------------------------------------------------ full layer, small
