@@ -254,22 +254,23 @@ hipError_t dense(DType t, const void* A, const void* B, void* C, int64_t M, int6
 }
 
 // Cayley VJP of every block: M = 1/2 (R^T + I) G (R^T + I), packed as
-// g_theta(i, j) = M[i][j] - M[j][i]. Computed as S = R G^T + G^T (= T^T for
-// T = G (R^T + I)) and M^T = 1/2 (S R + S), so only one operand of one
-// product is read transposed; the pack then flips the sign. When a second
-// block set of the same size is given, both run in the same launches.
+// g_theta(i, j) = M[i][j] - M[j][i]. Computed as T = G R^T + G
+// (= G (R^T + I): both operands and the addend read in their stored order)
+// and M = 1/2 (R^T T + T), whose A operand R^T the GEMM reads column-wise
+// (its MN-major loader). When a second block set of the same size is given,
+// both run in the same launches.
 //
 // float32 activations: float32 products throughout. bf16 activations: G and
-// S are rounded to bf16 and both products run on bf16 MFMA with float32
-// accumulation (S R in float32; the 1/2 S term is added in float32 by the
+// T are rounded to bf16 and both products run on bf16 MFMA with float32
+// accumulation (R^T T in float32; the 1/2 T term is added in float32 by the
 // pack), which adds about 2^-8 relative error to a gradient already formed
 // from bf16 activations.
 struct VjpSet {
   const void* G;       // float32 or bf16 (the activation type)
   const float* R;      // float32 blocks
   const void* R_act;   // activation-type blocks
-  void* S;             // same type as G
-  float* M;            // M^T (float32) or 1/2 S R (bf16 path)
+  void* T;             // same type as G
+  float* M;            // M (float32) or 1/2 R^T T (bf16 path)
   float* g_theta;
   int64_t d;
 };
@@ -279,38 +280,36 @@ hipError_t cayley_vjp(DType t, const VjpSet& a, const VjpSet* b2, int b, hipStre
   const int64_t bb = (int64_t)b * b;
   const bool lowp = t == DType::BF16;
   GemmParams g;
-  // S = R G^T + G^T: A = R (K-major), B(n, k) = G[n][k], addend G transposed
-  g.A = lowp ? a.R_act : a.R; g.lda = b; g.sA = bb;
-  g.B = a.G; g.ldb = b; g.sB = bb;
-  g.C = a.S; g.ldc = b; g.sC = bb;
-  g.D = a.G; g.ldd = b; g.sD = bb; g.d_trans = true;
+  // T = G R^T + G: A = G (K-major), B(n, k) = R[n][k] (K-major), addend G
+  g.A = a.G; g.lda = b; g.sA = bb;
+  g.B = lowp ? a.R_act : a.R; g.ldb = b; g.sB = bb;
+  g.C = a.T; g.ldc = b; g.sC = bb;
+  g.D = a.G; g.ldd = b; g.sD = bb;
   g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = b;
   g.batch = (int)(nb1 + nb2);
   g.kchunk = b;
   g.alpha = 1.0f; g.beta = 1.0f;
   if (b2) {
     g.batch_split = (int)nb1;
-    g.A2 = lowp ? b2->R_act : b2->R; g.B2 = b2->G; g.C2 = b2->S; g.D2 = b2->G;
+    g.A2 = b2->G; g.B2 = lowp ? b2->R_act : b2->R; g.C2 = b2->T; g.D2 = b2->G;
   }
   hipError_t e = poetx::launch_gemm(t, t, true, true, g, s);
   if (e != hipSuccess) return e;
-  // M^T = 1/2 (S R + S): A = S (K-major), B(n, k) = R[k][n]; in the bf16 path
-  // the GEMM writes 1/2 S R and the pack adds 1/2 S
-  g.A = a.S; g.B = lowp ? a.R_act : a.R; g.C = a.M; g.d_trans = false;
+  // M = 1/2 (R^T T + T): A(m, k) = R[k][m] (MN-major), B(n, k) = T[k][n]; in
+  // the bf16 path the GEMM writes 1/2 R^T T and the pack adds 1/2 T
+  g.A = lowp ? a.R_act : a.R; g.B = a.T; g.C = a.M;
   g.alpha = 0.5f;
-  g.D = lowp ? nullptr : a.S; g.beta = lowp ? 0.0f : 0.5f;
+  g.D = lowp ? nullptr : a.T; g.beta = lowp ? 0.0f : 0.5f;
   if (b2) {
-    g.A2 = b2->S; g.B2 = lowp ? b2->R_act : b2->R; g.C2 = b2->M; g.D2 = lowp ? nullptr : b2->S;
+    g.A2 = lowp ? b2->R_act : b2->R; g.B2 = b2->T; g.C2 = b2->M; g.D2 = lowp ? nullptr : b2->T;
   }
-  e = poetx::launch_gemm(t, DType::F32, true, false, g, s);
+  e = poetx::launch_gemm(t, DType::F32, false, false, g, s);
   if (e != hipSuccess) return e;
-  const void* add1 = lowp ? a.S : nullptr;
-  e = poetx::launch_pack_skew_grad(a.M, add1, 0.5f, nb1, b, (int)(a.d - (nb1 - 1) * b), -1.0f,
-                                   a.g_theta, s);
-  if (e != hipSuccess || !b2) return e;
-  const void* add2 = lowp ? b2->S : nullptr;
-  return poetx::launch_pack_skew_grad(b2->M, add2, 0.5f, nb2, b, (int)(b2->d - (nb2 - 1) * b),
-                                      -1.0f, b2->g_theta, s);
+  const poetx::PackSet p1{a.M, lowp ? a.T : nullptr, nb1, (int)(a.d - (nb1 - 1) * b), a.g_theta};
+  if (!b2) return poetx::launch_pack_skew_grad(p1, nullptr, 0.5f, b, 1.0f, s);
+  const poetx::PackSet p2{b2->M, lowp ? b2->T : nullptr, nb2, (int)(b2->d - (nb2 - 1) * b),
+                          b2->g_theta};
+  return poetx::launch_pack_skew_grad(p1, &p2, 0.5f, b, 1.0f, s);
 }
 
 // VJP of the truncated Cayley-Neumann series R = I + 2 (Q + Q^2 + Q^3 + Q^4)
@@ -360,12 +359,10 @@ hipError_t cnp_vjp(const CnpVjpSet& a, const CnpVjpSet* b2, int b, hipStream_t s
   if ((e = poetx::launch_sym_sum(a.w3, a.w1, a.w2, nb1, b, s)) != hipSuccess) return e;
   if (b2 && (e = poetx::launch_sym_sum(c.w3, c.w1, c.w2, nb2, b, s)) != hipSuccess) return e;
   if ((e = mm(a.w2, a.Q, a.w1, a.w3, c.w2, c.Q, c.w1, c.w3, -1.0f, 1.0f)) != hipSuccess) return e;
-  if ((e = poetx::launch_pack_skew_grad(a.w1, nullptr, 0.0f, nb1, b, (int)(a.d - (nb1 - 1) * b),
-                                        1.0f, a.g_theta, s)) != hipSuccess)
-    return e;
-  if (!b2) return hipSuccess;
-  return poetx::launch_pack_skew_grad(c.w1, nullptr, 0.0f, nb2, b, (int)(c.d - (nb2 - 1) * b),
-                                      1.0f, c.g_theta, s);
+  const poetx::PackSet p1{a.w1, nullptr, nb1, (int)(a.d - (nb1 - 1) * b), a.g_theta};
+  if (!b2) return poetx::launch_pack_skew_grad(p1, nullptr, 0.0f, b, 1.0f, s);
+  const poetx::PackSet p2{c.w1, nullptr, nb2, (int)(c.d - (nb2 - 1) * b), c.g_theta};
+  return poetx::launch_pack_skew_grad(p1, &p2, 0.0f, b, 1.0f, s);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? POETX_OK : POETX_ERR_HIP; }

@@ -689,9 +689,9 @@ split_reduce_kernel(const float* __restrict__ part, int nsplit, int nblocks, int
 // for the upper tile (TI, TJ), TI <= TJ, reads it and its mirror (TJ, TI)
 // row by row (coalesced) into LDS and writes the packed entries of (TI, TJ),
 // which are contiguous along j for each row i.
+// grid.y covers the blocks of the first set, then those of the second.
 __global__ void __launch_bounds__(kNT)
-pack_skew_grad_kernel(const float* __restrict__ M, const bf16_t* __restrict__ S, float c, int nblocks,
-                      int b, int last_valid, float sign, float* __restrict__ g) {
+pack_skew_grad_kernel(PackSet s1, PackSet s2, float c, int b, float sign) {
   __shared__ float up[32][33], lo[32][33];
   const int nt = (b + 31) / 32;
   int p = blockIdx.x, TI = 0;
@@ -700,8 +700,13 @@ pack_skew_grad_kernel(const float* __restrict__ M, const bf16_t* __restrict__ S,
     ++TI;
   }
   const int TJ = TI + p;
-  const int blk = blockIdx.y;
-  const int r = (blk == nblocks - 1) ? last_valid : b;
+  const bool second = blockIdx.y >= s1.nblocks;
+  const float* __restrict__ M = second ? s2.M : s1.M;
+  const bf16_t* __restrict__ S = static_cast<const bf16_t*>(second ? s2.S : s1.S);
+  float* __restrict__ g = second ? s2.g_theta : s1.g_theta;
+  const int nblocks = (int)(second ? s2.nblocks : s1.nblocks);
+  const int blk = second ? (int)(blockIdx.y - s1.nblocks) : (int)blockIdx.y;
+  const int r = (blk == nblocks - 1) ? (second ? s2.last_valid : s1.last_valid) : b;
   const int64_t base = (int64_t)blk * b * b;
   const int tx = threadIdx.x & 31, ty0 = threadIdx.x >> 5;
   for (int ty = ty0; ty < 32; ty += 8) {
@@ -801,12 +806,14 @@ hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, i
   return hipGetLastError();
 }
 
-hipError_t launch_pack_skew_grad(const float* M, const void* S, float c, int64_t nblocks, int b,
-                                 int last_valid, float sign, float* g_theta, hipStream_t stream) {
+hipError_t launch_pack_skew_grad(const PackSet& a, const PackSet* b2, float c, int b, float sign,
+                                 hipStream_t stream) {
   const int nt = (b + 31) / 32;
-  hipLaunchKernelGGL(pack_skew_grad_kernel, dim3(nt * (nt + 1) / 2, (int)nblocks), dim3(kNT), 0,
-                     stream, M, static_cast<const bf16_t*>(S), c, (int)nblocks, b, last_valid, sign,
-                     g_theta);
+  const PackSet none{nullptr, nullptr, 0, 0, nullptr};
+  const int64_t total = a.nblocks + (b2 ? b2->nblocks : 0);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_skew_grad_kernel, dim3(nt * (nt + 1) / 2, (unsigned)total), dim3(kNT), 0,
+                     stream, a, b2 ? *b2 : none, c, b, sign);
   return hipGetLastError();
 }
 

@@ -128,8 +128,16 @@ hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, i
                                const float* col_scale = nullptr);
 // g_theta[blk][idx(i,j)] = sign ((M + c S)[i][j] - (M + c S)[j][i]) (i < j),
 // S an optional bf16 addend; zero for entries of the last block at rows or
-// columns >= last_valid.
-hipError_t launch_pack_skew_grad(const float* M, const void* S, float c, int64_t nblocks, int b,
-                                 int last_valid, float sign, float* g_theta, hipStream_t stream);
+// columns >= last_valid. A second set of blocks of the same size shares the
+// launch.
+struct PackSet {
+  const float* M;
+  const void* S;
+  int64_t nblocks;
+  int last_valid;
+  float* g_theta;
+};
+hipError_t launch_pack_skew_grad(const PackSet& a, const PackSet* b2, float c, int b, float sign,
+                                 hipStream_t stream);
 
 }  // namespace poetx
