@@ -274,7 +274,7 @@ int poetx_linear_fwd(const poetx_linear_desc* desc, const void* x, const void* W
  *   g_X = g_U blockdiag(P)
  *   Cayley VJP per block: M = 1/2 (R^T + I) G (R^T + I),
  *   g_theta(i, j) = M[i][j] - M[j][i] for i < j
- *   (bf16 mode: G and S = R G^T + G^T are rounded to bf16 for the two VJP
+ *   (bf16 mode: G and T = G R^T + G are rounded to bf16 for the two VJP
  *   products, which accumulate in float32).
  *   With POETX_CAYLEY_NEUMANN, the series' VJP instead:
  *   D = 2 sum_{k=1..4} sum_{i+j=k-1} (Q^T)^i G (Q^T)^j,
