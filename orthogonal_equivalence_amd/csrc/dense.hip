@@ -9,8 +9,10 @@
 // C[M][N] = A[M][K] B(n, k) with B(n, k) = B[n][k] (K-major) or B[k][n]
 // (N-major); bf16 in and out, float32 accumulation.
 //
-// One workgroup (4 waves, 2 x 2, each 128 x 128 as 8 x 8 tiles of
-// v_mfma_f32_16x16x32_bf16) computes a 256 x 256 tile. On random operands the
+// One workgroup (8 waves, 2 x 4, each 128 x 64 as 8 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16, two waves per SIMD) computes a 256 x 256 tile;
+// waves 0-3 issue the operand loads and waves 4-7 write the output, so each
+// wave's vmcnt only counts its own kind of access. On random operands the
 // 16x16x32 shape sustains a markedly higher rate than 32x32x16 under the
 // chip's power limit, so it is the one used here. K tiles of 32 are copied
 // from global memory straight into a 4-slot LDS ring with
