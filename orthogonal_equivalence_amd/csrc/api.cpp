@@ -105,7 +105,7 @@ struct SplitK {
 SplitK choose_split(int64_t nblocks, int b, int64_t d, int64_t tokens, DType in) {
   if (poetx::blockgram_supported(in, d, b)) {
     // streaming gram: one round of about 256 workgroups
-    int64_t s = std::max<int64_t>(1, 256 / nblocks);
+    int64_t s = std::max<int64_t>(1, 256 / (nblocks * poetx::blockgram_wg_per_block(b)));
     s = std::min<int64_t>(s, std::max<int64_t>(1, tokens / 256));
     const int64_t chunk = ceil_div(ceil_div(tokens, s), 64) * 64;
     SplitK r;

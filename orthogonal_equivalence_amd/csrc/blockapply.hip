@@ -1,5 +1,5 @@
 // Streaming block-diagonal apply for bf16 activations: for every block k of
-// b features (b = 128 or 256) and every token t,
+// b features (b = 128, 256 or 512) and every token t,
 //   Y[t, kb + n] = sum_k X[t, kb + k] B(n, k),  B(n, k) = M_k[n][k] (transpose)
 //                                               or      M_k[k][n],
 // i.e. the batch-parallel block products of the POET-X layer (gist.science
@@ -13,7 +13,13 @@
 // (about one workgroup per CU). It loads M_k once (through LDS, using the
 // gfx950 transposing LDS read ds_read_b64_tr_b16 when the fragments need M_k's
 // columns) and keeps it in registers as MFMA B fragments: wave w owns output
-// columns [w b/4, (w+1) b/4). Token tiles of 64 rows are copied from global
+// columns [w b/4, (w+1) b/4). At b = 512 the block (512 KB) does not fit one
+// CU's registers: four workgroups share a block and token range, each holding
+// the 128 output columns of its slab (512 x 128, the same 128 KB as a whole
+// b = 256 block) and streaming 32-token tiles of all 512 input columns; the
+// four are launched 8 workgroup ids apart, so they run on one XCD at about
+// the same time and the input tile they all read comes from HBM about once.
+// Token tiles of 64 rows (b <= 256) are copied from global
 // memory straight into a 4-stage LDS ring (global_load_lds_dwordx4, three
 // tiles in flight) and multiplied on v_mfma_f32_32x32x16_bf16 with the block
 // as the first operand, so the accumulators hold the transposed output tile:
@@ -39,10 +45,8 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kTT = 64;    // tokens per tile
 constexpr int kNT = 256;   // threads
-constexpr int kMaxB = 256;
-constexpr int kStage = kTT * kMaxB;  // bf16 elements per ring slot (sized for b = 256)
+constexpr int kStage = 64 * 256;  // bf16 elements per ring slot (a 64 x 256 or 32 x 512 tile)
 
 // The ring slots are separate arrays so that the compiler can tell which slot
 // an LDS read touches while loads into the other slots are in flight.
@@ -84,24 +88,28 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int B, bool TRANS>
+// B: block size (the K extent); NC: output columns per workgroup (B, or 128
+// at B = 512); TT: tokens per tile.
+template <int B, int NC, int TT, bool TRANS>
 struct BlockApply {
-  static constexpr int CB = B / 128;          // 32-wide column blocks per wave
+  static constexpr int CB = NC / 128;         // 32-wide column blocks per wave
   static constexpr int KS = B / 16;           // MFMA K steps
-  static constexpr int STAGE = kTT * B;       // elements of one tile
+  static constexpr int RB = TT / 32;          // 32-token row blocks per tile
+  static constexpr int STAGE = TT * B;        // elements of one input tile
   static constexpr int LPW = STAGE * 2 / 1024 / 4;  // 1 KB tile loads per wave
-  static constexpr int CPT = STAGE / 8 / kNT; // 16-byte output chunks per thread
+  static constexpr int CPT = TT * NC / 8 / kNT;     // 16-byte output chunks per thread
+  static_assert(STAGE <= kStage && TT % 32 == 0 && NC % 128 == 0 && CPT >= 1, "tile shape");
 
   const bf16_t* X;
   bf16_t* Y;
-  int64_t d, col0;
+  int64_t d, col0, ocol0;  // first input column of the block, first output column
   int t_begin, t_end, ntiles;
   int tid, lane, wave, nw;
   bf16x8_t bfr[CB][KS];
 
   // Issues the LDS-bound loads of token tile `tile` into ring slot `dst`.
   __device__ __forceinline__ void load_tile(int tile, bf16_t* dst) {
-    const int t0 = t_begin + tile * kTT;
+    const int t0 = t_begin + tile * TT;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
       const int Q = wave * LPW + q;            // 1 KB piece of the tile
@@ -127,17 +135,17 @@ struct BlockApply {
     __builtin_amdgcn_s_barrier();  // every wave's part of tile t landed; slot of t-1 free
     if (t + 3 < ntiles) load_tile(t + 3, ring<(S + 3) & 3>());
 
-    floatx16 acc[2][CB];
+    floatx16 acc[RB][CB];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
       for (int j = 0; j < CB; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[r][j][e] = 0.f;
-    bf16x8_t af[2][2];
+    bf16x8_t af[2][RB];
     auto rd = [&](int ks, bf16x8_t* a) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+      for (int r = 0; r < RB; ++r)
         a[r] = *reinterpret_cast<const bf16x8_t*>(st + sw<B>(32 * r + (ln & 31), 16 * ks + 8 * (ln >> 5)));
     };
     rd(0, af[0]);
@@ -145,14 +153,14 @@ struct BlockApply {
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS) rd(ks + 1, af[(ks + 1) & 1]);
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+      for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int j = 0; j < CB; ++j)
           acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j][ks], af[ks & 1][r], acc[r][j], 0, 0, 0);
     }
     __builtin_amdgcn_s_barrier();  // all waves done reading slot S
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         // acc[r][j] holds Y^T: lane l has token 32 r + l % 32 and, for
@@ -167,32 +175,44 @@ struct BlockApply {
           v[1] = (short)f32_to_bf16(acc[r][j][4 * g + 1]);
           v[2] = (short)f32_to_bf16(acc[r][j][4 * g + 2]);
           v[3] = (short)f32_to_bf16(acc[r][j][4 * g + 3]);
-          *reinterpret_cast<short4_t*>(st + sw<B>(m, n)) = v;
+          *reinterpret_cast<short4_t*>(st + sw<NC>(m, n)) = v;
         }
       }
     __syncthreads();  // output tile staged
-    const int t0 = t_begin + t * kTT;
+    const int t0 = t_begin + t * TT;
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int c = td + q * kNT;
-      const int row = c / (B / 8), ch = c % (B / 8);
-      const uint4 v = *reinterpret_cast<const uint4*>(st + sw<B>(row, ch * 8));
-      if (t0 + row < t_end) *reinterpret_cast<uint4*>(Y + (int64_t)(t0 + row) * d + col0 + ch * 8) = v;
+      const int row = c / (NC / 8), ch = c % (NC / 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(st + sw<NC>(row, ch * 8));
+      if (t0 + row < t_end) *reinterpret_cast<uint4*>(Y + (int64_t)(t0 + row) * d + ocol0 + ch * 8) = v;
     }
   }
 };
 
-template <int B, bool TRANS>
+// Workgroup (split, blk, slab) for NSLAB = B / NC slabs per block: ids are
+// unit = split * nb + blk when NSLAB = 1, else 32 g + 8 slab + r for
+// unit 8 g + r (the slabs of one unit 8 ids apart, on one XCD).
+template <int B, int NC, int TT, bool TRANS>
 __global__ void __launch_bounds__(kNT)
 blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
-                  bf16_t* __restrict__ Y, int tokens, int64_t d, int nb, int tok_per_wg) {
-  typedef BlockApply<B, TRANS> K;
+                  bf16_t* __restrict__ Y, int tokens, int64_t d, int nb, int nsplit, int tok_per_wg) {
+  typedef BlockApply<B, NC, TT, TRANS> K;
+  constexpr int NSLAB = B / NC;
   K k;
   k.tid = threadIdx.x;
   k.lane = k.tid & 63;
   k.wave = k.tid >> 6;
-  const int blk = blockIdx.x % nb;
-  const int split = blockIdx.x / nb;
+  int unit, slab = 0;
+  if (NSLAB == 1) {
+    unit = blockIdx.x;
+  } else {
+    unit = (int)(blockIdx.x >> 5) * 8 + (int)(blockIdx.x & 7);
+    slab = (int)(blockIdx.x >> 3) & 3;
+  }
+  if (unit >= nb * nsplit) return;  // padding id of the last group (uniform, before any barrier)
+  const int blk = unit % nb;
+  const int split = unit / nb;
   k.t_begin = split * tok_per_wg;
   k.t_end = min(tokens, k.t_begin + tok_per_wg);
   if (k.t_begin >= k.t_end) return;
@@ -200,18 +220,25 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
   k.Y = Y;
   k.d = d;
   k.col0 = (int64_t)blk * B;
-  k.nw = k.wave * (B / 4);
-  k.ntiles = (k.t_end - k.t_begin + kTT - 1) / kTT;
+  k.ocol0 = k.col0 + slab * NC;
+  k.nw = k.wave * (NC / 4);
+  k.ntiles = (k.t_end - k.t_begin + TT - 1) / TT;
 
-  // ---- M_k -> LDS (rows spread over the ring slots) -> register fragments
+  // ---- this slab of M_k -> LDS (rows spread over the ring slots) -> register
+  // fragments. TRANS needs rows slab NC .. of M (NC rows of B); otherwise the
+  // columns slab NC .. of every row (B rows of NC).
   {
     const bf16_t* Mk = Mb + (int64_t)blk * B * B;
-    constexpr int ROWS_PER_SLOT = kStage / B;
-    for (int c = k.tid; c < B * B / 8; c += kNT) {
-      const int row = c / (B / 8), ch = c % (B / 8);
+    constexpr int SR = TRANS ? NC : B;       // staged rows
+    constexpr int SW = TRANS ? B : NC;       // staged row width
+    constexpr int ROWS_PER_SLOT = kStage / SW;
+    static_assert(SR <= 4 * ROWS_PER_SLOT, "slab fits the ring");
+    const bf16_t* src0 = TRANS ? Mk + (int64_t)slab * NC * B : Mk + slab * NC;
+    for (int c = k.tid; c < SR * SW / 8; c += kNT) {
+      const int row = c / (SW / 8), ch = c % (SW / 8);
       bf16_t* slot = ring_rt(row / ROWS_PER_SLOT);
-      *reinterpret_cast<uint4*>(slot + sw<B>(row % ROWS_PER_SLOT, ch * 8)) =
-          *reinterpret_cast<const uint4*>(Mk + (int64_t)row * B + ch * 8);
+      *reinterpret_cast<uint4*>(slot + sw<SW>(row % ROWS_PER_SLOT, ch * 8)) =
+          *reinterpret_cast<const uint4*>(src0 + (int64_t)row * B + ch * 8);
     }
     __syncthreads();
     const int lane = k.lane;
@@ -223,7 +250,7 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
           const int n = k.nw + 32 * j + (lane & 31);
           const int kk = 16 * ks + 8 * (lane >> 5);
           k.bfr[j][ks] = *reinterpret_cast<const bf16x8_t*>(ring_rt(n / ROWS_PER_SLOT) +
-                                                            sw<B>(n % ROWS_PER_SLOT, kk));
+                                                            sw<SW>(n % ROWS_PER_SLOT, kk));
         } else {      // B(n, k) = M[k][n]: two transposing reads of 4 k each
           const int g = lane >> 4, i = lane & 15;
           const int n = k.nw + 32 * j + 16 * (g & 1) + 4 * (i & 3);
@@ -232,7 +259,7 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
           for (int hh = 0; hh < 2; ++hh) {
             const int kk = 16 * ks + 8 * (g >> 1) + 4 * hh + (i >> 2);
             h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_short4*)(ring_rt(kk / ROWS_PER_SLOT) + sw<B>(kk % ROWS_PER_SLOT, n)));
+                (lds_short4*)(ring_rt(kk / ROWS_PER_SLOT) + sw<SW>(kk % ROWS_PER_SLOT, n)));
           }
           union { short4_t s[2]; bf16x8_t v; } u;
           u.s[0] = h[0];
@@ -259,27 +286,30 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
   if (t < nt) k.template tile<2>(t++);
 }
 
-template <int B, bool TRANS>
+template <int B, int NC, int TT, bool TRANS>
 hipError_t launch_b(const bf16_t* X, const bf16_t* M, bf16_t* Y, int64_t tokens, int64_t d,
                     hipStream_t s) {
+  constexpr int NSLAB = B / NC;
   const int nb = (int)(d / B);
   // one round of at most 256 workgroups (one per CU), token ranges in whole tiles
-  int splits = 256 / nb;
-  const int max_splits = (int)((tokens + kTT - 1) / kTT);
+  int splits = 256 / (nb * NSLAB);
+  const int max_splits = (int)((tokens + TT - 1) / TT);
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int per = (int)((tokens + splits - 1) / splits);
-  per = (per + kTT - 1) / kTT * kTT;
+  per = (per + TT - 1) / TT * TT;
   splits = (int)((tokens + per - 1) / per);
-  hipLaunchKernelGGL((blockapply_kernel<B, TRANS>), dim3(nb * splits), dim3(kNT), 0, s, X, M, Y,
-                     (int)tokens, d, nb, per);
+  const int units = nb * splits;
+  const int grid = NSLAB == 1 ? units : (units + 7) / 8 * 32;
+  hipLaunchKernelGGL((blockapply_kernel<B, NC, TT, TRANS>), dim3(grid), dim3(kNT), 0, s, X, M, Y,
+                     (int)tokens, d, nb, splits, per);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool blockapply_supported(DType t, int64_t d, int b) {
-  return t == DType::BF16 && (b == 128 || b == 256) && d % b == 0;
+  return t == DType::BF16 && (b == 128 || b == 256 || b == 512) && d % b == 0;
 }
 
 hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,
@@ -287,10 +317,12 @@ hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t toke
   const bf16_t* x = static_cast<const bf16_t*>(X);
   const bf16_t* m = static_cast<const bf16_t*>(M);
   bf16_t* y = static_cast<bf16_t*>(Y);
-  if (b == 256) return transpose ? launch_b<256, true>(x, m, y, tokens, d, s)
-                                 : launch_b<256, false>(x, m, y, tokens, d, s);
-  return transpose ? launch_b<128, true>(x, m, y, tokens, d, s)
-                   : launch_b<128, false>(x, m, y, tokens, d, s);
+  if (b == 512) return transpose ? launch_b<512, 128, 32, true>(x, m, y, tokens, d, s)
+                                 : launch_b<512, 128, 32, false>(x, m, y, tokens, d, s);
+  if (b == 256) return transpose ? launch_b<256, 256, 64, true>(x, m, y, tokens, d, s)
+                                 : launch_b<256, 256, 64, false>(x, m, y, tokens, d, s);
+  return transpose ? launch_b<128, 128, 64, true>(x, m, y, tokens, d, s)
+                   : launch_b<128, 128, 64, false>(x, m, y, tokens, d, s);
 }
 
 }  // namespace poetx

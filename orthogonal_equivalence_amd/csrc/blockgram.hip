@@ -1,13 +1,17 @@
 // Streaming token-reduction grams of the POET-X backward: for every block k
-// of b features (b = 128 or 256) and a range of tokens,
+// of b features (b = 128, 256 or 512) and a range of tokens,
 //   part[s][k] = sum_{t in split s} A[t, kb:kb+b]^T C[t, kb:kb+b]   (fp32, b x b)
 // which gives dL/dR_k = g_Y[:, k]^T Z[:, k] and dL/dP_j = g_U[:, j]^T X[:, j]
 // (chain rule of the block-diagonal products; gist.science technical summary
 // of "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
 // Transformation", section 2 Methodik, block-diagonal item).
 //
-// One workgroup owns one block and one token range and keeps the whole b x b
-// result in accumulators (a 2 x 2 wave grid, v_mfma_f32_32x32x16_bf16). Both
+// One workgroup owns one block (b = 512: one 256 x 256 quadrant of it) and
+// one token range and keeps that b x b (256 x 256) result in accumulators (a
+// 2 x 2 wave grid, v_mfma_f32_32x32x16_bf16). The four quadrant workgroups of
+// a 512 block and token range are launched 8 workgroup ids apart, so they run
+// on one XCD at about the same time and each 256-column half of A and C
+// streamed by two of them is read from HBM about once. Both
 // operands are token-major, so the MFMA fragments (8 consecutive tokens for a
 // fixed feature) are read from the row-major LDS tiles with the gfx950
 // transposing read ds_read_b64_tr_b16. Token tiles of 32 rows of both inputs
@@ -55,6 +59,7 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// B: width of the streamed column ranges (and of the workgroup's result)
 template <int B>
 struct BlockGram {
   static constexpr int WT = B / 2;            // wave tile (2 x 2 waves)
@@ -62,9 +67,9 @@ struct BlockGram {
   static constexpr int TILE = kTT * B;        // elements of one operand tile
   static constexpr int LPW = 2 * TILE * 2 / 1024 / 4;  // 1 KB loads per wave per tile
 
-  const bf16_t* A;
-  const bf16_t* C;
-  int64_t d, col0;
+  const bf16_t* A;  // first column of this workgroup's A range
+  const bf16_t* C;  // first column of its C range
+  int64_t d;
   int t_begin, t_end, ntiles;
   int lane, wave, wm, wn;
   floatx16 acc[FB][FB];
@@ -80,7 +85,7 @@ struct BlockGram {
       const int row = e / B, pch = (e % B) >> 3;
       const int lch = pch ^ (row & 15);
       const int grow = min(t0 + row, t_end - 1);
-      const bf16_t* src = (half == 0 ? A : C) + (int64_t)grow * d + col0 + lch * 8;
+      const bf16_t* src = (half == 0 ? A : C) + (int64_t)grow * d + lch * 8;
       dma16(src, dst + half * TILE + Qh * 512);
     }
   }
@@ -144,25 +149,39 @@ struct BlockGram {
   }
 };
 
-template <int B>
+// QS x QS workgroups per block of size QS * B (QS = 1, or 2 for b = 512):
+// workgroup (split, blk, p, q) accumulates rows p B.. and columns q B.. of
+// part[split][blk] (row stride QS * B) from A's columns p B.. and C's columns
+// q B.. of the block.
+template <int B, int QS>
 __global__ void __launch_bounds__(kNT)
 blockgram_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ C, float* __restrict__ part,
-                 int tokens, int64_t d, int nb, int tok_per_split) {
+                 int tokens, int64_t d, int nb, int nsplit, int tok_per_split) {
   typedef BlockGram<B> K;
+  constexpr int BB = QS * B;  // block size
   K k;
   const int tid = threadIdx.x;
   k.lane = tid & 63;
   k.wave = tid >> 6;
   k.wm = k.wave & 1;
   k.wn = k.wave >> 1;
-  const int blk = blockIdx.x % nb;
-  const int split = blockIdx.x / nb;
+  int unit, quad = 0;
+  if (QS == 1) {
+    unit = blockIdx.x;
+  } else {
+    // ids 32 g + 8 quad + r: unit 8 g + r, its four quadrants 8 ids apart
+    unit = (int)(blockIdx.x >> 5) * 8 + (int)(blockIdx.x & 7);
+    quad = (int)(blockIdx.x >> 3) & 3;
+  }
+  if (unit >= nb * nsplit) return;  // padding id of the last group (uniform, before any barrier)
+  const int blk = unit % nb;
+  const int split = unit / nb;
+  const int p = quad >> 1, q = quad & 1;
   k.t_begin = split * tok_per_split;
   k.t_end = min(tokens, k.t_begin + tok_per_split);
-  k.A = A;
-  k.C = C;
+  k.A = A + (int64_t)blk * BB + p * B;
+  k.C = C + (int64_t)blk * BB + q * B;
   k.d = d;
-  k.col0 = (int64_t)blk * B;
 #pragma unroll
   for (int i = 0; i < K::FB; ++i)
 #pragma unroll
@@ -186,7 +205,7 @@ blockgram_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ C, flo
   if (t < nt) k.template tile<1>(t++);
   if (t < nt) k.template tile<2>(t++);
 
-  float* out = part + ((int64_t)split * nb + blk) * B * B;
+  float* out = part + ((int64_t)split * nb + blk) * BB * BB + (int64_t)(p * B) * BB + q * B;
   const int lane = k.lane;
 #pragma unroll
   for (int i = 0; i < K::FB; ++i)
@@ -196,7 +215,7 @@ blockgram_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ C, flo
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int m = k.wm * K::WT + 32 * i + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        out[(int64_t)m * B + n] = k.acc[i][j][e];
+        out[(int64_t)m * BB + n] = k.acc[i][j][e];
       }
     }
 }
@@ -204,20 +223,27 @@ blockgram_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ C, flo
 }  // namespace
 
 bool blockgram_supported(DType t, int64_t d, int b) {
-  return t == DType::BF16 && (b == 128 || b == 256) && d % b == 0;
+  return t == DType::BF16 && (b == 128 || b == 256 || b == 512) && d % b == 0;
 }
+
+int blockgram_wg_per_block(int b) { return b == 512 ? 4 : 1; }
 
 hipError_t launch_blockgram(const void* A, const void* C, float* part, int64_t tokens, int64_t d,
                             int b, int nsplit, int kchunk, hipStream_t s) {
   const int nb = (int)(d / b);
   const bf16_t* a = static_cast<const bf16_t*>(A);
   const bf16_t* c = static_cast<const bf16_t*>(C);
-  if (b == 256)
-    hipLaunchKernelGGL(blockgram_kernel<256>, dim3(nb * nsplit), dim3(kNT), 0, s, a, c, part,
-                       (int)tokens, d, nb, kchunk);
-  else
-    hipLaunchKernelGGL(blockgram_kernel<128>, dim3(nb * nsplit), dim3(kNT), 0, s, a, c, part,
-                       (int)tokens, d, nb, kchunk);
+  if (b == 512) {
+    const int units = nb * nsplit;
+    hipLaunchKernelGGL((blockgram_kernel<256, 2>), dim3((units + 7) / 8 * 32), dim3(kNT), 0, s, a, c,
+                       part, (int)tokens, d, nb, nsplit, kchunk);
+  } else if (b == 256) {
+    hipLaunchKernelGGL((blockgram_kernel<256, 1>), dim3(nb * nsplit), dim3(kNT), 0, s, a, c, part,
+                       (int)tokens, d, nb, nsplit, kchunk);
+  } else {
+    hipLaunchKernelGGL((blockgram_kernel<128, 1>), dim3(nb * nsplit), dim3(kNT), 0, s, a, c, part,
+                       (int)tokens, d, nb, nsplit, kchunk);
+  }
   return hipGetLastError();
 }
 

@@ -65,10 +65,12 @@ bool blockapply_supported(DType t, int64_t d, int b);
 hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,
                              bool transpose, hipStream_t s);
 
-// ---- streaming token-reduction grams (bf16, b = 128 or 256, b | d) ----
+// ---- streaming token-reduction grams (bf16, b = 128, 256 or 512, b | d) ----
 // part[s][blk] = sum over tokens of split s (kchunk tokens each) of
 // A[t, blk]^T C[t, blk], float32 b x b; nsplit * kchunk >= tokens.
 bool blockgram_supported(DType t, int64_t d, int b);
+// Workgroups per block and token split (b = 512: one per 256 x 256 quadrant).
+int blockgram_wg_per_block(int b);
 hipError_t launch_blockgram(const void* A, const void* C, float* part, int64_t tokens, int64_t d,
                             int b, int nsplit, int kchunk, hipStream_t s);
 
