@@ -14,11 +14,13 @@
 // gfx950 transposing LDS read ds_read_b64_tr_b16 when the fragments need M_k's
 // columns) and keeps it in registers as MFMA B fragments: wave w owns output
 // columns [w b/4, (w+1) b/4). At b = 512 the block (512 KB) does not fit one
-// CU's registers: four workgroups share a block and token range, each holding
-// the 128 output columns of its slab (512 x 128, the same 128 KB as a whole
-// b = 256 block) and streaming 32-token tiles of all 512 input columns; the
-// four are launched 8 workgroup ids apart, so they run on one XCD at about
-// the same time and the input tile they all read comes from HBM about once.
+// CU's registers: two workgroups share a block and token range, each holding
+// the 256 output columns of its slab (512 x 256 bf16, 256 KB: 256 VGPRs per
+// lane, staged through the LDS ring in two passes) and streaming 32-token
+// tiles of all 512 input columns; the two are launched 8 workgroup ids apart,
+// so they run on one XCD at about the same time and the input tile they both
+// read comes from HBM about once. (Four 128-column slabs per block were ~10 %
+// slower: each input fragment then fed one MFMA instead of two.)
 // Token tiles of 64 rows (b <= 256) are copied from global
 // memory straight into a 4-stage LDS ring (global_load_lds_dwordx4, three
 // tiles in flight) and multiplied on v_mfma_f32_32x32x16_bf16 with the block
@@ -88,7 +90,7 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// B: block size (the K extent); NC: output columns per workgroup (B, or 128
+// B: block size (the K extent); NC: output columns per workgroup (B, or 256
 // at B = 512); TT: tokens per tile.
 template <int B, int NC, int TT, bool TRANS>
 struct BlockApply {
@@ -191,7 +193,7 @@ struct BlockApply {
 };
 
 // Workgroup (split, blk, slab) for NSLAB = B / NC slabs per block: ids are
-// unit = split * nb + blk when NSLAB = 1, else 32 g + 8 slab + r for
+// unit = split * nb + blk when NSLAB = 1, else 8 NSLAB g + 8 slab + r for
 // unit 8 g + r (the slabs of one unit 8 ids apart, on one XCD).
 template <int B, int NC, int TT, bool TRANS>
 __global__ void __launch_bounds__(kNT)
@@ -207,8 +209,8 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
   if (NSLAB == 1) {
     unit = blockIdx.x;
   } else {
-    unit = (int)(blockIdx.x >> 5) * 8 + (int)(blockIdx.x & 7);
-    slab = (int)(blockIdx.x >> 3) & 3;
+    unit = (int)(blockIdx.x / (8 * NSLAB)) * 8 + (int)(blockIdx.x & 7);
+    slab = (int)(blockIdx.x >> 3) % NSLAB;
   }
   if (unit >= nb * nsplit) return;  // padding id of the last group (uniform, before any barrier)
   const int blk = unit % nb;
@@ -232,42 +234,50 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
     constexpr int SR = TRANS ? NC : B;       // staged rows
     constexpr int SW = TRANS ? B : NC;       // staged row width
     constexpr int ROWS_PER_SLOT = kStage / SW;
-    static_assert(SR <= 4 * ROWS_PER_SLOT, "slab fits the ring");
+    constexpr int PASS_ROWS = 4 * ROWS_PER_SLOT < SR ? 4 * ROWS_PER_SLOT : SR;
+    constexpr int NPASS = SR / PASS_ROWS;    // the ring holds PASS_ROWS rows at a time
+    static_assert(NPASS * PASS_ROWS == SR, "whole passes");
     const bf16_t* src0 = TRANS ? Mk + (int64_t)slab * NC * B : Mk + slab * NC;
-    for (int c = k.tid; c < SR * SW / 8; c += kNT) {
-      const int row = c / (SW / 8), ch = c % (SW / 8);
-      bf16_t* slot = ring_rt(row / ROWS_PER_SLOT);
-      *reinterpret_cast<uint4*>(slot + sw<SW>(row % ROWS_PER_SLOT, ch * 8)) =
-          *reinterpret_cast<const uint4*>(src0 + (int64_t)row * B + ch * 8);
-    }
-    __syncthreads();
     const int lane = k.lane;
 #pragma unroll
-    for (int j = 0; j < K::CB; ++j)
-#pragma unroll
-      for (int ks = 0; ks < K::KS; ++ks) {
-        if (TRANS) {  // B(n, k) = M[n][k]: 8 consecutive k of row n
-          const int n = k.nw + 32 * j + (lane & 31);
-          const int kk = 16 * ks + 8 * (lane >> 5);
-          k.bfr[j][ks] = *reinterpret_cast<const bf16x8_t*>(ring_rt(n / ROWS_PER_SLOT) +
-                                                            sw<SW>(n % ROWS_PER_SLOT, kk));
-        } else {      // B(n, k) = M[k][n]: two transposing reads of 4 k each
-          const int g = lane >> 4, i = lane & 15;
-          const int n = k.nw + 32 * j + 16 * (g & 1) + 4 * (i & 3);
-          short4_t h[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int kk = 16 * ks + 8 * (g >> 1) + 4 * hh + (i >> 2);
-            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_short4*)(ring_rt(kk / ROWS_PER_SLOT) + sw<SW>(kk % ROWS_PER_SLOT, n)));
-          }
-          union { short4_t s[2]; bf16x8_t v; } u;
-          u.s[0] = h[0];
-          u.s[1] = h[1];
-          k.bfr[j][ks] = u.v;
-        }
+    for (int pass = 0; pass < NPASS; ++pass) {
+      for (int c = k.tid; c < PASS_ROWS * SW / 8; c += kNT) {
+        const int row = c / (SW / 8), ch = c % (SW / 8);
+        bf16_t* slot = ring_rt(row / ROWS_PER_SLOT);
+        *reinterpret_cast<uint4*>(slot + sw<SW>(row % ROWS_PER_SLOT, ch * 8)) =
+            *reinterpret_cast<const uint4*>(src0 + (int64_t)(pass * PASS_ROWS + row) * B + ch * 8);
       }
-    __syncthreads();  // the ring is reused for token tiles from here on
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < K::CB; ++j)
+#pragma unroll
+        for (int ks = 0; ks < K::KS; ++ks) {
+          if (TRANS) {  // B(n, k) = M[n][k]: 8 consecutive k of row n
+            // rows nw + 32 j .. + 31 lie in one pass (wave-uniform test)
+            if ((k.nw + 32 * j) / PASS_ROWS != pass) continue;
+            const int n = k.nw + 32 * j + (lane & 31) - pass * PASS_ROWS;
+            const int kk = 16 * ks + 8 * (lane >> 5);
+            k.bfr[j][ks] = *reinterpret_cast<const bf16x8_t*>(ring_rt(n / ROWS_PER_SLOT) +
+                                                              sw<SW>(n % ROWS_PER_SLOT, kk));
+          } else {      // B(n, k) = M[k][n]: two transposing reads of 4 k each
+            if ((16 * ks) / PASS_ROWS != pass) continue;
+            const int g = lane >> 4, i = lane & 15;
+            const int n = k.nw + 32 * j + 16 * (g & 1) + 4 * (i & 3);
+            short4_t h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int kk = 16 * ks + 8 * (g >> 1) + 4 * hh + (i >> 2) - pass * PASS_ROWS;
+              h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_short4*)(ring_rt(kk / ROWS_PER_SLOT) + sw<SW>(kk % ROWS_PER_SLOT, n)));
+            }
+            union { short4_t s[2]; bf16x8_t v; } u;
+            u.s[0] = h[0];
+            u.s[1] = h[1];
+            k.bfr[j][ks] = u.v;
+          }
+        }
+      __syncthreads();  // the ring is restaged, then reused for token tiles
+    }
   }
 
   const int nt = k.ntiles;
@@ -300,7 +310,7 @@ hipError_t launch_b(const bf16_t* X, const bf16_t* M, bf16_t* Y, int64_t tokens,
   per = (per + TT - 1) / TT * TT;
   splits = (int)((tokens + per - 1) / per);
   const int units = nb * splits;
-  const int grid = NSLAB == 1 ? units : (units + 7) / 8 * 32;
+  const int grid = NSLAB == 1 ? units : (units + 7) / 8 * (8 * NSLAB);
   hipLaunchKernelGGL((blockapply_kernel<B, NC, TT, TRANS>), dim3(grid), dim3(kNT), 0, s, X, M, Y,
                      (int)tokens, d, nb, splits, per);
   return hipGetLastError();
@@ -317,8 +327,8 @@ hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t toke
   const bf16_t* x = static_cast<const bf16_t*>(X);
   const bf16_t* m = static_cast<const bf16_t*>(M);
   bf16_t* y = static_cast<bf16_t*>(Y);
-  if (b == 512) return transpose ? launch_b<512, 128, 32, true>(x, m, y, tokens, d, s)
-                                 : launch_b<512, 128, 32, false>(x, m, y, tokens, d, s);
+  if (b == 512) return transpose ? launch_b<512, 256, 32, true>(x, m, y, tokens, d, s)
+                                 : launch_b<512, 256, 32, false>(x, m, y, tokens, d, s);
   if (b == 256) return transpose ? launch_b<256, 256, 64, true>(x, m, y, tokens, d, s)
                                  : launch_b<256, 256, 64, false>(x, m, y, tokens, d, s);
   return transpose ? launch_b<128, 128, 64, true>(x, m, y, tokens, d, s)
