@@ -241,7 +241,7 @@ def test_full_size_layer_set_8b(layer):
 
 
 # ------------------------------------------- POET-Xmem: Z recomputed
-@pytest.mark.parametrize("case", [SMALL_CASES[i] for i in (0, 2, 3, 5, 6)], ids=lambda c: c[0])
+@pytest.mark.parametrize("case", [SMALL_CASES[i] for i in (0, 2, 3, 5, 6, 9)], ids=lambda c: c[0])
 def test_recompute_z_small(case):
     """POETX_RECOMPUTE_Z: the oracle's results, and bit for bit those of the
     path that keeps Z (the same kernels recompute the same Z)."""
@@ -437,6 +437,7 @@ PERM_CASES = [
     ("perm_bf16_b128", 512, 768, 128, 1000, "bf16", 0.02, "cayley"),
     ("perm_bf16_b256_cnp", 512, 1024, 256, 300, "bf16", 0.01, "cnp"),
     ("perm_bf16_padded", 320, 200, 128, 257, "bf16", 0.02, "cayley"),
+    ("perm_bf16_b512", 1024, 1536, 512, 300, "bf16", 0.01, "cayley"),
 ]
 
 
@@ -521,6 +522,7 @@ INT8_CASES = [
     ("q8_bf16_b128", 512, 768, 128, 1000, "bf16", 0.02, "cayley", False, False),
     ("q8_bf16_padded_cnp", 320, 200, 128, 257, "bf16", 0.02, "cnp", False, False),
     ("q8_bf16_b256_perm_mem", 512, 1024, 256, 300, "bf16", 0.01, "cayley", True, True),
+    ("q8_bf16_b512_mem", 1024, 1536, 512, 200, "bf16", 0.01, "cayley", False, True),
 ]
 
 
