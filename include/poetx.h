@@ -110,8 +110,9 @@ typedef struct poetx_linear_desc {
    * first, and stage 1 then runs before stage 0). With permutations, forward
    * stage 3 gathers x and stage 4 scatters y; backward stage 8 gathers g_y
    * and x and stage 9 scatters g_x. With an INT8 weight, forward stage 5 and
-   * backward stage 10 widen the codes and scale R's block columns. May be
-   * NULL when n_events is 0. */
+   * backward stage 10 widen the codes and scale R's block columns. A NULL
+   * entry is skipped, so a caller can time one stage alone (each record adds
+   * a few microseconds between kernels). May be NULL when n_events is 0. */
   void* const* events;
   /* Optional block-mixing permutations (section 2 Methodik, permutation
    * item): index maps perm_in [d_in] and perm_out [d_out], int32 device
@@ -303,7 +304,11 @@ int poetx_linear_bwd(const poetx_linear_desc* desc, const void* g_y, const void*
                      void* ws, size_t ws_bytes, void* stream);
 
 /* Thin hipEvent helpers so a caller without HIP headers can time stages.
- * Each returns a poetx_status. */
+ * Each returns a poetx_status. The events are for timing only: they are
+ * created with hipEventDisableSystemFence, so recording one between two
+ * kernels does not write back the caches, and synchronizing on one does not
+ * make the timed work's results visible to the host (synchronize the stream
+ * or device for that). */
 int poetx_event_create(void** event);
 int poetx_event_destroy(void* event);
 int poetx_event_record(void* event, void* stream);

@@ -173,7 +173,7 @@ struct Stages {
   hipError_t begin(int i) const { return mark(2 * i); }
   hipError_t end(int i) const { return mark(2 * i + 1); }
   hipError_t mark(int e) const {
-    if (e + 1 > d->n_events) return hipSuccess;
+    if (e + 1 > d->n_events || d->events[e] == nullptr) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(d->events[e]), s);
   }
 };
@@ -828,7 +828,9 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 int poetx_event_create(void** ev) {
   if (!ev) return POETX_ERR_NULL;
   hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) return POETX_ERR_HIP;
+  // timing only: recording it skips the system-scope release (a write-back of
+  // the caches) that a default event performs between two kernels
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return POETX_ERR_HIP;
   *ev = e;
   return POETX_OK;
 }

@@ -162,6 +162,27 @@ def test_deterministic_bitwise():
         assert torch.equal(a[k], c[k]), k
 
 
+def test_stage_events_with_null_entries():
+    """Stage timing with NULL entries records only the given stages and leaves
+    the results bit for bit unchanged (the benchmark times the dense product
+    alone this way)."""
+    from orthogonal_equivalence_amd.layer import PoetxLinear
+    spec = LayerSpec("ev", 512, 1024, 256, 300, "bf16", 0.01, seed=4)
+    L = make_layer(spec)
+    _, ref = U.run_layer(L)
+    lay = PoetxLinear(U.dev(L.W0, "bf16"), 256, 256, "bf16")
+    lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
+    x, g_y = U.dev(L.x, "bf16"), U.dev(L.g_y, "bf16")
+    e0, e1 = P.Event(), P.Event()
+    lay.build()
+    y, z = lay.forward(x, events=[None, None, e0.handle, e1.handle])
+    g_x, gR, gP = lay.backward(g_y, x, z, events=[None] * 4 + [e0.handle, e1.handle])
+    torch.cuda.synchronize()
+    assert e0.elapsed_ms(e1) > 0.0
+    for k, v in (("y", y), ("z", z), ("g_x", g_x), ("g_theta_R", gR), ("g_theta_P", gP)):
+        assert torch.equal(v, ref[k]), k
+
+
 def test_theta_zero_is_plain_linear():
     """theta = 0 gives R = P = I: y = x W0^T and g_x = g_y W0 (bf16 path)."""
     spec = LayerSpec("zero", 256, 512, 64, 130, "bf16", 0.0, seed=9)
