@@ -25,9 +25,12 @@
 // memory straight into a 4-stage LDS ring (global_load_lds_dwordx4, three
 // tiles in flight) and multiplied on v_mfma_f32_32x32x16_bf16 with the block
 // as the first operand, so the accumulators hold the transposed output tile:
-// each lane has four consecutive output columns of one token, which go to the
-// consumed ring slot as one 8-byte LDS write (not four 2-byte ones) and leave
-// with 16-byte stores. Each tile derives its addresses from an opaque copy of
+// each lane has four consecutive output columns of one token, which go to an
+// output staging buffer as one 8-byte LDS write (not four 2-byte ones). The
+// staged tile leaves with 16-byte stores spread over the next tile's products
+// (the staging buffer is not a ring slot, so nothing waits for the stores
+// before the ring moves on; 5-7 % faster than staging into the consumed slot
+// and storing before the next tile). Each tile derives its addresses from an opaque copy of
 // the lane id, so none are hoisted out of the tile loop to hold registers
 // (322 VGPRs at b = 256, against 509 with the hoisted form).
 //
@@ -56,6 +59,9 @@ __shared__ __attribute__((aligned(16))) bf16_t g_ring0[kStage];
 __shared__ __attribute__((aligned(16))) bf16_t g_ring1[kStage];
 __shared__ __attribute__((aligned(16))) bf16_t g_ring2[kStage];
 __shared__ __attribute__((aligned(16))) bf16_t g_ring3[kStage];
+// output staging: tile t's result (at most 64 x 256) waits here while tile
+// t+1's products run; with the ring, 160 KB of LDS
+__shared__ __attribute__((aligned(16))) bf16_t g_out[kStage];
 
 template <int S> __device__ __forceinline__ bf16_t* ring() {
   return S == 0 ? g_ring0 : S == 1 ? g_ring1 : S == 2 ? g_ring2 : g_ring3;
@@ -134,6 +140,8 @@ struct BlockApply {
     if (t + 2 < ntiles) wait_vm<2 * LPW>();
     else if (t + 1 < ntiles) wait_vm<LPW>();
     else wait_vm<0>();
+    // this wave's staging writes of tile t-1 have landed (s_waitcnt lgkmcnt(0))
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
     __builtin_amdgcn_s_barrier();  // every wave's part of tile t landed; slot of t-1 free
     if (t + 3 < ntiles) load_tile(t + 3, ring<(S + 3) & 3>());
 
@@ -151,16 +159,19 @@ struct BlockApply {
         a[r] = *reinterpret_cast<const bf16x8_t*>(st + sw<B>(32 * r + (ln & 31), 16 * ks + 8 * (ln >> 5)));
     };
     rd(0, af[0]);
+    static_assert(KS % CPT == 0, "stores spread evenly over the K steps");
+    const int tp0 = t_begin + (t - 1) * TT;  // first token of the staged tile t-1
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS) rd(ks + 1, af[(ks + 1) & 1]);
+      if (t > 0 && ks % (KS / CPT) == 0) store_chunk(ks / (KS / CPT), tp0, td);
 #pragma unroll
       for (int r = 0; r < RB; ++r)
 #pragma unroll
         for (int j = 0; j < CB; ++j)
           acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j][ks], af[ks & 1][r], acc[r][j], 0, 0, 0);
     }
-    __builtin_amdgcn_s_barrier();  // all waves done reading slot S
+    __builtin_amdgcn_s_barrier();  // all waves done reading slot S and the staged tile t-1
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -177,18 +188,19 @@ struct BlockApply {
           v[1] = (short)f32_to_bf16(acc[r][j][4 * g + 1]);
           v[2] = (short)f32_to_bf16(acc[r][j][4 * g + 2]);
           v[3] = (short)f32_to_bf16(acc[r][j][4 * g + 3]);
-          *reinterpret_cast<short4_t*>(st + sw<NC>(m, n)) = v;
+          *reinterpret_cast<short4_t*>(g_out + sw<NC>(m, n)) = v;
         }
       }
-    __syncthreads();  // output tile staged
-    const int t0 = t_begin + t * TT;
-#pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int c = td + q * kNT;
-      const int row = c / (NC / 8), ch = c % (NC / 8);
-      const uint4 v = *reinterpret_cast<const uint4*>(st + sw<NC>(row, ch * 8));
-      if (t0 + row < t_end) *reinterpret_cast<uint4*>(Y + (int64_t)(t0 + row) * d + ocol0 + ch * 8) = v;
-    }
+    // no barrier: the next tile's first barrier orders these writes before
+    // its reads of g_out
+  }
+
+  // output chunk q of the staged tile whose first token is t0
+  __device__ __forceinline__ void store_chunk(int q, int t0, int td) {
+    const int c = td + q * kNT;
+    const int row = c / (NC / 8), ch = c % (NC / 8);
+    const uint4 v = *reinterpret_cast<const uint4*>(g_out + sw<NC>(row, ch * 8));
+    if (t0 + row < t_end) *reinterpret_cast<uint4*>(Y + (int64_t)(t0 + row) * d + ocol0 + ch * 8) = v;
   }
 };
 
@@ -294,6 +306,9 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
   if (t < nt) k.template tile<0>(t++);
   if (t < nt) k.template tile<1>(t++);
   if (t < nt) k.template tile<2>(t++);
+  __syncthreads();  // the last tile is staged
+#pragma unroll
+  for (int q = 0; q < K::CPT; ++q) k.store_chunk(q, k.t_begin + (nt - 1) * TT, k.tid);
 }
 
 template <int B, int NC, int TT, bool TRANS>
