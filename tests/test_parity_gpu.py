@@ -116,6 +116,9 @@ SMALL_CASES = [
     # units is partly padding
     ("bf16_b512_blocks", 2048, 1536, 512, 1000, "bf16", 0.01),
     ("bf16_b512_padded_units", 1536, 1024, 512, 100, "bf16", 0.01),
+    # one token: every streamed tile is ragged, every split but one empty
+    ("bf16_b512_one_token", 512, 1024, 512, 1, "bf16", 0.01),
+    ("bf16_b256_one_token", 768, 512, 256, 1, "bf16", 0.01),
 ]
 
 
