@@ -70,8 +70,19 @@ size_t weight_bytes(const poetx_linear_desc* d) {
 }
 
 struct FwdPlan {
-  size_t u_off, z_off, xp_off, yp_off, inv_off, wq_off, rs_off, total;
+  size_t u_off, z_off, xp_off, yp_off, inv_off, wq_off, rs_off, sb_off, total;
 };
+
+// Bytes of the super-block buffer (block-diagonal 128 x 128 super blocks of
+// b = 32 or 64 blocks, for the b = 128 streaming kernels): one side at a
+// time, so the larger of the two.
+size_t superblock_bytes(const poetx_linear_desc* d) {
+  const DType t = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
+  size_t n = 0;
+  if (int S = poetx::superblock_size(t, d->d_in, d->b_in)) n = std::max(n, (size_t)d->d_in * S);
+  if (int S = poetx::superblock_size(t, d->d_out, d->b_out)) n = std::max(n, (size_t)d->d_out * S);
+  return n * act_size(d->act);
+}
 FwdPlan plan_fwd(const poetx_linear_desc* d) {
   FwdPlan p;
   const size_t es = act_size(d->act);
@@ -92,6 +103,7 @@ FwdPlan plan_fwd(const poetx_linear_desc* d) {
     p.wq_off = off; off += align_up((size_t)d->d_out * d->d_in * es);
     p.rs_off = off; off += align_up((size_t)ceil_div(d->d_out, d->b_out) * d->b_out * d->b_out * es);
   }
+  p.sb_off = off; off += align_up(superblock_bytes(d));
   p.total = off;
   return p;
 }
@@ -127,21 +139,30 @@ SplitK choose_split(int64_t nblocks, int b, int64_t d, int64_t tokens, DType in)
 }
 
 struct BwdPlan {
-  size_t gz, gu, partR, partP, GR, GP, TR, TP, MR, MP, gyp, xp, inv, wq, rs, total;
+  size_t gz, gu, partR, partP, GR, GP, TR, TP, MR, MP, gyp, xp, inv, wq, rs, sb, total;
   SplitK sR, sP;
+  int subR, subP;  // blocks per super block of the grams (1: none)
 };
 BwdPlan plan_bwd(const poetx_linear_desc* d) {
   BwdPlan p;
   const DType in = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
   const int64_t nbR = ceil_div(d->d_out, d->b_out), nbP = ceil_div(d->d_in, d->b_in);
   const size_t bbR = (size_t)d->b_out * d->b_out * 4, bbP = (size_t)d->b_in * d->b_in * 4;
-  p.sR = choose_split(nbR, d->b_out, d->d_out, d->tokens, in);
-  p.sP = choose_split(nbP, d->b_in, d->d_in, d->tokens, in);
+  // the grams of b = 32 / 64 blocks run as grams of their 128 x 128 super
+  // blocks, whose diagonal pieces the reduction keeps
+  const int SR = poetx::superblock_size(in, d->d_out, d->b_out);
+  const int SP = poetx::superblock_size(in, d->d_in, d->b_in);
+  p.subR = SR ? SR / d->b_out : 1;
+  p.subP = SP ? SP / d->b_in : 1;
+  p.sR = SR ? choose_split(d->d_out / SR, SR, d->d_out, d->tokens, in)
+            : choose_split(nbR, d->b_out, d->d_out, d->tokens, in);
+  p.sP = SP ? choose_split(d->d_in / SP, SP, d->d_in, d->tokens, in)
+            : choose_split(nbP, d->b_in, d->d_in, d->tokens, in);
   size_t off = 0;
   p.gz = off; off += align_up((size_t)d->tokens * d->d_out * act_size(d->act));
   p.gu = off; off += align_up((size_t)d->tokens * d->d_in * act_size(d->act));
-  p.partR = off; off += align_up((size_t)p.sR.nsplit * nbR * bbR);
-  p.partP = off; off += align_up((size_t)p.sP.nsplit * nbP * bbP);
+  p.partR = off; off += align_up((size_t)p.sR.nsplit * nbR * bbR * p.subR);
+  p.partP = off; off += align_up((size_t)p.sP.nsplit * nbP * bbP * p.subP);
   p.GR = off; off += align_up(nbR * bbR);
   p.GP = off; off += align_up(nbP * bbP);
   p.TR = off; off += align_up(nbR * bbR);
@@ -162,6 +183,7 @@ BwdPlan plan_bwd(const poetx_linear_desc* d) {
     p.wq = off; off += align_up((size_t)d->d_out * d->d_in * es);
     p.rs = off; off += align_up((size_t)nbR * d->b_out * d->b_out * es);
   }
+  p.sb = off; off += align_up(superblock_bytes(d));
   p.total = off;
   return p;
 }
@@ -200,7 +222,14 @@ GemmParams blockdiag_params(const void* in, const void* blocks, void* out, int64
 // out[:, blk] = in[:, blk] M_blk^T (transpose) or in[:, blk] M_blk, on the
 // streaming kernel when it supports the shape, else on the batched GEMM.
 hipError_t block_apply(DType t, const void* in, const void* blocks, void* out, int64_t tokens,
-                       int64_t d, int b, bool transpose, hipStream_t s) {
+                       int64_t d, int b, bool transpose, hipStream_t s, void* super_ws) {
+  if (const int S = poetx::superblock_size(t, d, b)) {
+    // b = 32 / 64: the blocks placed on the diagonals of 128 x 128 super
+    // blocks (zeros elsewhere) and applied by the b = 128 streaming kernel
+    hipError_t e = poetx::launch_superblocks(blocks, d / b, b, S, super_ws, s);
+    if (e != hipSuccess) return e;
+    return poetx::launch_blockapply(in, super_ws, out, tokens, d, S, transpose, s);
+  }
   if (poetx::blockapply_supported(t, d, b))
     return poetx::launch_blockapply(in, blocks, out, tokens, d, b, transpose, s);
   bool bk;
@@ -231,6 +260,8 @@ GemmParams gram_params(const void* a, const void* c, float* part, int64_t tokens
 // when it supports the shape, else on the batched split-K GEMM.
 hipError_t block_gram(DType t, const void* a, const void* c, float* part, int64_t tokens, int64_t d,
                       int b, SplitK sk, hipStream_t s) {
+  if (const int S = poetx::superblock_size(t, d, b))  // grams of the 128 x 128 super blocks
+    return poetx::launch_blockgram(a, c, part, tokens, d, S, sk.nsplit, sk.kchunk, s);
   if (poetx::blockgram_supported(t, d, b))
     return poetx::launch_blockgram(a, c, part, tokens, d, b, sk.nsplit, sk.kchunk, s);
   GemmParams g = gram_params(a, c, part, tokens, d, b, sk);
@@ -614,7 +645,8 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
 
   // S2: U = X blockdiag(P)^T
   if ((e = sg.begin(0)) != hipSuccess) return hip_status(e);
-  if ((e = block_apply(t, X, P_act, U, N, n, d->b_in, true, s)) != hipSuccess) return hip_status(e);
+  void* SB = w + plan.sb_off;  // super blocks of b = 32 / 64 blocks
+  if ((e = block_apply(t, X, P_act, U, N, n, d->b_in, true, s, SB)) != hipSuccess) return hip_status(e);
   if ((e = sg.end(0)) != hipSuccess) return hip_status(e);
 
   // S3: Z = U W0^T
@@ -624,7 +656,7 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
 
   // S4: Y = Z blockdiag(R)^T
   if ((e = sg.begin(2)) != hipSuccess) return hip_status(e);
-  if ((e = block_apply(t, Z, Rb, perm ? Yp : y, N, m, d->b_out, true, s)) != hipSuccess)
+  if ((e = block_apply(t, Z, Rb, perm ? Yp : y, N, m, d->b_out, true, s, SB)) != hipSuccess)
     return hip_status(e);
   if ((e = sg.end(2)) != hipSuccess) return hip_status(e);
 
@@ -685,6 +717,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   char* w = static_cast<char*>(ws);
   void* gZ = w + plan.gz;
   void* gU = w + plan.gu;
+  void* SB = w + plan.sb;  // super blocks of b = 32 / 64 blocks
   float* partR = reinterpret_cast<float*>(w + plan.partR);
   float* partP = reinterpret_cast<float*>(w + plan.partP);
   float* GR = reinterpret_cast<float*>(w + plan.GR);
@@ -742,7 +775,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   auto grad_r = [&]() -> hipError_t {  // B1: g_Z = g_Y blockdiag(R)
     hipError_t r;
     if ((r = sg.begin(0)) != hipSuccess) return r;
-    if ((r = block_apply(t, gY, Rb, gZ, N, m, bR, false, s)) != hipSuccess) return r;
+    if ((r = block_apply(t, gY, Rb, gZ, N, m, bR, false, s, SB)) != hipSuccess) return r;
     return sg.end(0);
   };
   auto gram_r = [&](const void* Z) -> hipError_t {
@@ -751,7 +784,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     if ((r = sg.begin(1)) != hipSuccess) return r;
     if ((r = block_gram(t, gY, Z, partR, N, m, bR, plan.sR, s)) != hipSuccess) return r;
     if ((r = poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, gt, s,
-                                        d->w_scale)) != hipSuccess)
+                                        d->w_scale, plan.subR)) != hipSuccess)
       return r;
     return sg.end(1);
   };
@@ -762,7 +795,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     // POET-Xmem: U = X P^T into the g_U buffer and Z = U W0^T into the g_Z
     // buffer (both overwritten later), the R gram on Z, then g_Z over Z
     POETX_TRY(sg.begin(7));
-    POETX_TRY(block_apply(t, X, P_act, gU, N, n, bP, true, s));
+    POETX_TRY(block_apply(t, X, P_act, gU, N, n, bP, true, s, SB));
     POETX_TRY(dense(t, gU, Wmat, gZ, N, m, n, n, n, m, true, s));
     POETX_TRY(sg.end(7));
     POETX_TRY(gram_r(gZ));
@@ -777,12 +810,13 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   // B4: G_P[j] = g_U[:, j]^T X[:, j]
   POETX_TRY(sg.begin(3));
   POETX_TRY(block_gram(t, gU, X, partP, N, n, bP, plan.sP, s));
-  POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, gt, s));
+  POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, gt, s, nullptr,
+                                       plan.subP));
   POETX_TRY(sg.end(3));
 
   // B5: g_X = g_U blockdiag(P)
   POETX_TRY(sg.begin(4));
-  POETX_TRY(block_apply(t, gU, P_act, gX, N, n, bP, false, s));
+  POETX_TRY(block_apply(t, gU, P_act, gX, N, n, bP, false, s, SB));
   POETX_TRY(sg.end(4));
 
   // stage 9 (permutations only): g_x[:, perm_in[j]] = g_X[:, j]

@@ -331,7 +331,42 @@ hipError_t launch_b(const bf16_t* X, const bf16_t* M, bf16_t* Y, int64_t tokens,
   return hipGetLastError();
 }
 
+// One thread per 16-byte chunk of the super blocks: the chunk at (row r,
+// columns c0 .. c0 + 7) of super block sb lies in block column c0 / b (b is a
+// multiple of 8); it is a row piece of block sb S/b + r / b when that is the
+// block's own column, else zeros.
+__global__ void __launch_bounds__(kNT)
+superblock_kernel(const bf16_t* __restrict__ blocks, int b, int S, int64_t nchunks,
+                  bf16_t* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (c >= nchunks) return;
+  const int per_row = S / 8;
+  const int64_t row_all = c / per_row;           // row over all super blocks
+  const int sb = (int)(row_all / S), r = (int)(row_all % S);
+  const int c0 = (int)(c % per_row) * 8;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (r / b == c0 / b) {
+    const int64_t blk = (int64_t)sb * (S / b) + r / b;
+    v = *reinterpret_cast<const uint4*>(blocks + (blk * b + r % b) * b + c0 % b);
+  }
+  *reinterpret_cast<uint4*>(out + c * 8) = v;
+}
+
 }  // namespace
+
+int superblock_size(DType t, int64_t d, int b) {
+  return (t == DType::BF16 && (b == 32 || b == 64) && d % 128 == 0) ? 128 : 0;
+}
+
+hipError_t launch_superblocks(const void* blocks, int64_t nblocks, int b, int S, void* out,
+                              hipStream_t s) {
+  if (b % 8 != 0 || S % b != 0 || nblocks % (S / b) != 0) return hipErrorInvalidValue;
+  const int64_t nchunks = nblocks / (S / b) * S * S / 8;
+  const int64_t grid = (nchunks + kNT - 1) / kNT;
+  hipLaunchKernelGGL(superblock_kernel, dim3((unsigned)grid), dim3(kNT), 0, s,
+                     static_cast<const bf16_t*>(blocks), b, S, nchunks, static_cast<bf16_t*>(out));
+  return hipGetLastError();
+}
 
 bool blockapply_supported(DType t, int64_t d, int b) {
   return t == DType::BF16 && (b == 128 || b == 256 || b == 512) && d % b == 0;

@@ -649,19 +649,26 @@ cayley_block_kernel(const float* __restrict__ theta, int nblocks, int last_valid
 
 // grid (ceil(b*b / (4 kNT)), nblocks); b*b is a multiple of 4. col_scale
 // (optional) multiplies column j of block blk by col_scale[blk b + j].
+// sub > 1: the partials are grams of (sub b) x (sub b) super blocks (sub
+// consecutive blocks each) and block blk is the diagonal piece
+// (blk % sub) of super block blk / sub.
 template <typename TOut>
 __global__ void __launch_bounds__(kNT)
 split_reduce_kernel(const float* __restrict__ part, int nsplit, int nblocks, int b,
-                    int last_valid, const float* __restrict__ col_scale, TOut* __restrict__ G) {
+                    int last_valid, const float* __restrict__ col_scale, TOut* __restrict__ G,
+                    int sub) {
   const int q = blockIdx.x * kNT + threadIdx.x;  // float4 index within the block
   const int bb = b * b;
   if (4 * q >= bb) return;
   const int blk = blockIdx.y;
-  const int64_t total = (int64_t)nblocks * bb;
+  const int64_t total = (int64_t)nblocks * bb * sub;  // floats of one split's partials
   const int64_t off = (int64_t)blk * bb + 4 * q;
+  const int ld = b * sub, piece = (blk % sub) * b;
+  const int i0 = (4 * q) / b, j0 = (4 * q) % b;
+  const int64_t src = ((int64_t)(blk / sub) * ld + piece + i0) * ld + piece + j0;
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < nsplit; ++s) {
-    const float4 t = *reinterpret_cast<const float4*>(part + (int64_t)s * total + off);
+    const float4 t = *reinterpret_cast<const float4*>(part + (int64_t)s * total + src);
     v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
   }
   float e[4] = {v.x, v.y, v.z, v.w};
@@ -795,14 +802,15 @@ hipError_t launch_expand_skew(const float* theta, int64_t nblocks, int b, int la
 
 hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, int b,
                                int last_valid, void* G, DType out, hipStream_t stream,
-                               const float* col_scale) {
+                               const float* col_scale, int sub) {
+  if (sub < 1 || nblocks % sub != 0 || (sub > 1 && last_valid != b)) return hipErrorInvalidValue;
   const dim3 grid((b * b / 4 + kNT - 1) / kNT, (int)nblocks);
   if (out == DType::BF16)
     hipLaunchKernelGGL(split_reduce_kernel<bf16_t>, grid, dim3(kNT), 0, stream, part, nsplit,
-                       (int)nblocks, b, last_valid, col_scale, static_cast<bf16_t*>(G));
+                       (int)nblocks, b, last_valid, col_scale, static_cast<bf16_t*>(G), sub);
   else
     hipLaunchKernelGGL(split_reduce_kernel<float>, grid, dim3(kNT), 0, stream, part, nsplit,
-                       (int)nblocks, b, last_valid, col_scale, static_cast<float*>(G));
+                       (int)nblocks, b, last_valid, col_scale, static_cast<float*>(G), sub);
   return hipGetLastError();
 }
 

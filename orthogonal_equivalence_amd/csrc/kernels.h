@@ -62,6 +62,14 @@ hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_
 // Y[:, blk] = X[:, blk] M_blk^T (transpose) or X[:, blk] M_blk, token-major
 // with row stride d.
 bool blockapply_supported(DType t, int64_t d, int b);
+// Super-block size for block size b (0: none): blocks of b = 32 or 64 are
+// run through the b = 128 streaming kernels as block-diagonal 128 x 128
+// super blocks (exact zeros off the diagonal), when 128 divides d.
+int superblock_size(DType t, int64_t d, int b);
+// out[s] = blockdiag(blocks[s S/b], ..., blocks[s S/b + S/b - 1]), S x S bf16,
+// for the nblocks (a multiple of S/b) b x b bf16 blocks.
+hipError_t launch_superblocks(const void* blocks, int64_t nblocks, int b, int S, void* out,
+                              hipStream_t s);
 hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,
                              bool transpose, hipStream_t s);
 
@@ -127,7 +135,7 @@ hipError_t launch_scale_block_columns(DType t, const void* M, const float* scale
 // col_scale, column j of block blk is multiplied by col_scale[blk b + j].
 hipError_t launch_split_reduce(const float* part, int nsplit, int64_t nblocks, int b,
                                int last_valid, void* G, DType out, hipStream_t stream,
-                               const float* col_scale = nullptr);
+                               const float* col_scale = nullptr, int sub = 1);
 // g_theta[blk][idx(i,j)] = sign ((M + c S)[i][j] - (M + c S)[j][i]) (i < j),
 // S an optional bf16 addend; zero for entries of the last block at rows or
 // columns >= last_valid. A second set of blocks of the same size shares the

@@ -119,6 +119,10 @@ SMALL_CASES = [
     # one token: every streamed tile is ragged, every split but one empty
     ("bf16_b512_one_token", 512, 1024, 512, 1, "bf16", 0.01),
     ("bf16_b256_one_token", 768, 512, 256, 1, "bf16", 0.01),
+    # b = 32 / 64 run as block-diagonal 128 x 128 super blocks on the b = 128
+    # streaming kernels (128 divides d)
+    ("bf16_b64_super", 384, 640, 64, 300, "bf16", 0.02),
+    ("bf16_b32_super", 256, 384, 32, 200, "bf16", 0.05),
 ]
 
 
@@ -462,6 +466,7 @@ PERM_CASES = [
     ("perm_bf16_b256_cnp", 512, 1024, 256, 300, "bf16", 0.01, "cnp"),
     ("perm_bf16_padded", 320, 200, 128, 257, "bf16", 0.02, "cayley"),
     ("perm_bf16_b512", 1024, 1536, 512, 300, "bf16", 0.01, "cayley"),
+    ("perm_bf16_b64_super", 384, 640, 64, 300, "bf16", 0.02, "cayley"),
 ]
 
 
@@ -547,6 +552,7 @@ INT8_CASES = [
     ("q8_bf16_padded_cnp", 320, 200, 128, 257, "bf16", 0.02, "cnp", False, False),
     ("q8_bf16_b256_perm_mem", 512, 1024, 256, 300, "bf16", 0.01, "cayley", True, True),
     ("q8_bf16_b512_mem", 1024, 1536, 512, 200, "bf16", 0.01, "cayley", False, True),
+    ("q8_bf16_b64_super", 384, 640, 64, 300, "bf16", 0.02, "cayley", False, False),
 ]
 
 
