@@ -235,6 +235,27 @@ def test_recompute_z_forward_workspace_holds_z():
                                             flags=P.POETX_RECOMPUTE_Z))
 
 
+def test_small_blocks_reserve_their_super_blocks():
+    """b = 32 / 64 in bf16 with 128 | d run on 128 x 128 block-diagonal super
+    blocks: both workspaces hold the larger side's super blocks (d x 128
+    bf16), and the backward's gram partials are those of the super blocks;
+    float32, or a d that 128 does not divide, reserve none of it."""
+    def ws(b, act, d_in=4096, d_out=6144):
+        d = P.make_desc(1000, d_in, d_out, b, b, act)
+        return P.poetx_fwd_workspace_size(d), P.poetx_bwd_workspace_size(d)
+    f128, _ = ws(128, P.POETX_BF16)
+    f128_f32, _ = ws(128, P.POETX_F32)
+    for b in (32, 64):
+        f, bw = ws(b, P.POETX_BF16)
+        assert f >= 1000 * 4096 * 2 + 6144 * 128 * 2
+        assert f - 6144 * 128 * 2 <= f128
+        assert bw >= 6144 * 128 * 2
+        assert ws(b, P.POETX_F32)[0] == f128_f32  # float32: no super blocks
+    # 128 divides neither 4032 (63 x 64) nor 4000: no super blocks
+    f_odd, _ = ws(64, P.POETX_BF16, d_in=4032, d_out=4000)
+    assert f_odd == 1000 * 4032 * 2
+
+
 def test_recompute_z_alias_checks_skip_null_z():
     d = desc(flags=P.POETX_RECOMPUTE_Z)
     assert _fwd(d, z=None, y=ALIGNED) == P.POETX_ERR_ALIAS
