@@ -198,7 +198,7 @@ def main():
 
     from orthogonal_equivalence_amd import poetx as P
     from orthogonal_equivalence_amd.inputs import CONFIGS, make_layer, make_permutations
-    from orthogonal_equivalence_amd.layer import PoetxLinear
+    from orthogonal_equivalence_amd.layer import PoetxLinear, PoetxLinearSet
 
     specs = CONFIGS[args.config]
     torch.cuda.set_device(0)
@@ -222,6 +222,14 @@ def main():
                    g_x=torch.empty(s.tokens, s.d_in, dtype=tdt[s.dtype], device=dev),
                    gR=torch.empty_like(lay.theta_R), gP=torch.empty_like(lay.theta_P))
         layers.append((s, L if len(specs) == 1 else None, lay, x, g_y, out))
+    # a workload of several layers with one block size rebuilds all of their
+    # blocks with one call (the same work, batched), as a training step would
+    layer_set = None
+    if len(layers) > 1:
+        try:
+            layer_set = PoetxLinearSet([lay for _, _, lay, _, _, _ in layers])
+        except ValueError:
+            layer_set = None
     stream = torch.cuda.current_stream()
     fwd_stages = FWD_STAGES + (FWD_PERM_STAGES if args.permute else [None, None])
     bwd_stages = BWD_STAGES + (["recompute_z" if args.recompute_z else None] +
@@ -235,13 +243,21 @@ def main():
         bwd_stages.pop()
 
     def step(ev=None):
-        for li, (s, _, lay, x, g_y, o) in enumerate(layers):
-            e = None if ev is None else ev[li]
+        if layer_set is not None:  # its build events are the first layer's
+            e = None if ev is None else ev[0]
             if e is not None and e["build"] is not None:
                 e["build"][0].record(stream)
-            lay.build(stream)
+            layer_set.build(stream)
             if e is not None and e["build"] is not None:
                 e["build"][1].record(stream)
+        for li, (s, _, lay, x, g_y, o) in enumerate(layers):
+            e = None if ev is None else ev[li]
+            if layer_set is None:
+                if e is not None and e["build"] is not None:
+                    e["build"][0].record(stream)
+                lay.build(stream)
+                if e is not None and e["build"] is not None:
+                    e["build"][1].record(stream)
             lay.forward(x, o["y"], o["z"], stream=stream, events=None if e is None else e["fwd"])
             lay.backward(g_y, x, o["z"], o["g_x"], o["gR"], o["gP"], stream=stream,
                          events=None if e is None else e["bwd"])
@@ -306,11 +322,16 @@ def main():
     step_ms = [a.elapsed_ms(b) for a, b in per_step]
 
     stage_ms = {}
+    if layer_set is not None:
+        stage_ms["build"] = statistics.mean(
+            step_events[k][0]["build"][0].elapsed_ms(step_events[k][0]["build"][1])
+            for k in range(args.steps))
     for li, (s, _, _, _, _, _) in enumerate(layers):
         pre = "" if len(layers) == 1 else f"{s.name}."
-        vals = [step_events[k][li]["build"][0].elapsed_ms(step_events[k][li]["build"][1])
-                for k in range(args.steps)]
-        stage_ms[pre + "build"] = statistics.mean(vals)
+        if layer_set is None:
+            vals = [step_events[k][li]["build"][0].elapsed_ms(step_events[k][li]["build"][1])
+                    for k in range(args.steps)]
+            stage_ms[pre + "build"] = statistics.mean(vals)
         for grp, names in (("fwd", fwd_stages), ("bwd", bwd_stages)):
             for si, nm in enumerate(names):
                 if nm is None:
@@ -346,6 +367,8 @@ def main():
                    "orthogonal_map": ("exact Cayley" if args.map == "cayley"
                                       else "Cayley-Neumann series to Q^4"),
                    "permutations": bool(args.permute),
+                   "build": ("one call for the blocks of all layers" if layer_set is not None
+                             else "one call per layer"),
                    "weight": "int8 codes + per-row float32 scales" if args.int8 else specs[0].dtype},
         "roofline": roofline,
         "layer_roofline": {"flops": F, "bytes": B, "t_roof_ms": t_roof * 1e3,

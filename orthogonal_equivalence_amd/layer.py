@@ -166,3 +166,68 @@ class PoetxLinear:
                            g_x, g_theta_R if g_theta_R.numel() else None,
                            g_theta_P if g_theta_P.numel() else None, ws, stream)
         return g_x, g_theta_R, g_theta_P
+
+
+class PoetxLinearSet:
+    """Several POET-X layers with one block size b whose generators and
+    orthogonal blocks live in shared buffers, layer after layer (each layer's
+    R blocks, then its P blocks), so that one build call rebuilds every
+    layer's R and P: the blocks are independent, so this is the same work as
+    one call per layer, batched over all of them. Every layer must combine its
+    two sets (b_in == b_out == b, b dividing d_in and d_out), and all must
+    share the activation type and the orthogonal map. Each layer keeps working
+    on its own views; its own build() still builds just that layer."""
+
+    def __init__(self, layers):
+        if not layers:
+            raise ValueError("no layers")
+        first = layers[0]
+        self.layers = list(layers)
+        self.b, self.act, self.map = first.b_out, first.act, first.map
+        self.device, self.torch_dtype = first.device, first.torch_dtype
+        for lay in self.layers:
+            if not lay.combined or lay.b_in != self.b or lay.b_out != self.b:
+                raise ValueError("every layer must have b_in == b_out == b dividing its sizes")
+            if lay.act != self.act or lay.map != self.map or lay.device != self.device:
+                raise ValueError("the layers must share the activation type, map and device")
+        f32 = dict(device=self.device, dtype=torch.float32)
+        n_theta = sum(lay.theta_R.numel() + lay.theta_P.numel() for lay in self.layers)
+        n_blk = sum(lay._blocks_f32.numel() for lay in self.layers)
+        self._theta = torch.empty(n_theta, **f32)
+        self._blocks_f32 = torch.empty(n_blk, **f32)
+        self._blocks_act = torch.empty(n_blk, device=self.device, dtype=self.torch_dtype)
+        self._q = torch.empty(n_blk, **f32) if self.map == "cnp" else None
+        ot = ob = 0
+        for lay in self.layers:
+            b = self.b
+            n_tR, n_tP = lay.theta_R.numel(), lay.theta_P.numel()
+            nR, nP = lay.nb_out * b * b, lay.nb_in * b * b
+            th = self._theta[ot:ot + n_tR + n_tP]
+            th.copy_(lay._theta[:n_tR + n_tP])
+            lay._theta = th
+            lay.theta_R = th[:n_tR].view(lay.nb_out, -1)
+            lay.theta_P = th[n_tR:].view(lay.nb_in, -1)
+            bf, ba = self._blocks_f32[ob:ob + nR + nP], self._blocks_act[ob:ob + nR + nP]
+            lay._blocks_f32, lay._blocks_act = bf, ba
+            lay.R_f32, lay.P_f32 = bf[:nR].view(lay.nb_out, b, b), bf[nR:].view(lay.nb_in, b, b)
+            lay.R_act, lay.P_act = ba[:nR].view(lay.nb_out, b, b), ba[nR:].view(lay.nb_in, b, b)
+            if self._q is not None:
+                q = self._q[ob:ob + nR + nP]
+                lay._q = q
+                lay.Q_R, lay.Q_P = q[:nR].view(lay.nb_out, b, b), q[nR:].view(lay.nb_in, b, b)
+            ot += n_tR + n_tP
+            ob += nR + nP
+        self.d_total = sum(lay.d_out + lay.d_in for lay in self.layers)
+        wsz = P.poetx_build_cnp_workspace_size if self.map == "cnp" else P.poetx_build_workspace_size
+        self._build_ws = torch.empty(max(wsz(self.d_total, self.b), 1), device=self.device,
+                                     dtype=torch.uint8)
+
+    def build(self, stream=None):
+        """One call: the R and P blocks of every layer."""
+        act_all = self._blocks_act if self.act == P.POETX_BF16 else None
+        if self.map == "cnp":
+            P.poetx_build_cnp(self._theta, self.d_total, self.b, self._q, self._blocks_f32,
+                              act_all, self.act, self._build_ws, stream)
+        else:
+            P.poetx_build_orthogonal(self._theta, self.d_total, self.b, self._blocks_f32, act_all,
+                                     self.act, self._build_ws, stream)

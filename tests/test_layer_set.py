@@ -1,0 +1,68 @@
+"""PoetxLinearSet: several layers' generators and blocks in shared buffers,
+built by one call."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from orthogonal_equivalence_amd.layer import PoetxLinear, PoetxLinearSet  # noqa: E402
+
+SHAPES = [(256, 384), (512, 128), (128, 640)]  # (d_in, d_out), multiples of b
+
+
+def _layers(device, b=128, act="bf16"):
+    rng = np.random.default_rng(5)
+    out = []
+    for n, m in SHAPES:
+        dt = torch.bfloat16 if act == "bf16" else torch.float32
+        W0 = torch.from_numpy(rng.standard_normal((m, n)) / np.sqrt(n)).to(dt)
+        lay = PoetxLinear(W0, b, b, act, device=device)
+        tri = b * (b - 1) // 2
+        lay.set_theta(torch.from_numpy(0.02 * rng.standard_normal((m // b, tri))).float(),
+                      torch.from_numpy(0.02 * rng.standard_normal((n // b, tri))).float())
+        out.append(lay)
+    return out
+
+
+def test_set_views_alias_the_shared_buffers_and_keep_theta():
+    layers = _layers("cpu")
+    before = [(lay.theta_R.clone(), lay.theta_P.clone()) for lay in layers]
+    s = PoetxLinearSet(layers)
+    base, end = s._theta.data_ptr(), s._theta.data_ptr() + s._theta.numel() * 4
+    prev_end = base
+    for lay, (tR, tP) in zip(layers, before):
+        assert torch.equal(lay.theta_R, tR) and torch.equal(lay.theta_P, tP)
+        # R generators, then P generators, layer after layer
+        assert lay.theta_R.data_ptr() == prev_end
+        assert lay.theta_P.data_ptr() == lay.theta_R.data_ptr() + lay.theta_R.numel() * 4
+        prev_end = lay.theta_P.data_ptr() + lay.theta_P.numel() * 4
+        blo = s._blocks_f32.data_ptr()
+        bhi = blo + s._blocks_f32.numel() * 4
+        assert blo <= lay.R_f32.data_ptr() < bhi
+        assert lay.P_f32.data_ptr() == lay.R_f32.data_ptr() + lay.R_f32.numel() * 4
+        assert lay.P_f32.data_ptr() + lay.P_f32.numel() * 4 <= bhi
+    assert prev_end == end
+    assert s.d_total == sum(n + m for n, m in SHAPES)
+
+
+def test_set_rejects_mixed_block_sizes():
+    a, b = _layers("cpu", b=128)[0], _layers("cpu", b=64)[1]
+    with pytest.raises(ValueError):
+        PoetxLinearSet([a, b])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("b", [128, 64])
+def test_set_build_equals_per_layer_builds(b):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ref = _layers("cuda", b=b)
+    for lay in ref:
+        lay.build()
+    grouped = _layers("cuda", b=b)
+    s = PoetxLinearSet(grouped)
+    s.build()
+    torch.cuda.synchronize()
+    for r, g in zip(ref, grouped):
+        for name in ("R_f32", "P_f32", "R_act", "P_act"):
+            assert torch.equal(getattr(r, name), getattr(g, name)), name
