@@ -1,8 +1,10 @@
-"""A POET-X linear layer on top of the libpoetx binding.
+"""POET-X linear layers on top of the libpoetx binding.
 
-Holds the device buffers of one layer (theta, orthogonal blocks, workspaces)
-allocated with torch and drives the three library calls. It allocates and
-calls; every step of the computation runs in libpoetx's kernels.
+PoetxLinear holds the device buffers of one layer (theta, orthogonal blocks,
+workspaces) allocated with torch and drives the three library calls;
+PoetxLinearSet puts several layers' generators and blocks into shared buffers
+so that one build call rebuilds all of them. Both allocate and call; every
+step of the computation runs in libpoetx's kernels.
 """
 from __future__ import annotations
 
