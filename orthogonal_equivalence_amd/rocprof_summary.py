@@ -12,6 +12,14 @@
       the counter instances of a dispatch), each scaled by what the same counter
       reads for a plain device copy of 1 GiB (read 1 GiB, write 1 GiB).
 
+  python -m orthogonal_equivalence_amd.rocprof_summary dispatches \
+      --mfma DIR --fetch DIR --write DIR --per-step N --stages NAME... \
+      --calibration profiles/dense_fwd_traffic.json --title "..." --command "..." > profile.txt
+      the last N dispatches (one step) in launch order: duration, MFMA
+      utilisation (the derived MfmaUtil counter: MFMA-busy SIMD cycles over
+      active cycles x SIMDs), and HBM bytes read and written (FETCH_SIZE and
+      WRITE_SIZE, scaled by the copy calibration) with the rate they imply.
+
 Reads CSV files only; nothing here touches the GPU.
 """
 import argparse
@@ -107,6 +115,56 @@ def traffic(args):
     print(json.dumps(res, indent=1))
 
 
+def _dispatch_rows(d, counter):
+    """{Dispatch_Id: (kernel, value summed over rows, start ns, end ns)}."""
+    rows = _csv_rows(d, "*counter_collection.csv")
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        k = int(r["Dispatch_Id"])
+        v = float(r["Counter_Value"])
+        if k in out:
+            name, acc, t0, t1 = out[k]
+            out[k] = (name, acc + v, t0, t1)
+        else:
+            out[k] = (r["Kernel_Name"], v, int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    return out
+
+
+def dispatches(args):
+    mf = _dispatch_rows(args.mfma, "MfmaUtil")
+    fe = _dispatch_rows(args.fetch, "FETCH_SIZE")
+    wr = _dispatch_rows(args.write, "WRITE_SIZE")
+    cal = json.load(open(args.calibration))["copy_calibration"]
+    ff, wf = cal["fetch_factor"], cal["write_factor"]
+    def last(d):
+        return [d[k] for k in sorted(d)][-args.per_step:]
+    m, f, w = last(mf), last(fe), last(wr)
+    stages = args.stages or [""] * len(m)
+    if not (len(m) == len(f) == len(w) == len(stages) == args.per_step):
+        raise SystemExit("dispatch counts differ between the passes")
+    out = [f"# rocprofv3 counter summary: {args.title}", "#",
+           "# commands (from the repository root, TMPDIR=/tmp):"]
+    out += [f"#   {c}" for c in args.command]
+    out += ["# one step, launch order; duration from the MfmaUtil pass's timestamps; bytes = counter",
+            f"# KiB x 1024 x the copy calibration (FETCH x{ff:.3f}, WRITE x{wf:.3f}); rate against 8 TB/s",
+            "",
+            f"{'stage':12s} {'us':>8s} {'MFMA %':>7s} {'read MB':>9s} {'write MB':>9s} {'TB/s':>6s} {'of 8':>5s}  kernel"]
+    tot_us = 0.0
+    for st, (name, util, t0, t1), (nf, kf, _, _), (nw, kw, _, _) in zip(stages, m, f, w):
+        if not (name == nf == nw):
+            raise SystemExit(f"kernel order differs between the passes: {name} / {nf} / {nw}")
+        us = (t1 - t0) / 1e3
+        tot_us += us
+        rd, wb = kf * 1024 * ff, kw * 1024 * wf
+        rate = (rd + wb) / (us * 1e-6) / 1e12 if us > 0 else 0.0
+        out.append(f"{st:12s} {us:8.1f} {util:7.1f} {rd / 1e6:9.1f} {wb / 1e6:9.1f} {rate:6.2f} "
+                   f"{rate / 8.0:5.2f}  {short_name(name, 80)}")
+    out.append(f"{'total':12s} {tot_us:8.1f}")
+    print("\n".join(out))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -126,8 +184,17 @@ def main(argv=None):
     r.add_argument("--sources", nargs="+", required=True)
     r.add_argument("--root", default=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     r.add_argument("--command", action="append", default=[])
+    g = sub.add_parser("dispatches")
+    g.add_argument("--mfma", required=True)
+    g.add_argument("--fetch", required=True)
+    g.add_argument("--write", required=True)
+    g.add_argument("--per-step", type=int, required=True)
+    g.add_argument("--stages", nargs="*", default=None)
+    g.add_argument("--calibration", required=True)
+    g.add_argument("--title", required=True)
+    g.add_argument("--command", action="append", default=[])
     a = ap.parse_args(argv)
-    (trace if a.cmd == "trace" else traffic)(a)
+    {"trace": trace, "traffic": traffic, "dispatches": dispatches}[a.cmd](a)
 
 
 if __name__ == "__main__":
