@@ -25,7 +25,11 @@
 // LDS layouts (16-byte chunks XOR-swizzled so that the fragment reads are
 // free of bank conflicts):
 //   K-major tile  [256 rows][32 k]  (64-byte rows): chunk c of row r at
-//                 c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
+//                 c ^ ((r >> 1) & 3). Measured on gfx950 (whose LDS returns
+//                 256 bytes per clock for these reads): this pattern of
+//                 ds_read_b128 fragment reads streams 234 B/clk per CU, while
+//                 c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)), r & 3, (r >> 2) & 3
+//                 or no swizzle all give 128 B/clk (two-way conflicts);
 //   N-major tile  [32 k][256 n]     (512-byte rows): chunk c of row k at
 //                 c ^ 2 (k & 3), read with the transposing ds_read_b64_tr_b16.
 // M and N must be at least 256 and K a multiple of 32: a tile that would
@@ -65,7 +69,7 @@ __device__ __forceinline__ int stage_off(int row, int col) {
 
 // swizzle of a K-major row: depends only on row % 16, so the fragments of
 // one wave (16-row steps) share one address pattern
-__device__ __forceinline__ int kmaj_swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int kmaj_swz(int row) { return (row >> 1) & 3; }
 __device__ __forceinline__ int kmaj_off(int row, int chunk) {
   return row * BK + ((chunk ^ kmaj_swz(row)) << 3);
 }
