@@ -390,11 +390,14 @@ panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
 // panel with the pivot block inverted by the first 256 threads in 4 x 4
 // register pieces (gj_invert_regs) and every 64 x 64 x 64 product on MFMA:
 //   pivot      D = A[p][p]          -> D^-1
-//   row        A[p][J]              -> W_J = D^-1 A[p][J]
-//   column     A[I][p] (= C_I)      -> -C_I D^-1
-//   the rest   A[I][J]              -> A[I][J] - C_I W_J
-// LDS holds D^-1 in both operand layouts, the row panel (B layout) and the
-// negated column panel (A layout).
+//   column     A[I][p] (= C_I)      -> C'_I = -C_I D^-1
+//   row        A[p][J]              -> D^-1 A[p][J]
+//   the rest   A[I][J]              -> A[I][J] + C'_I A[p][J]
+// The column panel goes first; the row panel and the rest then all read the
+// row panel as published, so they run together (three 64 x 64 x 64 products
+// per SIMD for NT = 4, against two then three when the rest waits for the
+// new row panel). LDS holds D^-1 in both operand layouts, the row panel
+// (B layout) and the column panel (A layout: -C_I, then C'_I).
 
 // acc[mi][ni] += A B for one wave's full 64 x 64 tile, K = 64, operands in
 // the permuted LDS layouts of a_off / b_off.
@@ -562,17 +565,19 @@ cayley_block_kernel(const float* __restrict__ theta, int nblocks, int last_valid
     }
     __syncthreads();
 
-    // pivot, row and column panels
+    // column panel C'_I = -A[I][p] D^-1 (sC holds -A[I][p]) and the pivot
+    // block D^-1; the wave of tile (I, p) is the only reader of sC tile I, so
+    // it overwrites it with C'_I once its product is done
 #pragma unroll
     for (int s = 0; s < TPW; ++s) {
       int I, J;
       tile_of<NT>(wave, s, I, J);
-      if (I != p && J != p) continue;
+      if (J != p) continue;
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) t[s][mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (I == p && J == p) {
+      if (I == p) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -580,36 +585,36 @@ cayley_block_kernel(const float* __restrict__ theta, int nblocks, int last_valid
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               t[s][mi][ni][e] = sDa[a_off(tile_row(mi, e, lane), tile_col(ni, lane))];
-      } else if (I == p) {
-        wave_mma64(sDa, sW + (J < p ? J : J - 1) * TILE, t[s], lane);
       } else {
-        wave_mma64(sC + (I < p ? I : I - 1) * TILE, sDb, t[s], lane);
+        float* cp = sC + (I < p ? I : I - 1) * TILE;
+        wave_mma64(cp, sDb, t[s], lane);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              cp[a_off(tile_row(mi, e, lane), tile_col(ni, lane))] = t[s][mi][ni][e];
       }
-    }
-    __syncthreads();  // the old row panel is no longer read
-#pragma unroll
-    for (int s = 0; s < TPW; ++s) {
-      int I, J;
-      tile_of<NT>(wave, s, I, J);
-      if (I != p || J == p) continue;
-      float* dst = sW + (J < p ? J : J - 1) * TILE;
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dst[b_off(tile_row(mi, e, lane), tile_col(ni, lane))] = t[s][mi][ni][e];
     }
     __syncthreads();
 
-    // trailing update A[I][J] += (-C_I) W_J
+    // row panel W_J = D^-1 A[p][J] and trailing update A[I][J] += C'_I A[p][J],
+    // both from the row panel as published
 #pragma unroll
     for (int s = 0; s < TPW; ++s) {
       int I, J;
       tile_of<NT>(wave, s, I, J);
-      if (I == p || J == p) continue;
-      wave_mma64(sC + (I < p ? I : I - 1) * TILE, sW + (J < p ? J : J - 1) * TILE, t[s], lane);
+      if (J == p) continue;
+      if (I == p) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) t[s][mi][ni] = floatx4{0.f, 0.f, 0.f, 0.f};
+        wave_mma64(sDa, sW + (J < p ? J : J - 1) * TILE, t[s], lane);
+      } else {
+        wave_mma64(sC + (I < p ? I : I - 1) * TILE, sW + (J < p ? J : J - 1) * TILE, t[s], lane);
+      }
     }
     __syncthreads();  // panels are rewritten by the next step (and by the staging below)
   }
