@@ -788,9 +788,31 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
       return r;
     return sg.end(1);
   };
+  // bf16, b = 256: B1 and B2 in one pass over g_Y (stage 0), then the
+  // gram's reduction (stage 1). Each Z element is read by the one workgroup
+  // that later writes g_Z at the same place, so Z may sit in the g_Z buffer.
+  auto fused_r = [&](const void* Z) -> hipError_t {
+    hipError_t r;
+    int ns = 0;
+    if ((r = sg.begin(0)) != hipSuccess) return r;
+    if ((r = poetx::launch_blockgramapply(gY, Rb, Z, gZ, partR, N, m, bR, plan.sR.nsplit, &ns, s)) !=
+        hipSuccess)
+      return r;
+    if ((r = sg.end(0)) != hipSuccess) return r;
+    if ((r = sg.begin(1)) != hipSuccess) return r;
+    if ((r = poetx::launch_split_reduce(partR, ns, nbR, bR, lastR, GR, gt, s, d->w_scale,
+                                        plan.subR)) != hipSuccess)
+      return r;
+    return sg.end(1);
+  };
+  const bool fuse_r = poetx::blockgramapply_supported(t, m, bR);
   if (z_saved) {
-    POETX_TRY(grad_r());
-    POETX_TRY(gram_r(z_saved));
+    if (fuse_r) {
+      POETX_TRY(fused_r(z_saved));
+    } else {
+      POETX_TRY(grad_r());
+      POETX_TRY(gram_r(z_saved));
+    }
   } else {
     // POET-Xmem: U = X P^T into the g_U buffer and Z = U W0^T into the g_Z
     // buffer (both overwritten later), the R gram on Z, then g_Z over Z
@@ -798,8 +820,12 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     POETX_TRY(block_apply(t, X, P_act, gU, N, n, bP, true, s, SB));
     POETX_TRY(dense(t, gU, Wmat, gZ, N, m, n, n, n, m, true, s));
     POETX_TRY(sg.end(7));
-    POETX_TRY(gram_r(gZ));
-    POETX_TRY(grad_r());
+    if (fuse_r) {
+      POETX_TRY(fused_r(gZ));
+    } else {
+      POETX_TRY(gram_r(gZ));
+      POETX_TRY(grad_r());
+    }
   }
 
   // B3: g_U = g_Z W0   (B(n, k) = W0[k][n])
@@ -807,17 +833,29 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   POETX_TRY(dense(t, gZ, Wmat, gU, N, n, m, m, n, n, false, s));
   POETX_TRY(sg.end(2));
 
-  // B4: G_P[j] = g_U[:, j]^T X[:, j]
-  POETX_TRY(sg.begin(3));
-  POETX_TRY(block_gram(t, gU, X, partP, N, n, bP, plan.sP, s));
-  POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, gt, s, nullptr,
-                                       plan.subP));
-  POETX_TRY(sg.end(3));
+  if (poetx::blockgramapply_supported(t, n, bP)) {
+    // B4 and B5 in one pass over g_U (stage 4), then the gram's reduction
+    // (stage 3)
+    int ns = 0;
+    POETX_TRY(sg.begin(4));
+    POETX_TRY(poetx::launch_blockgramapply(gU, P_act, X, gX, partP, N, n, bP, plan.sP.nsplit, &ns, s));
+    POETX_TRY(sg.end(4));
+    POETX_TRY(sg.begin(3));
+    POETX_TRY(poetx::launch_split_reduce(partP, ns, nbP, bP, lastP, GP, gt, s, nullptr, plan.subP));
+    POETX_TRY(sg.end(3));
+  } else {
+    // B4: G_P[j] = g_U[:, j]^T X[:, j]
+    POETX_TRY(sg.begin(3));
+    POETX_TRY(block_gram(t, gU, X, partP, N, n, bP, plan.sP, s));
+    POETX_TRY(poetx::launch_split_reduce(partP, plan.sP.nsplit, nbP, bP, lastP, GP, gt, s, nullptr,
+                                         plan.subP));
+    POETX_TRY(sg.end(3));
 
-  // B5: g_X = g_U blockdiag(P)
-  POETX_TRY(sg.begin(4));
-  POETX_TRY(block_apply(t, gU, P_act, gX, N, n, bP, false, s, SB));
-  POETX_TRY(sg.end(4));
+    // B5: g_X = g_U blockdiag(P)
+    POETX_TRY(sg.begin(4));
+    POETX_TRY(block_apply(t, gU, P_act, gX, N, n, bP, false, s, SB));
+    POETX_TRY(sg.end(4));
+  }
 
   // stage 9 (permutations only): g_x[:, perm_in[j]] = g_X[:, j]
   if (perm) {

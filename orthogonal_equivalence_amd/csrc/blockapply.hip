@@ -97,8 +97,13 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 }
 
 // B: block size (the K extent); NC: output columns per workgroup (B, or 256
-// at B = 512); TT: tokens per tile.
-template <int B, int NC, int TT, bool TRANS>
+// at B = 512); TT: tokens per tile. GRAM (B = 256, NC = 128, TT = 32, no
+// transpose): the workgroup also accumulates the gram
+//   part[split][blk][:, slab NC ..] = X[t, blk]^T C[t, blk cols slab NC ..]
+// over its tokens from the same input tiles (C's NC columns ride in each
+// ring slot after the input tile), so the backward's gradient apply and its
+// gram read the shared operand X once.
+template <int B, int NC, int TT, bool TRANS, bool GRAM = false>
 struct BlockApply {
   static constexpr int CB = NC / 128;         // 32-wide column blocks per wave
   static constexpr int KS = B / 16;           // MFMA K steps
@@ -106,7 +111,13 @@ struct BlockApply {
   static constexpr int STAGE = TT * B;        // elements of one input tile
   static constexpr int LPW = STAGE * 2 / 1024 / 4;  // 1 KB tile loads per wave
   static constexpr int CPT = TT * NC / 8 / kNT;     // 16-byte output chunks per thread
-  static_assert(STAGE <= kStage && TT % 32 == 0 && NC % 128 == 0 && CPT >= 1, "tile shape");
+  static constexpr int LPC = GRAM ? TT * NC * 2 / 1024 / 4 : 0;  // 1 KB C-tile loads per wave
+  static constexpr int LPT = LPW + LPC;             // loads per wave per tile
+  static_assert(STAGE + (GRAM ? TT * NC : 0) <= kStage && TT % 32 == 0 && NC % 128 == 0 && CPT >= 1,
+                "tile shape");
+  static_assert(!GRAM || (B == 256 && NC == 128 && TT == 32 && !TRANS), "gram variant shape");
+  // gram: 2 x 2 waves over the B x NC result, wave tile (B/2) x (NC/2)
+  static constexpr int GM = B / 2 / 32, GN = NC / 2 / 32;
 
   const bf16_t* X;
   bf16_t* Y;
@@ -114,6 +125,8 @@ struct BlockApply {
   int t_begin, t_end, ntiles;
   int tid, lane, wave, nw;
   bf16x8_t bfr[CB][KS];
+  const bf16_t* C;  // gram: first of this slab's C columns
+  floatx16 gacc[GRAM ? GM : 1][GRAM ? GN : 1];
 
   // Issues the LDS-bound loads of token tile `tile` into ring slot `dst`.
   __device__ __forceinline__ void load_tile(int tile, bf16_t* dst) {
@@ -127,6 +140,35 @@ struct BlockApply {
       const int grow = min(t0 + row, t_end - 1);  // rows past the end read a valid row
       dma16(X + (int64_t)grow * d + col0 + lch * 8, dst + Q * 512);
     }
+    if constexpr (GRAM) {
+#pragma unroll
+      for (int q = 0; q < LPC; ++q) {
+        const int Q = wave * LPC + q;
+        const int e = Q * 512 + lane * 8;
+        const int row = e / NC, pch = (e % NC) >> 3;
+        const int lch = pch ^ (row & 15);
+        const int grow = min(t0 + row, t_end - 1);
+        dma16(C + (int64_t)grow * d + lch * 8, dst + STAGE + Q * 512);
+      }
+    }
+  }
+
+  // gram fragment: 8 consecutive tokens (k) x 32 features (m) of a
+  // [token][feature] tile of width W, two transposing reads
+  template <int W>
+  __device__ __forceinline__ bf16x8_t gfrag(const bf16_t* tl, int m0, int k0, int ln) const {
+    const int g = ln >> 4, i = ln & 15;
+    const int m = m0 + 16 * (g & 1) + 4 * (i & 3);
+    short4_t h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int kk = k0 + 8 * (g >> 1) + 4 * hh + (i >> 2);
+      h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tl + sw<W>(kk, m)));
+    }
+    union { short4_t s[2]; bf16x8_t v; } u;
+    u.s[0] = h[0];
+    u.s[1] = h[1];
+    return u.v;
   }
 
   template <int S>
@@ -137,13 +179,39 @@ struct BlockApply {
     int ln = lane, td = tid;
     asm volatile("" : "+v"(ln), "+v"(td));
     // tile t is in LDS once at most (tiles issued after it) x LPW loads are pending
-    if (t + 2 < ntiles) wait_vm<2 * LPW>();
-    else if (t + 1 < ntiles) wait_vm<LPW>();
+    if (t + 2 < ntiles) wait_vm<2 * LPT>();
+    else if (t + 1 < ntiles) wait_vm<LPT>();
     else wait_vm<0>();
     // this wave's staging writes of tile t-1 have landed (s_waitcnt lgkmcnt(0))
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
     __builtin_amdgcn_s_barrier();  // every wave's part of tile t landed; slot of t-1 free
     if (t + 3 < ntiles) load_tile(t + 3, ring<(S + 3) & 3>());
+
+    if constexpr (GRAM) {
+      const int valid = t_end - (t_begin + t * TT);
+      if (valid < TT) {
+        // ragged last tile: rows past the end hold a repeated valid token;
+        // zero them in the input tile so they add nothing to the gram (their
+        // apply outputs are not stored)
+        for (int e = td; e < (TT - valid) * B; e += kNT) st[sw<B>(valid + e / B, e % B)] = 0;
+        __syncthreads();
+      }
+      const int wm = wave & 1, wn = wave >> 1;
+      const bf16_t* tc = st + STAGE;
+#pragma unroll
+      for (int kk = 0; kk < TT / 16; ++kk) {
+        bf16x8_t fa[GM], fc[GN];
+#pragma unroll
+        for (int i = 0; i < GM; ++i) fa[i] = gfrag<B>(st, wm * (B / 2) + 32 * i, 16 * kk, ln);
+#pragma unroll
+        for (int j = 0; j < GN; ++j) fc[j] = gfrag<NC>(tc, wn * (NC / 2) + 32 * j, 16 * kk, ln);
+#pragma unroll
+        for (int i = 0; i < GM; ++i)
+#pragma unroll
+          for (int j = 0; j < GN; ++j)
+            gacc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fc[j], gacc[i][j], 0, 0, 0);
+      }
+    }
 
     floatx16 acc[RB][CB];
 #pragma unroll
@@ -207,11 +275,14 @@ struct BlockApply {
 // Workgroup (split, blk, slab) for NSLAB = B / NC slabs per block: ids are
 // unit = split * nb + blk when NSLAB = 1, else 8 NSLAB g + 8 slab + r for
 // unit 8 g + r (the slabs of one unit 8 ids apart, on one XCD).
-template <int B, int NC, int TT, bool TRANS>
+template <int B, int NC, int TT, bool TRANS, bool GRAM = false>
 __global__ void __launch_bounds__(kNT)
-blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
-                  bf16_t* __restrict__ Y, int tokens, int64_t d, int nb, int nsplit, int tok_per_wg) {
-  typedef BlockApply<B, NC, TT, TRANS> K;
+blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb, bf16_t* Y, int tokens,
+                  int64_t d, int nb, int nsplit, int tok_per_wg, const bf16_t* C = nullptr,
+                  float* __restrict__ part = nullptr) {
+  // (Y and C may be one buffer in the gram variant: every element of C is
+  // read by the workgroup that writes Y at the same place, before it does)
+  typedef BlockApply<B, NC, TT, TRANS, GRAM> K;
   constexpr int NSLAB = B / NC;
   K k;
   k.tid = threadIdx.x;
@@ -237,6 +308,15 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
   k.ocol0 = k.col0 + slab * NC;
   k.nw = k.wave * (NC / 4);
   k.ntiles = (k.t_end - k.t_begin + TT - 1) / TT;
+  if constexpr (GRAM) {
+    k.C = C + k.ocol0;
+#pragma unroll
+    for (int i = 0; i < K::GM; ++i)
+#pragma unroll
+      for (int j = 0; j < K::GN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) k.gacc[i][j][e] = 0.f;
+  }
 
   // ---- this slab of M_k -> LDS (rows spread over the ring slots) -> register
   // fragments. TRANS needs rows slab NC .. of M (NC rows of B); otherwise the
@@ -309,6 +389,23 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
   __syncthreads();  // the last tile is staged
 #pragma unroll
   for (int q = 0; q < K::CPT; ++q) k.store_chunk(q, k.t_begin + (nt - 1) * TT, k.tid);
+  if constexpr (GRAM) {
+    // gram accumulators: lane l of fragment (i, j) holds rows
+    // 8 (e / 4) + 4 (l / 32) + e % 4 of the 32-row block and column l % 32
+    float* out = part + ((int64_t)split * nb + blk) * B * B + slab * NC;
+    const int wm = k.wave & 1, wn = k.wave >> 1, lane = k.lane;
+#pragma unroll
+    for (int i = 0; i < K::GM; ++i)
+#pragma unroll
+      for (int j = 0; j < K::GN; ++j) {
+        const int n = wn * (NC / 2) + 32 * j + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = wm * (B / 2) + 32 * i + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+          out[(int64_t)m * B + n] = k.gacc[i][j][e];
+        }
+      }
+  }
 }
 
 template <int B, int NC, int TT, bool TRANS>
@@ -365,6 +462,36 @@ hipError_t launch_superblocks(const void* blocks, int64_t nblocks, int b, int S,
   const int64_t grid = (nchunks + kNT - 1) / kNT;
   hipLaunchKernelGGL(superblock_kernel, dim3((unsigned)grid), dim3(kNT), 0, s,
                      static_cast<const bf16_t*>(blocks), b, S, nchunks, static_cast<bf16_t*>(out));
+  return hipGetLastError();
+}
+
+bool blockgramapply_supported(DType t, int64_t d, int b) {
+  return t == DType::BF16 && b == 256 && d % b == 0;
+}
+
+hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, void* Y, float* part,
+                                 int64_t tokens, int64_t d, int b, int max_split, int* nsplit,
+                                 hipStream_t s) {
+  constexpr int B = 256, NC = 128, TT = 32, NSLAB = B / NC;
+  if (b != B || d % B != 0 || tokens < 1 || max_split < 1) return hipErrorInvalidValue;
+  const int nb = (int)(d / B);
+  // one round of at most 256 workgroups, whole tiles per split, and no more
+  // splits than the caller's partial buffer holds
+  int splits = 256 / (nb * NSLAB);
+  const int max_tiles = (int)((tokens + TT - 1) / TT);
+  if (splits > max_tiles) splits = max_tiles;
+  if (splits > max_split) splits = max_split;
+  if (splits < 1) splits = 1;
+  int per = (int)((tokens + splits - 1) / splits);
+  per = (per + TT - 1) / TT * TT;
+  splits = (int)((tokens + per - 1) / per);  // every split holds at least one token
+  const int units = nb * splits;
+  const int grid = (units + 7) / 8 * (8 * NSLAB);
+  hipLaunchKernelGGL((blockapply_kernel<B, NC, TT, false, true>), dim3(grid), dim3(kNT), 0, s,
+                     static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(M),
+                     static_cast<bf16_t*>(Y), (int)tokens, d, nb, splits, per,
+                     static_cast<const bf16_t*>(C), part);
+  *nsplit = splits;
   return hipGetLastError();
 }
 

@@ -73,6 +73,15 @@ hipError_t launch_superblocks(const void* blocks, int64_t nblocks, int b, int S,
 hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,
                              bool transpose, hipStream_t s);
 
+// Gradient apply and gram of the backward in one pass over X (bf16, b = 256):
+//   Y[:, blk] = X[:, blk] M_blk   and   part[s][blk] = X[t, blk]^T C[t, blk]
+// summed over the tokens of split s. *nsplit (<= max_split) receives the
+// number of splits written; the splits cover the tokens in order.
+bool blockgramapply_supported(DType t, int64_t d, int b);
+hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, void* Y, float* part,
+                                 int64_t tokens, int64_t d, int b, int max_split, int* nsplit,
+                                 hipStream_t s);
+
 // ---- streaming token-reduction grams (bf16, b = 128, 256 or 512, b | d) ----
 // part[s][blk] = sum over tokens of split s (kchunk tokens each) of
 // A[t, blk]^T C[t, blk], float32 b x b; nsplit * kchunk >= tokens.

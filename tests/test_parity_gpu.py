@@ -123,6 +123,10 @@ SMALL_CASES = [
     # streaming kernels (128 divides d)
     ("bf16_b64_super", 384, 640, 64, 300, "bf16", 0.02),
     ("bf16_b32_super", 256, 384, 32, 200, "bf16", 0.05),
+    # b = 256: the backward's gradient apply and gram share one pass over g_Y
+    # (and over g_U); seven token splits, the last one ragged, and a padded
+    # last group of units
+    ("bf16_b256_splits", 768, 1280, 256, 2100, "bf16", 0.01),
 ]
 
 
