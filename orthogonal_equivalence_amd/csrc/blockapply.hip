@@ -34,6 +34,15 @@
 // the lane id, so none are hoisted out of the tile loop to hold registers
 // (322 VGPRs at b = 256, against 509 with the hoisted form).
 //
+// The backward's gradient apply and gram share their streamed operand (g_Y
+// for R, g_U for P). At b = 256 one launch does both: slab workgroups of 128
+// output columns (two per block and token range, 8 ids apart) also carry the
+// 32-token tile of C's matching 128 columns in each ring slot and accumulate
+// their 256 x 128 half of the gram X^T C (v_mfma_f32_32x32x16_bf16, the
+// fragments read with the transposing LDS read). The gradient is then read
+// from HBM about once instead of twice, and the gram partials are half as
+// many (half the token splits).
+//
 // Waits on the LDS-bound loads are explicit: before tile t, the wave waits
 // until at most (number of its tile loads issued after tile t) vector memory
 // operations are outstanding. Stores only add to that counter, so the wait is
