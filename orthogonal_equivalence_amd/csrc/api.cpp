@@ -788,14 +788,26 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
       return r;
     return sg.end(1);
   };
-  // bf16, b = 256: B1 and B2 in one pass over g_Y (stage 0), then the
-  // gram's reduction (stage 1). Each Z element is read by the one workgroup
-  // that later writes g_Z at the same place, so Z may sit in the g_Z buffer.
+  // Block size the one-pass gradient apply + gram runs at for a side (bf16,
+  // b = 128 or 256, or b = 32 / 64 as 128 x 128 super blocks), 0 if none.
+  auto one_pass_size = [&](int64_t dd, int bb) -> int {
+    if (const int S = poetx::superblock_size(t, dd, bb)) return S;
+    return poetx::blockgramapply_supported(t, dd, bb) ? bb : 0;
+  };
+  // B1 and B2 in one pass over g_Y (stage 0), then the gram's reduction
+  // (stage 1). Each Z element is read by the one workgroup that later writes
+  // g_Z at the same place, so Z may sit in the g_Z buffer.
+  const int opR = one_pass_size(m, bR);
   auto fused_r = [&](const void* Z) -> hipError_t {
     hipError_t r;
     int ns = 0;
     if ((r = sg.begin(0)) != hipSuccess) return r;
-    if ((r = poetx::launch_blockgramapply(gY, Rb, Z, gZ, partR, N, m, bR, plan.sR.nsplit, &ns, s)) !=
+    const void* Mr = Rb;
+    if (opR != bR) {
+      if ((r = poetx::launch_superblocks(Rb, nbR, bR, opR, SB, s)) != hipSuccess) return r;
+      Mr = SB;
+    }
+    if ((r = poetx::launch_blockgramapply(gY, Mr, Z, gZ, partR, N, m, opR, plan.sR.nsplit, &ns, s)) !=
         hipSuccess)
       return r;
     if ((r = sg.end(0)) != hipSuccess) return r;
@@ -805,7 +817,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
       return r;
     return sg.end(1);
   };
-  const bool fuse_r = poetx::blockgramapply_supported(t, m, bR);
+  const bool fuse_r = opR != 0;
   if (z_saved) {
     if (fuse_r) {
       POETX_TRY(fused_r(z_saved));
@@ -833,12 +845,17 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   POETX_TRY(dense(t, gZ, Wmat, gU, N, n, m, m, n, n, false, s));
   POETX_TRY(sg.end(2));
 
-  if (poetx::blockgramapply_supported(t, n, bP)) {
+  if (const int opP = one_pass_size(n, bP)) {
     // B4 and B5 in one pass over g_U (stage 4), then the gram's reduction
     // (stage 3)
     int ns = 0;
     POETX_TRY(sg.begin(4));
-    POETX_TRY(poetx::launch_blockgramapply(gU, P_act, X, gX, partP, N, n, bP, plan.sP.nsplit, &ns, s));
+    const void* Mp = P_act;
+    if (opP != bP) {
+      POETX_TRY(poetx::launch_superblocks(P_act, nbP, bP, opP, SB, s));
+      Mp = SB;
+    }
+    POETX_TRY(poetx::launch_blockgramapply(gU, Mp, X, gX, partP, N, n, opP, plan.sP.nsplit, &ns, s));
     POETX_TRY(sg.end(4));
     POETX_TRY(sg.begin(3));
     POETX_TRY(poetx::launch_split_reduce(partP, ns, nbP, bP, lastP, GP, gt, s, nullptr, plan.subP));

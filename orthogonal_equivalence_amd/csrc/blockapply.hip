@@ -124,7 +124,9 @@ struct BlockApply {
   static constexpr int LPT = LPW + LPC;             // loads per wave per tile
   static_assert(STAGE + (GRAM ? TT * NC : 0) <= kStage && TT % 32 == 0 && NC % 128 == 0 && CPT >= 1,
                 "tile shape");
-  static_assert(!GRAM || (B == 256 && NC == 128 && TT == 32 && !TRANS), "gram variant shape");
+  static_assert(!GRAM || (!TRANS && ((B == 256 && NC == 128 && TT == 32) ||
+                                      (B == 128 && NC == 128 && TT == 64))),
+                "gram variant shape");
   // gram: 2 x 2 waves over the B x NC result, wave tile (B/2) x (NC/2)
   static constexpr int GM = B / 2 / 32, GN = NC / 2 / 32;
 
@@ -475,14 +477,13 @@ hipError_t launch_superblocks(const void* blocks, int64_t nblocks, int b, int S,
 }
 
 bool blockgramapply_supported(DType t, int64_t d, int b) {
-  return t == DType::BF16 && b == 256 && d % b == 0;
+  return t == DType::BF16 && (b == 128 || b == 256) && d % b == 0;
 }
 
-hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, void* Y, float* part,
-                                 int64_t tokens, int64_t d, int b, int max_split, int* nsplit,
-                                 hipStream_t s) {
-  constexpr int B = 256, NC = 128, TT = 32, NSLAB = B / NC;
-  if (b != B || d % B != 0 || tokens < 1 || max_split < 1) return hipErrorInvalidValue;
+template <int B, int NC, int TT>
+hipError_t launch_gram_b(const void* X, const void* M, const void* C, void* Y, float* part,
+                         int64_t tokens, int64_t d, int max_split, int* nsplit, hipStream_t s) {
+  constexpr int NSLAB = B / NC;
   const int nb = (int)(d / B);
   // one round of at most 256 workgroups, whole tiles per split, and no more
   // splits than the caller's partial buffer holds
@@ -495,13 +496,21 @@ hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, vo
   per = (per + TT - 1) / TT * TT;
   splits = (int)((tokens + per - 1) / per);  // every split holds at least one token
   const int units = nb * splits;
-  const int grid = (units + 7) / 8 * (8 * NSLAB);
+  const int grid = NSLAB == 1 ? units : (units + 7) / 8 * (8 * NSLAB);
   hipLaunchKernelGGL((blockapply_kernel<B, NC, TT, false, true>), dim3(grid), dim3(kNT), 0, s,
                      static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(M),
                      static_cast<bf16_t*>(Y), (int)tokens, d, nb, splits, per,
                      static_cast<const bf16_t*>(C), part);
   *nsplit = splits;
   return hipGetLastError();
+}
+
+hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, void* Y, float* part,
+                                 int64_t tokens, int64_t d, int b, int max_split, int* nsplit,
+                                 hipStream_t s) {
+  if ((b != 128 && b != 256) || d % b != 0 || tokens < 1 || max_split < 1) return hipErrorInvalidValue;
+  if (b == 256) return launch_gram_b<256, 128, 32>(X, M, C, Y, part, tokens, d, max_split, nsplit, s);
+  return launch_gram_b<128, 128, 64>(X, M, C, Y, part, tokens, d, max_split, nsplit, s);
 }
 
 bool blockapply_supported(DType t, int64_t d, int b) {
