@@ -108,9 +108,10 @@ typedef struct poetx_linear_desc {
    * GEMM, 3 P gram (+ reduction), 4 grad to x, 5 Cayley VJP of R,
    * 6 Cayley VJP of P, 7 recompute of Z (POETX_RECOMPUTE_Z only; it runs
    * first, and stage 1 then runs before stage 0). Where the gradient apply
-   * and the gram of a side share one pass (bf16, b = 256), stage 0 (R side)
-   * or 4 (P side) holds that pass and stage 1 or 3 the gram's reduction
-   * alone, run after it. With permutations, forward
+   * and the gram of a side share one pass (bf16 with b = 128 or 256, or
+   * b = 32 / 64 when 128 divides the side's width), stage 0 (R side) or 4
+   * (P side) holds that pass and stage 1 or 3 the gram's reduction alone,
+   * run after it. With permutations, forward
    * stage 3 gathers x and stage 4 scatters y; backward stage 8 gathers g_y
    * and x and stage 9 scatters g_x. With an INT8 weight, forward stage 5 and
    * backward stage 10 widen the codes and scale R's block columns. A NULL

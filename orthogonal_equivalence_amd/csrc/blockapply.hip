@@ -35,13 +35,16 @@
 // (322 VGPRs at b = 256, against 509 with the hoisted form).
 //
 // The backward's gradient apply and gram share their streamed operand (g_Y
-// for R, g_U for P). At b = 256 one launch does both: slab workgroups of 128
-// output columns (two per block and token range, 8 ids apart) also carry the
-// 32-token tile of C's matching 128 columns in each ring slot and accumulate
-// their 256 x 128 half of the gram X^T C (v_mfma_f32_32x32x16_bf16, the
-// fragments read with the transposing LDS read). The gradient is then read
-// from HBM about once instead of twice, and the gram partials are half as
-// many (half the token splits).
+// for R, g_U for P), so one launch does both (GRAM): each ring slot also
+// carries the tile of C's columns matching the workgroup's output columns,
+// and the workgroup accumulates that part of the gram X^T C
+// (v_mfma_f32_32x32x16_bf16, fragments read with the transposing LDS read).
+// At b = 128 a workgroup holds the whole block and its whole 128 x 128 gram
+// (64-token tiles), so every operand crosses the CU once. At b = 256 the
+// block and the gram together would need about 450 registers, so two slab
+// workgroups of 128 output columns (8 ids apart) each take 32-token tiles of
+// all 256 input columns and their 256 x 128 half of the gram: the gradient
+// still comes from HBM about once, and the gram partials are half as many.
 //
 // Waits on the LDS-bound loads are explicit: before tile t, the wave waits
 // until at most (number of its tile loads issued after tile t) vector memory

@@ -73,7 +73,8 @@ hipError_t launch_superblocks(const void* blocks, int64_t nblocks, int b, int S,
 hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,
                              bool transpose, hipStream_t s);
 
-// Gradient apply and gram of the backward in one pass over X (bf16, b = 256):
+// Gradient apply and gram of the backward in one pass over X (bf16, b = 128
+// or 256):
 //   Y[:, blk] = X[:, blk] M_blk   and   part[s][blk] = X[t, blk]^T C[t, blk]
 // summed over the tokens of split s. *nsplit (<= max_split) receives the
 // number of splits written; the splits cover the tokens in order.
