@@ -332,25 +332,39 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb, b
         for (int e = 0; e < 16; ++e) k.gacc[i][j][e] = 0.f;
   }
 
-  // ---- this slab of M_k -> LDS (rows spread over the ring slots) -> register
-  // fragments. TRANS needs rows slab NC .. of M (NC rows of B); otherwise the
-  // columns slab NC .. of every row (B rows of NC).
-  {
-    const bf16_t* Mk = Mb + (int64_t)blk * B * B;
-    constexpr int SR = TRANS ? NC : B;       // staged rows
-    constexpr int SW = TRANS ? B : NC;       // staged row width
-    constexpr int ROWS_PER_SLOT = kStage / SW;
-    constexpr int PASS_ROWS = 4 * ROWS_PER_SLOT < SR ? 4 * ROWS_PER_SLOT : SR;
-    constexpr int NPASS = SR / PASS_ROWS;    // the ring holds PASS_ROWS rows at a time
-    static_assert(NPASS * PASS_ROWS == SR, "whole passes");
-    const bf16_t* src0 = TRANS ? Mk + (int64_t)slab * NC * B : Mk + slab * NC;
+  const int nt = k.ntiles;
+  if constexpr (TRANS) {
+    // B(n, k) = M[n][k]: fragment (j, ks) of lane l is 8 consecutive k
+    // (16 ks + 8 (l / 32) ..) of slab row nw + 32 j + l % 32, one 16-byte
+    // global load each, issued after the first token tiles so that both are
+    // in flight together (no LDS staging pass, no barriers before tile 0)
+    k.load_tile(0, ring<0>());
+    if (nt > 1) k.load_tile(1, ring<1>());
+    if (nt > 2) k.load_tile(2, ring<2>());
+    const bf16_t* mrow = Mb + (int64_t)blk * B * B + (int64_t)(slab * NC + k.nw + (k.lane & 31)) * B +
+                         8 * (k.lane >> 5);
+#pragma unroll
+    for (int j = 0; j < K::CB; ++j)
+#pragma unroll
+      for (int ks = 0; ks < K::KS; ++ks)
+        k.bfr[j][ks] = *reinterpret_cast<const bf16x8_t*>(mrow + (int64_t)(32 * j) * B + 16 * ks);
+  } else {
+    // B(n, k) = M[k][n]: the columns slab NC .. of every row of M_k go to LDS
+    // (rows spread over the ring slots, in passes when they do not fit), and
+    // each fragment (8 consecutive k of column n) comes back with two
+    // transposing reads of 4 k each
+    const bf16_t* src0 = Mb + (int64_t)blk * B * B + slab * NC;
+    constexpr int ROWS_PER_SLOT = kStage / NC;
+    constexpr int PASS_ROWS = 4 * ROWS_PER_SLOT < B ? 4 * ROWS_PER_SLOT : B;
+    constexpr int NPASS = B / PASS_ROWS;    // the ring holds PASS_ROWS rows at a time
+    static_assert(NPASS * PASS_ROWS == B, "whole passes");
     const int lane = k.lane;
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
-      for (int c = k.tid; c < PASS_ROWS * SW / 8; c += kNT) {
-        const int row = c / (SW / 8), ch = c % (SW / 8);
+      for (int c = k.tid; c < PASS_ROWS * NC / 8; c += kNT) {
+        const int row = c / (NC / 8), ch = c % (NC / 8);
         bf16_t* slot = ring_rt(row / ROWS_PER_SLOT);
-        *reinterpret_cast<uint4*>(slot + sw<SW>(row % ROWS_PER_SLOT, ch * 8)) =
+        *reinterpret_cast<uint4*>(slot + sw<NC>(row % ROWS_PER_SLOT, ch * 8)) =
             *reinterpret_cast<const uint4*>(src0 + (int64_t)(pass * PASS_ROWS + row) * B + ch * 8);
       }
       __syncthreads();
@@ -358,38 +372,27 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb, b
       for (int j = 0; j < K::CB; ++j)
 #pragma unroll
         for (int ks = 0; ks < K::KS; ++ks) {
-          if (TRANS) {  // B(n, k) = M[n][k]: 8 consecutive k of row n
-            // rows nw + 32 j .. + 31 lie in one pass (wave-uniform test)
-            if ((k.nw + 32 * j) / PASS_ROWS != pass) continue;
-            const int n = k.nw + 32 * j + (lane & 31) - pass * PASS_ROWS;
-            const int kk = 16 * ks + 8 * (lane >> 5);
-            k.bfr[j][ks] = *reinterpret_cast<const bf16x8_t*>(ring_rt(n / ROWS_PER_SLOT) +
-                                                              sw<SW>(n % ROWS_PER_SLOT, kk));
-          } else {      // B(n, k) = M[k][n]: two transposing reads of 4 k each
-            if ((16 * ks) / PASS_ROWS != pass) continue;
-            const int g = lane >> 4, i = lane & 15;
-            const int n = k.nw + 32 * j + 16 * (g & 1) + 4 * (i & 3);
-            short4_t h[2];
+          if ((16 * ks) / PASS_ROWS != pass) continue;
+          const int g = lane >> 4, i = lane & 15;
+          const int n = k.nw + 32 * j + 16 * (g & 1) + 4 * (i & 3);
+          short4_t h[2];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int kk = 16 * ks + 8 * (g >> 1) + 4 * hh + (i >> 2) - pass * PASS_ROWS;
-              h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_short4*)(ring_rt(kk / ROWS_PER_SLOT) + sw<SW>(kk % ROWS_PER_SLOT, n)));
-            }
-            union { short4_t s[2]; bf16x8_t v; } u;
-            u.s[0] = h[0];
-            u.s[1] = h[1];
-            k.bfr[j][ks] = u.v;
+          for (int hh = 0; hh < 2; ++hh) {
+            const int kk = 16 * ks + 8 * (g >> 1) + 4 * hh + (i >> 2) - pass * PASS_ROWS;
+            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4*)(ring_rt(kk / ROWS_PER_SLOT) + sw<NC>(kk % ROWS_PER_SLOT, n)));
           }
+          union { short4_t s[2]; bf16x8_t v; } u;
+          u.s[0] = h[0];
+          u.s[1] = h[1];
+          k.bfr[j][ks] = u.v;
         }
       __syncthreads();  // the ring is restaged, then reused for token tiles
     }
+    k.load_tile(0, ring<0>());
+    if (nt > 1) k.load_tile(1, ring<1>());
+    if (nt > 2) k.load_tile(2, ring<2>());
   }
-
-  const int nt = k.ntiles;
-  k.load_tile(0, ring<0>());
-  if (nt > 1) k.load_tile(1, ring<1>());
-  if (nt > 2) k.load_tile(2, ring<2>());
   int t = 0;
   for (; t + 4 <= nt; t += 4) {
     k.template tile<0>(t);
