@@ -10,13 +10,15 @@
 //
 // These products are HBM-bound (about b/2 flop per byte), so the kernel is
 // built to stream: one workgroup owns one block and a contiguous token range
-// (about one workgroup per CU). It loads M_k once (through LDS, using the
-// gfx950 transposing LDS read ds_read_b64_tr_b16 when the fragments need M_k's
-// columns) and keeps it in registers as MFMA B fragments: wave w owns output
-// columns [w b/4, (w+1) b/4). At b = 512 the block (512 KB) does not fit one
+// (about one workgroup per CU). It loads M_k once and keeps it in registers
+// as MFMA B fragments: wave w owns output columns [w b/4, (w+1) b/4). With the
+// transpose a fragment is part of one row of M_k, loaded straight from global
+// memory while the first token tiles are in flight; otherwise it is part of a
+// column, so M_k goes through LDS and comes back with the gfx950 transposing
+// LDS read ds_read_b64_tr_b16. At b = 512 the block (512 KB) does not fit one
 // CU's registers: two workgroups share a block and token range, each holding
 // the 256 output columns of its slab (512 x 256 bf16, 256 KB: 256 VGPRs per
-// lane, staged through the LDS ring in two passes) and streaming 32-token
+// lane; through the LDS ring in two passes when staged) and streaming 32-token
 // tiles of all 512 input columns; the two are launched 8 workgroup ids apart,
 // so they run on one XCD at about the same time and the input tile they both
 // read comes from HBM about once. (Four 128-column slabs per block were ~10 %
