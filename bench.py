@@ -43,6 +43,8 @@ FWD_STAGES = ["p_apply", "dense_fwd", "r_apply"]
 FWD_PERM_STAGES = ["gather_x", "scatter_y"]
 FWD_INT8_STAGE = 5       # widen the INT8 codes, scale R's block columns
 BWD_INT8_STAGE = 10
+# Where a side's gradient apply and gram share one launch (bf16, b = 32-256),
+# grad_r / grad_x time that launch and gram_r / gram_p the gram's reduction.
 BWD_STAGES = ["grad_r", "gram_r", "dense_bwd", "gram_p", "grad_x", "vjp_r", "vjp_p"]
 BWD_PERM_STAGES = ["gather_gy_x", "scatter_gx"]
 
