@@ -8,16 +8,21 @@ layer of the workload, with all inputs resident in HBM. The default workload
 is the 8B-class MLP up-projection: W0 14336 x 4096 (out x in), b = 256,
 8192 tokens, bf16 storage with float32 accumulation.
 
+Order of work: the float64 oracle on the host's cores (a bounded token
+sample, timed before any GPU timing), W warm-up steps, K timed steps (mean
+and median per step), K "cold" steps each after a 512 MB scratch write that
+evicts the Infinity Cache, K instrumented steps for the per-stage breakdown,
+then a sampled parity check of every layer against the oracle.
+
 Prints ONE JSON line: tokens/s of the whole step, the roofline of the
 dominant kernel (the dense W0 GEMM of the forward, timed live with HIP events
-on the launch stream), the layer's algorithmic roofline fraction, a sampled
-parity check against the oracle, and the oracle's own throughput on the
-host's cores on a bounded token sample.
+on the launch stream), the layer's algorithmic roofline fraction, the cold
+variant, the parity sample and the oracle's own throughput.
 
 Each event record puts a few microseconds between two kernels, so the timed
-steps hold only the event pair around the dominant kernel; the per-stage
-breakdown (stages_ms, instrumented_step_ms) comes from as many further steps
-with an event pair around every stage.
+steps hold only an event at every step boundary and the pair around the
+dominant kernel; the per-stage breakdown (stages_ms, instrumented_step_ms)
+comes from as many further steps with an event pair around every stage.
 """
 from __future__ import annotations
 
@@ -69,9 +74,15 @@ def cpu_baseline(spec, sample_tokens, map="cayley", permute=False, int8=False):
 
     import oracle.poetx_oracle as O
     from orthogonal_equivalence_amd.inputs import make_layer, make_permutations
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max(i.get("num_threads", 1) for i in info) if info else 1
+        if info:
+            i = info[0]
+            blas = (f"{i.get('internal_api', '?')} {i.get('version', '?')} "
+                    f"({os.path.basename(i.get('filepath', '?'))}, {i.get('num_threads', '?')} threads)")
     except Exception:  # noqa: BLE001
         threads = os.cpu_count()
     L = make_layer(spec)
@@ -90,11 +101,23 @@ def cpu_baseline(spec, sample_tokens, map="cayley", permute=False, int8=False):
         if dt >= 10.0 or reps >= 6:
             break
     return {"value": reps * sample_tokens / dt, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas": blas, "timed": "before the GPU timing, same process",
             "sample": f"{reps} float64 oracle steps (exact Cayley solves, block-local "
                       f"materialisation of R W0 P, forward, backward) on the first "
                       f"{sample_tokens} of {spec.tokens} tokens of {spec.name} "
                       f"{spec.d_out}x{spec.d_in} b={spec.b}; {dt:.1f} s"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def parity_sample(L, out, lay, rows=32, map="cayley", perms=None, int8=False):
@@ -223,7 +246,7 @@ def main():
                    torch.empty(s.tokens, s.d_out, dtype=tdt[s.dtype], device=dev),
                    g_x=torch.empty(s.tokens, s.d_in, dtype=tdt[s.dtype], device=dev),
                    gR=torch.empty_like(lay.theta_R), gP=torch.empty_like(lay.theta_P))
-        layers.append((s, L if len(specs) == 1 else None, lay, x, g_y, out))
+        layers.append((s, L, lay, x, g_y, out))
     # a workload of several layers with one block size rebuilds all of their
     # blocks with one call (the same work, batched), as a training step would
     layer_set = None
@@ -276,6 +299,13 @@ def main():
         return [{"build": e["build"], "fwd": [x.handle for x in e["fwd"]],
                  "bwd": [x.handle for x in e["bwd"]]} for e in ev]
 
+    # ---- the oracle on the host's cores, before any GPU timing
+    cpu = None
+    if args.cpu_sample > 0:
+        cpu = cpu_baseline(specs[-1] if len(specs) == 1 else specs[0],
+                           min(args.cpu_sample, specs[0].tokens), map=args.map,
+                           permute=args.permute, int8=args.int8)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -286,29 +316,46 @@ def main():
 
     # ---- timed region: K steps bracketed by synchronize. Each event record
     # puts a few microseconds between two kernels, so the only ones inside are
-    # the pair around the dominant kernel's launch (its live duration).
+    # one at every step boundary (per-step times, for the median) and the
+    # pair around the dominant kernel's launch (its live duration).
     dense_ev = [(P.Event(), P.Event()) for _ in range(args.steps)]
     timed_handles = []
     for k in range(args.steps):
         fwd_ev = [None] * (2 * dense_stage) + [dense_ev[k][0].handle, dense_ev[k][1].handle]
         timed_handles.append([{"build": None, "fwd": fwd_ev if li == big else None, "bwd": None}
                               for li in range(len(layers))])
-    t_start, t_stop = P.Event(), P.Event()
+    bound = [P.Event() for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record(stream)
+    bound[0].record(stream)
     for k in range(args.steps):
         step(timed_handles[k])
-    t_stop.record(stream)
-    t_stop.synchronize()
+        bound[k + 1].record(stream)
+    bound[-1].synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    total_ms = t_start.elapsed_ms(t_stop)
+    total_ms = bound[0].elapsed_ms(bound[-1])
     ms_per_step = total_ms / args.steps
+    timed_ms = [bound[k].elapsed_ms(bound[k + 1]) for k in range(args.steps)]
     tokens = specs[0].tokens
     value = tokens / (ms_per_step / 1e3)
     dense_ms = statistics.mean(a.elapsed_ms(b) for a, b in dense_ev)
+
+    # ---- cold variant: K more steps, each after a 512 MB scratch write (more
+    # than the 256 MB Infinity Cache), so W0 and the activations are not left
+    # resident by the previous step; the write itself is outside the events
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_ev = [(P.Event(), P.Event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        scratch.fill_(k & 0xFF)
+        cold_ev[k][0].record(stream)
+        step()
+        cold_ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    cold_ms = [a.elapsed_ms(b) for a, b in cold_ev]
+    del scratch
 
     # ---- stage breakdown: K more steps with an event pair around every stage
     # and every step (slower than the timed steps by the records themselves)
@@ -348,8 +395,11 @@ def main():
     achieved = dense_flops / (dense_ms / 1e3)
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": measured_traffic(),
+                "traffic_kind": "L2-miss bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a "
+                                "plain copy): requests leaving the L2, answered by the Infinity "
+                                "Cache or HBM; null when the kernel changed since the passes",
                 "kernel": "dense_fwd: Z = U W0^T (dense_kernel<true>: bf16, K-major W0, "
-                          "persistent, direct-to-LDS, 16x16x32 MFMA)",
+                          "persistent, direct-to-LDS, 4 waves of 128x128, 16x16x32 MFMA)",
                 "flops_per_launch": dense_flops, "avg_launch_ms": dense_ms}
 
     F = sum(layer_work(s)[0] for s, *_ in layers)
@@ -358,6 +408,8 @@ def main():
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "ms_per_step_median": statistics.median(timed_ms),
+        "ms_per_step_min": min(timed_ms), "ms_per_step_max": max(timed_ms),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": specs[0].dtype, "data": "synthetic (seeded N(0,1) activations, N(0,1/d_in) W0, "
                                           "N(0, sigma^2) generators)",
@@ -377,20 +429,26 @@ def main():
                            "frac": t_roof / (ms_per_step / 1e3),
                            "tflops": F / (ms_per_step / 1e3) / 1e12},
         "wall_s": wall,
+        "cold": {"what": "the same step after a 512 MB scratch write (evicts the Infinity "
+                         "Cache); one event pair around each step",
+                 "ms_per_step_median": statistics.median(cold_ms),
+                 "ms_per_step_mean": statistics.mean(cold_ms),
+                 "ms_per_step_min": min(cold_ms), "ms_per_step_max": max(cold_ms),
+                 "tokens_per_s_median": tokens / (statistics.median(cold_ms) / 1e3)},
         # from the instrumented steps that follow the timed ones
         "instrumented_step_ms": {"median": statistics.median(step_ms), "min": min(step_ms),
                                  "max": max(step_ms)},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
     }
-    if not args.no_parity and len(layers) == 1:
-        s, L, lay, x, g_y, o = layers[0]
-        res["parity"] = parity_sample(L, dict(y=o["y"], g_x=o["g_x"]), lay, map=args.map,
-                                      perms=make_permutations(s) if args.permute else None,
-                                      int8=args.int8)
-    if args.cpu_sample > 0:
-        res["cpu_baseline"] = cpu_baseline(specs[-1] if len(specs) == 1 else specs[0],
-                                           min(args.cpu_sample, specs[0].tokens), map=args.map,
-                                           permute=args.permute, int8=args.int8)
+    if not args.no_parity:
+        par = {}
+        for s, L, lay, x, g_y, o in layers:
+            par[s.name] = parity_sample(L, dict(y=o["y"], g_x=o["g_x"]), lay, map=args.map,
+                                        perms=make_permutations(s) if args.permute else None,
+                                        int8=args.int8)
+        res["parity"] = par[specs[0].name] if len(layers) == 1 else par
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     res["gpu"] = torch.cuda.get_device_name(0)
     print(json.dumps(res), flush=True)
 

@@ -445,8 +445,9 @@ int poetx_build_orthogonal(const float* theta, int64_t d, int32_t b, float* bloc
   const Range out_act = range_of(blocks_act, act == POETX_BF16 ? blocks_bytes / 2 : 0);
   const Range in_theta = range_of(theta, (size_t)poetx_theta_count(d, b) * 4);
   const Range r_ws = range_of(ws, need);
+  // the workspace is written too, so it may not overlap theta either
   if (overlap(out_f32, in_theta) || overlap(out_f32, r_ws) || overlap(out_act, in_theta) ||
-      overlap(out_act, r_ws) || overlap(out_f32, out_act))
+      overlap(out_act, r_ws) || overlap(out_f32, out_act) || overlap(r_ws, in_theta))
     return POETX_ERR_ALIAS;
   const int last = (int)(d - (nb - 1) * b);
   return hip_status(poetx::launch_cayley_build(theta, nb, b, last, blocks_f32, blocks_act,
@@ -482,6 +483,7 @@ int poetx_build_cnp(const float* theta, int64_t d, int32_t b, float* q_f32, floa
   const Range in_theta = range_of(theta, (size_t)poetx_theta_count(d, b) * 4);
   const Range r_ws = range_of(ws, need);
   const Range outs[] = {out_q, out_f32, out_act};
+  if (overlap(r_ws, in_theta)) return POETX_ERR_ALIAS;  // the workspace is written
   for (int i = 0; i < 3; ++i) {
     if (overlap(outs[i], in_theta) || overlap(outs[i], r_ws)) return POETX_ERR_ALIAS;
     for (int j = i + 1; j < 3; ++j)
@@ -590,15 +592,17 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   const int64_t nbR = ceil_div(m, d->b_out), nbP = ceil_div(n, d->b_in);
   const Range r_y = range_of(y, N * m * es);
   const Range r_z = z_save ? range_of(z_save, N * m * es) : Range{0, 0};
+  // written: y, z and the workspace; read: everything else
+  const Range r_ws = range_of(ws, plan.total);
   const Range ins[] = {range_of(x, N * n * es), range_of(W0, weight_bytes(d)),
                        range_of(R_act, nbR * d->b_out * d->b_out * es),
-                       range_of(P_act, nbP * d->b_in * d->b_in * es), range_of(ws, plan.total),
+                       range_of(P_act, nbP * d->b_in * d->b_in * es),
                        range_of(d->perm_in, permuted(d) ? n * 4 : 0),
                        range_of(d->perm_out, permuted(d) ? m * 4 : 0),
                        range_of(d->w_scale, int8_weight(d) ? m * 4 : 0)};
   for (const Range& r : ins)
-    if (overlap(r, r_y) || overlap(r, r_z)) return POETX_ERR_ALIAS;
-  if (overlap(r_y, r_z)) return POETX_ERR_ALIAS;
+    if (overlap(r, r_y) || overlap(r, r_z) || overlap(r, r_ws)) return POETX_ERR_ALIAS;
+  if (overlap(r_y, r_z) || overlap(r_y, r_ws) || overlap(r_z, r_ws)) return POETX_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const DType t = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
@@ -693,15 +697,16 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   const int64_t N = d->tokens, n = d->d_in, m = d->d_out;
   const int bR = d->b_out, bP = d->b_in;
   const int64_t nbR = ceil_div(m, bR), nbP = ceil_div(n, bP);
+  // written: g_x, both g_theta and the workspace; read: everything else
   const Range outs[] = {range_of(g_x, N * n * es),
                         range_of(g_theta_R, (size_t)poetx_theta_count(m, bR) * 4),
-                        range_of(g_theta_P, (size_t)poetx_theta_count(n, bP) * 4)};
+                        range_of(g_theta_P, (size_t)poetx_theta_count(n, bP) * 4),
+                        range_of(ws, plan.total)};
   const Range ins[] = {range_of(g_y, N * m * es), range_of(x, N * n * es),
                        range_of(W0, weight_bytes(d)), range_of(R_f32, nbR * bR * bR * 4),
                        range_of(P_f32, nbP * bP * bP * 4), range_of(R_act, nbR * bR * bR * es),
                        range_of(P_act, nbP * bP * bP * es),
                        z_saved ? range_of(z_saved, N * m * es) : Range{0, 0},
-                       range_of(ws, plan.total),
                        range_of(d->perm_in, permuted(d) ? n * 4 : 0),
                        range_of(d->perm_out, permuted(d) ? m * 4 : 0),
                        range_of(d->w_scale, int8_weight(d) ? m * 4 : 0)};
@@ -709,8 +714,9 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     for (const Range& r : ins)
       if (overlap(o, r)) return POETX_ERR_ALIAS;
   }
-  if (overlap(outs[0], outs[1]) || overlap(outs[0], outs[2]) || overlap(outs[1], outs[2]))
-    return POETX_ERR_ALIAS;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return POETX_ERR_ALIAS;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const DType t = d->act == POETX_BF16 ? DType::BF16 : DType::F32;

@@ -9,18 +9,36 @@
 // C[M][N] = A[M][K] B(n, k) with B(n, k) = B[n][k] (K-major) or B[k][n]
 // (N-major); bf16 in and out, float32 accumulation.
 //
-// One workgroup (8 waves, 2 x 4, each 128 x 64 as 8 x 4 tiles of
-// v_mfma_f32_16x16x32_bf16, two waves per SIMD) computes a 256 x 256 tile;
-// waves 0-3 issue the operand loads and waves 4-7 write the output, so each
-// wave's vmcnt only counts its own kind of access. On random operands the
-// 16x16x32 shape sustains a markedly higher rate than 32x32x16 under the
-// chip's power limit, so it is the one used here. K tiles of 32 are copied
-// from global memory straight into a 4-slot LDS ring with
-// global_load_lds_dwordx4 (no register staging, no LDS store instructions),
-// three tiles ahead of the MFMAs. Each K tile is one MFMA step; the barrier
-// that publishes the next tile sits between the two halves of the current
-// tile's MFMAs, and the next tile's fragments are read into a second register
-// set while the second half runs.
+// One workgroup of four waves, one per SIMD, computes a 256 x 256 tile; each
+// wave owns a 128 x 128 quarter as 8 x 8 tiles of v_mfma_f32_16x16x32_bf16
+// whose 256 accumulator registers live in AGPRs. A 128 x 128 wave tile is
+// the largest the register file allows and reads the fewest operand bytes
+// from LDS per product (64 KB per 32-deep K tile for the workgroup, against
+// 96 KB for eight 128 x 64 waves). Measured on gfx950 at one wave per SIMD:
+// a back-to-back 16x16x32 stream issues every 16.2 cycles, and every
+// ds_read_b128 interleaved with it costs about 8 more, so operand bytes read
+// into registers, not the products, set the pace; the fewer of them, the
+// less power the LDS draws, and the chip's clock under this load is power
+// limited.
+//
+// K tiles of 32 are copied from global memory straight into a 4-slot LDS
+// ring with global_load_lds_dwordx4 (no register staging, no LDS store
+// instructions), three tiles ahead of the products. Every wave issues its
+// share of the copies, one 1 KB piece after each row of eight products, so
+// the address unit sees a steady stream rather than a burst that would block
+// the issuing wave (in-order issue: a blocked copy holds back the products
+// behind it). Per K tile: the first row of products runs on registers, then
+// one barrier publishes the next K tile and frees the slot of the current
+// one, then the other seven rows run while the next tile's fragments are
+// read, two per row, into the second register set.
+//
+// The products are inline asm with the accumulator tied to an AGPR operand:
+// with the compiler's builtin the register allocator rotated the
+// accumulators between AGPRs on every iteration (hundreds of
+// v_accvgpr_mov per K tile). The first K tile uses a zero addend, so the
+// accumulators are never cleared by VALU writes. The compiler does not see
+// the asm products, so the wait states before the epilogue reads them are
+// explicit.
 //
 // LDS layouts (16-byte chunks XOR-swizzled so that the fragment reads are
 // free of bank conflicts):
@@ -31,11 +49,20 @@
 //                 c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)), r & 3, (r >> 2) & 3
 //                 or no swizzle all give 128 B/clk (two-way conflicts);
 //   N-major tile  [32 k][256 n]     (512-byte rows): chunk c of row k at
-//                 c ^ 2 (k & 3), read with the transposing ds_read_b64_tr_b16.
+//                 c ^ 2 (k & 3), read with the transposing ds_read_b64_tr_b16;
+//   epilogue      [256 m][256 n] bf16 (the whole ring): chunk c of row m at
+//                 c ^ (m & 15).
+// The products are issued as D' = B A^T (the operand roles swapped), so each
+// lane ends up holding four consecutive output columns of one row and stages
+// them with one 8-byte LDS write; the staged tile leaves as 16-byte stores of
+// whole 512-byte row segments.
+//
 // M and N must be at least 256 and K a multiple of 32: a tile that would
 // cross the end of M or N is shifted back to end there (it recomputes, and
 // rewrites with identical values, part of its neighbour), so no load or
-// store needs a bounds test.
+// store needs a bounds test. The kernel is persistent: workgroup g computes
+// tiles g, g + G, ... (G = grid size, a multiple of 8, so each workgroup
+// stays on one XCD's share of the grouped tile order).
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -44,38 +71,27 @@ namespace poetx {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int NWAVE = 8;                  // 2 x (NWAVE / 2) waves
-constexpr int NT = 64 * NWAVE;
-constexpr int TN = 2 * BN / NWAVE;        // wave tile: 128 rows x TN columns
-constexpr int FN = TN / 16;               // 16-column B fragments per wave
-constexpr int TILE = BM * BK;             // bf16 elements of one operand tile
-constexpr int SLOT = 2 * TILE;            // A and B tiles
+constexpr int NW = 4, NT = 64 * NW;        // one wave per SIMD
+constexpr int FM = 8, FN = 8;              // 16-row / 16-column fragments per wave
+constexpr int TILE = BM * BK;              // bf16 elements of one operand tile (16 KB)
+constexpr int SLOT = 2 * TILE;             // A and B tiles
 constexpr int NSLOT = 4;
-constexpr int NLOADW = NWAVE / 2;         // waves 0 .. NLOADW-1 issue the loads
-constexpr int PPW = 16 / NLOADW;          // 1 KB pieces per loading wave per operand tile
-constexpr int LPW = 2 * PPW;              // 1 KB loads per loading wave per K tile
-constexpr int SROWS = 64;                 // output rows staged per epilogue pass
-constexpr int RING = NSLOT * SLOT;
-constexpr int LDS_ELEMS = RING + SROWS * BN;  // 160 KB: ring + epilogue staging
+constexpr int RING = NSLOT * SLOT;         // 128 KB, also the epilogue's staging tile
+constexpr int PPW = TILE * 2 / 1024 / NW;  // 1 KB pieces per wave per operand tile
+constexpr int LPW = 2 * PPW;               // copies per wave per K tile
+static_assert(RING == BM * BN, "the epilogue stages the whole output tile in the ring");
+static_assert(PPW == 4 && LPW == 8, "one copy after each of the eight rows of products");
 
 // 1 KB alignment: the fragment addressing XORs bits 4..6 of element offsets
-__shared__ __attribute__((aligned(1024))) bf16_t g_dense_lds[LDS_ELEMS];
+__shared__ __attribute__((aligned(1024))) bf16_t g_dense_lds[RING];
 
-// element offset of (row, col) in the epilogue staging tile [SROWS][BN]:
-// 16-byte chunks XOR-swizzled by bits 2..3 of the row
-__device__ __forceinline__ int stage_off(int row, int col) {
-  return RING + row * BN + ((((col >> 3) ^ (((row >> 2) & 3) << 1))) << 3) + (col & 7);
-}
-
-// swizzle of a K-major row: depends only on row % 16, so the fragments of
-// one wave (16-row steps) share one address pattern
 __device__ __forceinline__ int kmaj_swz(int row) { return (row >> 1) & 3; }
-__device__ __forceinline__ int kmaj_off(int row, int chunk) {
-  return row * BK + ((chunk ^ kmaj_swz(row)) << 3);
-}
 __device__ __forceinline__ int nmaj_swz(int k) { return (k & 3) << 1; }
 __device__ __forceinline__ int nmaj_off(int k, int n) {
   return k * BN + ((((n >> 3) ^ nmaj_swz(k))) << 3) + (n & 7);
+}
+__device__ __forceinline__ int stage_off(int m, int n) {
+  return m * BN + ((((n >> 3) ^ (m & 15))) << 3) + (n & 7);
 }
 
 // One global_load_lds_dwordx4 in the scalar-base form: lane l copies the 16
@@ -96,241 +112,228 @@ __device__ __forceinline__ const bf16_t* uniform_ptr(const bf16_t* p) {
 
 template <bool B_KMAJ>
 struct Dense {
-  // wave-uniform bases of the current tile's A and B panels; per-lane byte
-  // offsets of this (loading) wave's first 1 KB load per operand at k = 0
-  // (its other loads add a wave-uniform stride to the base)
-  const bf16_t* baseA;
+  const bf16_t* baseA;  // wave-uniform bases of the current tile's A and B panels
   const bf16_t* baseB;
-  int64_t stepB;   // elements between consecutive K tiles of B
-  int64_t pieceA, pieceB;  // elements between this wave's consecutive loads
-  uint32_t offA, offB;
-  uint32_t lds0;  // LDS byte address of the ring, wave-uniform
+  int64_t stepB;        // elements between consecutive K tiles of B
+  uint32_t offA, offB;  // per-lane byte offsets of this wave's first piece at k = 0
+  uint32_t strA, strB;  // bytes between this wave's consecutive pieces
+  uint32_t lds0;        // LDS byte address of the ring, wave-uniform
   int wave, lane, wm, wn;
-  bool loader;    // this wave issues the tile loads
-  int rdA, rdB;   // per-lane element offsets of fragment 0 within a tile
-  floatx4 acc[8][FN];
-  bf16x8_t fa[8], fb[2][FN];
+  int rdA, rdB;         // per-lane element offsets of fragment 0 within a tile
+  floatx4 acc[FM][FN];
+  bf16x8_t fa[2][FM], fb[2][FN];
 
-  __device__ __forceinline__ void init(int64_t ldb) {
+  __device__ __forceinline__ void init(int64_t lda, int64_t ldb) {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     lane = threadIdx.x & 63;
     wm = wave & 1;
     wn = wave >> 1;
-    loader = wave < NLOADW;
     lds0 = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)g_dense_lds)));
     stepB = B_KMAJ ? BK : (int64_t)BK * ldb;
     const int r = lane & 15;
     rdA = (wm * 128 + r) * BK + (((lane >> 4) ^ kmaj_swz(r)) << 3);
     if (B_KMAJ) {
-      rdB = (wn * TN + r) * BK + (((lane >> 4) ^ kmaj_swz(r)) << 3);
+      rdB = (wn * 128 + r) * BK + (((lane >> 4) ^ kmaj_swz(r)) << 3);
     } else {
       // fragment j adds 16 j columns: chunk index + 2 j, which the swizzle
       // turns into an XOR of the element offset with 16 j
       const int k = 8 * (lane >> 4) + (r >> 2);
-      rdB = nmaj_off(k, wn * TN + 4 * (r & 3));
+      rdB = nmaj_off(k, wn * 128 + 4 * (r & 3));
+    }
+    // wave w copies pieces q = w + 4 j (j < 4) of each operand tile: K-major
+    // piece q holds rows 16 q .. 16 q + 15, N-major piece q holds k rows
+    // 2 q, 2 q + 1; either way the swizzle of a lane's data is the same for
+    // all of its pieces
+    const int row = 16 * wave + (lane >> 2);
+    const int c = (lane & 3) ^ kmaj_swz(row);
+    offA = (uint32_t)(row * lda + 8 * c) * 2u;
+    strA = (uint32_t)(16 * NW * lda) * 2u;
+    if (B_KMAJ) {
+      offB = (uint32_t)(row * ldb + 8 * c) * 2u;
+      strB = (uint32_t)(16 * NW * ldb) * 2u;
+    } else {
+      const int k = 2 * wave + (lane >> 5);
+      const int cn = (lane & 31) ^ nmaj_swz(k);
+      offB = (uint32_t)(k * ldb + 8 * cn) * 2u;
+      strB = (uint32_t)(2 * NW * ldb) * 2u;
     }
   }
 
-  // load addressing of the output tile at (m0, n0) (wholly inside M x N).
-  // Loading wave w issues pieces q = w + NLOADW j (j < PPW) of each operand
-  // tile: K-major piece q holds rows 16 q .. 16 q + 15, N-major piece q
-  // holds k rows 2 q, 2 q + 1; either way the swizzle of a lane's data is
-  // the same for all of its pieces.
+  // panels of the output tile at (m0, n0) (wholly inside M x N)
   __device__ __forceinline__ void set_tile(const bf16_t* A, const bf16_t* B, int64_t lda,
                                            int64_t ldb, int m0, int n0) {
     baseA = uniform_ptr(A + (int64_t)m0 * lda);
     baseB = uniform_ptr(B_KMAJ ? B + (int64_t)n0 * ldb : B + n0);
-    const int w = wave % NLOADW;
-    const int row = 16 * w + (lane >> 2);
-    const int c = (lane & 3) ^ kmaj_swz(row);
-    offA = (uint32_t)(row * lda + 8 * c) * 2u;
-    pieceA = 16 * NLOADW * lda;
-    if (B_KMAJ) {
-      offB = (uint32_t)(row * ldb + 8 * c) * 2u;
-      pieceB = 16 * NLOADW * ldb;
-    } else {
-      const int k = 2 * w + (lane >> 5);
-      const int cn = (lane & 31) ^ nmaj_swz(k);
-      offB = (uint32_t)(k * ldb + 8 * cn) * 2u;
-      pieceB = 2 * NLOADW * ldb;
-    }
   }
 
-  // loads of K tile t into ring slot S (loading waves only)
+  // piece J of K tile t of operand OP (0: A, 1: B) into ring slot S
+  template <int S, int OP, int J>
+  __device__ __forceinline__ void dma(int t) {
+    const uint32_t m = lds0 + (uint32_t)(S * SLOT * 2 + OP * TILE * 2 + (wave + NW * J) * 1024);
+    if (OP == 0)
+      dma16_sb(uniform_ptr(baseA + (int64_t)t * BK), offA + J * strA, m);
+    else
+      dma16_sb(uniform_ptr(baseB + (int64_t)t * stepB), offB + J * strB, m);
+  }
   template <int S>
   __device__ __forceinline__ void issue(int t) {
-    const uint32_t m = lds0 + (uint32_t)(S * SLOT * 2 + wave * 1024);
-#pragma unroll
-    for (int j = 0; j < PPW; ++j)
-      dma16_sb(uniform_ptr(baseA + (int64_t)t * BK + j * pieceA), offA, m + NLOADW * 1024 * j);
-#pragma unroll
-    for (int j = 0; j < PPW; ++j)
-      dma16_sb(uniform_ptr(baseB + (int64_t)t * stepB + j * pieceB), offB,
-               m + TILE * 2 + NLOADW * 1024 * j);
+    dma<S, 0, 0>(t); dma<S, 0, 1>(t); dma<S, 0, 2>(t); dma<S, 0, 3>(t);
+    dma<S, 1, 0>(t); dma<S, 1, 1>(t); dma<S, 1, 2>(t); dma<S, 1, 3>(t);
   }
 
-  // A fragment i: rows 16 i .. of this wave's 128, lane l holds row l % 16,
-  // k = 8 (l / 16) .. +7; B fragments likewise over this wave's columns.
-  // A fragments i0 .. i1-1 (rows 16 i .. of this wave's 128; lane l holds
-  // row l % 16, k = 8 (l / 16) .. +7) from ring slot S
-  template <int S, int I0, int I1>
+  // A fragment I (rows 16 I .. of this wave's 128; lane l holds row l % 16,
+  // k = 8 (l / 16) .. +7) from ring slot S into set P
+  template <int S, int P, int I>
   __device__ __forceinline__ void read_a() {
-    const bf16_t* s = g_dense_lds + S * SLOT;
-#pragma unroll
-    for (int i = I0; i < I1; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(s + rdA + 512 * i);
+    fa[P][I] = *reinterpret_cast<const bf16x8_t*>(g_dense_lds + S * SLOT + rdA + 512 * I);
   }
-  // B fragments j0 .. j1-1 (16 of this wave's columns each) from ring slot S
-  // into set P
-  template <int S, int P, int J0 = 0, int J1 = FN>
+  // B fragment J (16 of this wave's columns) likewise
+  template <int S, int P, int J>
   __device__ __forceinline__ void read_b() {
     const bf16_t* sb = g_dense_lds + S * SLOT + TILE;
     if (B_KMAJ) {
-#pragma unroll
-      for (int j = J0; j < J1; ++j) fb[P][j] = *reinterpret_cast<const bf16x8_t*>(sb + rdB + 512 * j);
+      fb[P][J] = *reinterpret_cast<const bf16x8_t*>(sb + rdB + 512 * J);
     } else {
-      // recomputed per read (one XOR) rather than held in registers
-      int rb = rdB;
-      asm volatile("" : "+v"(rb));
-#pragma unroll
-      for (int j = J0; j < J1; ++j) {
-        const int o = rb ^ (16 * j);
-        union { short4_t h[2]; bf16x8_t v; } u;
-        u.h[0] = ds_read_tr4(sb + o);
-        u.h[1] = ds_read_tr4(sb + o + 4 * BN);
-        fb[P][j] = u.v;
-      }
+      const int o = rdB ^ (16 * J);
+      union { short4_t h[2]; bf16x8_t v; } u;
+      u.h[0] = ds_read_tr4(sb + o);
+      u.h[1] = ds_read_tr4(sb + o + 4 * BN);
+      fb[P][J] = u.v;
     }
   }
 
-  template <int I0, int P, int J0 = 0, int J1 = FN>
-  __device__ __forceinline__ void mma_rows() {
-#pragma unroll
-    for (int i = I0; i < I0 + 4; ++i)
-#pragma unroll
-      for (int j = J0; j < J1; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[P][j], acc[i][j], 0, 0, 0);
+  // acc[I][J] += B fragment J x A fragment I (D' = B A^T: lane l holds
+  // output row 16 I + l % 16, columns 16 J + 4 (l / 16) .. +3)
+  template <int P, int I, int J, bool FIRST>
+  __device__ __forceinline__ void mma() {
+    if (FIRST)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0"
+                   : "=a"(acc[I][J])
+                   : "v"(fb[P][J]), "v"(fa[P][I]));
+    else
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                   : "+a"(acc[I][J])
+                   : "v"(fb[P][J]), "v"(fa[P][I]));
+  }
+  template <int P, int I, bool FIRST>
+  __device__ __forceinline__ void mma_row() {
+    mma<P, I, 0, FIRST>(); mma<P, I, 1, FIRST>(); mma<P, I, 2, FIRST>(); mma<P, I, 3, FIRST>();
+    mma<P, I, 4, FIRST>(); mma<P, I, 5, FIRST>(); mma<P, I, 6, FIRST>(); mma<P, I, 7, FIRST>();
   }
 
-  // K tile t, held in ring slot S, its B fragments in set P. The fragments
-  // of tile t+1 are read as those of tile t are consumed, which keeps the
-  // live fragment registers near one set: after the barrier that publishes
-  // tile t+1, A rows 0..3 and the first half of B; after the MFMAs on the
-  // second half of B, the rest of B; after the last MFMAs, A rows 4..7.
-  // STEADY: tiles t+1 .. t+4 all exist, so every step below is taken
-  template <int S, int P, bool STEADY>
+  // K tile t, held in ring slot S, its fragments in set P. STEADY: tiles
+  // t+1 .. t+4 all exist, so every step below is taken. FIRST: t == 0.
+  template <int S, int P, bool STEADY, bool FIRST = false>
   __device__ __forceinline__ void tile(int t, int ntiles) {
-    mma_rows<0, P>();
-    __builtin_amdgcn_sched_barrier(0);  // keep these MFMAs ahead of the waits
+    constexpr int S1 = (S + 1) & 3;
     const bool more = STEADY || t + 1 < ntiles;
+    const bool iss = STEADY || t + 4 < ntiles;
+    mma_row<P, 0, FIRST>();
+    __builtin_amdgcn_sched_barrier(0);
     if (more) {
-      // tile t+1 landed (each loading wave's part; tiles t+2 and t+3 may
-      // still be in flight); then every part, and every wave is done with
-      // slot S
-      if (loader) {
-        if (STEADY || t + 3 < ntiles) wait_vm<2 * LPW>();
-        else if (t + 2 < ntiles) wait_vm<LPW>();
-        else wait_vm<0>();
-      }
+      // this wave's part of tile t+1 landed (tiles t+2, t+3 may still be in
+      // flight) and its reads of tile t are done; after the barrier every
+      // part has landed and slot S is free
+      if (STEADY || t + 3 < ntiles) wait_vm<2 * LPW>();
+      else if (t + 2 < ntiles) wait_vm<LPW>();
+      else wait_vm<0>();
       wait_lds();
       barrier_nofence();
-      if (loader && (STEADY || t + 4 < ntiles)) issue<S>(t + 4);
-      read_a<(S + 1) & 3, 0, 4>();
-      read_b<(S + 1) & 3, P ^ 1, 0, FN / 2>();
     }
-    mma_rows<4, P, FN / 2, FN>();
+    if (iss) dma<S, 0, 0>(t + 4);
     __builtin_amdgcn_sched_barrier(0);
-    if (more) read_b<(S + 1) & 3, P ^ 1, FN / 2, FN>();
-    mma_rows<4, P, 0, FN / 2>();
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) read_a<(S + 1) & 3, 4, 8>();
+#define POETX_DENSE_ROW(I)                                                          \
+  mma_row<P, I, FIRST>();                                                           \
+  if (iss) dma<S, (I) / 4, (I) % 4>(t + 4);                                         \
+  if (more) { read_a<S1, P ^ 1, (I) - 1>(); read_b<S1, P ^ 1, (I) - 1>(); }         \
+  __builtin_amdgcn_sched_barrier(0);
+    POETX_DENSE_ROW(1) POETX_DENSE_ROW(2) POETX_DENSE_ROW(3) POETX_DENSE_ROW(4)
+    POETX_DENSE_ROW(5) POETX_DENSE_ROW(6) POETX_DENSE_ROW(7)
+#undef POETX_DENSE_ROW
+    if (more) { read_a<S1, P ^ 1, 7>(); read_b<S1, P ^ 1, 7>(); }
   }
 
-  // loads of the first (up to) four K tiles of the current output tile
+  // copies of the first (up to) four K tiles of the current output tile
   __device__ __forceinline__ void prefetch(int ntiles) {
-    if (!loader) return;
     issue<0>(0);
     if (ntiles > 1) issue<1>(1);
     if (ntiles > 2) issue<2>(2);
     if (ntiles > 3) issue<3>(3);
   }
 
-  // every part of K tile 0 landed; its fragments read
+  // every part of K tile 0 landed (this wave's earlier stores too: the
+  // count is conservative); its fragments read
   __device__ __forceinline__ void start(int ntiles) {
-    if (loader) {
-      if (ntiles > 3) wait_vm<3 * LPW>();
-      else if (ntiles > 2) wait_vm<2 * LPW>();
-      else if (ntiles > 1) wait_vm<LPW>();
-      else wait_vm<0>();
-    }
+    if (ntiles > 3) wait_vm<3 * LPW>();
+    else if (ntiles > 2) wait_vm<2 * LPW>();
+    else if (ntiles > 1) wait_vm<LPW>();
+    else wait_vm<0>();
     barrier_nofence();
-    read_a<0, 0, 8>();
-    read_b<0, 0>();
+    read_a<0, 0, 0>(); read_a<0, 0, 1>(); read_a<0, 0, 2>(); read_a<0, 0, 3>();
+    read_a<0, 0, 4>(); read_a<0, 0, 5>(); read_a<0, 0, 6>(); read_a<0, 0, 7>();
+    read_b<0, 0, 0>(); read_b<0, 0, 1>(); read_b<0, 0, 2>(); read_b<0, 0, 3>();
+    read_b<0, 0, 4>(); read_b<0, 0, 5>(); read_b<0, 0, 6>(); read_b<0, 0, 7>();
   }
 
   __device__ __forceinline__ void mainloop(int ntiles) {
-    int t = 0;
+    // tile 0 writes the accumulators; then slots 1, 2, 3, 0, 1, ...
+    if (ntiles > 4) tile<0, 0, true, true>(0, ntiles);
+    else tile<0, 0, false, true>(0, ntiles);
+    int t = 1;
     for (; t + 8 <= ntiles; t += 4) {  // branch-free steady state
-      tile<0, 0, true>(t, ntiles);
-      tile<1, 1, true>(t + 1, ntiles);
-      tile<2, 0, true>(t + 2, ntiles);
-      tile<3, 1, true>(t + 3, ntiles);
+      tile<1, 1, true>(t, ntiles);
+      tile<2, 0, true>(t + 1, ntiles);
+      tile<3, 1, true>(t + 2, ntiles);
+      tile<0, 0, true>(t + 3, ntiles);
     }
-    // the last 1 .. 7 tiles
-    if (t < ntiles) tile<0, 0, false>(t++, ntiles);
+    // the last 0 .. 7 tiles
     if (t < ntiles) tile<1, 1, false>(t++, ntiles);
     if (t < ntiles) tile<2, 0, false>(t++, ntiles);
     if (t < ntiles) tile<3, 1, false>(t++, ntiles);
     if (t < ntiles) tile<0, 0, false>(t++, ntiles);
     if (t < ntiles) tile<1, 1, false>(t++, ntiles);
     if (t < ntiles) tile<2, 0, false>(t++, ntiles);
+    if (t < ntiles) tile<3, 1, false>(t++, ntiles);
+    // wait states between the last products and the VALU reads of their
+    // results in the epilogue (more than any 16x16x32 product needs)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // accumulators -> bf16 -> 16-byte row segments of C, SROWS rows per pass
-  // through the staging tile; the waves that do not load write to global
-  // memory, so the loading waves' counters only ever see their own loads
+  // accumulators -> bf16 staging tile (the whole ring) -> 16-byte stores of
+  // whole 512-byte row segments; the ring is free again on return
   __device__ __forceinline__ void epilogue(bf16_t* __restrict__ C, int64_t ldc, int m0, int n0) {
     // opaque copies of the lane and thread ids: keeps the compiler from
-    // hoisting the epilogue's address arithmetic out of the tile loop, where
-    // it would hold registers through the main loop
-    int ln = lane, tid = (int)threadIdx.x - 64 * NLOADW;
+    // hoisting the epilogue's address arithmetic out of the tile loop
+    int ln = lane, tid = (int)threadIdx.x;
     asm volatile("" : "+v"(ln), "+v"(tid));
 #pragma unroll
-    for (int pass = 0; pass < BM / SROWS; ++pass) {
-      if (wm == (pass >> 1)) {
-        const int i0 = 4 * (pass & 1);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < FN; ++j) {
+        const int m = wm * 128 + 16 * i + (ln & 15);
+        const int n = wn * 128 + 16 * j + 4 * (ln >> 4);
+        union { bf16_t h[4]; uint2 v; } u;
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int n = wn * TN + 16 * j + (ln & 15);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 16 * i + 4 * (ln >> 4) + e;
-              g_dense_lds[stage_off(r, n)] = f32_to_bf16(acc[i0 + i][j][e]);
-            }
-          }
+        for (int e = 0; e < 4; ++e) u.h[e] = f32_to_bf16(acc[i][j][e]);
+        *reinterpret_cast<uint2*>(g_dense_lds + stage_off(m, n)) = u.v;
+        __builtin_amdgcn_sched_barrier(0);  // one fragment's registers at a time
       }
-      __syncthreads();
-      if (!loader) {
+    __syncthreads();
 #pragma unroll
-        for (int q = 0; q < SROWS * BN / 8 / (NT - 64 * NLOADW); ++q) {
-          const int c = tid + q * (NT - 64 * NLOADW);
-          const int rl = c >> 5, nl = (c & 31) * 8;
-          const int m = m0 + pass * SROWS + rl, n = n0 + nl;
-          const uint4 v = *reinterpret_cast<const uint4*>(g_dense_lds + stage_off(rl, nl));
-          *reinterpret_cast<uint4*>(C + (int64_t)m * ldc + n) = v;
-        }
-      }
-      __syncthreads();
+    for (int q = 0; q < BM * BN / 8 / NT; ++q) {
+      const int c = tid + q * NT;
+      const int rl = c >> 5, nl = (c & 31) * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(g_dense_lds + stage_off(rl, nl));
+      *reinterpret_cast<uint4*>(C + (int64_t)(m0 + rl) * ldc + n0 + nl) = v;
     }
+    wait_lds();
+    barrier_nofence();
   }
 };
 
-// Persistent: workgroup g computes output tiles g, g + G, ... (G = grid
-// size, a multiple of 8, so each workgroup stays on one XCD's share of the
-// grouped tile order). The first K tiles of the next output tile are loaded
-// while the current one is written out.
 template <bool B_KMAJ>
 __global__ void __launch_bounds__(NT)
 dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C,
@@ -342,47 +345,37 @@ dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
   if (tile >= total) return;
 
   Dense<B_KMAJ> d;
-  d.init(ldb);
-  int mt, nt;
-  xcd_grouped_tile_at(tile, total, num_mt, num_nt, mt, nt);
-  d.set_tile(A, B, lda, ldb, min(mt * BM, M - BM), min(nt * BN, N - BN));
-  d.prefetch(ntiles);
+  d.init(lda, ldb);
   for (;;) {
+    int mt, nt;
+    xcd_grouped_tile_at(tile, total, num_mt, num_nt, mt, nt);
     const int m0 = min(mt * BM, M - BM), n0 = min(nt * BN, N - BN);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d.acc[i][j][e] = 0.f;
+    d.set_tile(A, B, lda, ldb, m0, n0);
+    d.prefetch(ntiles);
     d.start(ntiles);
     d.mainloop(ntiles);
     wait_lds();
     barrier_nofence();  // every wave is done with the ring
-    const int next = tile + (int)gridDim.x;
-    if (next < total) {
-      xcd_grouped_tile_at(next, total, num_mt, num_nt, mt, nt);
-      d.set_tile(A, B, lda, ldb, min(mt * BM, M - BM), min(nt * BN, N - BN));
-      d.prefetch(ntiles);
-    }
     d.epilogue(C, ldc, m0, n0);
-    if (next >= total) break;
-    tile = next;
+    tile += (int)gridDim.x;
+    if (tile >= total) break;
   }
 }
 
 }  // namespace
 
 bool dense_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+  // the per-lane copy offsets within one 256-row (or 32-row) panel are 32-bit
   return M >= BM && N >= BN && K >= BK && K % BK == 0 && N % 8 == 0 && lda % 8 == 0 &&
-         ldb % 8 == 0 && ldc % 8 == 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX;
+         ldb % 8 == 0 && ldc % 8 == 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX &&
+         lda <= (1 << 22) && ldb <= (1 << 22);
 }
 
 hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                         int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s) {
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  // one workgroup per CU (the LDS footprint allows no more), rounded down to
-  // a multiple of the 8 XCDs
+  // one workgroup per CU (the register and LDS footprints allow no more),
+  // rounded down to a multiple of the 8 XCDs
   static thread_local int cached_dev = -1, cached_cus = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

@@ -13,7 +13,9 @@ import os
 import torch  # loads torch's HIP runtime first, so libpoetx binds to the same one
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpoetx.so")
+# POETX_LIBRARY may name another build of the same library (the host
+# sanitizer build of the CPU tests); by default the in-tree libpoetx.so
+LIB_PATH = os.environ.get("POETX_LIBRARY") or os.path.join(_HERE, "libpoetx.so")
 
 POETX_OK = 0
 POETX_ERR_NULL = 1

@@ -48,6 +48,50 @@ def check(name: str, got, ref, dtype: str) -> float:
     return err
 
 
+def check_tiles(name: str, got, ref, dtype: str, tile=(256, 256)) -> float:
+    """Element-by-element comparison of a whole 2-D output: the tolerance
+    metric over the whole tensor and over every tile x tile piece (so one
+    wrong output tile cannot hide in the norm of a large tensor), plus the
+    max-abs error relative to max |ref| for the log."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), name
+    metric, tol = TOL[dtype]
+    whole = metric(got, ref)
+    worst, where = 0.0, None
+    r0, c0 = tile
+    for i in range(0, ref.shape[0], r0):
+        for j in range(0, ref.shape[1], c0):
+            e = metric(got[i:i + r0, j:j + c0], ref[i:i + r0, j:j + c0])
+            if e > worst:
+                worst, where = e, (i, j)
+    mx = max_rel(got, ref)
+    log(f"    {name:10s} {metric.__name__} = {whole:.3e}, worst {r0}x{c0} tile {worst:.3e} at {where}, "
+        f"max-abs/max|ref| = {mx:.3e} (tol {tol:.0e})")
+    assert whole <= tol, (name, whole, tol)
+    assert worst <= tol, (name, "tile", where, worst, tol)
+    return whole
+
+
+def check_blocks(name: str, got, ref, dtype: str) -> float:
+    """Per-block comparison of a [nblocks, ...] output (every generator
+    block of g_theta), with the metric over the whole tensor as well."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), name
+    metric, tol = TOL[dtype]
+    whole = metric(got, ref)
+    errs = [metric(got[k], ref[k]) for k in range(ref.shape[0])]
+    k = int(np.argmax(errs))
+    log(f"    {name:10s} {metric.__name__} = {whole:.3e}, worst of {len(errs)} blocks {errs[k]:.3e} "
+        f"(block {k}), max-abs/max|ref| = {max_rel(got, ref):.3e} (tol {tol:.0e})")
+    assert whole <= tol, (name, whole, tol)
+    assert errs[k] <= tol, (name, "block", k, errs[k], tol)
+    return whole
+
+
 def run_layer(L, stream=None, recompute_z=False, map="cayley", perms=None):
     """Build, forward and backward one layer on the GPU (the bench's path).
     Returns the PoetxLinear and a dict of device results (z is None when the

@@ -160,6 +160,26 @@ def test_aliasing_is_rejected():
     assert _bwd(d, gR=ALIGNED * 256) == P.POETX_ERR_ALIAS    # g_theta_R inside the workspace
 
 
+def test_workspace_is_a_written_buffer_for_alias_checks():
+    """The kernels write U, Z, g_Z, g_U and the gram partials into the
+    workspace, so a workspace on top of any input is an alias too."""
+    d = desc()
+    assert _fwd(d, ws=ALIGNED) == P.POETX_ERR_ALIAS            # on top of x
+    assert _fwd(d, ws=ALIGNED * 2) == P.POETX_ERR_ALIAS        # on top of W0
+    assert _fwd(d, ws=ALIGNED * 4) == P.POETX_ERR_ALIAS        # on top of P_act
+    assert _fwd(d, ws=ALIGNED * 64) == P.POETX_ERR_ALIAS       # on top of y
+    assert _bwd(d, ws=ALIGNED) == P.POETX_ERR_ALIAS            # on top of g_y
+    assert _bwd(d, ws=ALIGNED * 2) == P.POETX_ERR_ALIAS        # on top of x
+    assert _bwd(d, ws=ALIGNED * 5) == P.POETX_ERR_ALIAS        # on top of P_f32
+    assert _bwd(d, ws=ALIGNED * 8) == P.POETX_ERR_ALIAS        # on top of z
+    assert _bwd(d, ws=ALIGNED * 64) == P.POETX_ERR_ALIAS       # on top of g_x
+    dp = desc(**PERMS)
+    assert _fwd(dp, ws=ALIGNED * 300) == P.POETX_ERR_ALIAS     # on top of perm_in
+    assert _bwd(dp, ws=ALIGNED * 301) == P.POETX_ERR_ALIAS     # on top of perm_out
+    dq = desc(w_scale=ALIGNED * 500)
+    assert _fwd(dq, ws=ALIGNED * 500) == P.POETX_ERR_ALIAS     # on top of the row scales
+
+
 def test_events_without_array_rejected():
     d = desc()
     d.n_events = 4
@@ -193,6 +213,7 @@ def test_build_errors():
     assert call(ws=None) == P.POETX_ERR_WORKSPACE
     assert call(f32=ALIGNED) == P.POETX_ERR_ALIAS          # output on top of theta
     assert call(act_ptr=ALIGNED * 4) == P.POETX_ERR_ALIAS  # act copy inside the workspace
+    assert call(ws=ALIGNED) == P.POETX_ERR_ALIAS           # workspace on top of theta
 
 
 # -- POETX_RECOMPUTE_Z (POET-Xmem: Z is not kept by the forward) --------------
@@ -315,6 +336,7 @@ def test_build_cnp_errors():
     assert call(q=ALIGNED) == P.POETX_ERR_ALIAS             # Q on top of theta
     assert call(f32=ALIGNED * 2) == P.POETX_ERR_ALIAS       # R on top of Q
     assert call(act_ptr=ALIGNED * 5) == P.POETX_ERR_ALIAS   # act copy inside the workspace
+    assert call(ws=ALIGNED) == P.POETX_ERR_ALIAS            # workspace on top of theta
 
 
 # -- block-mixing permutations: descriptor maps and poetx_fold_weight --------

@@ -1,9 +1,9 @@
 """GPU parity: libpoetx (through the C ABI) against the float64 oracle on the
 same seeded inputs.
 
-Small cases compare every output element; the full-size workloads compare
-sampled outputs the oracle computes directly (token rows of y and g_x, whole
-generator blocks of g_theta) plus properties that hold at any size.
+Every case compares every output element (y, z, g_x and every generator
+block of g_theta), the full-size workloads tile by tile as well, plus
+properties that hold at any size.
 """
 import math
 import os
@@ -205,40 +205,27 @@ def test_theta_zero_is_plain_linear():
 
 
 # ------------------------------------------------- full-size workloads
-def _sampled_check(L, lay, out, n_rows=48, rng_seed=0, map="cayley", perms=None):
+def _full_check(L, lay, out, map="cayley", perms=None, check_z=True):
+    """Every output element of a full-size run against the oracle: y, z
+    (the forward's saved product), g_x and every generator block of g_theta,
+    each also tile by tile (256 x 256 pieces, or per block), so that a single
+    wrong output tile fails. Plus a property that holds at any size: R is
+    orthogonal per block, so ||y_t,k|| = ||z_t,k||."""
     s = L.spec
     b = s.b
     po, pi = perms if perms is not None else (None, None)
     ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, b, b, map=map, perm_out=po, perm_in=pi)
     U.check("R", U.host(lay.R_f32), ora.R, "f32")
     U.check("P", U.host(lay.P_f32), ora.P, "f32")
-    rng = np.random.default_rng(rng_seed)
-    rows = np.sort(rng.choice(s.tokens, size=min(n_rows, s.tokens), replace=False))
-    rows = np.unique(np.concatenate([rows, [0, s.tokens - 1]]))
-    y_gpu = U.host(out["y"][torch.from_numpy(rows).cuda()])
-    U.check("y rows", y_gpu, ora.forward(L.x[rows]), s.dtype)
-    gx_gpu = U.host(out["g_x"][torch.from_numpy(rows).cuda()])
-    U.check("g_x rows", gx_gpu, L.g_y[rows] @ ora.W, s.dtype)
-    # whole generator blocks: first and last R block, last P block (with
-    # permutations the blocks see the folded W0 and the gathered g_y and x)
-    W0f, gy, xx = L.W0, L.g_y, L.x
-    if perms is not None:
-        W0f, gy, xx = O.fold_permutations(L.W0, po, pi), L.g_y[:, po], L.x[:, pi]
-    W0P = O.materialise(W0f, np.broadcast_to(np.eye(b), ora.R.shape), ora.P, b, b)
-    RW0 = O.materialise(W0f, ora.R, np.broadcast_to(np.eye(b), ora.P.shape), b, b)
-    gR = U.host(out["g_theta_R"])
-    gP = U.host(out["g_theta_P"])
-    for k in sorted({0, ora.R.shape[0] - 1}):
-        rk = slice(k * b, (k + 1) * b)
-        G = (gy[:, rk].T @ xx) @ W0P[rk, :].T
-        ref = ora.vjp(ora.B_R[k:k + 1], G[None])[0]
-        U.check(f"gthR[{k}]", gR[k], ref, s.dtype)
-    j = ora.P.shape[0] - 1
-    cj = slice(j * b, (j + 1) * b)
-    G = RW0[:, cj].T @ (gy.T @ xx[:, cj])
-    ref = ora.vjp(ora.B_P[j:j + 1], G[None])[0]
-    U.check(f"gthP[{j}]", gP[j], ref, s.dtype)
-    # property at full size: R is orthogonal per block, so ||y_t,k|| = ||z_t,k||
+    U.check_tiles("y", U.host(out["y"]), ora.forward(L.x), s.dtype)
+    if check_z and out.get("z") is not None and perms is None:
+        _, z_ref, _ = O.forward_input_centric(L.x, L.W0, ora.R, ora.P, b, b)
+        U.check_tiles("z", U.host(out["z"]), z_ref, s.dtype)
+        del z_ref
+    gx_ref, gR_ref, gP_ref = ora.backward(L.g_y, L.x)
+    U.check_tiles("g_x", U.host(out["g_x"]), gx_ref, s.dtype)
+    U.check_blocks("g_theta_R", U.host(out["g_theta_R"]), gR_ref, s.dtype)
+    U.check_blocks("g_theta_P", U.host(out["g_theta_P"]), gP_ref, s.dtype)
     # (the series is orthogonal to O(|Q|^6), far below bf16 at these sizes)
     if out.get("z") is not None and perms is None:
         y = out["y"].float().view(s.tokens, -1, b)
@@ -249,6 +236,19 @@ def _sampled_check(L, lay, out, n_rows=48, rng_seed=0, map="cayley", perms=None)
         assert rel <= 2e-2
 
 
+def test_persistent_dense_ragged_full_compare():
+    """4400 tokens, d_in = d_out = 4096, b = 256: 18 x 16 = 288 output tiles
+    of 256 x 256 in both dense products, more than one per CU, so the
+    persistent tile loop runs (several tiles per workgroup, the epilogue of
+    one tile before the copies of the next), and the last row of tiles is
+    ragged (shifted back inside M). Every element compared."""
+    spec = LayerSpec("persistent_ragged", 4096, 4096, 256, 4400, "bf16", 0.01, seed=11)
+    U.log(f"[layer] {spec.name}: d_in={spec.d_in} d_out={spec.d_out} b={spec.b} tokens={spec.tokens}")
+    L = make_layer(spec)
+    lay, out = U.run_layer(L)
+    _full_check(L, lay, out)
+
+
 @pytest.mark.parametrize("cfg", ["proj_1b", "mlp_up_8b", "sweep_b64", "sweep_b128", "sweep_b256",
                                  "sweep_b512", "sweep_b1024"])
 def test_full_size_workload(cfg):
@@ -256,7 +256,7 @@ def test_full_size_workload(cfg):
         U.log(f"[full] {cfg}/{spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
         L = make_layer(spec)
         lay, out = U.run_layer(L)
-        _sampled_check(L, lay, out)
+        _full_check(L, lay, out)
         del lay, out
         torch.cuda.empty_cache()
 
@@ -267,7 +267,7 @@ def test_full_size_layer_set_8b(layer):
     U.log(f"[full] layer_set_8b/{spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
     L = make_layer(spec)
     lay, out = U.run_layer(L)
-    _sampled_check(L, lay, out)
+    _full_check(L, lay, out)
     del lay, out
     torch.cuda.empty_cache()
 
@@ -297,7 +297,7 @@ def test_recompute_z_small(case):
 
 def test_recompute_z_full_size_mlp_up_8b():
     """The 8B MLP up-projection (14336 x 4096, b = 256, 8192 tokens) with Z
-    recomputed: sampled oracle checks, and equal to the stored-Z path."""
+    recomputed: every element against the oracle, and equal to the stored-Z path."""
     spec = CONFIGS["mlp_up_8b"][0]
     U.log(f"[recompute-z full] {spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
     L = make_layer(spec)
@@ -305,7 +305,7 @@ def test_recompute_z_full_size_mlp_up_8b():
     _, keep = U.run_layer(L)
     for k in ("y", "g_x", "g_theta_R", "g_theta_P"):
         assert torch.equal(mem[k], keep[k]), k
-    _sampled_check(L, lay, keep)
+    _full_check(L, lay, keep)
     del lay, mem, keep
     torch.cuda.empty_cache()
 
@@ -412,12 +412,12 @@ def test_cnp_deterministic_bitwise():
 
 def test_cnp_full_size_mlp_up_8b():
     """The 8B MLP up-projection (14336 x 4096, b = 256, 8192 tokens) with the
-    series map: sampled oracle checks."""
+    series map: every element against the oracle."""
     spec = CONFIGS["mlp_up_8b"][0]
     U.log(f"[cnp full] {spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
     L = make_layer(spec)
     lay, out = U.run_layer(L, map="cnp")
-    _sampled_check(L, lay, out, map="cnp")
+    _full_check(L, lay, out, map="cnp")
     del lay, out
     torch.cuda.empty_cache()
 
@@ -511,13 +511,13 @@ def test_perm_identity_maps_bitwise():
 
 def test_perm_full_size_mlp_up_8b():
     """The 8B MLP up-projection (14336 x 4096, b = 256, 8192 tokens) with
-    random block-mixing permutations: sampled oracle checks."""
+    random block-mixing permutations: every element against the oracle."""
     spec = CONFIGS["mlp_up_8b"][0]
     U.log(f"[perm full] {spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
     L = make_layer(spec)
     po, pi = make_permutations(spec)
     lay, out = U.run_layer(L, perms=(po, pi))
-    _sampled_check(L, lay, out, perms=(po, pi))
+    _full_check(L, lay, out, perms=(po, pi))
     del lay, out
     torch.cuda.empty_cache()
 
@@ -591,8 +591,8 @@ def test_int8_layer_small_full_compare(case):
 
 
 def test_int8_full_size_mlp_up_8b():
-    """The 8B MLP up-projection with an INT8 weight: sampled oracle checks
-    against the dequantised weight."""
+    """The 8B MLP up-projection with an INT8 weight: oracle checks
+    against the dequantised weight, every element."""
     spec = CONFIGS["mlp_up_8b"][0]
     U.log(f"[int8 full] {spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
     L = make_layer(spec)
@@ -605,6 +605,6 @@ def test_int8_full_size_mlp_up_8b():
     g_x, gR, gP = lay.backward(g_y, x, z)
     torch.cuda.synchronize()
     out = dict(y=y, z=None, g_x=g_x, g_theta_R=gR, g_theta_P=gP)
-    _sampled_check(_int8_reference_inputs(L), lay, out)
+    _full_check(_int8_reference_inputs(L), lay, out, check_z=False)
     del lay, out, y, z, g_x
     torch.cuda.empty_cache()
