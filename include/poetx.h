@@ -47,7 +47,8 @@
  *     returned as a status; nothing is enqueued then. A failed launch returns
  *     POETX_ERR_HIP. Non-finite inputs are not trapped (NaN in, NaN out).
  *     Nothing throws across this interface and the library keeps no state
- *     between calls.
+ *     between calls, except the fixed scratch area of
+ *     poetx_linear_fwd_noalloc.
  */
 #ifndef POETX_H
 #define POETX_H
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define POETX_ABI_VERSION 5
+#define POETX_ABI_VERSION 6
 
 typedef enum poetx_status {
   POETX_OK = 0,
@@ -269,6 +270,35 @@ size_t poetx_bwd_workspace_size(const poetx_linear_desc* desc);
 int poetx_linear_fwd(const poetx_linear_desc* desc, const void* x, const void* W0,
                      const void* R_act, const void* P_act, void* y, void* z_save,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the library's fixed device scratch area used by
+ * poetx_linear_fwd_noalloc (one copy per GPU, held until the process ends). */
+#define POETX_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * poetx_linear_fwd_noalloc - poetx_linear_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, with the
+ * forward's workspace taken from a scratch array inside the library instead
+ * of a caller-provided buffer. The call itself allocates and frees nothing.
+ *
+ *   desc, x, W0, R_act, P_act, y, z_save, stream  as for poetx_linear_fwd.
+ *
+ * Limit: poetx_fwd_workspace_size(desc) must not exceed
+ * POETX_NOALLOC_SCRATCH_BYTES (64 MiB: for example 8192 tokens x 4096 input
+ * features in bf16); a larger workspace returns POETX_ERR_WORKSPACE before
+ * anything is enqueued. Other argument faults are reported as by
+ * poetx_linear_fwd, also before anything is enqueued; POETX_ERR_HIP if the
+ * scratch area's device address cannot be obtained (it is looked up once per
+ * device, on that device's first call).
+ * Every call on one GPU uses the same scratch area, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap
+ * on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.
+ */
+int poetx_linear_fwd_noalloc(const poetx_linear_desc* desc, const void* x, const void* W0,
+                             const void* R_act, const void* P_act, void* y, void* z_save,
+                             void* stream);
 
 /*
  * poetx_linear_bwd - backward of the layer to the activations and to the

@@ -398,6 +398,19 @@ hipError_t cnp_vjp(const CnpVjpSet& a, const CnpVjpSet* b2, int b, hipStream_t s
 
 int hip_status(hipError_t e) { return e == hipSuccess ? POETX_OK : POETX_ERR_HIP; }
 
+// The forward's host-detectable argument faults other than the workspace.
+int check_fwd_args(const poetx_linear_desc* d, const void* x, const void* W0, const void* R_act,
+                   const void* P_act, const void* y, const void* z_save) {
+  int st = check_desc(d);
+  if (st != POETX_OK) return st;
+  if (!x || !W0 || !R_act || !P_act || !y) return POETX_ERR_NULL;
+  if (recompute_z(d) ? z_save != nullptr : z_save == nullptr) return POETX_ERR_NULL;
+  const void* ptrs[] = {x, W0, R_act, P_act, y, z_save};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return POETX_ERR_ALIGN;
+  return POETX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -577,13 +590,9 @@ size_t poetx_bwd_workspace_size(const poetx_linear_desc* d) {
 int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, const void* R_act,
                      const void* P_act, void* y, void* z_save, void* ws, size_t ws_bytes,
                      void* stream) {
-  int st = check_desc(d);
+  int st = check_fwd_args(d, x, W0, R_act, P_act, y, z_save);
   if (st != POETX_OK) return st;
-  if (!x || !W0 || !R_act || !P_act || !y) return POETX_ERR_NULL;
-  if (recompute_z(d) ? z_save != nullptr : z_save == nullptr) return POETX_ERR_NULL;
-  const void* ptrs[] = {x, W0, R_act, P_act, y, z_save, ws};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return POETX_ERR_ALIGN;
+  if (ws && !aligned16(ws)) return POETX_ERR_ALIGN;
   const FwdPlan plan = plan_fwd(d);
   if (!ws || ws_bytes < plan.total) return POETX_ERR_WORKSPACE;
 
@@ -676,6 +685,20 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
     if ((e = sg.end(4)) != hipSuccess) return hip_status(e);
   }
   return POETX_OK;
+}
+
+int poetx_linear_fwd_noalloc(const poetx_linear_desc* d, const void* x, const void* W0,
+                             const void* R_act, const void* P_act, void* y, void* z_save,
+                             void* stream) {
+  // every argument check that needs no HIP call comes first
+  int st = check_fwd_args(d, x, W0, R_act, P_act, y, z_save);
+  if (st != POETX_OK) return st;
+  if (plan_fwd(d).total > (size_t)POETX_NOALLOC_SCRATCH_BYTES) return POETX_ERR_WORKSPACE;
+  void* scratch = nullptr;  // this device's copy of the library's scratch array
+  hipError_t e = poetx::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return POETX_ERR_HIP;
+  return poetx_linear_fwd(d, x, W0, R_act, P_act, y, z_save, scratch,
+                          (size_t)POETX_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x, const void* W0,

@@ -42,6 +42,10 @@ struct GemmParams {
   const void* D2 = nullptr;
 };
 
+// Device address of the library's fixed scratch array (POETX_NOALLOC_SCRATCH_BYTES)
+// on the current device, looked up once per device; no allocation.
+hipError_t noalloc_scratch(void** ptr);
+
 // Returns hipSuccess or the launch error.
 hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor,
                        const GemmParams& p, hipStream_t stream);

@@ -29,7 +29,7 @@ POETX_ERR_ALIAS = 7
 POETX_F32 = 0
 POETX_BF16 = 1
 
-POETX_ABI_VERSION = 5
+POETX_ABI_VERSION = 6
 POETX_RECOMPUTE_Z = 1
 POETX_CAYLEY_NEUMANN = 2
 
@@ -37,7 +37,7 @@ EXPORTS = (
     "poetx_abi_version", "poetx_status_string", "poetx_num_blocks", "poetx_theta_count",
     "poetx_build_workspace_size", "poetx_build_orthogonal", "poetx_build_cnp_workspace_size",
     "poetx_build_cnp", "poetx_fold_weight", "poetx_quantize_weight", "poetx_fwd_workspace_size",
-    "poetx_bwd_workspace_size", "poetx_linear_fwd", "poetx_linear_bwd",
+    "poetx_bwd_workspace_size", "poetx_linear_fwd", "poetx_linear_fwd_noalloc", "poetx_linear_bwd",
     "poetx_event_create", "poetx_event_destroy", "poetx_event_record",
     "poetx_event_synchronize", "poetx_event_elapsed_ms",
 )
@@ -89,6 +89,7 @@ def _load() -> ctypes.CDLL:
         "poetx_fwd_workspace_size": (sz, [dp]),
         "poetx_bwd_workspace_size": (sz, [dp]),
         "poetx_linear_fwd": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "poetx_linear_fwd_noalloc": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp]),
         "poetx_linear_bwd": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "poetx_event_create": (ctypes.c_int, [ctypes.POINTER(vp)]),
         "poetx_event_destroy": (ctypes.c_int, [vp]),
@@ -216,6 +217,17 @@ def poetx_linear_fwd(desc, x, W0, R_act, P_act, y, z_save, ws, stream=None, raw=
     if raw:
         return st
     _check(st, "poetx_linear_fwd")
+
+
+POETX_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def poetx_linear_fwd_noalloc(desc, x, W0, R_act, P_act, y, z_save, stream=None, raw=False):
+    st = _lib.poetx_linear_fwd_noalloc(ctypes.byref(desc), _ptr(x), _ptr(W0), _ptr(R_act),
+                                       _ptr(P_act), _ptr(y), _ptr(z_save), _stream(stream))
+    if raw:
+        return st
+    _check(st, "poetx_linear_fwd_noalloc")
 
 
 def poetx_linear_bwd(desc, g_y, x, W0, R_f32, P_f32, R_act, P_act, z_saved, g_x, g_theta_R,

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 5
+    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 6
     for s in range(8):
         assert P.status_string(s) and P.status_string(s) != "unknown status"
     assert P.status_string(99) == "unknown status"
@@ -439,3 +439,34 @@ def test_quantize_weight_errors():
     assert call(sc=ALIGNED * 3 + 2) == P.POETX_ERR_ALIGN
     assert call(q=ALIGNED) == P.POETX_ERR_ALIAS                 # codes on top of W0
     assert call(sc=ALIGNED * 2 + 64) == P.POETX_ERR_ALIAS       # scales inside the codes
+
+
+# -- poetx_linear_fwd_noalloc: the forward with the library's fixed scratch ---
+
+def _fwd_noalloc(desc, **over):
+    args = dict(x=ALIGNED, W0=ALIGNED * 2, R=ALIGNED * 3, P=ALIGNED * 4, y=ALIGNED * 64,
+                z=ALIGNED * 128)
+    args.update(over)
+    return P._lib.poetx_linear_fwd_noalloc(ctypes.byref(desc), args["x"], args["W0"], args["R"],
+                                           args["P"], args["y"], args["z"], None)
+
+
+def test_noalloc_forward_host_checks():
+    """Argument faults and a workspace beyond the scratch area are reported
+    before any HIP call (so they are seen here, without a GPU)."""
+    assert P.POETX_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert _fwd_noalloc(desc(tokens=0)) == P.POETX_ERR_SHAPE
+    assert _fwd_noalloc(desc(act=5)) == P.POETX_ERR_DTYPE
+    assert _fwd_noalloc(desc(), x=None) == P.POETX_ERR_NULL
+    assert _fwd_noalloc(desc(), z=None) == P.POETX_ERR_NULL
+    assert _fwd_noalloc(desc(flags=P.POETX_RECOMPUTE_Z)) == P.POETX_ERR_NULL  # z must be NULL then
+    assert _fwd_noalloc(desc(), y=ALIGNED * 64 + 2) == P.POETX_ERR_ALIGN
+    # the 8B-class MLP up-projection's forward fits exactly; one more token does not
+    fits = desc(tokens=8192, d_in=4096, d_out=14336, b_in=256, b_out=256)
+    assert P.poetx_fwd_workspace_size(fits) == P.POETX_NOALLOC_SCRATCH_BYTES
+    over = desc(tokens=8193, d_in=4096, d_out=14336, b_in=256, b_out=256)
+    assert P.poetx_fwd_workspace_size(over) > P.POETX_NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(over) == P.POETX_ERR_WORKSPACE
+    # POET-Xmem keeps Z in the forward's workspace: too large here
+    mem = desc(tokens=8192, d_in=4096, d_out=14336, b_in=256, b_out=256, flags=P.POETX_RECOMPUTE_Z)
+    assert _fwd_noalloc(mem, z=None) == P.POETX_ERR_WORKSPACE

@@ -1,0 +1,79 @@
+"""poetx_linear_fwd_noalloc (the forward with the library's fixed device
+scratch instead of a caller workspace) against poetx_linear_fwd, through the
+C ABI: two calls in a row, the second with a smaller layer, each compared
+with the workspace entry point's output (bit for bit: the same kernels in the
+same order) and with the float64 oracle at the bf16 tolerance.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU too; every test here is gpu-marked
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle.poetx_oracle as O  # noqa: E402
+from orthogonal_equivalence_amd import poetx as P  # noqa: E402
+from orthogonal_equivalence_amd.inputs import LayerSpec, make_layer  # noqa: E402
+from orthogonal_equivalence_amd.layer import PoetxLinear  # noqa: E402
+from tests import gpu_util as U  # noqa: E402
+
+CALLS = [
+    # the first call fills most of the scratch area, the second is smaller
+    LayerSpec("noalloc_big", 2048, 4096, 256, 8192, "bf16", 0.01, seed=21),  # 32 MiB of U
+    LayerSpec("noalloc_small", 512, 768, 128, 300, "bf16", 0.02, seed=22),
+]
+
+
+def _layer(spec):
+    L = make_layer(spec)
+    lay = PoetxLinear(U.dev(L.W0, spec.dtype), spec.b, spec.b, spec.dtype)
+    lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
+    lay.build()
+    return L, lay
+
+
+def test_noalloc_forward_matches_workspace_forward():
+    for spec in CALLS:
+        U.log(f"[noalloc] {spec.name}: d_in={spec.d_in} d_out={spec.d_out} b={spec.b} "
+              f"tokens={spec.tokens}")
+        L, lay = _layer(spec)
+        x = U.dev(L.x, spec.dtype)
+        d = lay.desc(spec.tokens)
+        assert P.poetx_fwd_workspace_size(d) <= P.POETX_NOALLOC_SCRATCH_BYTES
+        shape = (spec.tokens, spec.d_out)
+        y_ws = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        z_ws = torch.empty_like(y_ws)
+        ws = torch.empty(P.poetx_fwd_workspace_size(d), dtype=torch.uint8, device="cuda")
+        P.poetx_linear_fwd(d, x, lay.W0, lay.R_act, lay.P_act, y_ws, z_ws, ws)
+        # NaN-filled outputs: every element must be written by the call
+        y_na = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        z_na = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        P.poetx_linear_fwd_noalloc(d, x, lay.W0, lay.R_act, lay.P_act, y_na, z_na)
+        torch.cuda.synchronize()
+        assert torch.equal(y_na, y_ws) and torch.equal(z_na, z_ws)
+        ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b)
+        U.check("y", U.host(y_na), ora.forward(L.x), spec.dtype)
+        _, z_ref, _ = O.forward_input_centric(L.x, L.W0, ora.R, ora.P, spec.b, spec.b)
+        U.check("z", U.host(z_na), z_ref, spec.dtype)
+        del lay, ws, x, y_ws, z_ws, y_na, z_na
+        torch.cuda.empty_cache()
+
+
+def test_noalloc_forward_rejects_oversize_workspace():
+    """A forward whose workspace exceeds the scratch area is refused before
+    anything is enqueued (outputs untouched)."""
+    spec = LayerSpec("noalloc_over", 4096, 512, 256, 8200, "bf16", 0.01, seed=23)
+    L, lay = _layer(spec)
+    d = lay.desc(spec.tokens)
+    assert P.poetx_fwd_workspace_size(d) > P.POETX_NOALLOC_SCRATCH_BYTES
+    x = U.dev(L.x, spec.dtype)
+    y = torch.full((spec.tokens, spec.d_out), 7.0, dtype=torch.bfloat16, device="cuda")
+    z = torch.full_like(y, 7.0)
+    st = P.poetx_linear_fwd_noalloc(d, x, lay.W0, lay.R_act, lay.P_act, y, z, raw=True)
+    torch.cuda.synchronize()
+    assert st == P.POETX_ERR_WORKSPACE
+    assert bool((y == 7.0).all()) and bool((z == 7.0).all())
+    np.testing.assert_equal(P.status_string(st), "workspace missing or too small")
