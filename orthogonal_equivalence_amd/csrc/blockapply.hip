@@ -42,11 +42,9 @@
 // and the workgroup accumulates that part of the gram X^T C
 // (v_mfma_f32_32x32x16_bf16, fragments read with the transposing LDS read).
 // At b = 128 a workgroup holds the whole block and its whole 128 x 128 gram
-// (64-token tiles), so every operand crosses the CU once. At b = 256 the
-// block and the gram together would need about 450 registers, so two slab
-// workgroups of 128 output columns (8 ids apart) each take 32-token tiles of
-// all 256 input columns and their 256 x 128 half of the gram: the gradient
-// still comes from HBM about once, and the gram partials are half as many.
+// (64-token tiles), so every operand crosses the CU once. The b = 256 case,
+// whose block and gram need about 480 registers per lane, is its own kernel
+// (gramapply.hip).
 //
 // Waits on the LDS-bound loads are explicit: before tile t, the wave waits
 // until at most (number of its tile loads issued after tile t) vector memory
@@ -111,7 +109,7 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 }
 
 // B: block size (the K extent); NC: output columns per workgroup (B, or 256
-// at B = 512); TT: tokens per tile. GRAM (B = 256, NC = 128, TT = 32, no
+// at B = 512); TT: tokens per tile. GRAM (B = 128, NC = 128, TT = 64, no
 // transpose): the workgroup also accumulates the gram
 //   part[split][blk][:, slab NC ..] = X[t, blk]^T C[t, blk cols slab NC ..]
 // over its tokens from the same input tiles (C's NC columns ride in each
@@ -129,9 +127,7 @@ struct BlockApply {
   static constexpr int LPT = LPW + LPC;             // loads per wave per tile
   static_assert(STAGE + (GRAM ? TT * NC : 0) <= kStage && TT % 32 == 0 && NC % 128 == 0 && CPT >= 1,
                 "tile shape");
-  static_assert(!GRAM || (!TRANS && ((B == 256 && NC == 128 && TT == 32) ||
-                                      (B == 128 && NC == 128 && TT == 64))),
-                "gram variant shape");
+  static_assert(!GRAM || (!TRANS && B == 128 && NC == 128 && TT == 64), "gram variant shape");
   // gram: 2 x 2 waves over the B x NC result, wave tile (B/2) x (NC/2)
   static constexpr int GM = B / 2 / 32, GN = NC / 2 / 32;
 
@@ -517,7 +513,7 @@ hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, vo
                                  int64_t tokens, int64_t d, int b, int max_split, int* nsplit,
                                  hipStream_t s) {
   if ((b != 128 && b != 256) || d % b != 0 || tokens < 1 || max_split < 1) return hipErrorInvalidValue;
-  if (b == 256) return launch_gram_b<256, 128, 32>(X, M, C, Y, part, tokens, d, max_split, nsplit, s);
+  if (b == 256) return launch_gramapply256(X, M, C, Y, part, tokens, d, max_split, nsplit, s);
   return launch_gram_b<128, 128, 64>(X, M, C, Y, part, tokens, d, max_split, nsplit, s);
 }
 

@@ -83,6 +83,11 @@ hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t toke
 // summed over the tokens of split s. *nsplit (<= max_split) receives the
 // number of splits written; the splits cover the tokens in order.
 bool blockgramapply_supported(DType t, int64_t d, int b);
+// The b = 256 case of launch_blockgramapply: one workgroup per block and
+// token range holding the whole block and its whole gram.
+hipError_t launch_gramapply256(const void* X, const void* M, const void* C, void* Y, float* part,
+                               int64_t tokens, int64_t d, int max_split, int* nsplit,
+                               hipStream_t s);
 hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, void* Y, float* part,
                                  int64_t tokens, int64_t d, int b, int max_split, int* nsplit,
                                  hipStream_t s);
