@@ -197,6 +197,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=8192,
                     help="tokens of the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache steps (profiling runs)")
     ap.add_argument("--recompute-z", action="store_true",
                     help="POET-Xmem variant: the forward keeps no Z, the backward recomputes it")
     ap.add_argument("--permute", action="store_true",
@@ -345,17 +347,19 @@ def main():
     # ---- cold variant: K more steps, each after a 512 MB scratch write (more
     # than the 256 MB Infinity Cache), so W0 and the activations are not left
     # resident by the previous step; the write itself is outside the events
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold_ev = [(P.Event(), P.Event()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        scratch.fill_(k & 0xFF)
-        cold_ev[k][0].record(stream)
-        step()
-        cold_ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    cold_ms = [a.elapsed_ms(b) for a, b in cold_ev]
-    del scratch
+    cold_ms = []
+    if not args.no_cold:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ev = [(P.Event(), P.Event()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for k in range(args.steps):
+            scratch.fill_(k & 0xFF)
+            cold_ev[k][0].record(stream)
+            step()
+            cold_ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        cold_ms = [a.elapsed_ms(b) for a, b in cold_ev]
+        del scratch
 
     # ---- stage breakdown: K more steps with an event pair around every stage
     # and every step (slower than the timed steps by the records themselves)
@@ -429,12 +433,13 @@ def main():
                            "frac": t_roof / (ms_per_step / 1e3),
                            "tflops": F / (ms_per_step / 1e3) / 1e12},
         "wall_s": wall,
-        "cold": {"what": "the same step after a 512 MB scratch write (evicts the Infinity "
-                         "Cache); one event pair around each step",
-                 "ms_per_step_median": statistics.median(cold_ms),
-                 "ms_per_step_mean": statistics.mean(cold_ms),
-                 "ms_per_step_min": min(cold_ms), "ms_per_step_max": max(cold_ms),
-                 "tokens_per_s_median": tokens / (statistics.median(cold_ms) / 1e3)},
+        "cold": None if not cold_ms else {
+            "what": "the same step after a 512 MB scratch write (evicts the Infinity Cache); "
+                    "one event pair around each step",
+            "ms_per_step_median": statistics.median(cold_ms),
+            "ms_per_step_mean": statistics.mean(cold_ms),
+            "ms_per_step_min": min(cold_ms), "ms_per_step_max": max(cold_ms),
+            "tokens_per_s_median": tokens / (statistics.median(cold_ms) / 1e3)},
         # from the instrumented steps that follow the timed ones
         "instrumented_step_ms": {"median": statistics.median(step_ms), "min": min(step_ms),
                                  "max": max(step_ms)},
