@@ -395,6 +395,12 @@ def main():
 
     sb = layers[big][0]
     dense_flops = 2.0 * sb.tokens * sb.d_in * sb.d_out
+    # with bf16 and 256 x 256 R blocks the forward's R-apply runs in the dense
+    # kernel's epilogue (dense_kernel<true, true>), so that launch also does
+    # the R-apply's 2 N d_out b flops
+    fused_r = sb.dtype == "bf16" and sb.b == 256 and sb.d_out % 256 == 0
+    if fused_r:
+        dense_flops += 2.0 * sb.tokens * sb.d_out * sb.b
     peak = PEAK_BF16 if sb.dtype == "bf16" else PEAK_F32
     achieved = dense_flops / (dense_ms / 1e3)
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
@@ -402,8 +408,11 @@ def main():
                 "traffic_kind": "L2-miss bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a "
                                 "plain copy): requests leaving the L2, answered by the Infinity "
                                 "Cache or HBM; null when the kernel changed since the passes",
-                "kernel": "dense_fwd: Z = U W0^T (dense_kernel<true>: bf16, K-major W0, "
-                          "persistent, direct-to-LDS, 4 waves of 128x128, 16x16x32 MFMA)",
+                "kernel": ("dense_fwd: Z = U W0^T with Y = Z blockdiag(R)^T in its epilogue "
+                           "(dense_kernel<true, true>" if fused_r else
+                           "dense_fwd: Z = U W0^T (dense_kernel<true, false>") +
+                          ": bf16, K-major W0, persistent, direct-to-LDS, 4 waves of 128x128, "
+                          "16x16x32 MFMA)",
                 "flops_per_launch": dense_flops, "avg_launch_ms": dense_ms}
 
     F = sum(layer_work(s)[0] for s, *_ in layers)

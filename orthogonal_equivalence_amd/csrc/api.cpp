@@ -662,14 +662,24 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   if ((e = block_apply(t, X, P_act, U, N, n, d->b_in, true, s, SB)) != hipSuccess) return hip_status(e);
   if ((e = sg.end(0)) != hipSuccess) return hip_status(e);
 
-  // S3: Z = U W0^T
+  // S3: Z = U W0^T, and S4: Y = Z blockdiag(R)^T. With 256 x 256 R blocks in
+  // bf16 the R-apply runs in the dense kernel's epilogue: every 256-column
+  // output tile is one R block, so the tile's Z, still on the CU, is
+  // multiplied by its block before it leaves (stage 1 then holds both and
+  // stage 2 is empty).
+  void* Yout = perm ? Yp : y;
+  const bool fuse_r = t == DType::BF16 && d->b_out == 256 && m % 256 == 0 &&
+                      poetx::dense_fused_r_supported(N, m, n, n, n, m, m);
   if ((e = sg.begin(1)) != hipSuccess) return hip_status(e);
-  if ((e = dense(t, U, Wmat, Z, N, m, n, n, n, m, true, s)) != hipSuccess) return hip_status(e);
+  if (fuse_r) {
+    if ((e = poetx::launch_dense_fused_r(U, Wmat, Z, N, m, n, n, n, m, Rb, Yout, m, s)) != hipSuccess)
+      return hip_status(e);
+  } else if ((e = dense(t, U, Wmat, Z, N, m, n, n, n, m, true, s)) != hipSuccess) {
+    return hip_status(e);
+  }
   if ((e = sg.end(1)) != hipSuccess) return hip_status(e);
-
-  // S4: Y = Z blockdiag(R)^T
   if ((e = sg.begin(2)) != hipSuccess) return hip_status(e);
-  if ((e = block_apply(t, Z, Rb, perm ? Yp : y, N, m, d->b_out, true, s, SB)) != hipSuccess)
+  if (!fuse_r && (e = block_apply(t, Z, Rb, Yout, N, m, d->b_out, true, s, SB)) != hipSuccess)
     return hip_status(e);
   if ((e = sg.end(2)) != hipSuccess) return hip_status(e);
 

@@ -332,12 +332,92 @@ struct Dense {
     wait_lds();
     barrier_nofence();
   }
+
+  // ---- forward with the R-apply fused (B K-major, 256 x 256 R blocks) ----
+  // Y tile = Z tile R_k^T for the output tile's R block R_k (its 256 columns
+  // are one block): the bf16 Z tile staged in the ring is the A operand, R_k's
+  // rows are the B fragments (loaded from global memory, the block stays in
+  // L2), K = 256 in 8 steps of 32, accumulated in the same AGPRs.
+  template <int S>
+  __device__ __forceinline__ void load_r(const bf16_t* rrow) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[S & 1][j] = *reinterpret_cast<const bf16x8_t*>(rrow + j * 16 * 256 + S * 32);
+  }
+  template <int S>
+  __device__ __forceinline__ void r_step(const bf16_t* rrow, int ln) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[S & 1][i] = *reinterpret_cast<const bf16x8_t*>(
+          g_dense_lds + stage_off(wm * 128 + 16 * i + (ln & 15), 32 * S + 8 * (ln >> 4)));
+    if (S + 1 < 8) load_r<(S + 1) & 7>(rrow);
+    mma_row<S & 1, 0, S == 0>(); mma_row<S & 1, 1, S == 0>();
+    mma_row<S & 1, 2, S == 0>(); mma_row<S & 1, 3, S == 0>();
+    mma_row<S & 1, 4, S == 0>(); mma_row<S & 1, 5, S == 0>();
+    mma_row<S & 1, 6, S == 0>(); mma_row<S & 1, 7, S == 0>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the accumulators -> bf16 -> staging tile (the whole ring)
+  __device__ __forceinline__ void stage_acc(int ln) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int m = wm * 128 + 16 * i + (ln & 15);
+        const int n = wn * 128 + 16 * j + 4 * (ln >> 4);
+        union { bf16_t h[4]; uint2 v; } u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u.h[e] = f32_to_bf16(acc[i][j][e]);
+        *reinterpret_cast<uint2*>(g_dense_lds + stage_off(m, n)) = u.v;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+  // the staging tile -> 16-byte stores of whole row segments of C (row stride ldc)
+  __device__ __forceinline__ void store_staged(bf16_t* __restrict__ C, int64_t ldc, int m0, int n0,
+                                               int tid) {
+#pragma unroll
+    for (int q = 0; q < BM * BN / 8 / NT; ++q) {
+      const int c = tid + q * NT;
+      const int rl = c >> 5, nl = (c & 31) * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(g_dense_lds + stage_off(rl, nl));
+      *reinterpret_cast<uint4*>(C + (int64_t)(m0 + rl) * ldc + n0 + nl) = v;
+    }
+  }
+  __device__ __forceinline__ void epilogue_fused(bf16_t* __restrict__ C, int64_t ldc, int m0,
+                                                 int n0, const bf16_t* __restrict__ Rk,
+                                                 bf16_t* __restrict__ Y, int64_t ldy) {
+    int ln = lane, tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(ln), "+v"(tid));
+    // B fragment (j, step s) of lane l: R_k row wn 128 + 16 j + l % 16,
+    // columns 32 s + 8 (l / 16) .. + 7
+    const bf16_t* rrow = Rk + (wn * 128 + (ln & 15)) * 256 + 8 * (ln >> 4);
+    load_r<0>(rrow);  // in flight while Z is staged
+    stage_acc(ln);
+    wait_lds();
+    barrier_nofence();  // (no memory fence: nothing waits for the loads or stores here)
+    r_step<0>(rrow, ln); r_step<1>(rrow, ln); r_step<2>(rrow, ln); r_step<3>(rrow, ln);
+    r_step<4>(rrow, ln); r_step<5>(rrow, ln); r_step<6>(rrow, ln); r_step<7>(rrow, ln);
+    // wait states before the VALU reads of the products' results
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    store_staged(C, ldc, m0, n0, tid);  // Z
+    wait_lds();
+    barrier_nofence();  // every wave is done reading the staged Z
+    stage_acc(ln);
+    wait_lds();
+    barrier_nofence();  // Z's stores stay in flight
+    store_staged(Y, ldy, m0, n0, tid);  // Y
+    wait_lds();
+    barrier_nofence();
+  }
 };
 
-template <bool B_KMAJ>
+template <bool B_KMAJ, bool FUSE_R = false>
 __global__ void __launch_bounds__(NT)
 dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C,
-             int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc) {
+             int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc,
+             const bf16_t* __restrict__ R = nullptr, bf16_t* __restrict__ Y = nullptr,
+             int64_t ldy = 0) {
   const int num_mt = (M + BM - 1) / BM, num_nt = (N + BN - 1) / BN;
   const int total = num_mt * num_nt;
   const int ntiles = K / BK;
@@ -356,7 +436,10 @@ dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
     d.mainloop(ntiles);
     wait_lds();
     barrier_nofence();  // every wave is done with the ring
-    d.epilogue(C, ldc, m0, n0);
+    if constexpr (FUSE_R)
+      d.epilogue_fused(C, ldc, m0, n0, R + (int64_t)(n0 / 256) * 256 * 256, Y, ldy);
+    else
+      d.epilogue(C, ldc, m0, n0);
     tile += (int)gridDim.x;
     if (tile >= total) break;
   }
@@ -371,8 +454,8 @@ bool dense_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, 
          lda <= (1 << 22) && ldb <= (1 << 22);
 }
 
-hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                        int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s) {
+namespace {
+hipError_t dense_grid(int64_t M, int64_t N, int* grid_out) {
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
   // one workgroup per CU (the register and LDS footprints allow no more),
   // rounded down to a multiple of the 8 XCDs
@@ -388,6 +471,16 @@ hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_
   int grid = cached_cus >= 8 ? cached_cus & ~7 : cached_cus;
   if (grid > tiles) grid = tiles;
   if (grid < 1) grid = 1;
+  *grid_out = grid;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s) {
+  int grid = 0;
+  hipError_t e = dense_grid(M, N, &grid);
+  if (e != hipSuccess) return e;
   const bf16_t* a = static_cast<const bf16_t*>(A);
   const bf16_t* b = static_cast<const bf16_t*>(B);
   bf16_t* c = static_cast<bf16_t*>(C);
@@ -397,6 +490,24 @@ hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_
   else
     hipLaunchKernelGGL(dense_kernel<false>, dim3(grid), dim3(NT), 0, s, a, b, c, (int)M, (int)N,
                        (int)K, lda, ldb, ldc);
+  return hipGetLastError();
+}
+
+bool dense_fused_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                             int64_t ldc, int64_t ldy) {
+  return dense_supported(M, N, K, lda, ldb, ldc) && N % 256 == 0 && ldy % 8 == 0;
+}
+
+hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                                int64_t K, int64_t lda, int64_t ldb, int64_t ldc, const void* R,
+                                void* Y, int64_t ldy, hipStream_t s) {
+  int grid = 0;
+  hipError_t e = dense_grid(M, N, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dense_kernel<true, true>), dim3(grid), dim3(NT), 0, s,
+                     static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B),
+                     static_cast<bf16_t*>(C), (int)M, (int)N, (int)K, lda, ldb, ldc,
+                     static_cast<const bf16_t*>(R), static_cast<bf16_t*>(Y), ldy);
   return hipGetLastError();
 }
 

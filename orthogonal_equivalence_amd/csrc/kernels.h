@@ -61,6 +61,15 @@ int gemm_tile_m(DType in, int M, int N);
 bool dense_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc);
 hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                         int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s);
+// The forward's dense product with the R-apply fused into its epilogue
+// (256 x 256 R blocks, bf16): C = A B^T (B K-major) and Y = C blockdiag(R)^T
+// with C rounded to bf16 before the second product, as the separate R-apply
+// would read it. N must be a multiple of 256; R is [N / 256][256][256].
+bool dense_fused_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                             int64_t ldc, int64_t ldy);
+hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                                int64_t K, int64_t lda, int64_t ldb, int64_t ldc, const void* R,
+                                void* Y, int64_t ldy, hipStream_t s);
 
 // ---- streaming block-diagonal apply (bf16, b = 128 or 256, b | d) ----
 // Y[:, blk] = X[:, blk] M_blk^T (transpose) or X[:, blk] M_blk, token-major
