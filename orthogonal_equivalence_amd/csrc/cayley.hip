@@ -766,7 +766,13 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
                                float* blocks_f32, void* blocks_act, DType act, float* ws,
                                hipStream_t stream) {
   bf16_t* act_bf16 = (act == DType::BF16) ? static_cast<bf16_t*>(blocks_act) : nullptr;
-  if (b == 128 || b == 256) {  // the whole block on one CU
+  // The whole-block kernel takes about the same time for any number of blocks
+  // up to one per CU (its latency is the elimination's sequence of pivots on
+  // one CU); the panel kernels spread every block's products over the chip, so
+  // with few blocks of 256 they finish first (measured: 16 blocks 164 -> 119
+  // us, 32 blocks 172 -> 140 us), with 64 or more the whole-block kernel does.
+  const bool whole_block = b == 128 || (b == 256 && nblocks >= 48);
+  if (whole_block) {  // the whole block on one CU
     if (b == 256)
       hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nblocks), dim3(BlockShape<4>::THREADS),
                          0, stream, theta, (int)nblocks, last_valid, blocks_f32, act_bf16);
