@@ -230,7 +230,21 @@ hipError_t block_apply(DType t, const void* in, const void* blocks, void* out, i
     if (e != hipSuccess) return e;
     return poetx::launch_blockapply(in, super_ws, out, tokens, d, S, transpose, s);
   }
-  if (poetx::blockapply_supported(t, d, b))
+  const bool streaming = poetx::blockapply_supported(t, d, b);
+  if (t == DType::BF16 && b >= 512 && b % 256 == 0 && d % b == 0 &&
+      poetx::dense_supported(tokens, b, b, d, b, d) &&
+      (!streaming || poetx::blockapply_tokens_per_workgroup(tokens, d, b) <= 512)) {
+    // blocks of 512 and more: the batched dense kernel, one 256 x 256 output
+    // tile of one block per workgroup, all blocks in one launch. For b = 512
+    // the streaming kernel is faster once each of its workgroups covers more
+    // than 512 tokens: with K = 512 the dense kernel's tile fill and store
+    // take about as long as its 16 K steps (measured: 16384 tokens of
+    // d = 14336, 306 us streaming against 385 us dense; 8192 tokens of
+    // d = 4096, 54 us streaming against 48 us dense).
+    return poetx::launch_dense_batched(in, blocks, out, tokens, b, b, d, b, d, transpose, d / b, b,
+                                       (int64_t)b * b, b, s);
+  }
+  if (streaming)
     return poetx::launch_blockapply(in, blocks, out, tokens, d, b, transpose, s);
   bool bk;
   GemmParams g = blockdiag_params(in, blocks, out, tokens, d, b, transpose, &bk);

@@ -423,19 +423,25 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb, b
   }
 }
 
+// Token range of one workgroup: one round of at most 256 workgroups (one per
+// CU), token ranges in whole tiles of TT.
+int tokens_per_workgroup(int64_t tokens, int64_t d, int B, int NC, int TT) {
+  const int nb = (int)(d / B);
+  int splits = 256 / (nb * (B / NC));
+  const int max_splits = (int)((tokens + TT - 1) / TT);
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int per = (int)((tokens + splits - 1) / splits);
+  return (per + TT - 1) / TT * TT;
+}
+
 template <int B, int NC, int TT, bool TRANS>
 hipError_t launch_b(const bf16_t* X, const bf16_t* M, bf16_t* Y, int64_t tokens, int64_t d,
                     hipStream_t s) {
   constexpr int NSLAB = B / NC;
   const int nb = (int)(d / B);
-  // one round of at most 256 workgroups (one per CU), token ranges in whole tiles
-  int splits = 256 / (nb * NSLAB);
-  const int max_splits = (int)((tokens + TT - 1) / TT);
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  int per = (int)((tokens + splits - 1) / splits);
-  per = (per + TT - 1) / TT * TT;
-  splits = (int)((tokens + per - 1) / per);
+  const int per = tokens_per_workgroup(tokens, d, B, NC, TT);
+  const int splits = (int)((tokens + per - 1) / per);
   const int units = nb * splits;
   const int grid = NSLAB == 1 ? units : (units + 7) / 8 * (8 * NSLAB);
   hipLaunchKernelGGL((blockapply_kernel<B, NC, TT, TRANS>), dim3(grid), dim3(kNT), 0, s, X, M, Y,
@@ -519,6 +525,12 @@ hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, vo
 
 bool blockapply_supported(DType t, int64_t d, int b) {
   return t == DType::BF16 && (b == 128 || b == 256 || b == 512) && d % b == 0;
+}
+
+int64_t blockapply_tokens_per_workgroup(int64_t tokens, int64_t d, int b) {
+  if (b == 512) return tokens_per_workgroup(tokens, d, 512, 256, 32);
+  if (b == 256) return tokens_per_workgroup(tokens, d, 256, 256, 64);
+  return tokens_per_workgroup(tokens, d, 128, 128, 64);
 }
 
 hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,

@@ -412,14 +412,18 @@ struct Dense {
   }
 };
 
+// nbatch independent products of the same shape, product q at A + q sA,
+// B + q sB, C + q sC (the block-diagonal products of b >= 512 blocks run as
+// one batched launch); their output tiles form one grid of num_mt x
+// (nbatch num_nt) tiles, products side by side along N.
 template <bool B_KMAJ, bool FUSE_R = false>
 __global__ void __launch_bounds__(NT)
 dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C,
              int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc,
-             const bf16_t* __restrict__ R = nullptr, bf16_t* __restrict__ Y = nullptr,
-             int64_t ldy = 0) {
+             const bf16_t* __restrict__ R, bf16_t* __restrict__ Y, int64_t ldy, int nbatch,
+             int64_t sA, int64_t sB, int64_t sC) {
   const int num_mt = (M + BM - 1) / BM, num_nt = (N + BN - 1) / BN;
-  const int total = num_mt * num_nt;
+  const int total = num_mt * num_nt * nbatch;
   const int ntiles = K / BK;
   int tile = blockIdx.x;
   if (tile >= total) return;
@@ -427,10 +431,11 @@ dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
   Dense<B_KMAJ> d;
   d.init(lda, ldb);
   for (;;) {
-    int mt, nt;
-    xcd_grouped_tile_at(tile, total, num_mt, num_nt, mt, nt);
+    int mt, ntb;
+    xcd_grouped_tile_at(tile, total, num_mt, num_nt * nbatch, mt, ntb);
+    const int q = ntb / num_nt, nt = ntb - q * num_nt;
     const int m0 = min(mt * BM, M - BM), n0 = min(nt * BN, N - BN);
-    d.set_tile(A, B, lda, ldb, m0, n0);
+    d.set_tile(A + q * sA, B + q * sB, lda, ldb, m0, n0);
     d.prefetch(ntiles);
     d.start(ntiles);
     d.mainloop(ntiles);
@@ -439,7 +444,7 @@ dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
     if constexpr (FUSE_R)
       d.epilogue_fused(C, ldc, m0, n0, R + (int64_t)(n0 / 256) * 256 * 256, Y, ldy);
     else
-      d.epilogue(C, ldc, m0, n0);
+      d.epilogue(C + q * sC, ldc, m0, n0);
     tile += (int)gridDim.x;
     if (tile >= total) break;
   }
@@ -485,11 +490,36 @@ hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_
   const bf16_t* b = static_cast<const bf16_t*>(B);
   bf16_t* c = static_cast<bf16_t*>(C);
   if (b_kmajor)
-    hipLaunchKernelGGL(dense_kernel<true>, dim3(grid), dim3(NT), 0, s, a, b, c, (int)M, (int)N,
-                       (int)K, lda, ldb, ldc);
+    hipLaunchKernelGGL((dense_kernel<true, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
+                       (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, 1, (int64_t)0,
+                       (int64_t)0, (int64_t)0);
   else
-    hipLaunchKernelGGL(dense_kernel<false>, dim3(grid), dim3(NT), 0, s, a, b, c, (int)M, (int)N,
-                       (int)K, lda, ldb, ldc);
+    hipLaunchKernelGGL((dense_kernel<false, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
+                       (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, 1, (int64_t)0,
+                       (int64_t)0, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_batched(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                                int64_t K, int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor,
+                                int64_t nbatch, int64_t sA, int64_t sB, int64_t sC,
+                                hipStream_t s) {
+  if (nbatch < 1 || nbatch * ((N + BN - 1) / BN) * ((M + BM - 1) / BM) > INT32_MAX)
+    return hipErrorInvalidValue;
+  int grid = 0;
+  hipError_t e = dense_grid(M, N * nbatch, &grid);
+  if (e != hipSuccess) return e;
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* b = static_cast<const bf16_t*>(B);
+  bf16_t* c = static_cast<bf16_t*>(C);
+  if (b_kmajor)
+    hipLaunchKernelGGL((dense_kernel<true, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
+                       (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, (int)nbatch,
+                       sA, sB, sC);
+  else
+    hipLaunchKernelGGL((dense_kernel<false, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
+                       (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, (int)nbatch,
+                       sA, sB, sC);
   return hipGetLastError();
 }
 
@@ -507,7 +537,8 @@ hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M
   hipLaunchKernelGGL((dense_kernel<true, true>), dim3(grid), dim3(NT), 0, s,
                      static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B),
                      static_cast<bf16_t*>(C), (int)M, (int)N, (int)K, lda, ldb, ldc,
-                     static_cast<const bf16_t*>(R), static_cast<bf16_t*>(Y), ldy);
+                     static_cast<const bf16_t*>(R), static_cast<bf16_t*>(Y), ldy, 1, (int64_t)0,
+                     (int64_t)0, (int64_t)0);
   return hipGetLastError();
 }
 

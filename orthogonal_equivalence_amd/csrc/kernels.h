@@ -61,6 +61,12 @@ int gemm_tile_m(DType in, int M, int N);
 bool dense_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc);
 hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                         int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s);
+// nbatch products of that shape, product q at A + q sA, B + q sB, C + q sC
+// (elements), in one launch.
+hipError_t launch_dense_batched(const void* A, const void* B, void* C, int64_t M, int64_t N,
+                                int64_t K, int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor,
+                                int64_t nbatch, int64_t sA, int64_t sB, int64_t sC,
+                                hipStream_t s);
 // The forward's dense product with the R-apply fused into its epilogue
 // (256 x 256 R blocks, bf16): C = A B^T (B K-major) and Y = C blockdiag(R)^T
 // with C rounded to bf16 before the second product, as the separate R-apply
@@ -75,6 +81,8 @@ hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M
 // Y[:, blk] = X[:, blk] M_blk^T (transpose) or X[:, blk] M_blk, token-major
 // with row stride d.
 bool blockapply_supported(DType t, int64_t d, int b);
+// Tokens that one workgroup of the streaming kernel covers for this shape.
+int64_t blockapply_tokens_per_workgroup(int64_t tokens, int64_t d, int b);
 // Super-block size for block size b (0: none): blocks of b = 32 or 64 are
 // run through the b = 128 streaming kernels as block-diagonal 128 x 128
 // super blocks (exact zeros off the diagonal), when 128 divides d.

@@ -119,6 +119,13 @@ SMALL_CASES = [
     # one token: every streamed tile is ragged, every split but one empty
     ("bf16_b512_one_token", 512, 1024, 512, 1, "bf16", 0.01),
     ("bf16_b256_one_token", 768, 512, 256, 1, "bf16", 0.01),
+    # b >= 512 on the batched dense kernel (ragged last 256-token tile), b =
+    # 512 with both kernels in one layer (input side streamed: 544 tokens per
+    # workgroup; output side dense), and b = 1024 below one 256-token tile
+    # (generic batched GEMM)
+    ("bf16_b1024_dense", 2048, 1024, 1024, 700, "bf16", 0.01),
+    ("bf16_b512_stream_and_dense", 4096, 512, 512, 8300, "bf16", 0.01),
+    ("bf16_b1024_few_tokens", 1024, 2048, 1024, 200, "bf16", 0.01),
     # b = 32 / 64 run as block-diagonal 128 x 128 super blocks on the b = 128
     # streaming kernels (128 divides d)
     ("bf16_b64_super", 384, 640, 64, 300, "bf16", 0.02),
