@@ -47,38 +47,44 @@ __device__ __forceinline__ int packed_index(int b, int i, int j) {
 
 // A = diag I + sign Q for every block (I - Q for the exact map, Q itself for
 // the series); the generators of the last block's rows/columns >= last_valid
-// are taken as zero. grid (tiles of 32 x 32, nblocks). A tile below the
-// diagonal reads its generators from the mirrored tile above it (coalesced
-// along the packed rows) and transposes through LDS.
+// are taken as zero. The bo x bo piece of the gb x gb matrix starting at row
+// ro and column co is written (ro == co, or a piece wholly above the
+// diagonal; ro, co multiples of 32); the whole matrix is gb = bo, ro = co =
+// 0. grid (tiles of 32 x 32, nblocks). A tile below the diagonal reads its
+// generators from the mirrored tile above it (coalesced along the packed
+// rows) and transposes through LDS.
 __global__ void __launch_bounds__(kNT)
-expand_kernel(const float* __restrict__ theta, int nblocks, int b, int last_valid, float diag,
-              float sign, float* __restrict__ A) {
+expand_kernel(const float* __restrict__ theta, int nblocks, int gb, int ro, int co, int bo,
+              int last_valid, float diag, float sign, float* __restrict__ A) {
   __shared__ float t[32][33];
-  const int ntile = (b + 31) / 32;
+  const int ntile = (bo + 31) / 32;
   const int TI = blockIdx.x / ntile, TJ = blockIdx.x - (blockIdx.x / ntile) * ntile;
   const int blk = blockIdx.y;
-  const int r = (blk == nblocks - 1) ? last_valid : b;
-  const float* th = theta + (int64_t)blk * (b * (b - 1) / 2);
-  float* Ab = A + (int64_t)blk * b * b;
+  const int r = (blk == nblocks - 1) ? last_valid : gb;
+  const float* th = theta + (int64_t)blk * ((int64_t)gb * (gb - 1) / 2);
+  float* Ab = A + (int64_t)blk * bo * bo;
   const int tx = threadIdx.x & 31, ty0 = threadIdx.x >> 5;  // 8 rows per pass
-  const bool lower = TI > TJ;
-  // read the upper-triangle tile (lower ? (TJ, TI) : (TI, TJ)) row by row
-  const int ui = lower ? TJ : TI, uj = lower ? TI : TJ;
+  // global position of the tile; read the upper-triangle tile of its
+  // position (its mirror when it lies below the diagonal) row by row
+  const int gi0 = ro + TI * 32, gj0 = co + TJ * 32;
+  const bool lower = gi0 > gj0;
+  const int ui = lower ? gj0 : gi0, uj = lower ? gi0 : gj0;
   for (int ty = ty0; ty < 32; ty += 8) {
-    const int i = ui * 32 + ty, j = uj * 32 + tx;
+    const int i = ui + ty, j = uj + tx;
     float q = 0.0f;  // Q[i][j]
-    if (i < j && j < b && i < r && j < r) q = th[packed_index(b, i, j)];
+    if (i < j && j < gb && j < r) q = th[packed_index(gb, i, j)];
     t[ty][tx] = q;
   }
   __syncthreads();
   for (int ty = ty0; ty < 32; ty += 8) {
     const int i = TI * 32 + ty, j = TJ * 32 + tx;
-    if (i >= b || j >= b) continue;
+    if (i >= bo || j >= bo) continue;
+    const int gi = ro + i, gj = co + j;
     float v;
-    if (i == j) v = diag;
-    else if (i > j) v = -sign * t[tx][ty];  // Q[i][j] = -Q[j][i]
+    if (gi == gj) v = diag;
+    else if (gi > gj) v = -sign * t[tx][ty];  // Q[i][j] = -Q[j][i]
     else v = sign * t[ty][tx];
-    Ab[(int64_t)i * b + j] = v;
+    Ab[(int64_t)i * bo + j] = v;
   }
 }
 
@@ -458,11 +464,16 @@ __device__ __forceinline__ void tile_of(int wave, int s, int& I, int& J) {
   }
 }
 
-// grid (nblocks); R (float32) to out and, when act is given, its bf16 copy.
+// grid (nblocks); R = 2 A^-1 - I (float32) to out + blk so (row stride ldo)
+// and, when act is given, its bf16 copy at the same offsets in act. A is
+// I - Q for the leading B x B piece of the gb x gb generator blocks in theta
+// (gb = B: the whole block), or, when dense is not null, the float32 matrix
+// dense[blk] (B x B, row-major).
 template <int NT>
 __global__ void __launch_bounds__(BlockShape<NT>::THREADS)
-cayley_block_kernel(const float* __restrict__ theta, int nblocks, int last_valid,
-                    float* __restrict__ out, bf16_t* __restrict__ act) {
+cayley_block_kernel(const float* __restrict__ theta, const float* __restrict__ dense, int nblocks,
+                    int last_valid, int gb, float* __restrict__ out, int64_t ldo, int64_t so,
+                    bf16_t* __restrict__ act) {
   typedef BlockShape<NT> S;
   constexpr int B = S::B, TPW = S::TPW, TILE = S::TILE;
   __shared__ __attribute__((aligned(16))) float lds[S::LDS];
@@ -474,46 +485,74 @@ cayley_block_kernel(const float* __restrict__ theta, int nblocks, int last_valid
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* const stage = lds + wave * TILE;    // this wave's 64 x 68 staging tile (start, end)
   const int blk = blockIdx.x;
-  const int r = (blk == nblocks - 1) ? last_valid : B;
-  const float* th = theta + (int64_t)blk * (B * (B - 1) / 2);
+  const int r = (blk == nblocks - 1) ? last_valid : gb;
+  const bool dense_in = dense != nullptr;
+  const float* th = dense_in ? nullptr : theta + (int64_t)blk * ((int64_t)gb * (gb - 1) / 2);
 
-  // A = I - Q from the packed generators (those of rows / columns >= r read
-  // as 0). Every tile stages the upper-triangle tile of its position,
-  // (min(I, J), max(I, J)), one row per load instruction: lane l reads
-  // column l, so a row is 64 consecutive generators (its packed index is
-  // rowbase(i) + j with rowbase uniform across the wave). The tile then takes
-  // -theta(i, j) above the diagonal and +theta(j, i) (the staged transpose)
-  // below it: (I - Q)[i][j] = theta(j, i) for i > j.
   floatx4 t[TPW][4][4];
+  if (dense_in) {
+    // A row by row (lane l reads column l) through the wave's staging tile
+    // into the accumulator layout
+    const float* src = dense + (int64_t)blk * B * B;
 #pragma unroll
-  for (int s = 0; s < TPW; ++s) {
-    int I, J;
-    tile_of<NT>(wave, s, I, J);
-    const int R0 = 64 * (I < J ? I : J), C0 = 64 * (I < J ? J : I);
-    const int j = C0 + lane;
-    float g[64];  // all 64 row loads in flight before the first LDS store
+    for (int s = 0; s < TPW; ++s) {
+      int I, J;
+      tile_of<NT>(wave, s, I, J);
+      const float* ts = src + (64 * I) * B + 64 * J + lane;
+#pragma unroll 1
+      for (int c = 0; c < 64; c += 16) {  // 16 rows in flight at a time
+        float g[16];
 #pragma unroll
-    for (int row = 0; row < 64; ++row) {
-      const int i = R0 + row;
-      const int rowbase = i * (2 * B - i - 1) / 2 - i - 1;
-      g[row] = (i < j && j < r) ? th[rowbase + j] : 0.0f;
+        for (int row = 0; row < 16; ++row) g[row] = ts[(c + row) * B];
+#pragma unroll
+        for (int row = 0; row < 16; ++row) stage[(c + row) * kLdP + lane] = g[row];
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            t[s][mi][ni][e] = stage[tile_row(mi, e, lane) * kLdP + tile_col(ni, lane)];
     }
+  } else {
+    // A = I - Q from the packed generators (those of rows / columns >= r
+    // read as 0). Every tile stages the upper-triangle tile of its position,
+    // (min(I, J), max(I, J)), one row per load instruction: lane l reads
+    // column l, so a row is 64 consecutive generators (its packed index is
+    // rowbase(i) + j with rowbase uniform across the wave). The tile then
+    // takes -theta(i, j) above the diagonal and +theta(j, i) (the staged
+    // transpose) below it: (I - Q)[i][j] = theta(j, i) for i > j.
 #pragma unroll
-    for (int row = 0; row < 64; ++row) stage[row * kLdP + lane] = g[row];
-    const bool diag = I == J, lower = I > J;
+    for (int s = 0; s < TPW; ++s) {
+      int I, J;
+      tile_of<NT>(wave, s, I, J);
+      const int R0 = 64 * (I < J ? I : J), C0 = 64 * (I < J ? J : I);
+      const int j = C0 + lane;
+      float g[64];  // all 64 row loads in flight before the first LDS store
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+      for (int row = 0; row < 64; ++row) {
+        const int i = R0 + row;
+        const int rowbase = i * (2 * gb - i - 1) / 2 - i - 1;
+        g[row] = (i < j && j < r) ? th[rowbase + j] : 0.0f;
+      }
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int row = 0; row < 64; ++row) stage[row * kLdP + lane] = g[row];
+      const bool diag = I == J, lower = I > J;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = tile_row(mi, e, lane), cc = tile_col(ni, lane);
-          float v;
-          if (diag) v = rr == cc ? 1.0f : rr < cc ? -stage[rr * kLdP + cc] : stage[cc * kLdP + rr];
-          else if (lower) v = stage[cc * kLdP + rr];
-          else v = -stage[rr * kLdP + cc];
-          t[s][mi][ni][e] = v;
-        }
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int rr = tile_row(mi, e, lane), cc = tile_col(ni, lane);
+            float v;
+            if (diag) v = rr == cc ? 1.0f : rr < cc ? -stage[rr * kLdP + cc] : stage[cc * kLdP + rr];
+            else if (lower) v = stage[cc * kLdP + rr];
+            else v = -stage[rr * kLdP + cc];
+            t[s][mi][ni][e] = v;
+          }
+    }
   }
   __syncthreads();  // the staging tiles overlap the panel buffers
 
@@ -621,8 +660,8 @@ cayley_block_kernel(const float* __restrict__ theta, int nblocks, int last_valid
 
   // R = 2 (I - Q)^-1 - I, staged row-major so that rows leave as 16-byte
   // (float32) and 8-byte (bf16) vectors
-  float* ob = out + (int64_t)blk * B * B;
-  bf16_t* ab = act ? act + (int64_t)blk * B * B : nullptr;
+  float* ob = out + (int64_t)blk * so;
+  bf16_t* ab = act ? act + (int64_t)blk * so : nullptr;
 #pragma unroll
   for (int s = 0; s < TPW; ++s) {
     int I, J;
@@ -640,7 +679,7 @@ cayley_block_kernel(const float* __restrict__ theta, int nblocks, int last_valid
     for (int q = 0; q < 16; ++q) {
       const int rr = 4 * q + (lane >> 4), c4 = 4 * (lane & 15);
       const float4 v = *reinterpret_cast<const float4*>(stage + rr * kLdP + c4);
-      const int64_t off = (int64_t)(64 * I + rr) * B + 64 * J + c4;
+      const int64_t off = (int64_t)(64 * I + rr) * ldo + 64 * J + c4;
       *reinterpret_cast<float4*>(ob + off) = v;
       if (ab) {
         union { uint2 u; bf16_t h[4]; } o;
@@ -748,6 +787,100 @@ pack_skew_grad_kernel(PackSet s1, PackSet s2, float c, int b, float sign) {
   }
 }
 
+// out = bf16(in) for nblocks b x b blocks, except the bottom-right h x h
+// piece of each block (h % 4 == 0, b % 4 == 0). grid-stride over float4s.
+__global__ void __launch_bounds__(kNT)
+to_bf16_kernel(const float* __restrict__ in, int64_t nblocks, int b, int h,
+               bf16_t* __restrict__ out) {
+  const int64_t per = (int64_t)b * b / 4, n4 = nblocks * per;
+  for (int64_t q = (int64_t)blockIdx.x * kNT + threadIdx.x; q < n4; q += (int64_t)gridDim.x * kNT) {
+    const int e = (int)(q % per) * 4;
+    if (e / b >= b - h && e % b >= b - h) continue;
+    const float4 v = reinterpret_cast<const float4*>(in)[q];
+    union { uint2 u; bf16_t h[4]; } o;
+    o.h[0] = f32_to_bf16(v.x); o.h[1] = f32_to_bf16(v.y);
+    o.h[2] = f32_to_bf16(v.z); o.h[3] = f32_to_bf16(v.w);
+    reinterpret_cast<uint2*>(out)[q] = o.u;
+  }
+}
+
+// Blocks of 512 as 2 x 2 pieces of 256 (Schur complement), for many blocks.
+// With A = I - Q = [[A11, A12], [A21, A22]] (A11 = I - Q11, A12 = -Q12,
+// A21 = Q12^T, A22 = I - Q22), Z = A11^-1, X = Z Q12 and Y = Q12^T Z:
+//   S = A22 - A21 Z A12 = (I - Q22) + Y Q12,
+//   A^-1 = [[Z - X S^-1 Y, X S^-1], [-S^-1 Y, S^-1]].
+// The two inversions run on the whole-block kernel, which returns T = 2 Z - I
+// and R22 = 2 S^-1 - I; with Z = (T + I) / 2 and S^-1 = (R22 + I) / 2 the
+// pieces of R = 2 A^-1 - I are
+//   R12 = X R22 + X,   R21 = -(R22 Y + Y),   R11 = T - R12 Y,
+// each a 256 x 256 float32 product of all blocks in one batched launch. A11
+// and S have positive definite symmetric parts (I, and a Schur complement of
+// a matrix whose symmetric part is I), so neither elimination pivots.
+constexpr int kSchurMinBlocks = 48;
+
+bool use_schur(int64_t nblocks, int b) { return b == 512 && nblocks >= kSchurMinBlocks; }
+
+hipError_t schur512_build(const float* theta, int nb, int last_valid, float* R, bf16_t* act,
+                          float* ws, hipStream_t stream) {
+  constexpr int H = 256, B = 512;
+  constexpr int64_t HH = (int64_t)H * H, BB = (int64_t)B * B;
+  float* T = ws;              // 2 Z - I
+  float* Q12 = T + nb * HH;
+  float* D22 = Q12 + nb * HH; // I - Q22
+  float* X = D22 + nb * HH;   // Z Q12
+  float* Y = X + nb * HH;     // Q12^T Z
+  float* S = Y + nb * HH;     // the Schur complement
+  hipError_t e;
+  const int et = H / 32;
+  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb), dim3(kNT), 0, stream, theta, nb, B, 0, H, H,
+                     last_valid, 0.0f, 1.0f, Q12);
+  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb), dim3(kNT), 0, stream, theta, nb, B, H, H, H,
+                     last_valid, 1.0f, -1.0f, D22);
+  hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nb), dim3(BlockShape<4>::THREADS),
+                     0, stream, theta, nullptr, nb, last_valid, B, T, (int64_t)H, HH, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  auto prod = [&](const float* A, int64_t lda, int64_t sA, bool a_k, const float* Bm, int64_t ldb,
+                  int64_t sB, float alpha, const float* D, bool d_trans, float beta, float* C,
+                  int64_t ldc, int64_t sC) {
+    GemmParams g;
+    g.A = A; g.lda = lda; g.sA = sA;
+    g.B = Bm; g.ldb = ldb; g.sB = sB;
+    g.C = C; g.ldc = ldc; g.sC = sC;
+    g.D = D; g.ldd = H; g.sD = HH; g.d_trans = d_trans;
+    g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = H;
+    g.batch = nb;
+    g.kchunk = H;
+    g.alpha = alpha; g.beta = beta;
+    // B operand is always B(n, k) = Bm[k ldb + n] (row-major right factor)
+    return launch_gemm(DType::F32, DType::F32, a_k, false, g, stream);
+  };
+  // X = Z Q12 = (T Q12 + Q12) / 2,  Y = Q12^T Z = (Q12^T T + Q12^T) / 2
+  if ((e = prod(T, H, HH, true, Q12, H, HH, 0.5f, Q12, false, 0.5f, X, H, HH)) != hipSuccess) return e;
+  if ((e = prod(Q12, H, HH, false, T, H, HH, 0.5f, Q12, true, 0.5f, Y, H, HH)) != hipSuccess) return e;
+  // S = (I - Q22) + Y Q12
+  if ((e = prod(Y, H, HH, true, Q12, H, HH, 1.0f, D22, false, 1.0f, S, H, HH)) != hipSuccess) return e;
+  // R22 = 2 S^-1 - I, written into the block
+  float* R22 = R + H * B + H;
+  hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nb), dim3(BlockShape<4>::THREADS),
+                     0, stream, nullptr, S, nb, last_valid, B, R22, (int64_t)B, BB,
+                     act ? act + H * B + H : nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // R12 = X R22 + X, R21 = -(R22 Y + Y), then R11 = T - R12 Y
+  float* R12 = R + H;
+  float* R21 = R + H * B;
+  if ((e = prod(X, H, HH, true, R22, B, BB, 1.0f, X, false, 1.0f, R12, B, BB)) != hipSuccess) return e;
+  if ((e = prod(R22, B, BB, true, Y, H, HH, -1.0f, Y, false, -1.0f, R21, B, BB)) != hipSuccess) return e;
+  if ((e = prod(R12, B, BB, true, Y, H, HH, -1.0f, T, false, 1.0f, R, B, BB)) != hipSuccess) return e;
+  if (act) {  // the bf16 copy of the other three pieces (R22's came with it)
+    const int64_t want = ((int64_t)nb * BB / 4 + kNT - 1) / kNT;
+    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(to_bf16_kernel, dim3(grid), dim3(kNT), 0, stream, R, (int64_t)nb, B, H, act);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 int cayley_panel_width(int b) {
@@ -758,6 +891,7 @@ int cayley_panel_width(int b) {
 }
 
 size_t cayley_workspace_floats(int64_t nblocks, int b) {
+  if (use_schur(nblocks, b)) return 6 * (size_t)nblocks * 256 * 256;
   const int pw = cayley_panel_width(b);
   return 2 * (size_t)nblocks * (size_t)pw * (size_t)b;
 }
@@ -774,13 +908,17 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
   const bool whole_block = b == 128 || (b == 256 && nblocks >= 48);
   if (whole_block) {  // the whole block on one CU
     if (b == 256)
-      hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nblocks), dim3(BlockShape<4>::THREADS),
-                         0, stream, theta, (int)nblocks, last_valid, blocks_f32, act_bf16);
+      hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nblocks),
+                         dim3(BlockShape<4>::THREADS), 0, stream, theta, nullptr, (int)nblocks,
+                         last_valid, b, blocks_f32, (int64_t)b, (int64_t)b * b, act_bf16);
     else
-      hipLaunchKernelGGL(cayley_block_kernel<2>, dim3((unsigned)nblocks), dim3(BlockShape<2>::THREADS),
-                         0, stream, theta, (int)nblocks, last_valid, blocks_f32, act_bf16);
+      hipLaunchKernelGGL(cayley_block_kernel<2>, dim3((unsigned)nblocks),
+                         dim3(BlockShape<2>::THREADS), 0, stream, theta, nullptr, (int)nblocks,
+                         last_valid, b, blocks_f32, (int64_t)b, (int64_t)b * b, act_bf16);
     return hipGetLastError();
   }
+  if (use_schur(nblocks, b))
+    return schur512_build(theta, (int)nblocks, last_valid, blocks_f32, act_bf16, ws, stream);
   const int pw = cayley_panel_width(b);
   const int nt = b / pw;
   const int nb = (int)nblocks;
@@ -788,7 +926,7 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
   float* colbuf = ws + (size_t)nblocks * pw * b;
   bf16_t* act_out = (act == DType::BF16) ? static_cast<bf16_t*>(blocks_act) : nullptr;
   const int et = (b + 31) / 32;
-  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb), dim3(kNT), 0, stream, theta, nb, b,
+  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb), dim3(kNT), 0, stream, theta, nb, b, 0, 0, b,
                      last_valid, 1.0f, -1.0f, blocks_f32);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -807,7 +945,7 @@ hipError_t launch_expand_skew(const float* theta, int64_t nblocks, int b, int la
                               float diag, float sign, float* out, hipStream_t stream) {
   const int et = (b + 31) / 32;
   hipLaunchKernelGGL(expand_kernel, dim3(et * et, (int)nblocks), dim3(kNT), 0, stream, theta,
-                     (int)nblocks, b, last_valid, diag, sign, out);
+                     (int)nblocks, b, 0, 0, b, last_valid, diag, sign, out);
   return hipGetLastError();
 }
 

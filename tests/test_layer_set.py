@@ -66,3 +66,35 @@ def test_set_build_equals_per_layer_builds(b):
     for r, g in zip(ref, grouped):
         for name in ("R_f32", "P_f32", "R_act", "P_act"):
             assert torch.equal(getattr(r, name), getattr(g, name)), name
+
+
+@pytest.mark.gpu
+def test_set_build_b512_many_blocks_matches_oracle():
+    """48 blocks of 512 in one build call (the Schur-complement build): every
+    layer's R and P blocks against the float64 Cayley map of its generators,
+    and the bf16 copies the RNE rounding of the float32 blocks."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle.poetx_oracle as O
+    b = 512
+    rng = np.random.default_rng(17)
+    layers = []
+    for n, m in [(4096, 2048), (2048, 4096), (4096, 4096), (2048, 2048)]:  # 48 blocks in all
+        W0 = torch.from_numpy(rng.standard_normal((m, n)) / np.sqrt(n)).to(torch.bfloat16)
+        lay = PoetxLinear(W0, b, b, "bf16", device="cuda")
+        tri = b * (b - 1) // 2
+        lay.set_theta(torch.from_numpy(0.01 * rng.standard_normal((m // b, tri))).float(),
+                      torch.from_numpy(0.01 * rng.standard_normal((n // b, tri))).float())
+        layers.append(lay)
+    s = PoetxLinearSet(layers)
+    assert s.d_total // b == 48
+    s.build()
+    torch.cuda.synchronize()
+    tol = 2e-5 * np.sqrt(b) / 8
+    for lay in layers:
+        for side in ("R", "P"):
+            th = getattr(lay, "theta_" + side).cpu().double().numpy()
+            f32 = getattr(lay, side + "_f32")
+            ref, _ = O.orthogonal_blocks(th, b, th.shape[0] * b)
+            assert np.max(np.abs(f32.cpu().double().numpy() - ref)) <= tol, side
+            assert torch.equal(getattr(lay, side + "_act").float(), f32.to(torch.bfloat16).float())

@@ -59,6 +59,9 @@ def test_build_golden_closed_forms():
     (2, 3, 0.5), (3, 2, 0.5), (8, 5, 0.3), (32, 8, 0.02), (48, 3, 0.1), (64, 4, 0.05),
     (96, 2, 0.05), (128, 3, 0.02), (256, 4, 0.01), (512, 2, 0.01), (1024, 1, 0.01),
     (256, 2, 0.2),
+    # 48 blocks and more: b = 256 on the whole-block kernel, b = 512 as 2 x 2
+    # pieces of 256 (Schur complement)
+    (256, 48, 0.01), (512, 48, 0.01), (512, 50, 0.05),
 ])
 def test_build_matches_oracle(b, nb, sigma):
     U.log(f"[build] b={b} nb={nb} sigma={sigma}")
@@ -81,16 +84,19 @@ def test_build_matches_oracle(b, nb, sigma):
     assert torch.equal(a, ref)
 
 
-@pytest.mark.parametrize("b,r", [(64, 24), (128, 77), (256, 24), (256, 193)])
-def test_build_padded_last_block(b, r):
-    """b does not divide d: the last block is diag(Cayley(Q_r), I) (b = 64 on
-    the panel kernels, b = 128 and 256 on the whole-block kernel, with the
-    valid part ending inside a 64-wide tile or at its first column)."""
-    d = b * 2 + r
+@pytest.mark.parametrize("b,r,nfull", [(64, 24, 2), (128, 77, 2), (256, 24, 2), (256, 193, 2),
+                                        (256, 193, 47), (512, 300, 47), (512, 200, 47)])
+def test_build_padded_last_block(b, r, nfull):
+    """b does not divide d: the last block is diag(Cayley(Q_r), I), with the
+    valid part ending inside a 64-wide tile or at its first column. Three
+    blocks run on the panel kernels (b = 64, 256) or the whole-block kernel
+    (b = 128); 48 blocks on the whole-block kernel (b = 256) or as Schur
+    pieces (b = 512, the valid part ending in either half)."""
+    d = b * nfull + r
     U.log(f"[build padded] b={b} d={d}")
-    rng = np.random.default_rng(5 + b + r)
+    rng = np.random.default_rng(5 + b + r + nfull)
     sigma = 0.05 if b == 64 else 0.01
-    theta = (rng.standard_normal((3, b * (b - 1) // 2)) * sigma).astype(np.float32).astype(np.float64)
+    theta = (rng.standard_normal((nfull + 1, b * (b - 1) // 2)) * sigma).astype(np.float32).astype(np.float64)
     R_ref, _ = O.orthogonal_blocks(theta, b, d)
     f32, act = _build(theta, d, b)
     R = U.host(f32)
