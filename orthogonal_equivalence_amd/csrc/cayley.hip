@@ -223,10 +223,13 @@ __device__ __forceinline__ int mma_col(int ni) {
   return (wave & 1) * 32 + ni * 16 + (lane & 15);
 }
 
-// grid (b / pw column tiles, nblocks)
+// grid (b / pw column tiles, nblocks). dinv (optional): the pivot block's
+// inverse (64 x 64 per block, identity outside pw x pw), inverted by the
+// previous panel's update; without it every workgroup inverts the pivot.
 __global__ void __launch_bounds__(kNT)
 panel_prep_kernel(const float* __restrict__ A, int b, int pw, int p,
-                  float* __restrict__ rowbuf, float* __restrict__ colbuf) {
+                  float* __restrict__ rowbuf, float* __restrict__ colbuf,
+                  const float* __restrict__ dinv) {
   __shared__ __attribute__((aligned(16))) float sD[kPW * kLdP];
   __shared__ __attribute__((aligned(16))) float sX[kPW * kLdP];
   __shared__ __attribute__((aligned(16))) float gjbuf[1024];
@@ -244,7 +247,8 @@ panel_prep_kernel(const float* __restrict__ A, int b, int pw, int p,
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int gi = min(4 * ty + ii, pw - 1), gj = min(4 * tx + jj, pw - 1);
-      av[ii][jj] = Ab[(int64_t)(p0 + gi) * b + p0 + gj];
+      av[ii][jj] = dinv ? dinv[blk * kPW * kPW + (4 * ty + ii) * kPW + 4 * tx + jj]
+                        : Ab[(int64_t)(p0 + gi) * b + p0 + gj];
       cv[ii][jj] = Ab[(int64_t)(j0 + gi) * b + p0 + gj];
       xv[ii][jj] = Ab[(int64_t)(p0 + gi) * b + j0 + gj];
     }
@@ -255,11 +259,11 @@ panel_prep_kernel(const float* __restrict__ A, int b, int pw, int p,
     for (int jj = 0; jj < 4; ++jj) {
       const int gi = 4 * ty + ii, gj = 4 * tx + jj;
       const bool in = gi < pw && gj < pw;
-      a[ii][jj] = in ? av[ii][jj] : (gi == gj ? 1.0f : 0.0f);
+      a[ii][jj] = (in || dinv) ? av[ii][jj] : (gi == gj ? 1.0f : 0.0f);
       if (in) colbuf[(blk * b + j0 + gi) * pw + gj] = cv[ii][jj];
       if (J != p) sX[b_off(gi, gj)] = in ? xv[ii][jj] : 0.0f;
     }
-  gj_invert_regs(a, pw, gjbuf);
+  if (!dinv) gj_invert_regs(a, pw, gjbuf);
 
   float* rb = rowbuf + blk * (int64_t)pw * b;
   if (J == p) {
@@ -296,16 +300,38 @@ panel_prep_kernel(const float* __restrict__ A, int b, int pw, int p,
 
 // grid (nt * nt tiles, nblocks). When `final` is set the tile is written as
 // R = 2 B - I to A (the float32 output) and to `act_out` (bf16), if given.
+// dinv_next (optional, not with `final`): the workgroup that updates the next
+// pivot block (p + 1, p + 1) also inverts it and writes the inverse there
+// (64 x 64 per block, identity outside pw x pw), for the next prep launch.
+// Those workgroups take the first ids (one per block), so the inversions run
+// beside the other tiles' updates.
 __global__ void __launch_bounds__(kNT)
 panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
                     const float* __restrict__ rowbuf, const float* __restrict__ colbuf,
-                    int final, bf16_t* __restrict__ act_out) {
+                    int final, bf16_t* __restrict__ act_out, float* __restrict__ dinv_next) {
   __shared__ __attribute__((aligned(16))) float sC[kPW * kLdP];
   __shared__ __attribute__((aligned(16))) float sW[kPW * kLdP];
+  __shared__ __attribute__((aligned(16))) float gjbuf[1024];
   const int tid = threadIdx.x;
   const int nt = b / pw;
-  const int I = blockIdx.x / nt, J = blockIdx.x - (blockIdx.x / nt) * nt;
-  const int64_t blk = blockIdx.y;
+  int tile = blockIdx.x;
+  int64_t blk = blockIdx.y;
+  if (dinv_next) {
+    const int per = nt * nt, nb = (int)gridDim.y;
+    const int64_t lin = (int64_t)blockIdx.y * per + blockIdx.x;
+    const int piv = (p + 1) * nt + (p + 1);
+    if (lin < nb) {
+      blk = lin;
+      tile = piv;
+    } else {
+      const int64_t rest = lin - nb;
+      blk = rest / (per - 1);
+      const int t = (int)(rest - blk * (per - 1));
+      tile = t < piv ? t : t + 1;
+    }
+  }
+  const int I = tile / nt, J = tile - (tile / nt) * nt;
+  const bool next_pivot = dinv_next && I == p + 1 && J == p + 1;
   float* Ab = A + blk * (int64_t)b * b;
   const float* rb = rowbuf + blk * (int64_t)pw * b;
   const float* cb = colbuf + blk * (int64_t)b * pw;
@@ -386,6 +412,32 @@ panel_update_kernel(float* __restrict__ A, int b, int pw, int p,
         const int gi = mma_row(mi, e), gj = mma_col(ni);
         if (gi < pw && gj < pw) emit(gi, gj, base[mi][ni][e] - acc[mi][ni][e]);
       }
+  if (!next_pivot) return;  // uniform across the workgroup
+  // the new pivot block, row-major through LDS into 4 x 4 register pieces
+  __syncthreads();  // every wave is done reading sC
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sC[mma_row(mi, e) * kLdP + mma_col(ni)] = base[mi][ni][e] - acc[mi][ni][e];
+  __syncthreads();
+  const int ty = tid >> 4, tx = tid & 15;
+  float a[4][4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int gi = 4 * ty + ii, gj = 4 * tx + jj;
+      a[ii][jj] = (gi < pw && gj < pw) ? sC[gi * kLdP + gj] : (gi == gj ? 1.0f : 0.0f);
+    }
+  gj_invert_regs(a, pw, gjbuf);
+  float* dn = dinv_next + blk * kPW * kPW;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+    *reinterpret_cast<float4*>(dn + (4 * ty + ii) * kPW + 4 * tx) =
+        make_float4(a[ii][0], a[ii][1], a[ii][2], a[ii][3]);
 }
 
 // ---- whole block per workgroup: b = 64 NT, NT = 2 or 4 ----
@@ -893,7 +945,8 @@ int cayley_panel_width(int b) {
 size_t cayley_workspace_floats(int64_t nblocks, int b) {
   if (use_schur(nblocks, b)) return 6 * (size_t)nblocks * 256 * 256;
   const int pw = cayley_panel_width(b);
-  return 2 * (size_t)nblocks * (size_t)pw * (size_t)b;
+  // row and column panels, and the next pivot block's inverse
+  return 2 * (size_t)nblocks * (size_t)pw * (size_t)b + (size_t)nblocks * kPW * kPW;
 }
 
 hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int last_valid,
@@ -924,17 +977,24 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
   const int nb = (int)nblocks;
   float* rowbuf = ws;
   float* colbuf = ws + (size_t)nblocks * pw * b;
+  float* dinv = colbuf + (size_t)nblocks * pw * b;
   bf16_t* act_out = (act == DType::BF16) ? static_cast<bf16_t*>(blocks_act) : nullptr;
   const int et = (b + 31) / 32;
   hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb), dim3(kNT), 0, stream, theta, nb, b, 0, 0, b,
                      last_valid, 1.0f, -1.0f, blocks_f32);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // With at least two update workgroups per CU, the next pivot's inversion
+  // runs in the update launch beside the other tiles (8 blocks of 1024:
+  // build 827 -> 662 us; 16 of 512: 327 -> 304 us); with one round of
+  // workgroups it would only lengthen the launch, so prep inverts it.
+  const bool early_pivot = (int64_t)nt * nt * nb >= 512;
   for (int p = 0; p < nt; ++p) {
+    const bool take = early_pivot && p > 0, give = early_pivot && p < nt - 1;
     hipLaunchKernelGGL(panel_prep_kernel, dim3(nt, nb), dim3(kNT), 0, stream, blocks_f32, b, pw, p,
-                       rowbuf, colbuf);
+                       rowbuf, colbuf, take ? (const float*)dinv : nullptr);
     hipLaunchKernelGGL(panel_update_kernel, dim3(nt * nt, nb), dim3(kNT), 0, stream, blocks_f32, b,
-                       pw, p, rowbuf, colbuf, (int)(p == nt - 1), act_out);
+                       pw, p, rowbuf, colbuf, (int)(p == nt - 1), act_out, give ? dinv : nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
