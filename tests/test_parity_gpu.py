@@ -62,6 +62,8 @@ def test_build_golden_closed_forms():
     # 48 blocks and more: b = 256 on the whole-block kernel, b = 512 as 2 x 2
     # pieces of 256 (Schur complement)
     (256, 48, 0.01), (512, 48, 0.01), (512, 50, 0.05),
+    # the largest blocks the library takes (4096) and one below it
+    (2048, 1, 0.004), (4096, 1, 0.002),
 ])
 def test_build_matches_oracle(b, nb, sigma):
     U.log(f"[build] b={b} nb={nb} sigma={sigma}")
@@ -132,6 +134,8 @@ SMALL_CASES = [
     ("bf16_b1024_dense", 2048, 1024, 1024, 700, "bf16", 0.01),
     ("bf16_b512_stream_and_dense", 4096, 512, 512, 8300, "bf16", 0.01),
     ("bf16_b1024_few_tokens", 1024, 2048, 1024, 200, "bf16", 0.01),
+    # b = 2048: two P blocks and one R block, batched dense block products
+    ("bf16_b2048", 4096, 2048, 2048, 300, "bf16", 0.004),
     # b = 32 / 64 run as block-diagonal 128 x 128 super blocks on the b = 128
     # streaming kernels (128 divides d)
     ("bf16_b64_super", 384, 640, 64, 300, "bf16", 0.02),
