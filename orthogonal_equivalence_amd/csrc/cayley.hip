@@ -47,22 +47,33 @@ __device__ __forceinline__ int packed_index(int b, int i, int j) {
 
 // A = diag I + sign Q for every block (I - Q for the exact map, Q itself for
 // the series); the generators of the last block's rows/columns >= last_valid
-// are taken as zero. The bo x bo piece of the gb x gb matrix starting at row
-// ro and column co is written (ro == co, or a piece wholly above the
-// diagonal; ro, co multiples of 32); the whole matrix is gb = bo, ro = co =
-// 0. grid (tiles of 32 x 32, nblocks). A tile below the diagonal reads its
-// generators from the mirrored tile above it (coalesced along the packed
-// rows) and transposes through LDS.
+// are taken as zero. Piece z (blockIdx.z) is the bo x bo piece of the gb x gb
+// matrix starting at row ro[z] and column co[z] (ro == co, or a piece wholly
+// on one side of the diagonal; multiples of 32), written to out[z] + blk so
+// with row stride ldo; the whole matrix is one piece with gb = bo, ro = co =
+// 0. grid (tiles of 32 x 32, nblocks, pieces). A tile below the diagonal
+// reads its generators from the mirrored tile above it (coalesced along the
+// packed rows) and transposes through LDS.
+struct ExpandPieces {
+  int ro[3], co[3];
+  float diag[3], sign[3];
+  float* out[3];
+  int64_t ldo, so;
+};
+
 __global__ void __launch_bounds__(kNT)
-expand_kernel(const float* __restrict__ theta, int nblocks, int gb, int ro, int co, int bo,
-              int last_valid, float diag, float sign, float* __restrict__ A) {
+expand_kernel(const float* __restrict__ theta, int nblocks, int gb, int bo, int last_valid,
+              ExpandPieces pc) {
   __shared__ float t[32][33];
+  const int z = blockIdx.z;
+  const int ro = pc.ro[z], co = pc.co[z];
+  const float diag = pc.diag[z], sign = pc.sign[z];
   const int ntile = (bo + 31) / 32;
   const int TI = blockIdx.x / ntile, TJ = blockIdx.x - (blockIdx.x / ntile) * ntile;
   const int blk = blockIdx.y;
   const int r = (blk == nblocks - 1) ? last_valid : gb;
   const float* th = theta + (int64_t)blk * ((int64_t)gb * (gb - 1) / 2);
-  float* Ab = A + (int64_t)blk * bo * bo;
+  float* Ab = pc.out[z] + (int64_t)blk * pc.so;
   const int tx = threadIdx.x & 31, ty0 = threadIdx.x >> 5;  // 8 rows per pass
   // global position of the tile; read the upper-triangle tile of its
   // position (its mirror when it lies below the diagonal) row by row
@@ -84,8 +95,20 @@ expand_kernel(const float* __restrict__ theta, int nblocks, int gb, int ro, int 
     if (gi == gj) v = diag;
     else if (gi > gj) v = -sign * t[tx][ty];  // Q[i][j] = -Q[j][i]
     else v = sign * t[ty][tx];
-    Ab[(int64_t)i * bo + j] = v;
+    Ab[(int64_t)i * pc.ldo + j] = v;
   }
+}
+
+// The whole b x b matrix as one piece, contiguous blocks.
+ExpandPieces whole_piece(int b, float diag, float sign, float* out) {
+  ExpandPieces pc{};
+  pc.ro[0] = pc.co[0] = 0;
+  pc.diag[0] = diag;
+  pc.sign[0] = sign;
+  pc.out[0] = out;
+  pc.ldo = b;
+  pc.so = (int64_t)b * b;
+  return pc;
 }
 
 // Reciprocal: hardware estimate refined by one Newton step (error ~1 ulp).
@@ -520,12 +543,12 @@ __device__ __forceinline__ void tile_of(int wave, int s, int& I, int& J) {
 // and, when act is given, its bf16 copy at the same offsets in act. A is
 // I - Q for the leading B x B piece of the gb x gb generator blocks in theta
 // (gb = B: the whole block), or, when dense is not null, the float32 matrix
-// dense[blk] (B x B, row-major).
+// at dense + blk si (B x B, row stride ldi).
 template <int NT>
 __global__ void __launch_bounds__(BlockShape<NT>::THREADS)
-cayley_block_kernel(const float* __restrict__ theta, const float* __restrict__ dense, int nblocks,
-                    int last_valid, int gb, float* __restrict__ out, int64_t ldo, int64_t so,
-                    bf16_t* __restrict__ act) {
+cayley_block_kernel(const float* __restrict__ theta, const float* __restrict__ dense, int64_t ldi,
+                    int64_t si, int nblocks, int last_valid, int gb, float* __restrict__ out,
+                    int64_t ldo, int64_t so, bf16_t* __restrict__ act) {
   typedef BlockShape<NT> S;
   constexpr int B = S::B, TPW = S::TPW, TILE = S::TILE;
   __shared__ __attribute__((aligned(16))) float lds[S::LDS];
@@ -545,17 +568,17 @@ cayley_block_kernel(const float* __restrict__ theta, const float* __restrict__ d
   if (dense_in) {
     // A row by row (lane l reads column l) through the wave's staging tile
     // into the accumulator layout
-    const float* src = dense + (int64_t)blk * B * B;
+    const float* src = dense + (int64_t)blk * si;
 #pragma unroll
     for (int s = 0; s < TPW; ++s) {
       int I, J;
       tile_of<NT>(wave, s, I, J);
-      const float* ts = src + (64 * I) * B + 64 * J + lane;
+      const float* ts = src + (64 * I) * ldi + 64 * J + lane;
 #pragma unroll 1
       for (int c = 0; c < 64; c += 16) {  // 16 rows in flight at a time
         float g[16];
 #pragma unroll
-        for (int row = 0; row < 16; ++row) g[row] = ts[(c + row) * B];
+        for (int row = 0; row < 16; ++row) g[row] = ts[(c + row) * ldi];
 #pragma unroll
         for (int row = 0; row < 16; ++row) stage[(c + row) * kLdP + lane] = g[row];
       }
@@ -858,14 +881,16 @@ to_bf16_kernel(const float* __restrict__ in, int64_t nblocks, int b, int h,
 
 // Blocks of 512 as 2 x 2 pieces of 256 (Schur complement), for many blocks.
 // With A = I - Q = [[A11, A12], [A21, A22]] (A11 = I - Q11, A12 = -Q12,
-// A21 = Q12^T, A22 = I - Q22), Z = A11^-1, X = Z Q12 and Y = Q12^T Z:
-//   S = A22 - A21 Z A12 = (I - Q22) + Y Q12,
-//   A^-1 = [[Z - X S^-1 Y, X S^-1], [-S^-1 Y, S^-1]].
+// A21 = Q12^T, A22 = I - Q22), Z = A11^-1, X = Z Q12 and V = -A21 Z = Q21 Z:
+//   S = A22 - A21 Z A12 = (I - Q22) - V Q12,
+//   A^-1 = [[Z + X S^-1 V, X S^-1], [S^-1 V, S^-1]].
 // The two inversions run on the whole-block kernel, which returns T = 2 Z - I
-// and R22 = 2 S^-1 - I; with Z = (T + I) / 2 and S^-1 = (R22 + I) / 2 the
-// pieces of R = 2 A^-1 - I are
-//   R12 = X R22 + X,   R21 = -(R22 Y + Y),   R11 = T - R12 Y,
-// each a 256 x 256 float32 product of all blocks in one batched launch. A11
+// and R22 = 2 S^-1 - I directly; with Z = (T + I) / 2 and S^-1 = (R22 + I) / 2
+// the pieces of R = 2 A^-1 - I are
+//   R12 = X R22 + X,   R21 = R22 V + V,   R11 = T + R12 V,
+// each a 256 x 256 float32 product of all blocks in a batched launch; X and V,
+// and then R12 and R21, are independent products with the same scale factors,
+// so each pair shares one launch. A11
 // and S have positive definite symmetric parts (I, and a Schur complement of
 // a matrix whose symmetric part is I), so neither elimination pivots.
 constexpr int kSchurMinBlocks = 48;
@@ -875,55 +900,73 @@ bool use_schur(int64_t nblocks, int b) { return b == 512 && nblocks >= kSchurMin
 hipError_t schur512_build(const float* theta, int nb, int last_valid, float* R, bf16_t* act,
                           float* ws, hipStream_t stream) {
   constexpr int H = 256, B = 512;
-  constexpr int64_t HH = (int64_t)H * H, BB = (int64_t)B * B;
-  float* T = ws;              // 2 Z - I
-  float* Q12 = T + nb * HH;
-  float* D22 = Q12 + nb * HH; // I - Q22
-  float* X = D22 + nb * HH;   // Z Q12
-  float* Y = X + nb * HH;     // Q12^T Z
-  float* S = Y + nb * HH;     // the Schur complement
-  hipError_t e;
-  const int et = H / 32;
-  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb), dim3(kNT), 0, stream, theta, nb, B, 0, H, H,
-                     last_valid, 0.0f, 1.0f, Q12);
-  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb), dim3(kNT), 0, stream, theta, nb, B, H, H, H,
-                     last_valid, 1.0f, -1.0f, D22);
-  hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nb), dim3(BlockShape<4>::THREADS),
-                     0, stream, theta, nullptr, nb, last_valid, B, T, (int64_t)H, HH, nullptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-
-  auto prod = [&](const float* A, int64_t lda, int64_t sA, bool a_k, const float* Bm, int64_t ldb,
-                  int64_t sB, float alpha, const float* D, bool d_trans, float beta, float* C,
-                  int64_t ldc, int64_t sC) {
-    GemmParams g;
-    g.A = A; g.lda = lda; g.sA = sA;
-    g.B = Bm; g.ldb = ldb; g.sB = sB;
-    g.C = C; g.ldc = ldc; g.sC = sC;
-    g.D = D; g.ldd = H; g.sD = HH; g.d_trans = d_trans;
-    g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = H;
-    g.batch = nb;
-    g.kchunk = H;
-    g.alpha = alpha; g.beta = beta;
-    // B operand is always B(n, k) = Bm[k ldb + n] (row-major right factor)
-    return launch_gemm(DType::F32, DType::F32, a_k, false, g, stream);
-  };
-  // X = Z Q12 = (T Q12 + Q12) / 2,  Y = Q12^T Z = (Q12^T T + Q12^T) / 2
-  if ((e = prod(T, H, HH, true, Q12, H, HH, 0.5f, Q12, false, 0.5f, X, H, HH)) != hipSuccess) return e;
-  if ((e = prod(Q12, H, HH, false, T, H, HH, 0.5f, Q12, true, 0.5f, Y, H, HH)) != hipSuccess) return e;
-  // S = (I - Q22) + Y Q12
-  if ((e = prod(Y, H, HH, true, Q12, H, HH, 1.0f, D22, false, 1.0f, S, H, HH)) != hipSuccess) return e;
-  // R22 = 2 S^-1 - I, written into the block
-  float* R22 = R + H * B + H;
-  hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nb), dim3(BlockShape<4>::THREADS),
-                     0, stream, nullptr, S, nb, last_valid, B, R22, (int64_t)B, BB,
-                     act ? act + H * B + H : nullptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // R12 = X R22 + X, R21 = -(R22 Y + Y), then R11 = T - R12 Y
+  constexpr int64_t BB = (int64_t)B * B;
+  // Every piece lives in a 512 x 512 frame per block (row stride 512, block
+  // stride 512^2), as the pieces of R do, so that the paired products share
+  // their strides: W1 holds T, Q12, Q21 and I - Q22 in its four quadrants,
+  // W2 holds V and S in its top half, and X sits in R's R11 quadrant until
+  // R11 is written.
+  float* W1 = ws;
+  float* W2 = ws + nb * BB;
+  float* T = W1;
+  float* Q12 = W1 + H;
+  float* Q21 = W1 + H * B;
+  float* D22 = W1 + H * B + H;
+  float* V = W2;
+  float* S = W2 + H;
+  float* X = R;
   float* R12 = R + H;
   float* R21 = R + H * B;
-  if ((e = prod(X, H, HH, true, R22, B, BB, 1.0f, X, false, 1.0f, R12, B, BB)) != hipSuccess) return e;
-  if ((e = prod(R22, B, BB, true, Y, H, HH, -1.0f, Y, false, -1.0f, R21, B, BB)) != hipSuccess) return e;
-  if ((e = prod(R12, B, BB, true, Y, H, HH, -1.0f, T, false, 1.0f, R, B, BB)) != hipSuccess) return e;
+  float* R22 = R + H * B + H;
+  hipError_t e;
+  const int et = H / 32;
+  ExpandPieces pc{};
+  pc.ro[0] = 0; pc.co[0] = H; pc.diag[0] = 0.0f; pc.sign[0] = 1.0f; pc.out[0] = Q12;   // Q12
+  pc.ro[1] = H; pc.co[1] = 0; pc.diag[1] = 0.0f; pc.sign[1] = 1.0f; pc.out[1] = Q21;   // Q21
+  pc.ro[2] = H; pc.co[2] = H; pc.diag[2] = 1.0f; pc.sign[2] = -1.0f; pc.out[2] = D22;  // I - Q22
+  pc.ldo = B;
+  pc.so = BB;
+  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb, 3), dim3(kNT), 0, stream, theta, nb, B, H,
+                     last_valid, pc);
+  hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nb), dim3(BlockShape<4>::THREADS),
+                     0, stream, theta, nullptr, (int64_t)0, (int64_t)0, nb, last_valid, B, T,
+                     (int64_t)B, BB, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // C = alpha A B + beta D per block (A row-major, B(n, k) = Bm[k][n]), every
+  // operand with row stride 512 and block stride 512^2; a second job of the
+  // same shape runs in the same launch
+  auto prod = [&](const float* A, const float* Bm, float alpha, const float* D, float beta,
+                  float* C, const float* A2, const float* B2, const float* D2, float* C2) {
+    GemmParams g;
+    g.A = A; g.B = Bm; g.C = C; g.D = D;
+    g.lda = g.ldb = g.ldc = g.ldd = B;
+    g.sA = g.sB = g.sC = g.sD = BB;
+    g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = H;
+    g.batch = A2 ? 2 * nb : nb;
+    g.kchunk = H;
+    g.alpha = alpha; g.beta = beta;
+    if (A2) {
+      g.batch_split = nb;
+      g.A2 = A2; g.B2 = B2; g.C2 = C2; g.D2 = D2;
+    }
+    return launch_gemm(DType::F32, DType::F32, true, false, g, stream);
+  };
+  // X = Z Q12 = (T Q12 + Q12) / 2 and V = Q21 Z = (Q21 T + Q21) / 2
+  if ((e = prod(T, Q12, 0.5f, Q12, 0.5f, X, Q21, T, Q21, V)) != hipSuccess) return e;
+  // S = (I - Q22) - V Q12
+  if ((e = prod(V, Q12, -1.0f, D22, 1.0f, S, nullptr, nullptr, nullptr, nullptr)) != hipSuccess)
+    return e;
+  // R22 = 2 S^-1 - I, written into the block with its bf16 copy
+  hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nb), dim3(BlockShape<4>::THREADS),
+                     0, stream, nullptr, S, (int64_t)B, BB, nb, last_valid, B, R22, (int64_t)B, BB,
+                     act ? act + H * B + H : nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // R12 = X R22 + X and R21 = R22 V + V in one launch, then R11 = T + R12 V
+  // (over X, which nothing reads any more)
+  if ((e = prod(X, R22, 1.0f, X, 1.0f, R12, R22, V, V, R21)) != hipSuccess) return e;
+  if ((e = prod(R12, V, 1.0f, T, 1.0f, R, nullptr, nullptr, nullptr, nullptr)) != hipSuccess)
+    return e;
   if (act) {  // the bf16 copy of the other three pieces (R22's came with it)
     const int64_t want = ((int64_t)nb * BB / 4 + kNT - 1) / kNT;
     const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
@@ -943,7 +986,7 @@ int cayley_panel_width(int b) {
 }
 
 size_t cayley_workspace_floats(int64_t nblocks, int b) {
-  if (use_schur(nblocks, b)) return 6 * (size_t)nblocks * 256 * 256;
+  if (use_schur(nblocks, b)) return 2 * (size_t)nblocks * 512 * 512;
   const int pw = cayley_panel_width(b);
   // row and column panels, and the next pivot block's inverse
   return 2 * (size_t)nblocks * (size_t)pw * (size_t)b + (size_t)nblocks * kPW * kPW;
@@ -962,12 +1005,14 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
   if (whole_block) {  // the whole block on one CU
     if (b == 256)
       hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nblocks),
-                         dim3(BlockShape<4>::THREADS), 0, stream, theta, nullptr, (int)nblocks,
-                         last_valid, b, blocks_f32, (int64_t)b, (int64_t)b * b, act_bf16);
+                         dim3(BlockShape<4>::THREADS), 0, stream, theta, nullptr, (int64_t)0,
+                         (int64_t)0, (int)nblocks, last_valid, b, blocks_f32, (int64_t)b,
+                         (int64_t)b * b, act_bf16);
     else
       hipLaunchKernelGGL(cayley_block_kernel<2>, dim3((unsigned)nblocks),
-                         dim3(BlockShape<2>::THREADS), 0, stream, theta, nullptr, (int)nblocks,
-                         last_valid, b, blocks_f32, (int64_t)b, (int64_t)b * b, act_bf16);
+                         dim3(BlockShape<2>::THREADS), 0, stream, theta, nullptr, (int64_t)0,
+                         (int64_t)0, (int)nblocks, last_valid, b, blocks_f32, (int64_t)b,
+                         (int64_t)b * b, act_bf16);
     return hipGetLastError();
   }
   if (use_schur(nblocks, b))
@@ -980,8 +1025,8 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
   float* dinv = colbuf + (size_t)nblocks * pw * b;
   bf16_t* act_out = (act == DType::BF16) ? static_cast<bf16_t*>(blocks_act) : nullptr;
   const int et = (b + 31) / 32;
-  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb), dim3(kNT), 0, stream, theta, nb, b, 0, 0, b,
-                     last_valid, 1.0f, -1.0f, blocks_f32);
+  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb, 1), dim3(kNT), 0, stream, theta, nb, b, b,
+                     last_valid, whole_piece(b, 1.0f, -1.0f, blocks_f32));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // With at least two update workgroups per CU, the next pivot's inversion
@@ -1004,8 +1049,8 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
 hipError_t launch_expand_skew(const float* theta, int64_t nblocks, int b, int last_valid,
                               float diag, float sign, float* out, hipStream_t stream) {
   const int et = (b + 31) / 32;
-  hipLaunchKernelGGL(expand_kernel, dim3(et * et, (int)nblocks), dim3(kNT), 0, stream, theta,
-                     (int)nblocks, b, 0, 0, b, last_valid, diag, sign, out);
+  hipLaunchKernelGGL(expand_kernel, dim3(et * et, (int)nblocks, 1), dim3(kNT), 0, stream, theta,
+                     (int)nblocks, b, b, last_valid, whole_piece(b, diag, sign, out));
   return hipGetLastError();
 }
 
