@@ -486,6 +486,7 @@ hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor, const 
     return big ? launch_layout<bf16_t, float, Big>(a_kmajor, b_kmajor, p, stream)
                : launch_layout<bf16_t, float, SmallBf16>(a_kmajor, b_kmajor, p, stream);
   }
+  if (out == DType::F32 && bmm32_supported(p, a_kmajor, b_kmajor)) return launch_bmm32(p, stream);
   if (out == DType::F32)
     return p.M >= 128 ? launch_layout<float, float, MidF32>(a_kmajor, b_kmajor, p, stream)
                       : launch_layout<float, float, SmallF32>(a_kmajor, b_kmajor, p, stream);

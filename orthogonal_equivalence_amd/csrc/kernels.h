@@ -50,6 +50,12 @@ hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor,
                        const GemmParams& p, hipStream_t stream);
 
+// Batched square float32 products (M = N = K a multiple of 128, A K-major,
+// B N-major, no split) on the LDS-DMA fp32 kernel; launch_gemm takes this
+// path by itself when the shape allows it.
+bool bmm32_supported(const GemmParams& p, bool a_kmajor, bool b_kmajor);
+hipError_t launch_bmm32(const GemmParams& p, hipStream_t stream);
+
 // K tile of the GEMM configurations for `in` (split-K chunks are multiples
 // of it) and the M/N tile chosen for an M x N problem.
 int gemm_k_tile(DType in);
