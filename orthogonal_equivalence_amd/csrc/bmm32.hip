@@ -1,4 +1,5 @@
-// Batched square float32 products C = alpha A B + beta D on fp32 MFMA, for the
+// Batched square float32 products C = alpha A B + beta D on fp32 MFMA (and,
+// when asked, C's bf16 copy), for the
 // b x b block products of the Cayley build (the 2 x 2 Schur pieces) and of
 // the Cayley-Neumann series and its VJP (b a multiple of 128).
 //
@@ -56,6 +57,8 @@ bmm32_kernel(const GemmParams p, int tiles_n) {
   const void* Dv = seg2 ? p.D2 : p.D;
   const float* D = Dv ? static_cast<const float*>(Dv) + sb * p.sD : nullptr;
   float* C = static_cast<float*>(seg2 ? p.C2 : p.C) + sb * p.sC;
+  void* Cav = seg2 ? p.C2_act : p.C_act;
+  bf16_t* Ca = Cav ? static_cast<bf16_t*>(Cav) + sb * p.sC : nullptr;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
   const int m0 = tm * kTile, n0 = tn * TN;
   const int nk = p.K / kBK;
@@ -158,7 +161,14 @@ bmm32_kernel(const GemmParams p, int tiles_n) {
       const float4 d = *reinterpret_cast<const float4*>(D + (int64_t)(m0 + r) * p.ldd + n0 + c4);
       v.x += p.beta * d.x; v.y += p.beta * d.y; v.z += p.beta * d.z; v.w += p.beta * d.w;
     }
-    *reinterpret_cast<float4*>(C + (int64_t)(m0 + r) * p.ldc + n0 + c4) = v;
+    const int64_t off = (int64_t)(m0 + r) * p.ldc + n0 + c4;
+    *reinterpret_cast<float4*>(C + off) = v;
+    if (Ca) {
+      union { uint2 u; bf16_t h[4]; } o;
+      o.h[0] = f32_to_bf16(v.x); o.h[1] = f32_to_bf16(v.y);
+      o.h[2] = f32_to_bf16(v.z); o.h[3] = f32_to_bf16(v.w);
+      *reinterpret_cast<uint2*>(Ca + off) = o.u;
+    }
   }
 }
 
@@ -179,6 +189,10 @@ bool bmm32_supported(const GemmParams& p, bool a_kmajor, bool b_kmajor) {
                         two ? p.C2 : nullptr, two ? p.D2 : nullptr};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return false;
+  // bf16 copies are written 8 bytes at a time
+  const void* acts[] = {p.C_act, two ? p.C2_act : nullptr};
+  for (const void* q : acts)
+    if (q && (reinterpret_cast<uintptr_t>(q) & 7u) != 0) return false;
   if (two && (!p.A2 || !p.B2 || !p.C2 || (p.D != nullptr) != (p.D2 != nullptr))) return false;
   return p.batch >= 1 && p.batch <= 65535;
 }

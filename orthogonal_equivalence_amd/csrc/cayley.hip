@@ -61,42 +61,64 @@ struct ExpandPieces {
   int64_t ldo, so;
 };
 
+constexpr int kExpandTiles = 4;  // 32 x 32 tiles per workgroup, along a tile row
+
 __global__ void __launch_bounds__(kNT)
 expand_kernel(const float* __restrict__ theta, int nblocks, int gb, int bo, int last_valid,
               ExpandPieces pc) {
-  __shared__ float t[32][33];
+  __shared__ float t[kExpandTiles][32][33];
   const int z = blockIdx.z;
   const int ro = pc.ro[z], co = pc.co[z];
   const float diag = pc.diag[z], sign = pc.sign[z];
   const int ntile = (bo + 31) / 32;
-  const int TI = blockIdx.x / ntile, TJ = blockIdx.x - (blockIdx.x / ntile) * ntile;
+  const int strips = (ntile + kExpandTiles - 1) / kExpandTiles;
+  const int TI = blockIdx.x / strips, TJ0 = (blockIdx.x - TI * strips) * kExpandTiles;
   const int blk = blockIdx.y;
   const int r = (blk == nblocks - 1) ? last_valid : gb;
   const float* th = theta + (int64_t)blk * ((int64_t)gb * (gb - 1) / 2);
   float* Ab = pc.out[z] + (int64_t)blk * pc.so;
   const int tx = threadIdx.x & 31, ty0 = threadIdx.x >> 5;  // 8 rows per pass
-  // global position of the tile; read the upper-triangle tile of its
-  // position (its mirror when it lies below the diagonal) row by row
-  const int gi0 = ro + TI * 32, gj0 = co + TJ * 32;
-  const bool lower = gi0 > gj0;
-  const int ui = lower ? gj0 : gi0, uj = lower ? gi0 : gj0;
-  for (int ty = ty0; ty < 32; ty += 8) {
-    const int i = ui + ty, j = uj + tx;
-    float q = 0.0f;  // Q[i][j]
-    if (i < j && j < gb && j < r) q = th[packed_index(gb, i, j)];
-    t[ty][tx] = q;
+  // every load of the strip first: for each tile, the upper-triangle tile of
+  // its global position (its mirror when it lies below the diagonal), row by row
+  float q[kExpandTiles][4];
+#pragma unroll
+  for (int s = 0; s < kExpandTiles; ++s) {
+    const int gi0 = ro + TI * 32, gj0 = co + (TJ0 + s) * 32;
+    const bool lower = gi0 > gj0;
+    const int ui = lower ? gj0 : gi0, uj = lower ? gi0 : gj0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int i = ui + ty0 + 8 * h, j = uj + tx;
+      q[s][h] = (TJ0 + s < ntile && i < j && j < gb && j < r) ? th[packed_index(gb, i, j)] : 0.0f;
+    }
   }
+#pragma unroll
+  for (int s = 0; s < kExpandTiles; ++s)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) t[s][ty0 + 8 * h][tx] = q[s][h];  // Q[i][j]
   __syncthreads();
-  for (int ty = ty0; ty < 32; ty += 8) {
-    const int i = TI * 32 + ty, j = TJ * 32 + tx;
-    if (i >= bo || j >= bo) continue;
-    const int gi = ro + i, gj = co + j;
-    float v;
-    if (gi == gj) v = diag;
-    else if (gi > gj) v = -sign * t[tx][ty];  // Q[i][j] = -Q[j][i]
-    else v = sign * t[ty][tx];
-    Ab[(int64_t)i * pc.ldo + j] = v;
+#pragma unroll
+  for (int s = 0; s < kExpandTiles; ++s) {
+    const int TJ = TJ0 + s;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int ty = ty0 + 8 * h;
+      const int i = TI * 32 + ty, j = TJ * 32 + tx;
+      if (TJ >= ntile || i >= bo || j >= bo) continue;
+      const int gi = ro + i, gj = co + j;
+      float v;
+      if (gi == gj) v = diag;
+      else if (gi > gj) v = -sign * t[s][tx][ty];  // Q[i][j] = -Q[j][i]
+      else v = sign * t[s][ty][tx];
+      Ab[(int64_t)i * pc.ldo + j] = v;
+    }
   }
+}
+
+// Grid width of expand_kernel for bo x bo pieces.
+int expand_grid_x(int bo) {
+  const int ntile = (bo + 31) / 32;
+  return ntile * ((ntile + kExpandTiles - 1) / kExpandTiles);
 }
 
 // The whole b x b matrix as one piece, contiguous blocks.
@@ -862,23 +884,6 @@ pack_skew_grad_kernel(PackSet s1, PackSet s2, float c, int b, float sign) {
   }
 }
 
-// out = bf16(in) for nblocks b x b blocks, except the bottom-right h x h
-// piece of each block (h % 4 == 0, b % 4 == 0). grid-stride over float4s.
-__global__ void __launch_bounds__(kNT)
-to_bf16_kernel(const float* __restrict__ in, int64_t nblocks, int b, int h,
-               bf16_t* __restrict__ out) {
-  const int64_t per = (int64_t)b * b / 4, n4 = nblocks * per;
-  for (int64_t q = (int64_t)blockIdx.x * kNT + threadIdx.x; q < n4; q += (int64_t)gridDim.x * kNT) {
-    const int e = (int)(q % per) * 4;
-    if (e / b >= b - h && e % b >= b - h) continue;
-    const float4 v = reinterpret_cast<const float4*>(in)[q];
-    union { uint2 u; bf16_t h[4]; } o;
-    o.h[0] = f32_to_bf16(v.x); o.h[1] = f32_to_bf16(v.y);
-    o.h[2] = f32_to_bf16(v.z); o.h[3] = f32_to_bf16(v.w);
-    reinterpret_cast<uint2*>(out)[q] = o.u;
-  }
-}
-
 // Blocks of 512 as 2 x 2 pieces of 256 (Schur complement), for many blocks.
 // With A = I - Q = [[A11, A12], [A21, A22]] (A11 = I - Q11, A12 = -Q12,
 // A21 = Q12^T, A22 = I - Q22), Z = A11^-1, X = Z Q12 and V = -A21 Z = Q21 Z:
@@ -919,15 +924,14 @@ hipError_t schur512_build(const float* theta, int nb, int last_valid, float* R, 
   float* R21 = R + H * B;
   float* R22 = R + H * B + H;
   hipError_t e;
-  const int et = H / 32;
   ExpandPieces pc{};
   pc.ro[0] = 0; pc.co[0] = H; pc.diag[0] = 0.0f; pc.sign[0] = 1.0f; pc.out[0] = Q12;   // Q12
   pc.ro[1] = H; pc.co[1] = 0; pc.diag[1] = 0.0f; pc.sign[1] = 1.0f; pc.out[1] = Q21;   // Q21
   pc.ro[2] = H; pc.co[2] = H; pc.diag[2] = 1.0f; pc.sign[2] = -1.0f; pc.out[2] = D22;  // I - Q22
   pc.ldo = B;
   pc.so = BB;
-  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb, 3), dim3(kNT), 0, stream, theta, nb, B, H,
-                     last_valid, pc);
+  hipLaunchKernelGGL(expand_kernel, dim3(expand_grid_x(H), nb, 3), dim3(kNT), 0, stream, theta, nb,
+                     B, H, last_valid, pc);
   hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nb), dim3(BlockShape<4>::THREADS),
                      0, stream, theta, nullptr, (int64_t)0, (int64_t)0, nb, last_valid, B, T,
                      (int64_t)B, BB, nullptr);
@@ -937,7 +941,8 @@ hipError_t schur512_build(const float* theta, int nb, int last_valid, float* R, 
   // operand with row stride 512 and block stride 512^2; a second job of the
   // same shape runs in the same launch
   auto prod = [&](const float* A, const float* Bm, float alpha, const float* D, float beta,
-                  float* C, const float* A2, const float* B2, const float* D2, float* C2) {
+                  float* C, const float* A2, const float* B2, const float* D2, float* C2,
+                  bf16_t* C_act = nullptr, bf16_t* C2_act = nullptr) {
     GemmParams g;
     g.A = A; g.B = Bm; g.C = C; g.D = D;
     g.lda = g.ldb = g.ldc = g.ldd = B;
@@ -946,9 +951,11 @@ hipError_t schur512_build(const float* theta, int nb, int last_valid, float* R, 
     g.batch = A2 ? 2 * nb : nb;
     g.kchunk = H;
     g.alpha = alpha; g.beta = beta;
+    g.C_act = C_act;
     if (A2) {
       g.batch_split = nb;
       g.A2 = A2; g.B2 = B2; g.C2 = C2; g.D2 = D2;
+      g.C2_act = C2_act;
     }
     return launch_gemm(DType::F32, DType::F32, true, false, g, stream);
   };
@@ -963,17 +970,11 @@ hipError_t schur512_build(const float* theta, int nb, int last_valid, float* R, 
                      act ? act + H * B + H : nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // R12 = X R22 + X and R21 = R22 V + V in one launch, then R11 = T + R12 V
-  // (over X, which nothing reads any more)
-  if ((e = prod(X, R22, 1.0f, X, 1.0f, R12, R22, V, V, R21)) != hipSuccess) return e;
-  if ((e = prod(R12, V, 1.0f, T, 1.0f, R, nullptr, nullptr, nullptr, nullptr)) != hipSuccess)
+  // (over X, which nothing reads any more); each with its bf16 copy
+  if ((e = prod(X, R22, 1.0f, X, 1.0f, R12, R22, V, V, R21, act ? act + H : nullptr,
+                act ? act + H * B : nullptr)) != hipSuccess)
     return e;
-  if (act) {  // the bf16 copy of the other three pieces (R22's came with it)
-    const int64_t want = ((int64_t)nb * BB / 4 + kNT - 1) / kNT;
-    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
-    hipLaunchKernelGGL(to_bf16_kernel, dim3(grid), dim3(kNT), 0, stream, R, (int64_t)nb, B, H, act);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return prod(R12, V, 1.0f, T, 1.0f, R, nullptr, nullptr, nullptr, nullptr, act);
 }
 
 }  // namespace
@@ -1024,9 +1025,8 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
   float* colbuf = ws + (size_t)nblocks * pw * b;
   float* dinv = colbuf + (size_t)nblocks * pw * b;
   bf16_t* act_out = (act == DType::BF16) ? static_cast<bf16_t*>(blocks_act) : nullptr;
-  const int et = (b + 31) / 32;
-  hipLaunchKernelGGL(expand_kernel, dim3(et * et, nb, 1), dim3(kNT), 0, stream, theta, nb, b, b,
-                     last_valid, whole_piece(b, 1.0f, -1.0f, blocks_f32));
+  hipLaunchKernelGGL(expand_kernel, dim3(expand_grid_x(b), nb, 1), dim3(kNT), 0, stream, theta, nb,
+                     b, b, last_valid, whole_piece(b, 1.0f, -1.0f, blocks_f32));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // With at least two update workgroups per CU, the next pivot's inversion
@@ -1048,9 +1048,8 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
 
 hipError_t launch_expand_skew(const float* theta, int64_t nblocks, int b, int last_valid,
                               float diag, float sign, float* out, hipStream_t stream) {
-  const int et = (b + 31) / 32;
-  hipLaunchKernelGGL(expand_kernel, dim3(et * et, (int)nblocks, 1), dim3(kNT), 0, stream, theta,
-                     (int)nblocks, b, b, last_valid, whole_piece(b, diag, sign, out));
+  hipLaunchKernelGGL(expand_kernel, dim3(expand_grid_x(b), (int)nblocks, 1), dim3(kNT), 0, stream,
+                     theta, (int)nblocks, b, b, last_valid, whole_piece(b, diag, sign, out));
   return hipGetLastError();
 }
 

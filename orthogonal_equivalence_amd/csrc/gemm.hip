@@ -487,6 +487,7 @@ hipError_t launch_gemm(DType in, DType out, bool a_kmajor, bool b_kmajor, const 
                : launch_layout<bf16_t, float, SmallBf16>(a_kmajor, b_kmajor, p, stream);
   }
   if (out == DType::F32 && bmm32_supported(p, a_kmajor, b_kmajor)) return launch_bmm32(p, stream);
+  if (p.C_act || p.C2_act) return hipErrorInvalidValue;  // only bmm32 writes the bf16 copies
   if (out == DType::F32)
     return p.M >= 128 ? launch_layout<float, float, MidF32>(a_kmajor, b_kmajor, p, stream)
                       : launch_layout<float, float, SmallF32>(a_kmajor, b_kmajor, p, stream);

@@ -40,6 +40,11 @@ struct GemmParams {
   const void* B2 = nullptr;
   void* C2 = nullptr;
   const void* D2 = nullptr;
+  // Optional bf16 copies of C (and C2) at the same element offsets; only the
+  // square float32 kernel (bmm32) writes them, so launch_gemm refuses them
+  // for any other path.
+  void* C_act = nullptr;
+  void* C2_act = nullptr;
 };
 
 // Device address of the library's fixed scratch array (POETX_NOALLOC_SCRATCH_BYTES)
