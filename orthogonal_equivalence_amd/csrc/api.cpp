@@ -219,8 +219,10 @@ GemmParams blockdiag_params(const void* in, const void* blocks, void* out, int64
   return g;
 }
 
-// out[:, blk] = in[:, blk] M_blk^T (transpose) or in[:, blk] M_blk, on the
-// streaming kernel when it supports the shape, else on the batched GEMM.
+// out[:, blk] = in[:, blk] M_blk^T (transpose) or in[:, blk] M_blk: b = 32 / 64
+// on 128 x 128 super blocks, b >= 512 on the batched dense kernel when the
+// streaming kernel would underfill, b = 128 / 256 / 512 on the streaming
+// kernel, else on the batched GEMM.
 hipError_t block_apply(DType t, const void* in, const void* blocks, void* out, int64_t tokens,
                        int64_t d, int b, bool transpose, hipStream_t s, void* super_ws) {
   if (const int S = poetx::superblock_size(t, d, b)) {

@@ -119,9 +119,11 @@ SMALL_CASES = [
     ("bf16_b64_one_token", 256, 384, 64, 1, "bf16", 0.05),
     ("bf16_padded_blocks", 320, 200, 128, 257, "bf16", 0.02),
     ("bf16_b512", 1024, 512, 512, 129, "bf16", 0.01),
-    # b = 512 streams in four slab / quadrant workgroups per block and token
-    # range: several blocks and splits, and launches whose last group of 8
-    # units is partly padding
+    # b = 512: the grams stream in four quadrant workgroups per block and
+    # token range; the applies take the batched dense kernel at 1000 tokens
+    # (several blocks, a ragged token tile) and the streaming slab
+    # workgroups below 256 tokens (launches whose last group of 8 units is
+    # partly padding)
     ("bf16_b512_blocks", 2048, 1536, 512, 1000, "bf16", 0.01),
     ("bf16_b512_padded_units", 1536, 1024, 512, 100, "bf16", 0.01),
     # one token: every streamed tile is ragged, every split but one empty
