@@ -177,7 +177,12 @@ size_t poetx_build_workspace_size(int64_t d, int32_t b);
  *   blocks_f32  out [nb, b, b] float32: R_k = (I + Q_k)(I - Q_k)^-1, computed
  *               as 2 (I - Q_k)^-1 - I by unpivoted blocked Gauss-Jordan
  *               elimination (I - Q has symmetric part I, so no pivot is ever
- *               needed).
+ *               needed); from 48 blocks of 512, as 2 x 2 pieces of 256 joined
+ *               through the Schur complement of the leading piece (whose
+ *               symmetric part is positive definite too). The rounding of
+ *               the float32 result depends on which of these forms runs, so
+ *               a block built alone and in a large set may differ in the last
+ *               bits.
  *   blocks_act  out [nb, b, b] copy in `act` type (bf16: round to nearest
  *               even). Required when act is POETX_BF16; ignored (may be NULL)
  *               when act is POETX_F32.
