@@ -161,16 +161,18 @@ def sources_digest():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dense forward GEMM from the committed
-    FETCH_SIZE / WRITE_SIZE counter passes, if they were taken on the current
-    kernel sources (else None)."""
+def measured_traffic(config):
+    """L2-miss bytes per launch of the dense forward GEMM from the committed
+    FETCH_SIZE / WRITE_SIZE counter passes, if they were taken on this
+    workload and on the current kernel sources (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("sources_sha256") != sources_digest():
+        return None
+    if not str(t.get("workload", "")).startswith(config + ":"):
         return None
     return t.get("bytes_per_launch")
 
@@ -404,10 +406,13 @@ def main():
     peak = PEAK_BF16 if sb.dtype == "bf16" else PEAK_F32
     achieved = dense_flops / (dense_ms / 1e3)
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": measured_traffic(),
+                "frac": achieved / peak,
+                "traffic": (measured_traffic(args.config) if args.map == "cayley" and not
+                            (args.permute or args.int8 or args.recompute_z) else None),
                 "traffic_kind": "L2-miss bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a "
                                 "plain copy): requests leaving the L2, answered by the Infinity "
-                                "Cache or HBM; null when the kernel changed since the passes",
+                                "Cache or HBM; null when the kernel changed since the passes "
+                                "or they were taken on another workload",
                 "kernel": ("dense_fwd: Z = U W0^T with Y = Z blockdiag(R)^T in its epilogue "
                            "(dense_kernel<true, true>" if fused_r else
                            "dense_fwd: Z = U W0^T (dense_kernel<true, false>") +

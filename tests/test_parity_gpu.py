@@ -86,6 +86,22 @@ def test_build_matches_oracle(b, nb, sigma):
     assert torch.equal(a, ref)
 
 
+@pytest.mark.parametrize("b,nb", [(256, 3), (256, 48), (512, 2), (512, 48)])
+def test_build_f32_only_matches_bf16_build(b, nb):
+    """With act = float32 (no bf16 copy requested) each build form (panels,
+    whole block, Schur pieces) writes the same float32 blocks as with the bf16
+    copy, and they match the oracle."""
+    U.log(f"[build f32] b={b} nb={nb}")
+    rng = np.random.default_rng(31 * b + nb)
+    theta = (rng.standard_normal((nb, b * (b - 1) // 2)) * 0.01).astype(np.float32).astype(np.float64)
+    f32_only, none = _build(theta, nb * b, b, P.POETX_F32)
+    assert none is None
+    f32, _ = _build(theta, nb * b, b)
+    assert torch.equal(f32_only, f32)
+    R_ref, _ = O.orthogonal_blocks(theta, b, nb * b)
+    assert np.max(np.abs(U.host(f32_only) - R_ref)) <= 2e-5 * max(1.0, math.sqrt(b) / 8)
+
+
 @pytest.mark.parametrize("b,r,nfull", [(64, 24, 2), (128, 77, 2), (256, 24, 2), (256, 193, 2),
                                         (256, 193, 47), (512, 300, 47), (512, 200, 47)])
 def test_build_padded_last_block(b, r, nfull):
