@@ -900,14 +900,19 @@ pack_skew_grad_kernel(PackSet s1, PackSet s2, float c, int b, float sign) {
 // a matrix whose symmetric part is I), so neither elimination pivots.
 constexpr int kSchurMinBlocks = 48;
 
+// (The same form for 72 blocks of 256, on pieces of 128, took 211 us against
+// 187 us for the whole-block kernel, so b = 256 keeps that kernel.)
 bool use_schur(int64_t nblocks, int b) { return b == 512 && nblocks >= kSchurMinBlocks; }
 
-hipError_t schur512_build(const float* theta, int nb, int last_valid, float* R, bf16_t* act,
-                          float* ws, hipStream_t stream) {
-  constexpr int H = 256, B = 512;
+// NT: the whole-block kernel's tile count per edge for the pieces (H = 64 NT,
+// B = 2 H).
+template <int NT>
+hipError_t schur_build(const float* theta, int nb, int last_valid, float* R, bf16_t* act,
+                       float* ws, hipStream_t stream) {
+  constexpr int H = 64 * NT, B = 2 * H;
   constexpr int64_t BB = (int64_t)B * B;
-  // Every piece lives in a 512 x 512 frame per block (row stride 512, block
-  // stride 512^2), as the pieces of R do, so that the paired products share
+  // Every piece lives in a B x B frame per block (row stride B, block
+  // stride B^2), as the pieces of R do, so that the paired products share
   // their strides: W1 holds T, Q12, Q21 and I - Q22 in its four quadrants,
   // W2 holds V and S in its top half, and X sits in R's R11 quadrant until
   // R11 is written.
@@ -932,7 +937,7 @@ hipError_t schur512_build(const float* theta, int nb, int last_valid, float* R, 
   pc.so = BB;
   hipLaunchKernelGGL(expand_kernel, dim3(expand_grid_x(H), nb, 3), dim3(kNT), 0, stream, theta, nb,
                      B, H, last_valid, pc);
-  hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nb), dim3(BlockShape<4>::THREADS),
+  hipLaunchKernelGGL(cayley_block_kernel<NT>, dim3((unsigned)nb), dim3(BlockShape<NT>::THREADS),
                      0, stream, theta, nullptr, (int64_t)0, (int64_t)0, nb, last_valid, B, T,
                      (int64_t)B, BB, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -965,7 +970,7 @@ hipError_t schur512_build(const float* theta, int nb, int last_valid, float* R, 
   if ((e = prod(V, Q12, -1.0f, D22, 1.0f, S, nullptr, nullptr, nullptr, nullptr)) != hipSuccess)
     return e;
   // R22 = 2 S^-1 - I, written into the block with its bf16 copy
-  hipLaunchKernelGGL(cayley_block_kernel<4>, dim3((unsigned)nb), dim3(BlockShape<4>::THREADS),
+  hipLaunchKernelGGL(cayley_block_kernel<NT>, dim3((unsigned)nb), dim3(BlockShape<NT>::THREADS),
                      0, stream, nullptr, S, (int64_t)B, BB, nb, last_valid, B, R22, (int64_t)B, BB,
                      act ? act + H * B + H : nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -987,7 +992,7 @@ int cayley_panel_width(int b) {
 }
 
 size_t cayley_workspace_floats(int64_t nblocks, int b) {
-  if (use_schur(nblocks, b)) return 2 * (size_t)nblocks * 512 * 512;
+  if (use_schur(nblocks, b)) return 2 * (size_t)nblocks * b * b;
   const int pw = cayley_panel_width(b);
   // row and column panels, and the next pivot block's inverse
   return 2 * (size_t)nblocks * (size_t)pw * (size_t)b + (size_t)nblocks * kPW * kPW;
@@ -1002,6 +1007,8 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
   // one CU); the panel kernels spread every block's products over the chip, so
   // with few blocks of 256 they finish first (measured: 16 blocks 164 -> 119
   // us, 32 blocks 172 -> 140 us), with 64 or more the whole-block kernel does.
+  if (use_schur(nblocks, b))
+    return schur_build<4>(theta, (int)nblocks, last_valid, blocks_f32, act_bf16, ws, stream);
   const bool whole_block = b == 128 || (b == 256 && nblocks >= 48);
   if (whole_block) {  // the whole block on one CU
     if (b == 256)
@@ -1016,8 +1023,6 @@ hipError_t launch_cayley_build(const float* theta, int64_t nblocks, int b, int l
                          (int64_t)b * b, act_bf16);
     return hipGetLastError();
   }
-  if (use_schur(nblocks, b))
-    return schur512_build(theta, (int)nblocks, last_valid, blocks_f32, act_bf16, ws, stream);
   const int pw = cayley_panel_width(b);
   const int nt = b / pw;
   const int nb = (int)nblocks;
