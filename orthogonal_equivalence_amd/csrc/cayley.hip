@@ -7,21 +7,30 @@
 // Cayley-Neumann parameterisation item). The map used here is the exact
 // Cayley map R = (I + Q)(I - Q)^-1 = 2 (I - Q)^-1 - I.
 //
-// (I - Q)^-1 is formed by blocked Gauss-Jordan elimination without pivoting,
-// in place in the float32 output buffer: I - Q has symmetric part I, which
-// is positive definite, so every pivot block (a Schur complement of I - Q)
-// again has a positive definite symmetric part and is invertible. Each panel
-// of width pw (<= 64) is one pair of launches over all blocks at once:
-//   prep:   D = A[p][p] is inverted in registers (each of 256 threads owns a
-//           4 x 4 piece; four pivots per step, the pivot row and column
-//           blocks through LDS, one barrier per step); the workgroup for
-//           column tile J writes
-//           W_J = Dinv A[p][J] (Dinv itself for J = p, an fp32 MFMA product
-//           otherwise) to a row-panel buffer and copies A[J][p] to a
-//           column-panel buffer;
-//   update: every tile (I, J) becomes W_J (I = p) or
-//           A[I][J] - colpanel[I] W_J (A[I][p] taken as zero), on MFMA.
-// The last update writes R = 2 B - I and the activation-type copy.
+// (I - Q)^-1 is formed by blocked Gauss-Jordan elimination without pivoting:
+// I - Q has symmetric part I, which is positive definite, so every pivot
+// block (a Schur complement of I - Q) again has a positive definite
+// symmetric part and is invertible. Three forms, by block size and count:
+//   - whole block on one CU (b = 128, and b = 256 from 48 blocks): the tiles
+//     in registers, the panels through LDS (cayley_block_kernel);
+//   - 2 x 2 pieces of 256 (b = 512 from 48 blocks): the leading piece and
+//     its Schur complement inverted by the whole-block kernel, joined by
+//     batched float32 products (schur_build);
+//   - panels over the chip (every other case), in place in the float32
+//     output buffer, each panel of width pw (<= 64) one pair of launches
+//     over all blocks at once:
+//       prep:   D = A[p][p] inverted in registers (each of 256 threads owns
+//               a 4 x 4 piece; four pivots per step, the pivot row and
+//               column blocks through LDS, one barrier per step), unless the
+//               previous update already did; the workgroup for column tile J
+//               writes W_J = Dinv A[p][J] (Dinv itself for J = p, an fp32
+//               MFMA product otherwise) to a row-panel buffer and copies
+//               A[J][p] to a column-panel buffer;
+//       update: every tile (I, J) becomes W_J (I = p) or
+//               A[I][J] - colpanel[I] W_J (A[I][p] taken as zero), on MFMA;
+//               the tile that becomes the next pivot block is inverted
+//               right away (with two or more update workgroups per CU).
+//     The last update writes R = 2 B - I and the activation-type copy.
 #include "common.h"
 #include "kernels.h"
 
