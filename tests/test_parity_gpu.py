@@ -103,13 +103,15 @@ def test_build_f32_only_matches_bf16_build(b, nb):
 
 
 @pytest.mark.parametrize("b,r,nfull", [(64, 24, 2), (128, 77, 2), (256, 24, 2), (256, 193, 2),
-                                        (256, 193, 47), (512, 300, 47), (512, 200, 47)])
+                                        (256, 193, 47), (512, 300, 47), (512, 200, 47),
+                                        (512, 256, 47), (512, 257, 47)])
 def test_build_padded_last_block(b, r, nfull):
     """b does not divide d: the last block is diag(Cayley(Q_r), I), with the
     valid part ending inside a 64-wide tile or at its first column. Three
     blocks run on the panel kernels (b = 64, 256) or the whole-block kernel
     (b = 128); 48 blocks on the whole-block kernel (b = 256) or as Schur
-    pieces (b = 512, the valid part ending in either half)."""
+    pieces (b = 512, the valid part ending in either half, exactly at the
+    half, or one row past it)."""
     d = b * nfull + r
     U.log(f"[build padded] b={b} d={d}")
     rng = np.random.default_rng(5 + b + r + nfull)
