@@ -219,35 +219,60 @@ GemmParams blockdiag_params(const void* in, const void* blocks, void* out, int64
   return g;
 }
 
-// out[:, blk] = in[:, blk] M_blk^T (transpose) or in[:, blk] M_blk: b = 32 / 64
-// on 128 x 128 super blocks, b >= 512 on the batched dense kernel when the
-// streaming kernel would underfill, b = 128 / 256 / 512 on the streaming
-// kernel, else on the batched GEMM.
-hipError_t block_apply(DType t, const void* in, const void* blocks, void* out, int64_t tokens,
-                       int64_t d, int b, bool transpose, hipStream_t s, void* super_ws) {
-  if (const int S = poetx::superblock_size(t, d, b)) {
-    // b = 32 / 64: the blocks placed on the diagonals of 128 x 128 super
-    // blocks (zeros elsewhere) and applied by the b = 128 streaming kernel
-    hipError_t e = poetx::launch_superblocks(blocks, d / b, b, S, super_ws, s);
-    if (e != hipSuccess) return e;
-    return poetx::launch_blockapply(in, super_ws, out, tokens, d, S, transpose, s);
-  }
+// How block_apply runs a shape: b = 32 / 64 on 128 x 128 super blocks
+// through the b = 128 streaming kernel, b >= 512 on the batched dense kernel
+// when the streaming kernel would underfill, b = 128 / 256 / 512 on the
+// streaming kernel, else on the batched GEMM.
+enum class ApplyPath { Super, DenseBatched, Stream, Gemm };
+ApplyPath apply_path(DType t, int64_t tokens, int64_t d, int b) {
+  if (poetx::superblock_size(t, d, b)) return ApplyPath::Super;
   const bool streaming = poetx::blockapply_supported(t, d, b);
+  // Blocks of 512 and more: the batched dense kernel, one 256 x 256 output
+  // tile of one block per workgroup, all blocks in one launch. For b = 512
+  // the streaming kernel is faster once each of its workgroups covers more
+  // than 512 tokens: with K = 512 the dense kernel's tile fill and store take
+  // about as long as its 16 K steps (measured: 16384 tokens of d = 14336,
+  // 306 us streaming against 385 us dense; 8192 tokens of d = 4096, 54 us
+  // streaming against 48 us dense).
   if (t == DType::BF16 && b >= 512 && b % 256 == 0 && d % b == 0 &&
       poetx::dense_supported(tokens, b, b, d, b, d) &&
-      (!streaming || poetx::blockapply_tokens_per_workgroup(tokens, d, b) <= 512)) {
-    // blocks of 512 and more: the batched dense kernel, one 256 x 256 output
-    // tile of one block per workgroup, all blocks in one launch. For b = 512
-    // the streaming kernel is faster once each of its workgroups covers more
-    // than 512 tokens: with K = 512 the dense kernel's tile fill and store
-    // take about as long as its 16 K steps (measured: 16384 tokens of
-    // d = 14336, 306 us streaming against 385 us dense; 8192 tokens of
-    // d = 4096, 54 us streaming against 48 us dense).
-    return poetx::launch_dense_batched(in, blocks, out, tokens, b, b, d, b, d, transpose, d / b, b,
-                                       (int64_t)b * b, b, s);
+      (!streaming || poetx::blockapply_tokens_per_workgroup(tokens, d, b) <= 512))
+    return ApplyPath::DenseBatched;
+  return streaming ? ApplyPath::Stream : ApplyPath::Gemm;
+}
+
+// Whether block_apply can write its output in the tiled layout for this shape
+// (a streaming kernel and whole 256-token panels).
+bool apply_tiles(DType t, int64_t tokens, int64_t d, int b) {
+  const ApplyPath a = apply_path(t, tokens, d, b);
+  return tokens % poetx::kTileRows == 0 && (a == ApplyPath::Super || a == ApplyPath::Stream);
+}
+
+// out[:, blk] = in[:, blk] M_blk^T (transpose) or in[:, blk] M_blk, along
+// apply_path; out_tiled (only where apply_tiles holds) writes out in the
+// tiled layout.
+hipError_t block_apply(DType t, const void* in, const void* blocks, void* out, int64_t tokens,
+                       int64_t d, int b, bool transpose, hipStream_t s, void* super_ws,
+                       bool out_tiled = false) {
+  const ApplyPath a = apply_path(t, tokens, d, b);
+  if (out_tiled && !apply_tiles(t, tokens, d, b)) return hipErrorInvalidValue;
+  switch (a) {
+    case ApplyPath::Super: {
+      // the blocks placed on the diagonals of 128 x 128 super blocks (zeros
+      // elsewhere) and applied by the b = 128 streaming kernel
+      const int S = poetx::superblock_size(t, d, b);
+      hipError_t e = poetx::launch_superblocks(blocks, d / b, b, S, super_ws, s);
+      if (e != hipSuccess) return e;
+      return poetx::launch_blockapply(in, super_ws, out, tokens, d, S, transpose, out_tiled, s);
+    }
+    case ApplyPath::DenseBatched:
+      return poetx::launch_dense_batched(in, blocks, out, tokens, b, b, d, b, d, transpose, d / b,
+                                         b, (int64_t)b * b, b, s);
+    case ApplyPath::Stream:
+      return poetx::launch_blockapply(in, blocks, out, tokens, d, b, transpose, out_tiled, s);
+    case ApplyPath::Gemm:
+      break;
   }
-  if (streaming)
-    return poetx::launch_blockapply(in, blocks, out, tokens, d, b, transpose, s);
   bool bk;
   GemmParams g = blockdiag_params(in, blocks, out, tokens, d, b, transpose, &bk);
   return poetx::launch_gemm(t, t, true, bk, g, s);
@@ -284,13 +309,22 @@ hipError_t block_gram(DType t, const void* a, const void* c, float* part, int64_
   return poetx::launch_gemm(t, DType::F32, false, false, g, s);
 }
 
+// Whether dense() runs on the persistent dense kernel, which can read A in
+// the tiled layout.
+bool dense_direct(DType t, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+  return t == DType::BF16 && poetx::dense_supported(M, N, K, lda, ldb, ldc);
+}
+
 // A dense W0 product C[M][N] = A[M][K] B(n, k) (B(n, k) = B[n][k] when
 // b_kmajor, else B[k][n]): the persistent direct-to-LDS bf16 kernel when the
-// shape allows it, else the general GEMM.
+// shape allows it, else the general GEMM. a_tiled (only where dense_direct
+// holds): A in the tiled layout.
 hipError_t dense(DType t, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                 int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s) {
-  if (t == DType::BF16 && poetx::dense_supported(M, N, K, lda, ldb, ldc))
-    return poetx::launch_dense(A, B, C, M, N, K, lda, ldb, ldc, b_kmajor, s);
+                 int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s,
+                 bool a_tiled = false) {
+  if (dense_direct(t, M, N, K, lda, ldb, ldc))
+    return poetx::launch_dense(A, B, C, M, N, K, lda, ldb, ldc, b_kmajor, a_tiled, s);
+  if (a_tiled) return hipErrorInvalidValue;
   GemmParams g;
   g.A = A; g.lda = lda;
   g.B = B; g.ldb = ldb;
@@ -672,10 +706,13 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
     X = Xp;
   }
 
-  // S2: U = X blockdiag(P)^T
+  // S2: U = X blockdiag(P)^T; U is only read by the dense kernel, so it is
+  // written in the tiled layout when both kernels take it
+  const bool u_tiled = dense_direct(t, N, m, n, n, n, m) && apply_tiles(t, N, n, d->b_in);
   if ((e = sg.begin(0)) != hipSuccess) return hip_status(e);
   void* SB = w + plan.sb_off;  // super blocks of b = 32 / 64 blocks
-  if ((e = block_apply(t, X, P_act, U, N, n, d->b_in, true, s, SB)) != hipSuccess) return hip_status(e);
+  if ((e = block_apply(t, X, P_act, U, N, n, d->b_in, true, s, SB, u_tiled)) != hipSuccess)
+    return hip_status(e);
   if ((e = sg.end(0)) != hipSuccess) return hip_status(e);
 
   // S3: Z = U W0^T, and S4: Y = Z blockdiag(R)^T. With 256 x 256 R blocks in
@@ -688,9 +725,10 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
                       poetx::dense_fused_r_supported(N, m, n, n, n, m, m);
   if ((e = sg.begin(1)) != hipSuccess) return hip_status(e);
   if (fuse_r) {
-    if ((e = poetx::launch_dense_fused_r(U, Wmat, Z, N, m, n, n, n, m, Rb, Yout, m, s)) != hipSuccess)
+    if ((e = poetx::launch_dense_fused_r(U, Wmat, Z, N, m, n, n, n, m, Rb, Yout, m, u_tiled, s)) !=
+        hipSuccess)
       return hip_status(e);
-  } else if ((e = dense(t, U, Wmat, Z, N, m, n, n, n, m, true, s)) != hipSuccess) {
+  } else if ((e = dense(t, U, Wmat, Z, N, m, n, n, n, m, true, s, u_tiled)) != hipSuccess) {
     return hip_status(e);
   }
   if ((e = sg.end(1)) != hipSuccess) return hip_status(e);
@@ -827,10 +865,24 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     Rb = Rs;
   }
 
+  // Block size the one-pass gradient apply + gram runs at for a side (bf16,
+  // b = 128 or 256, or b = 32 / 64 as 128 x 128 super blocks), 0 if none.
+  auto one_pass_size = [&](int64_t dd, int bb) -> int {
+    if (const int S = poetx::superblock_size(t, dd, bb)) return S;
+    return poetx::blockgramapply_supported(t, dd, bb) ? bb : 0;
+  };
+  const int opR = one_pass_size(m, bR);
+  const bool fuse_r = opR != 0;
+  // g_Z is only read by B3's dense kernel, so it is written in the tiled
+  // layout when both kernels take it; not when the one pass reads Z from
+  // the g_Z buffer itself (POET-Xmem), since tiled stores would overwrite Z
+  // that other workgroups still read
+  const bool gz_tiled = dense_direct(t, N, n, m, m, n, n) && N % poetx::kTileRows == 0 &&
+                        (fuse_r ? z_saved != nullptr : apply_tiles(t, N, m, bR));
   auto grad_r = [&]() -> hipError_t {  // B1: g_Z = g_Y blockdiag(R)
     hipError_t r;
     if ((r = sg.begin(0)) != hipSuccess) return r;
-    if ((r = block_apply(t, gY, Rb, gZ, N, m, bR, false, s, SB)) != hipSuccess) return r;
+    if ((r = block_apply(t, gY, Rb, gZ, N, m, bR, false, s, SB, gz_tiled)) != hipSuccess) return r;
     return sg.end(0);
   };
   auto gram_r = [&](const void* Z) -> hipError_t {
@@ -843,16 +895,9 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
       return r;
     return sg.end(1);
   };
-  // Block size the one-pass gradient apply + gram runs at for a side (bf16,
-  // b = 128 or 256, or b = 32 / 64 as 128 x 128 super blocks), 0 if none.
-  auto one_pass_size = [&](int64_t dd, int bb) -> int {
-    if (const int S = poetx::superblock_size(t, dd, bb)) return S;
-    return poetx::blockgramapply_supported(t, dd, bb) ? bb : 0;
-  };
   // B1 and B2 in one pass over g_Y (stage 0), then the gram's reduction
   // (stage 1). Each Z element is read by the one workgroup that later writes
-  // g_Z at the same place, so Z may sit in the g_Z buffer.
-  const int opR = one_pass_size(m, bR);
+  // g_Z at the same place, so Z may sit in the (row-major) g_Z buffer.
   auto fused_r = [&](const void* Z) -> hipError_t {
     hipError_t r;
     int ns = 0;
@@ -862,8 +907,8 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
       if ((r = poetx::launch_superblocks(Rb, nbR, bR, opR, SB, s)) != hipSuccess) return r;
       Mr = SB;
     }
-    if ((r = poetx::launch_blockgramapply(gY, Mr, Z, gZ, partR, N, m, opR, plan.sR.nsplit, &ns, s)) !=
-        hipSuccess)
+    if ((r = poetx::launch_blockgramapply(gY, Mr, Z, gZ, partR, N, m, opR, plan.sR.nsplit, &ns,
+                                          gz_tiled, s)) != hipSuccess)
       return r;
     if ((r = sg.end(0)) != hipSuccess) return r;
     if ((r = sg.begin(1)) != hipSuccess) return r;
@@ -872,7 +917,6 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
       return r;
     return sg.end(1);
   };
-  const bool fuse_r = opR != 0;
   if (z_saved) {
     if (fuse_r) {
       POETX_TRY(fused_r(z_saved));
@@ -883,9 +927,11 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   } else {
     // POET-Xmem: U = X P^T into the g_U buffer and Z = U W0^T into the g_Z
     // buffer (both overwritten later), the R gram on Z, then g_Z over Z
+    // (U, read only by the dense kernel, tiled as in the forward)
+    const bool u_tiled = dense_direct(t, N, m, n, n, n, m) && apply_tiles(t, N, n, bP);
     POETX_TRY(sg.begin(7));
-    POETX_TRY(block_apply(t, X, P_act, gU, N, n, bP, true, s, SB));
-    POETX_TRY(dense(t, gU, Wmat, gZ, N, m, n, n, n, m, true, s));
+    POETX_TRY(block_apply(t, X, P_act, gU, N, n, bP, true, s, SB, u_tiled));
+    POETX_TRY(dense(t, gU, Wmat, gZ, N, m, n, n, n, m, true, s, u_tiled));
     POETX_TRY(sg.end(7));
     if (fuse_r) {
       POETX_TRY(fused_r(gZ));
@@ -897,7 +943,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B3: g_U = g_Z W0   (B(n, k) = W0[k][n])
   POETX_TRY(sg.begin(2));
-  POETX_TRY(dense(t, gZ, Wmat, gU, N, n, m, m, n, n, false, s));
+  POETX_TRY(dense(t, gZ, Wmat, gU, N, n, m, m, n, n, false, s, gz_tiled));
   POETX_TRY(sg.end(2));
 
   if (const int opP = one_pass_size(n, bP)) {
@@ -910,7 +956,8 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
       POETX_TRY(poetx::launch_superblocks(P_act, nbP, bP, opP, SB, s));
       Mp = SB;
     }
-    POETX_TRY(poetx::launch_blockgramapply(gU, Mp, X, gX, partP, N, n, opP, plan.sP.nsplit, &ns, s));
+    POETX_TRY(poetx::launch_blockgramapply(gU, Mp, X, gX, partP, N, n, opP, plan.sP.nsplit, &ns,
+                                           false, s));
     POETX_TRY(sg.end(4));
     POETX_TRY(sg.begin(3));
     POETX_TRY(poetx::launch_split_reduce(partP, ns, nbP, bP, lastP, GP, gt, s, nullptr, plan.subP));

@@ -134,6 +134,7 @@ struct BlockApply {
   const bf16_t* X;
   bf16_t* Y;
   int64_t d, col0, ocol0;  // first input column of the block, first output column
+  bool y_tiled;            // Y in the tiled layout (kernels.h)
   int t_begin, t_end, ntiles;
   int tid, lane, wave, nw;
   bf16x8_t bfr[CB][KS];
@@ -280,7 +281,11 @@ struct BlockApply {
     const int c = td + q * kNT;
     const int row = c / (NC / 8), ch = c % (NC / 8);
     const uint4 v = *reinterpret_cast<const uint4*>(g_out + sw<NC>(row, ch * 8));
-    if (t0 + row < t_end) *reinterpret_cast<uint4*>(Y + (int64_t)(t0 + row) * d + ocol0 + ch * 8) = v;
+    if (t0 + row < t_end) {
+      const int64_t off = y_tiled ? tiled_offset(t0 + row, ocol0 + ch * 8, d)
+                                  : (int64_t)(t0 + row) * d + ocol0 + ch * 8;
+      *reinterpret_cast<uint4*>(Y + off) = v;
+    }
   }
 };
 
@@ -290,8 +295,8 @@ struct BlockApply {
 template <int B, int NC, int TT, bool TRANS, bool GRAM = false>
 __global__ void __launch_bounds__(kNT)
 blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb, bf16_t* Y, int tokens,
-                  int64_t d, int nb, int nsplit, int tok_per_wg, const bf16_t* C = nullptr,
-                  float* __restrict__ part = nullptr) {
+                  int64_t d, int nb, int nsplit, int tok_per_wg, int y_tiled,
+                  const bf16_t* C = nullptr, float* __restrict__ part = nullptr) {
   // (Y and C may be one buffer in the gram variant: every element of C is
   // read by the workgroup that writes Y at the same place, before it does)
   typedef BlockApply<B, NC, TT, TRANS, GRAM> K;
@@ -315,6 +320,7 @@ blockapply_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb, b
   if (k.t_begin >= k.t_end) return;
   k.X = X;
   k.Y = Y;
+  k.y_tiled = y_tiled != 0;
   k.d = d;
   k.col0 = (int64_t)blk * B;
   k.ocol0 = k.col0 + slab * NC;
@@ -437,7 +443,7 @@ int tokens_per_workgroup(int64_t tokens, int64_t d, int B, int NC, int TT) {
 
 template <int B, int NC, int TT, bool TRANS>
 hipError_t launch_b(const bf16_t* X, const bf16_t* M, bf16_t* Y, int64_t tokens, int64_t d,
-                    hipStream_t s) {
+                    bool y_tiled, hipStream_t s) {
   constexpr int NSLAB = B / NC;
   const int nb = (int)(d / B);
   const int per = tokens_per_workgroup(tokens, d, B, NC, TT);
@@ -445,7 +451,7 @@ hipError_t launch_b(const bf16_t* X, const bf16_t* M, bf16_t* Y, int64_t tokens,
   const int units = nb * splits;
   const int grid = NSLAB == 1 ? units : (units + 7) / 8 * (8 * NSLAB);
   hipLaunchKernelGGL((blockapply_kernel<B, NC, TT, TRANS>), dim3(grid), dim3(kNT), 0, s, X, M, Y,
-                     (int)tokens, d, nb, splits, per);
+                     (int)tokens, d, nb, splits, per, (int)y_tiled);
   return hipGetLastError();
 }
 
@@ -492,7 +498,8 @@ bool blockgramapply_supported(DType t, int64_t d, int b) {
 
 template <int B, int NC, int TT>
 hipError_t launch_gram_b(const void* X, const void* M, const void* C, void* Y, float* part,
-                         int64_t tokens, int64_t d, int max_split, int* nsplit, hipStream_t s) {
+                         int64_t tokens, int64_t d, int max_split, int* nsplit, bool y_tiled,
+                         hipStream_t s) {
   constexpr int NSLAB = B / NC;
   const int nb = (int)(d / B);
   // one round of at most 256 workgroups, whole tiles per split, and no more
@@ -509,7 +516,7 @@ hipError_t launch_gram_b(const void* X, const void* M, const void* C, void* Y, f
   const int grid = NSLAB == 1 ? units : (units + 7) / 8 * (8 * NSLAB);
   hipLaunchKernelGGL((blockapply_kernel<B, NC, TT, false, true>), dim3(grid), dim3(kNT), 0, s,
                      static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(M),
-                     static_cast<bf16_t*>(Y), (int)tokens, d, nb, splits, per,
+                     static_cast<bf16_t*>(Y), (int)tokens, d, nb, splits, per, (int)y_tiled,
                      static_cast<const bf16_t*>(C), part);
   *nsplit = splits;
   return hipGetLastError();
@@ -517,10 +524,12 @@ hipError_t launch_gram_b(const void* X, const void* M, const void* C, void* Y, f
 
 hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, void* Y, float* part,
                                  int64_t tokens, int64_t d, int b, int max_split, int* nsplit,
-                                 hipStream_t s) {
+                                 bool y_tiled, hipStream_t s) {
   if ((b != 128 && b != 256) || d % b != 0 || tokens < 1 || max_split < 1) return hipErrorInvalidValue;
-  if (b == 256) return launch_gramapply256(X, M, C, Y, part, tokens, d, max_split, nsplit, s);
-  return launch_gram_b<128, 128, 64>(X, M, C, Y, part, tokens, d, max_split, nsplit, s);
+  if (y_tiled && (tokens % kTileRows != 0 || C == Y)) return hipErrorInvalidValue;
+  if (b == 256)
+    return launch_gramapply256(X, M, C, Y, part, tokens, d, max_split, nsplit, y_tiled, s);
+  return launch_gram_b<128, 128, 64>(X, M, C, Y, part, tokens, d, max_split, nsplit, y_tiled, s);
 }
 
 bool blockapply_supported(DType t, int64_t d, int b) {
@@ -534,16 +543,18 @@ int64_t blockapply_tokens_per_workgroup(int64_t tokens, int64_t d, int b) {
 }
 
 hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,
-                             bool transpose, hipStream_t s) {
+                             bool transpose, bool y_tiled, hipStream_t s) {
+  if (y_tiled && tokens % kTileRows != 0) return hipErrorInvalidValue;
   const bf16_t* x = static_cast<const bf16_t*>(X);
   const bf16_t* m = static_cast<const bf16_t*>(M);
   bf16_t* y = static_cast<bf16_t*>(Y);
-  if (b == 512) return transpose ? launch_b<512, 256, 32, true>(x, m, y, tokens, d, s)
-                                 : launch_b<512, 256, 32, false>(x, m, y, tokens, d, s);
-  if (b == 256) return transpose ? launch_b<256, 256, 64, true>(x, m, y, tokens, d, s)
-                                 : launch_b<256, 256, 64, false>(x, m, y, tokens, d, s);
-  return transpose ? launch_b<128, 128, 64, true>(x, m, y, tokens, d, s)
-                   : launch_b<128, 128, 64, false>(x, m, y, tokens, d, s);
+  const bool yt = y_tiled;
+  if (b == 512) return transpose ? launch_b<512, 256, 32, true>(x, m, y, tokens, d, yt, s)
+                                 : launch_b<512, 256, 32, false>(x, m, y, tokens, d, yt, s);
+  if (b == 256) return transpose ? launch_b<256, 256, 64, true>(x, m, y, tokens, d, yt, s)
+                                 : launch_b<256, 256, 64, false>(x, m, y, tokens, d, yt, s);
+  return transpose ? launch_b<128, 128, 64, true>(x, m, y, tokens, d, yt, s)
+                   : launch_b<128, 128, 64, false>(x, m, y, tokens, d, yt, s);
 }
 
 }  // namespace poetx

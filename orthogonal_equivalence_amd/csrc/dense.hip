@@ -57,6 +57,13 @@
 // them with one 8-byte LDS write; the staged tile leaves as 16-byte stores of
 // whole 512-byte row segments.
 //
+// A may also be in the tiled layout (kernels.h): each 256 x 32 piece of the
+// matrix one contiguous 16 KB block, so a K tile of a 256-row panel is one
+// block and every copy reads 1 KB of consecutive bytes (eight whole 128-byte
+// lines), where the row-major layout gives each copy 16 half lines of 64
+// bytes; on the 8B MLP-up shapes the forward took 7 % less time and the
+// backward 4 % less.
+//
 // M and N must be at least 256 and K a multiple of 32: a tile that would
 // cross the end of M or N is shifted back to end there (it recomputes, and
 // rewrites with identical values, part of its neighbour), so no load or
@@ -114,7 +121,8 @@ template <bool B_KMAJ>
 struct Dense {
   const bf16_t* baseA;  // wave-uniform bases of the current tile's A and B panels
   const bf16_t* baseB;
-  int64_t stepB;        // elements between consecutive K tiles of B
+  int64_t stepA, stepB; // elements between consecutive K tiles of A and of B
+  bool a_tiled;         // A in the tiled layout (then M % 256 == 0 and lda == K)
   uint32_t offA, offB;  // per-lane byte offsets of this wave's first piece at k = 0
   uint32_t strA, strB;  // bytes between this wave's consecutive pieces
   uint32_t lds0;        // LDS byte address of the ring, wave-uniform
@@ -123,13 +131,15 @@ struct Dense {
   floatx4 acc[FM][FN];
   bf16x8_t fa[2][FM], fb[2][FN];
 
-  __device__ __forceinline__ void init(int64_t lda, int64_t ldb) {
+  __device__ __forceinline__ void init(int64_t lda, int64_t ldb, bool tiled) {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     lane = threadIdx.x & 63;
     wm = wave & 1;
     wn = wave >> 1;
     lds0 = __builtin_amdgcn_readfirstlane(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)g_dense_lds)));
+    a_tiled = tiled;
+    stepA = tiled ? (int64_t)BM * BK : BK;
     stepB = B_KMAJ ? BK : (int64_t)BK * ldb;
     const int r = lane & 15;
     rdA = (wm * 128 + r) * BK + (((lane >> 4) ^ kmaj_swz(r)) << 3);
@@ -147,8 +157,10 @@ struct Dense {
     // all of its pieces
     const int row = 16 * wave + (lane >> 2);
     const int c = (lane & 3) ^ kmaj_swz(row);
-    offA = (uint32_t)(row * lda + 8 * c) * 2u;
-    strA = (uint32_t)(16 * NW * lda) * 2u;
+    // (tiled: the rows of a K tile are 32 elements apart within its block)
+    const int64_t rsa = tiled ? BK : lda;
+    offA = (uint32_t)(row * rsa + 8 * c) * 2u;
+    strA = (uint32_t)(16 * NW * rsa) * 2u;
     if (B_KMAJ) {
       offB = (uint32_t)(row * ldb + 8 * c) * 2u;
       strB = (uint32_t)(16 * NW * ldb) * 2u;
@@ -163,6 +175,8 @@ struct Dense {
   // panels of the output tile at (m0, n0) (wholly inside M x N)
   __device__ __forceinline__ void set_tile(const bf16_t* A, const bf16_t* B, int64_t lda,
                                            int64_t ldb, int m0, int n0) {
+    // (tiled: the panel's blocks start at row m0 of the row-major count,
+    // since a panel of 256 rows holds 256 lda elements)
     baseA = uniform_ptr(A + (int64_t)m0 * lda);
     baseB = uniform_ptr(B_KMAJ ? B + (int64_t)n0 * ldb : B + n0);
   }
@@ -172,7 +186,7 @@ struct Dense {
   __device__ __forceinline__ void dma(int t) {
     const uint32_t m = lds0 + (uint32_t)(S * SLOT * 2 + OP * TILE * 2 + (wave + NW * J) * 1024);
     if (OP == 0)
-      dma16_sb(uniform_ptr(baseA + (int64_t)t * BK), offA + J * strA, m);
+      dma16_sb(uniform_ptr(baseA + (int64_t)t * stepA), offA + J * strA, m);
     else
       dma16_sb(uniform_ptr(baseB + (int64_t)t * stepB), offB + J * strB, m);
   }
@@ -421,7 +435,7 @@ __global__ void __launch_bounds__(NT)
 dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C,
              int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc,
              const bf16_t* __restrict__ R, bf16_t* __restrict__ Y, int64_t ldy, int nbatch,
-             int64_t sA, int64_t sB, int64_t sC) {
+             int64_t sA, int64_t sB, int64_t sC, int a_tiled) {
   const int num_mt = (M + BM - 1) / BM, num_nt = (N + BN - 1) / BN;
   const int total = num_mt * num_nt * nbatch;
   const int ntiles = K / BK;
@@ -429,7 +443,7 @@ dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
   if (tile >= total) return;
 
   Dense<B_KMAJ> d;
-  d.init(lda, ldb);
+  d.init(lda, ldb, a_tiled != 0);
   for (;;) {
     int mt, ntb;
     xcd_grouped_tile_at(tile, total, num_mt, num_nt * nbatch, mt, ntb);
@@ -482,7 +496,9 @@ hipError_t dense_grid(int64_t M, int64_t N, int* grid_out) {
 }  // namespace
 
 hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                        int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s) {
+                        int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, bool a_tiled,
+                        hipStream_t s) {
+  if (a_tiled && (M % BM != 0 || lda != K)) return hipErrorInvalidValue;
   int grid = 0;
   hipError_t e = dense_grid(M, N, &grid);
   if (e != hipSuccess) return e;
@@ -492,11 +508,11 @@ hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_
   if (b_kmajor)
     hipLaunchKernelGGL((dense_kernel<true, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, 1, (int64_t)0,
-                       (int64_t)0, (int64_t)0);
+                       (int64_t)0, (int64_t)0, (int)a_tiled);
   else
     hipLaunchKernelGGL((dense_kernel<false, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, 1, (int64_t)0,
-                       (int64_t)0, (int64_t)0);
+                       (int64_t)0, (int64_t)0, (int)a_tiled);
   return hipGetLastError();
 }
 
@@ -515,11 +531,11 @@ hipError_t launch_dense_batched(const void* A, const void* B, void* C, int64_t M
   if (b_kmajor)
     hipLaunchKernelGGL((dense_kernel<true, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, (int)nbatch,
-                       sA, sB, sC);
+                       sA, sB, sC, 0);
   else
     hipLaunchKernelGGL((dense_kernel<false, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, (int)nbatch,
-                       sA, sB, sC);
+                       sA, sB, sC, 0);
   return hipGetLastError();
 }
 
@@ -530,7 +546,8 @@ bool dense_fused_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64
 
 hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M, int64_t N,
                                 int64_t K, int64_t lda, int64_t ldb, int64_t ldc, const void* R,
-                                void* Y, int64_t ldy, hipStream_t s) {
+                                void* Y, int64_t ldy, bool a_tiled, hipStream_t s) {
+  if (a_tiled && (M % BM != 0 || lda != K)) return hipErrorInvalidValue;
   int grid = 0;
   hipError_t e = dense_grid(M, N, &grid);
   if (e != hipSuccess) return e;
@@ -538,7 +555,7 @@ hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M
                      static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B),
                      static_cast<bf16_t*>(C), (int)M, (int)N, (int)K, lda, ldb, ldc,
                      static_cast<const bf16_t*>(R), static_cast<bf16_t*>(Y), ldy, 1, (int64_t)0,
-                     (int64_t)0, (int64_t)0);
+                     (int64_t)0, (int64_t)0, (int)a_tiled);
   return hipGetLastError();
 }
 

@@ -35,7 +35,10 @@
 // buffer and leaves as 16-byte stores spread over the next tile's products.
 // Every element of C is read by the one workgroup that writes Y at the same
 // place (the same block columns and tokens), before it writes it, so C and Y
-// may be one buffer.
+// may be one buffer when Y is row-major. Y may instead be written in the
+// tiled layout (kernels.h) for the dense kernel that reads it next; its
+// 16-byte pieces then land 64-byte row pieces of 16 KB blocks, and the two
+// halves of each 128-byte line come from neighbouring tokens of one store.
 #include "common.h"
 #include "kernels.h"
 
@@ -96,6 +99,7 @@ struct GramApply {
   const bf16_t* C;
   bf16_t* Y;
   int64_t d, col0;
+  bool y_tiled;            // Y in the tiled layout (kernels.h)
   int t_begin, t_end, ntiles;
   int tid, lane, wave, wm, wn;
   bf16x8_t bfr[2][KS];     // M_k columns 64 w + 32 j + l % 32, k = 16 ks + 8 (l / 32) ..
@@ -163,7 +167,11 @@ struct GramApply {
     const int c = td + q * NT;
     const int row = c / (B / 8), ch = c % (B / 8);
     const uint4 v = *reinterpret_cast<const uint4*>(g_gaout + sw(row, ch * 8));
-    if (t0 + row < t_end) *reinterpret_cast<uint4*>(Y + (int64_t)(t0 + row) * d + col0 + ch * 8) = v;
+    if (t0 + row < t_end) {
+      const int64_t off = y_tiled ? tiled_offset(t0 + row, col0 + ch * 8, d)
+                                  : (int64_t)(t0 + row) * d + col0 + ch * 8;
+      *reinterpret_cast<uint4*>(Y + off) = v;
+    }
   }
 
   template <int S, bool FIRST>
@@ -244,7 +252,7 @@ struct GramApply {
 __global__ void __launch_bounds__(NT)
 gramapply256_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb, bf16_t* Y,
                     int tokens, int64_t d, int nb, int nsplit, int tok_per_wg, const bf16_t* C,
-                    float* __restrict__ part) {
+                    float* __restrict__ part, int y_tiled) {
   GramApply k;
   k.tid = threadIdx.x;
   k.lane = k.tid & 63;
@@ -261,6 +269,7 @@ gramapply256_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
   k.X = X;
   k.C = C;
   k.Y = Y;
+  k.y_tiled = y_tiled != 0;
   k.d = d;
   k.col0 = (int64_t)blk * B;
   k.ntiles = (k.t_end - k.t_begin + TT - 1) / TT;
@@ -340,9 +349,10 @@ gramapply256_kernel(const bf16_t* __restrict__ X, const bf16_t* __restrict__ Mb,
 }  // namespace
 
 hipError_t launch_gramapply256(const void* X, const void* M, const void* C, void* Y, float* part,
-                               int64_t tokens, int64_t d, int max_split, int* nsplit,
+                               int64_t tokens, int64_t d, int max_split, int* nsplit, bool y_tiled,
                                hipStream_t s) {
   if (d % B != 0 || tokens < 1 || max_split < 1) return hipErrorInvalidValue;
+  if (y_tiled && (tokens % kTileRows != 0 || C == Y)) return hipErrorInvalidValue;
   const int nb = (int)(d / B);
   // one round of at most 256 workgroups, whole tiles per split, and no more
   // splits than the caller's partial buffer holds
@@ -357,7 +367,7 @@ hipError_t launch_gramapply256(const void* X, const void* M, const void* C, void
   hipLaunchKernelGGL(gramapply256_kernel, dim3(nb * splits), dim3(NT), 0, s,
                      static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(M),
                      static_cast<bf16_t*>(Y), (int)tokens, d, nb, splits, per,
-                     static_cast<const bf16_t*>(C), part);
+                     static_cast<const bf16_t*>(C), part, (int)y_tiled);
   *nsplit = splits;
   return hipGetLastError();
 }

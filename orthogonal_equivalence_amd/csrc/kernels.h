@@ -66,12 +66,29 @@ hipError_t launch_bmm32(const GemmParams& p, hipStream_t stream);
 int gemm_k_tile(DType in);
 int gemm_tile_m(DType in, int M, int N);
 
+// ---- tiled activation layout ----
+// A bf16 matrix of R rows (R % 256 == 0) and row length K (K % 32 == 0) in
+// the tiled layout holds element (r, k) at
+//   ((r / 256) (K / 32) + k / 32) 8192 + (r % 256) 32 + k % 32:
+// each 256 x 32 piece is one contiguous 16 KB block, the blocks of a 256-row
+// panel in k order (so the panel starts at element 256 K (r / 256), as in the
+// row-major layout). The streaming applies can write their output this way
+// and the dense kernel can read its A operand this way.
+constexpr int kTileRows = 256, kTileCols = 32;
+__host__ __device__ inline int64_t tiled_offset(int64_t r, int64_t k, int64_t K) {
+  // (r, k >= 0: shifts and masks)
+  return (((r >> 8) * (K >> 5) + (k >> 5)) << 13) + ((r & 255) << 5) + (k & 31);
+}
+static_assert(kTileRows == 256 && kTileCols == 32, "tiled_offset's shifts");
+
 // ---- dense bf16 GEMM with direct-to-LDS loads (the W0 products) ----
 // C[M][N] = A[M][K] B(n, k), B(n, k) = B[n*ldb + k] (b_kmajor) or
-// B[k*ldb + n]; bf16 in and out, float32 accumulation.
+// B[k*ldb + n]; bf16 in and out, float32 accumulation. With a_tiled, A is in
+// the tiled layout (M % 256 == 0 and lda == K, else hipErrorInvalidValue).
 bool dense_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc);
 hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                        int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s);
+                        int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, bool a_tiled,
+                        hipStream_t s);
 // nbatch products of that shape, product q at A + q sA, B + q sB, C + q sC
 // (elements), in one launch.
 hipError_t launch_dense_batched(const void* A, const void* B, void* C, int64_t M, int64_t N,
@@ -86,7 +103,7 @@ bool dense_fused_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64
                              int64_t ldc, int64_t ldy);
 hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M, int64_t N,
                                 int64_t K, int64_t lda, int64_t ldb, int64_t ldc, const void* R,
-                                void* Y, int64_t ldy, hipStream_t s);
+                                void* Y, int64_t ldy, bool a_tiled, hipStream_t s);
 
 // ---- streaming block-diagonal apply (bf16, b = 128 or 256, b | d) ----
 // Y[:, blk] = X[:, blk] M_blk^T (transpose) or X[:, blk] M_blk, token-major
@@ -102,8 +119,10 @@ int superblock_size(DType t, int64_t d, int b);
 // for the nblocks (a multiple of S/b) b x b bf16 blocks.
 hipError_t launch_superblocks(const void* blocks, int64_t nblocks, int b, int S, void* out,
                               hipStream_t s);
+// With y_tiled, Y is written in the tiled layout (row length d; tokens % 256
+// == 0, else hipErrorInvalidValue).
 hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t tokens, int64_t d, int b,
-                             bool transpose, hipStream_t s);
+                             bool transpose, bool y_tiled, hipStream_t s);
 
 // Gradient apply and gram of the backward in one pass over X (bf16, b = 128
 // or 256):
@@ -113,12 +132,14 @@ hipError_t launch_blockapply(const void* X, const void* M, void* Y, int64_t toke
 bool blockgramapply_supported(DType t, int64_t d, int b);
 // The b = 256 case of launch_blockgramapply: one workgroup per block and
 // token range holding the whole block and its whole gram.
+// With y_tiled, Y is written in the tiled layout (row length d; tokens % 256
+// == 0, else hipErrorInvalidValue); C and Y must then be separate buffers.
 hipError_t launch_gramapply256(const void* X, const void* M, const void* C, void* Y, float* part,
-                               int64_t tokens, int64_t d, int max_split, int* nsplit,
+                               int64_t tokens, int64_t d, int max_split, int* nsplit, bool y_tiled,
                                hipStream_t s);
 hipError_t launch_blockgramapply(const void* X, const void* M, const void* C, void* Y, float* part,
                                  int64_t tokens, int64_t d, int b, int max_split, int* nsplit,
-                                 hipStream_t s);
+                                 bool y_tiled, hipStream_t s);
 
 // ---- streaming token-reduction grams (bf16, b = 128, 256 or 512, b | d) ----
 // part[s][blk] = sum over tokens of split s (kchunk tokens each) of

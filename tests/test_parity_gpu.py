@@ -164,7 +164,17 @@ SMALL_CASES = [
     # (and over g_U); seven token splits, the last one ragged, and a padded
     # last group of units
     ("bf16_b256_splits", 768, 1280, 256, 2100, "bf16", 0.01),
+    # whole 256-token panels: U (and g_Z) pass from the streaming applies to
+    # the dense kernel in the tiled layout; b = 256 (R-apply in the dense
+    # epilogue, one-pass backward), b = 128 (one-pass backward on the b = 128
+    # kernel), b = 64 on super blocks, and b = 512 with the input side
+    # streamed (544 tokens per workgroup) and the output side dense
+    ("bf16_b256_tiled", 768, 1280, 256, 1536, "bf16", 0.01),
+    ("bf16_b128_tiled", 512, 768, 128, 1024, "bf16", 0.02),
+    ("bf16_b64_super_tiled", 384, 640, 64, 512, "bf16", 0.02),
+    ("bf16_b512_stream_tiled", 4096, 512, 512, 8448, "bf16", 0.01),
 ]
+SMALL_BY_NAME = {c[0]: c for c in SMALL_CASES}
 
 
 @pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: c[0])
@@ -310,7 +320,9 @@ def test_full_size_layer_set_8b(layer):
 
 
 # ------------------------------------------- POET-Xmem: Z recomputed
-@pytest.mark.parametrize("case", [SMALL_CASES[i] for i in (0, 2, 3, 5, 6, 9)], ids=lambda c: c[0])
+@pytest.mark.parametrize("case", [SMALL_CASES[i] for i in (0, 2, 3, 5, 6, 9)] +
+                         [SMALL_BY_NAME[k] for k in ("bf16_b256_tiled", "bf16_b128_tiled")],
+                         ids=lambda c: c[0])
 def test_recompute_z_small(case):
     """POETX_RECOMPUTE_Z: the oracle's results, and bit for bit those of the
     path that keeps Z (the same kernels recompute the same Z)."""
