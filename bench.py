@@ -264,8 +264,8 @@ def main():
     bwd_stages = BWD_STAGES + (["recompute_z" if args.recompute_z else None] +
                                (BWD_PERM_STAGES if args.permute else [None, None]))
     if args.int8:
-        fwd_stages += [None] * (FWD_INT8_STAGE - len(fwd_stages)) + ["int8_widen_fwd"]
-        bwd_stages += [None] * (BWD_INT8_STAGE - len(bwd_stages)) + ["int8_widen_bwd"]
+        fwd_stages += [None] * (FWD_INT8_STAGE - len(fwd_stages)) + ["int8_scale_r_fwd"]
+        bwd_stages += [None] * (BWD_INT8_STAGE - len(bwd_stages)) + ["int8_scale_r_bwd"]
     while fwd_stages[-1] is None:
         fwd_stages.pop()
     while bwd_stages[-1] is None:

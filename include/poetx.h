@@ -115,7 +115,8 @@ typedef struct poetx_linear_desc {
    * run after it. With permutations, forward
    * stage 3 gathers x and stage 4 scatters y; backward stage 8 gathers g_y
    * and x and stage 9 scatters g_x. With an INT8 weight, forward stage 5 and
-   * backward stage 10 widen the codes and scale R's block columns. A NULL
+   * backward stage 10 scale R's block columns (the codes are widened chunk
+   * by chunk inside the dense stages: forward 1, backward 2 and 7). A NULL
    * entry is skipped, so a caller can time one stage alone (each record adds
    * a few microseconds between kernels). May be NULL when n_events is 0. */
   void* const* events;
@@ -138,7 +139,10 @@ typedef struct poetx_linear_desc {
    * q [d_out, d_in] and w_scale [d_out] float32 row scales
    * (poetx_quantize_weight), the layer's weight being diag(w_scale) q
    * exactly; d_in must be a multiple of 8. The codes are widened to the act
-   * type without rounding and the scales enter through R: the forward
+   * type without rounding, a chunk of weight rows (forward) or columns
+   * (backward) at a time, each enough for about one round of the dense
+   * product's output tiles, into the workspace; so the workspace holds only a
+   * fraction of the weight in the act type. The scales enter through R: the forward
    * computes Z_q = U q^T and Y = Z_q (blockdiag(R) diag(s))^T and keeps Z_q as
    * z_save; the backward uses g_Z' = g_Y blockdiag(R) diag(s),
    * g_U = g_Z' q and G_R = (g_Y^T Z_q) diag(s). */

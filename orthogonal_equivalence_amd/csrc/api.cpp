@@ -69,6 +69,39 @@ size_t weight_bytes(const poetx_linear_desc* d) {
   return (size_t)d->d_out * d->d_in * (int8_weight(d) ? 1 : act_size(d->act));
 }
 
+// An INT8 layer widens its codes to the activation type in chunks of weight
+// rows (the forward's product, whose output columns they are) or weight
+// columns (the backward's, likewise), so the transient act-type copy holds a
+// fraction of the weight. A forward chunk is enough for about two rounds of
+// 256 x 256 output tiles of the dense kernel (256 workgroups at 256 tokens
+// per tile row), a backward chunk for one: the forward's tiles are short
+// (K = d_in), so each launch's start costs more there (measured at 8192
+// tokens of the 8B MLP-up layer: one round per forward chunk, 7 launches,
+// added ~25 us to its 0.79 ms). int8_chunk: the nominal chunk (a multiple of
+// 256, or the whole width when that is smaller); next_chunk: the chunk at c0,
+// which also takes a remainder narrower than 256 (so no chunk but a whole
+// narrow width is under 256 wide, and the dense kernel takes every chunk
+// that the whole product would have); int8_chunk_max: the widest chunk.
+constexpr int kFwdChunkRounds = 2, kBwdChunkRounds = 1;
+int64_t int8_chunk(int64_t tokens, int64_t width, int rounds) {
+  const int64_t tile_rows = ceil_div(tokens, 256);
+  const int64_t c = std::max<int64_t>(1, 256 * rounds / tile_rows) * 256;
+  return std::min(c, width);
+}
+int64_t next_chunk(int64_t c0, int64_t width, int64_t cw) {
+  const int64_t rem = width - c0;
+  return (rem <= cw || rem - cw < 256) ? rem : cw;
+}
+int64_t int8_chunk_max(int64_t tokens, int64_t width, int rounds) {
+  const int64_t cw = int8_chunk(tokens, width, rounds);
+  int64_t widest = 0;
+  for (int64_t c0 = 0, cn; c0 < width; c0 += cn) {
+    cn = next_chunk(c0, width, cw);
+    widest = std::max(widest, cn);
+  }
+  return widest;
+}
+
 struct FwdPlan {
   size_t u_off, z_off, xp_off, yp_off, inv_off, wq_off, rs_off, sb_off, total;
 };
@@ -97,10 +130,10 @@ FwdPlan plan_fwd(const poetx_linear_desc* d) {
     p.yp_off = off; off += align_up((size_t)d->tokens * d->d_out * es);
     p.inv_off = off; off += align_up((size_t)d->d_out * 4);
   }
-  // INT8 weight: the widened codes and the column-scaled R blocks
+  // INT8 weight: one chunk of widened code rows and the column-scaled R blocks
   p.wq_off = p.rs_off = off;
   if (int8_weight(d)) {
-    p.wq_off = off; off += align_up((size_t)d->d_out * d->d_in * es);
+    p.wq_off = off; off += align_up((size_t)int8_chunk_max(d->tokens, d->d_out, kFwdChunkRounds) * d->d_in * es);
     p.rs_off = off; off += align_up((size_t)ceil_div(d->d_out, d->b_out) * d->b_out * d->b_out * es);
   }
   p.sb_off = off; off += align_up(superblock_bytes(d));
@@ -179,9 +212,16 @@ BwdPlan plan_bwd(const poetx_linear_desc* d) {
   }
   p.wq = p.rs = off;
   if (int8_weight(d)) {
+    // one region for a chunk of widened code columns (B3) or code rows (the
+    // recompute of Z), and, between those two uses, R's column-scaled
+    // blocks (read by B1 only)
     const size_t es = act_size(d->act);
-    p.wq = off; off += align_up((size_t)d->d_out * d->d_in * es);
-    p.rs = off; off += align_up((size_t)nbR * d->b_out * d->b_out * es);
+    const size_t cols = (size_t)d->d_out * int8_chunk_max(d->tokens, d->d_in, kBwdChunkRounds);
+    const size_t rows =
+        recompute_z(d) ? (size_t)int8_chunk_max(d->tokens, d->d_out, kFwdChunkRounds) * d->d_in : 0;
+    const size_t rsb = (size_t)nbR * d->b_out * d->b_out;
+    p.wq = p.rs = off;
+    off += align_up(std::max({cols, rows, rsb}) * es);
   }
   p.sb = off; off += align_up(superblock_bytes(d));
   p.total = off;
@@ -332,6 +372,63 @@ hipError_t dense(DType t, const void* A, const void* B, void* C, int64_t M, int6
   g.M = g.M_last = (int)M; g.N = g.N_last = (int)N; g.K = g.K_last = (int)K;
   g.kchunk = (int)K;
   return poetx::launch_gemm(t, t, true, b_kmajor, g, s);
+}
+
+// The forward's dense product Z = U W^T (W = W0, or the INT8 codes q), and
+// with R (256 x 256 blocks, fused) also Y = Z blockdiag(R)^T in the same
+// launches. With INT8 codes the output columns go in chunks (next_chunk):
+// each chunk's code rows widened into Wq, then its columns of Z (and Y).
+hipError_t dense_forward(DType t, const poetx_linear_desc* d, const void* U, const void* W0,
+                         void* Wq, void* Z, const void* R, void* Y, bool u_tiled, hipStream_t s) {
+  const int64_t N = d->tokens, n = d->d_in, m = d->d_out;
+  const size_t es = act_size(d->act);
+  const bool q8 = int8_weight(d);
+  const int64_t cw = q8 ? int8_chunk(N, m, kFwdChunkRounds) : m;
+  for (int64_t c0 = 0, cn; c0 < m; c0 += cn) {
+    cn = next_chunk(c0, m, cw);
+    const void* Wc = static_cast<const char*>(W0) + c0 * n * es;
+    hipError_t e;
+    if (q8) {
+      e = poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0) + c0 * n, cn, n, n, Wq, s);
+      if (e != hipSuccess) return e;
+      Wc = Wq;
+    }
+    void* Zc = static_cast<char*>(Z) + c0 * es;
+    if (R)  // (c0 and cn are multiples of 256 here: m is, and so is the nominal chunk)
+      e = poetx::launch_dense_fused_r(U, Wc, Zc, N, cn, n, n, n, m,
+                                      static_cast<const char*>(R) + (c0 / 256) * 256 * 256 * es,
+                                      static_cast<char*>(Y) + c0 * es, m, u_tiled, s);
+    else
+      e = dense(t, U, Wc, Zc, N, cn, n, n, n, m, true, s, u_tiled);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The backward's dense product g_U = g_Z W (B(n, k) = W[k][n]); with INT8
+// codes in chunks of output columns, each chunk's code columns widened into
+// Wq (d_out rows of cn).
+hipError_t dense_backward(DType t, const poetx_linear_desc* d, const void* gZ, const void* W0,
+                          void* Wq, void* gU, bool gz_tiled, hipStream_t s) {
+  const int64_t N = d->tokens, n = d->d_in, m = d->d_out;
+  const size_t es = act_size(d->act);
+  const bool q8 = int8_weight(d);
+  const int64_t cw = q8 ? int8_chunk(N, n, kBwdChunkRounds) : n;
+  for (int64_t c0 = 0, cn; c0 < n; c0 += cn) {
+    cn = next_chunk(c0, n, cw);
+    const void* B = static_cast<const char*>(W0) + c0 * es;
+    int64_t ldb = n;
+    hipError_t e;
+    if (q8) {
+      e = poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0) + c0, m, n, cn, Wq, s);
+      if (e != hipSuccess) return e;
+      B = Wq;
+      ldb = cn;
+    }
+    e = dense(t, gZ, B, static_cast<char*>(gU) + c0 * es, N, cn, m, m, ldb, n, false, s, gz_tiled);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Cayley VJP of every block: M = 1/2 (R^T + I) G (R^T + I), packed as
@@ -675,23 +772,18 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   Stages sg{d, s};
   hipError_t e;
 
-  // stage 5 (INT8 weight only): the codes widened exactly to the activation
-  // type, and R's blocks with column j scaled by the row scale s_j, so that
-  // Y = (U q^T) (R diag(s))^T
-  const void* Wmat = W0;
+  // stage 5 (INT8 weight only): R's blocks with column j scaled by the row
+  // scale s_j, so that Y = (U q^T) (R diag(s))^T; the codes themselves are
+  // widened chunk by chunk inside stage 1
   const void* Rb = R_act;
+  void* Wq = w + plan.wq_off;
   if (int8_weight(d)) {
-    void* Wq = w + plan.wq_off;
     void* Rs = w + plan.rs_off;
     if ((e = sg.begin(5)) != hipSuccess) return hip_status(e);
-    if ((e = poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0), m * n, Wq, s)) !=
-        hipSuccess)
-      return hip_status(e);
     if ((e = poetx::launch_scale_block_columns(t, R_act, d->w_scale, nbR, d->b_out, m, Rs, s)) !=
         hipSuccess)
       return hip_status(e);
     if ((e = sg.end(5)) != hipSuccess) return hip_status(e);
-    Wmat = Wq;
     Rb = Rs;
   }
 
@@ -724,13 +816,9 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   const bool fuse_r = t == DType::BF16 && d->b_out == 256 && m % 256 == 0 &&
                       poetx::dense_fused_r_supported(N, m, n, n, n, m, m);
   if ((e = sg.begin(1)) != hipSuccess) return hip_status(e);
-  if (fuse_r) {
-    if ((e = poetx::launch_dense_fused_r(U, Wmat, Z, N, m, n, n, n, m, Rb, Yout, m, u_tiled, s)) !=
-        hipSuccess)
-      return hip_status(e);
-  } else if ((e = dense(t, U, Wmat, Z, N, m, n, n, n, m, true, s, u_tiled)) != hipSuccess) {
+  if ((e = dense_forward(t, d, U, W0, Wq, Z, fuse_r ? Rb : nullptr, Yout, u_tiled, s)) !=
+      hipSuccess)
     return hip_status(e);
-  }
   if ((e = sg.end(1)) != hipSuccess) return hip_status(e);
   if ((e = sg.begin(2)) != hipSuccess) return hip_status(e);
   if (!fuse_r && (e = block_apply(t, Z, Rb, Yout, N, m, d->b_out, true, s, SB)) != hipSuccess)
@@ -849,21 +937,22 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     gX = xp;
   }
 
-  // stage 10 (INT8 weight only): widened codes and R blocks with scaled
-  // columns: g_Z' = g_Y R diag(s), g_U = g_Z' q, G_R = (g_Y^T Z_q) diag(s)
-  // with Z_q = U q^T the forward's saved product
-  const void* Wmat = W0;
-  const void* Rb = R_act;
-  if (int8_weight(d)) {
-    void* Wq = w + plan.wq;
-    void* Rs = w + plan.rs;
-    POETX_TRY(sg.begin(10));
-    POETX_TRY(poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0), m * n, Wq, s));
-    POETX_TRY(poetx::launch_scale_block_columns(t, R_act, d->w_scale, nbR, bR, m, Rs, s));
-    POETX_TRY(sg.end(10));
-    Wmat = Wq;
-    Rb = Rs;
-  }
+  // INT8 weight: R blocks with scaled columns, g_Z' = g_Y R diag(s),
+  // g_U = g_Z' q, G_R = (g_Y^T Z_q) diag(s) with Z_q = U q^T the forward's
+  // saved product. The codes are widened chunk by chunk inside stages 2 and
+  // 7 into the region that holds the scaled R blocks (stage 10, made after
+  // stage 7) while B1 reads them.
+  void* Wq = w + plan.wq;
+  const void* Rb = int8_weight(d) ? static_cast<const void*>(w + plan.rs) : R_act;
+  auto scale_r = [&]() -> hipError_t {
+    if (!int8_weight(d)) return hipSuccess;
+    hipError_t r;
+    if ((r = sg.begin(10)) != hipSuccess) return r;
+    if ((r = poetx::launch_scale_block_columns(t, R_act, d->w_scale, nbR, bR, m, w + plan.rs, s)) !=
+        hipSuccess)
+      return r;
+    return sg.end(10);
+  };
 
   // Block size the one-pass gradient apply + gram runs at for a side (bf16,
   // b = 128 or 256, or b = 32 / 64 as 128 x 128 super blocks), 0 if none.
@@ -918,6 +1007,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     return sg.end(1);
   };
   if (z_saved) {
+    POETX_TRY(scale_r());
     if (fuse_r) {
       POETX_TRY(fused_r(z_saved));
     } else {
@@ -931,8 +1021,9 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     const bool u_tiled = dense_direct(t, N, m, n, n, n, m) && apply_tiles(t, N, n, bP);
     POETX_TRY(sg.begin(7));
     POETX_TRY(block_apply(t, X, P_act, gU, N, n, bP, true, s, SB, u_tiled));
-    POETX_TRY(dense(t, gU, Wmat, gZ, N, m, n, n, n, m, true, s, u_tiled));
+    POETX_TRY(dense_forward(t, d, gU, W0, Wq, gZ, nullptr, nullptr, u_tiled, s));
     POETX_TRY(sg.end(7));
+    POETX_TRY(scale_r());
     if (fuse_r) {
       POETX_TRY(fused_r(gZ));
     } else {
@@ -943,7 +1034,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // B3: g_U = g_Z W0   (B(n, k) = W0[k][n])
   POETX_TRY(sg.begin(2));
-  POETX_TRY(dense(t, gZ, Wmat, gU, N, n, m, m, n, n, false, s, gz_tiled));
+  POETX_TRY(dense_backward(t, d, gZ, W0, Wq, gU, gz_tiled, s));
   POETX_TRY(sg.end(2));
 
   if (const int opP = one_pass_size(n, bP)) {

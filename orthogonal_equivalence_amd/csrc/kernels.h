@@ -191,8 +191,11 @@ hipError_t launch_invert_permutation(const int32_t* perm, int d, int32_t* inv, h
 // float32 correctly rounded divisions; d % 8 == 0.
 hipError_t launch_quantize_rows(DType t, const void* W, int64_t rows, int d, int8_t* q,
                                 float* scale, hipStream_t s);
-// out = q in the activation type (exact); n % 8 == 0.
-hipError_t launch_widen_codes(DType t, const int8_t* q, int64_t n, void* out, hipStream_t s);
+// out[r][j] = q[r ldq + j] in the activation type (exact) for r < rows,
+// j < cols: a rows x cols slice of the codes (row stride ldq) into a
+// contiguous rows x cols matrix; cols and ldq multiples of 8, q 8-byte aligned.
+hipError_t launch_widen_codes(DType t, const int8_t* q, int64_t rows, int64_t ldq, int64_t cols,
+                              void* out, hipStream_t s);
 // out[k][i][j] = M[k][i][j] * scale[k b + j] (0 past d), activation type.
 hipError_t launch_scale_block_columns(DType t, const void* M, const float* scale, int64_t nblocks,
                                       int b, int64_t d, void* out, hipStream_t s);

@@ -91,10 +91,14 @@ quantize_rows_kernel(const T* __restrict__ W, int64_t rows, int d, int8_t* __res
 // out = (activation type) q, exact; n % 8 == 0.
 template <typename T>
 __global__ void __launch_bounds__(kNT)
-widen_codes_kernel(const int8_t* __restrict__ q, int64_t n8, T* __restrict__ out) {
+widen_codes_kernel(const int8_t* __restrict__ q, int64_t ldq, int64_t cols8, int64_t n8,
+                   T* __restrict__ out) {
+  // group i: row i / cols8, codes 8 (i % cols8) .. + 7 of the slice (the
+  // slice's rows are ldq codes apart in q, cols8 groups apart in out)
   for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kNT) {
+    const int64_t r = i / cols8, g = i - r * cols8;
     union { uint2 u; int8_t b[8]; } in;
-    in.u = reinterpret_cast<const uint2*>(q)[i];
+    in.u = *reinterpret_cast<const uint2*>(q + r * ldq + 8 * g);
     if constexpr (sizeof(T) == 2) {
       union { uint4 u; bf16_t h[8]; } o;
 #pragma unroll
@@ -146,15 +150,17 @@ hipError_t launch_quantize_rows(DType t, const void* W, int64_t rows, int d, int
   return hipGetLastError();
 }
 
-hipError_t launch_widen_codes(DType t, const int8_t* q, int64_t n, void* out, hipStream_t s) {
-  const int64_t n8 = n / 8;
+hipError_t launch_widen_codes(DType t, const int8_t* q, int64_t rows, int64_t ldq, int64_t cols,
+                              void* out, hipStream_t s) {
+  if (cols % 8 != 0 || ldq % 8 != 0 || cols > ldq || rows < 0) return hipErrorInvalidValue;
+  const int64_t n8 = rows * (cols / 8);
   if (n8 == 0) return hipSuccess;
   if (t == DType::BF16)
-    hipLaunchKernelGGL(widen_codes_kernel<bf16_t>, dim3(flat_grid(n8)), dim3(kNT), 0, s, q, n8,
-                       static_cast<bf16_t*>(out));
+    hipLaunchKernelGGL(widen_codes_kernel<bf16_t>, dim3(flat_grid(n8)), dim3(kNT), 0, s, q, ldq,
+                       cols / 8, n8, static_cast<bf16_t*>(out));
   else
-    hipLaunchKernelGGL(widen_codes_kernel<float>, dim3(flat_grid(n8)), dim3(kNT), 0, s, q, n8,
-                       static_cast<float*>(out));
+    hipLaunchKernelGGL(widen_codes_kernel<float>, dim3(flat_grid(n8)), dim3(kNT), 0, s, q, ldq,
+                       cols / 8, n8, static_cast<float*>(out));
   return hipGetLastError();
 }
 

@@ -411,12 +411,40 @@ def test_int8_weight_descriptor_checks():
 
 
 def test_int8_workspace_holds_codes_and_scaled_blocks():
+    # few tokens: one chunk covers the whole weight
     N, n, m, b, es = 100, 512, 768, 128, 2
     base = desc(tokens=N, d_in=n, d_out=m, b_in=b, b_out=b)
     q8 = desc(tokens=N, d_in=n, d_out=m, b_in=b, b_out=b, w_scale=ALIGNED * 310)
+    # forward: the widened codes and the scaled R blocks; backward: one
+    # region for both (never live together there)
     extra = m * n * es + (m // b) * b * b * es
     assert P.poetx_fwd_workspace_size(q8) - P.poetx_fwd_workspace_size(base) >= extra
-    assert P.poetx_bwd_workspace_size(q8) - P.poetx_bwd_workspace_size(base) >= extra
+    assert P.poetx_bwd_workspace_size(q8) - P.poetx_bwd_workspace_size(base) >= m * n * es
+
+
+@pytest.mark.parametrize("flags", [0, P.POETX_RECOMPUTE_Z])
+def test_int8_layer_holds_no_more_than_the_act_type_weight(flags):
+    """The 8B MLP up-projection: the int8 codes plus the forward's workspace
+    take less memory than the bf16 weight plus the same call's workspace
+    without INT8, and the backward's no more, since the codes are widened a
+    chunk of 4096 weight rows (forward) or 2048 columns (backward) at a time
+    and the backward's chunks share their region with R's column-scaled
+    blocks."""
+    N, n, m, b = 8192, 4096, 14336, 256
+    base = desc(tokens=N, d_in=n, d_out=m, b_in=b, b_out=b, flags=flags)
+    q8 = desc(tokens=N, d_in=n, d_out=m, b_in=b, b_out=b, w_scale=ALIGNED * 310, flags=flags)
+    w_bf16, w_q8 = m * n * 2, m * n
+    fwd = lambda d: P.poetx_fwd_workspace_size(d)  # noqa: E731
+    bwd = lambda d: P.poetx_bwd_workspace_size(d)  # noqa: E731
+    assert w_q8 + fwd(q8) < w_bf16 + fwd(base)
+    assert w_q8 + bwd(q8) <= w_bf16 + bwd(base)
+    # exactly: forward 4096 code rows widened + the scaled R blocks; backward
+    # one region of m x 2048 widened code columns (the largest of its uses,
+    # also with Z recomputed: 4096 x n rows are fewer)
+    align = 256
+    up = lambda v: (v + align - 1) // align * align  # noqa: E731
+    assert fwd(q8) - fwd(base) == up(4096 * n * 2) + up(m * b * 2)
+    assert bwd(q8) - bwd(base) == up(m * 2048 * 2)
 
 
 def test_quantize_weight_errors():

@@ -608,6 +608,14 @@ INT8_CASES = [
     ("q8_bf16_b256_perm_mem", 512, 1024, 256, 300, "bf16", 0.01, "cayley", True, True),
     ("q8_bf16_b512_mem", 1024, 1536, 512, 200, "bf16", 0.01, "cayley", False, True),
     ("q8_bf16_b64_super", 384, 640, 64, 300, "bf16", 0.02, "cayley", False, False),
+    # enough tokens that the codes are widened in chunks (at 16384 tokens
+    # 2048 weight rows forward, 1024 columns backward): forward 2048 + 2048 +
+    # 512 rows with the fused R-apply, backward 1024 + 1024 + 256 columns;
+    # then b = 128 (separate R-apply) with Z recomputed, where the forward's
+    # last chunk takes the 128-row remainder (2048 + 2176) and the backward's
+    # too (1024 + 1152)
+    ("q8_bf16_b256_chunks", 2304, 4608, 256, 16384, "bf16", 0.01, "cayley", False, False),
+    ("q8_bf16_b128_chunks_mem", 2176, 4224, 128, 16384, "bf16", 0.02, "cayley", False, True),
 ]
 
 
