@@ -9,10 +9,12 @@ is the 8B-class MLP up-projection: W0 14336 x 4096 (out x in), b = 256,
 8192 tokens, bf16 storage with float32 accumulation.
 
 Order of work: the float64 oracle on the host's cores (a bounded token
-sample, timed before any GPU timing), W warm-up steps, K timed steps (mean
-and median per step), K "cold" steps each after a 512 MB scratch write that
-evicts the Infinity Cache, K instrumented steps for the per-stage breakdown,
-then a sampled parity check of every layer against the oracle.
+sample, timed before any GPU timing), W warm-up steps, K instrumented steps
+for the per-stage breakdown (untimed for `value`; they also bring the GPU's
+clock back up after the oracle's idle seconds), K timed steps (mean and
+median per step), K "cold" steps each after a 512 MB scratch write that
+evicts the Infinity Cache, then a sampled parity check of every layer
+against the oracle.
 
 Prints ONE JSON line: tokens/s of the whole step, the roofline of the
 dominant kernel (the dense W0 GEMM of the forward, timed live with HIP events
@@ -314,6 +316,24 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # ---- stage breakdown: K steps with an event pair around every stage and
+    # every step (slower than the timed steps by the records themselves),
+    # after the W warm-up steps and before the timed ones: after the oracle's
+    # seconds on the host the GPU has idled, and its clock took longer to come
+    # back up than W warm-up steps (~10 ms at W = 5; the first timed steps
+    # then ran 2-4 % slower than the rest), so the timed steps begin from a
+    # GPU that has run the step for a while, as it would in a training loop.
+    step_events = [make_events() for _ in range(args.steps)]
+    handles = [as_handles(e) for e in step_events]
+    per_step = [(P.Event(), P.Event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        per_step[k][0].record(stream)
+        step(handles[k])
+        per_step[k][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_ms(b) for a, b in per_step]
+
     # dominant kernel: the forward dense W0 GEMM (Z = U W0^T) of the largest layer
     big = max(range(len(layers)), key=lambda i: layers[i][0].d_in * layers[i][0].d_out)
     dense_stage = FWD_STAGES.index("dense_fwd")
@@ -363,18 +383,6 @@ def main():
         cold_ms = [a.elapsed_ms(b) for a, b in cold_ev]
         del scratch
 
-    # ---- stage breakdown: K more steps with an event pair around every stage
-    # and every step (slower than the timed steps by the records themselves)
-    step_events = [make_events() for _ in range(args.steps)]
-    handles = [as_handles(e) for e in step_events]
-    per_step = [(P.Event(), P.Event()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        per_step[k][0].record(stream)
-        step(handles[k])
-        per_step[k][1].record(stream)
-    torch.cuda.synchronize()
-    step_ms = [a.elapsed_ms(b) for a, b in per_step]
 
     stage_ms = {}
     if layer_set is not None:
@@ -428,6 +436,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "ms_per_step_median": statistics.median(timed_ms),
         "ms_per_step_min": min(timed_ms), "ms_per_step_max": max(timed_ms),
+        "ms_each_step": [round(v, 4) for v in timed_ms],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": specs[0].dtype, "data": "synthetic (seeded N(0,1) activations, N(0,1/d_in) W0, "
                                           "N(0, sigma^2) generators)",
@@ -454,7 +463,7 @@ def main():
             "ms_per_step_mean": statistics.mean(cold_ms),
             "ms_per_step_min": min(cold_ms), "ms_per_step_max": max(cold_ms),
             "tokens_per_s_median": tokens / (statistics.median(cold_ms) / 1e3)},
-        # from the instrumented steps that follow the timed ones
+        # from the instrumented steps that precede the timed ones
         "instrumented_step_ms": {"median": statistics.median(step_ms), "min": min(step_ms),
                                  "max": max(step_ms)},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
