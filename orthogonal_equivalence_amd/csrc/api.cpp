@@ -133,7 +133,8 @@ FwdPlan plan_fwd(const poetx_linear_desc* d) {
   // INT8 weight: one chunk of widened code rows and the column-scaled R blocks
   p.wq_off = p.rs_off = off;
   if (int8_weight(d)) {
-    p.wq_off = off; off += align_up((size_t)int8_chunk_max(d->tokens, d->d_out, kFwdChunkRounds) * d->d_in * es);
+    p.wq_off = off;
+    off += align_up((size_t)int8_chunk_max(d->tokens, d->d_out, kFwdChunkRounds) * d->d_in * es);
     p.rs_off = off; off += align_up((size_t)ceil_div(d->d_out, d->b_out) * d->b_out * d->b_out * es);
   }
   p.sb_off = off; off += align_up(superblock_bytes(d));
