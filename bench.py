@@ -29,6 +29,7 @@ comes from as many further steps with an event pair around every stage.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import statistics
@@ -312,6 +313,13 @@ def main():
                            min(args.cpu_sample, specs[0].tokens), map=args.map,
                            permute=args.permute, int8=args.int8)
 
+    # No garbage-collection pass from the warm-up to the end of the GPU work:
+    # one in the middle of the timed steps once held the host for 36-66 ms
+    # while the GPU waited for the next launch, and a collection just before
+    # them leaves the GPU idle long enough for its clock to drop (the next
+    # few steps then run slower), so the one collection comes first.
+    gc.collect()
+    gc.disable()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -382,6 +390,7 @@ def main():
         torch.cuda.synchronize()
         cold_ms = [a.elapsed_ms(b) for a, b in cold_ev]
         del scratch
+    gc.enable()
 
 
     stage_ms = {}
