@@ -665,3 +665,58 @@ def test_int8_full_size_mlp_up_8b():
     _full_check(_int8_reference_inputs(L), lay, out, check_z=False)
     del lay, out, y, z, g_x
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------- the step captured in a HIP graph
+@pytest.mark.parametrize("case,kw", [
+    (("bf16_b256_tiled", 768, 1280, 256, 1536), {}),
+    (("bf16_b128_int8", 512, 768, 128, 1000), {"int8": True}),
+    (("bf16_b256_mem", 512, 1024, 256, 300), {"recompute_z": True}),
+], ids=lambda c: c[0] if isinstance(c, tuple) else "-".join(c) or "plain")
+def test_step_in_hip_graph(case, kw):
+    """Build, forward and backward captured in one HIP graph (the library
+    allocates nothing and records no memset inside a call) and replayed three
+    times, with eager steps and synchronisations between the replays: every
+    replay's outputs bit for bit those of the eager step."""
+    from orthogonal_equivalence_amd.layer import PoetxLinear
+    name, n, m, b, N = case
+    spec = LayerSpec(name, n, m, b, N, "bf16", 0.01, seed=len(name) + 600)
+    U.log(f"[hip graph] {name}: d_in={n} d_out={m} b={b} tokens={N} {kw}")
+    L = make_layer(spec)
+    lay = PoetxLinear(U.dev(L.W0, "bf16"), b, b, "bf16", **kw)
+    lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
+    x, g_y = U.dev(L.x, "bf16"), U.dev(L.g_y, "bf16")
+    y = torch.empty(N, m, dtype=torch.bfloat16, device="cuda")
+    z = None if kw.get("recompute_z") else torch.empty_like(y)
+    g_x = torch.empty(N, n, dtype=torch.bfloat16, device="cuda")
+    gR, gP = torch.empty_like(lay.theta_R), torch.empty_like(lay.theta_P)
+    side = torch.cuda.Stream()
+
+    def step(stream):
+        lay.build(stream)
+        lay.forward(x, y, z, stream=stream)
+        lay.backward(g_y, x, z, g_x, gR, gP, stream=stream)
+
+    def outputs():
+        return [t.clone() for t in (y, g_x, gR, gP) + ((z,) if z is not None else ())]
+
+    with torch.cuda.stream(side):
+        step(side)  # workspaces allocated outside the capture
+    torch.cuda.synchronize()
+    ref = outputs()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (y, g_x, gR, gP):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, c in zip(ref, outputs()):
+            assert torch.equal(a, c), rep
+        step(torch.cuda.current_stream())  # eager work between the replays
+        torch.cuda.synchronize()
+        for a, c in zip(ref, outputs()):
+            assert torch.equal(a, c), rep
