@@ -358,14 +358,14 @@ bool dense_direct(DType t, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t
 
 // A dense W0 product C[M][N] = A[M][K] B(n, k) (B(n, k) = B[n][k] when
 // b_kmajor, else B[k][n]): the persistent direct-to-LDS bf16 kernel when the
-// shape allows it, else the general GEMM. a_tiled (only where dense_direct
-// holds): A in the tiled layout.
+// shape allows it, else the general GEMM. a_tiled, b_tiled (only where
+// dense_direct holds): A, a K-major B in the tiled layout.
 hipError_t dense(DType t, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, hipStream_t s,
-                 bool a_tiled = false) {
+                 bool a_tiled = false, bool b_tiled = false) {
   if (dense_direct(t, M, N, K, lda, ldb, ldc))
-    return poetx::launch_dense(A, B, C, M, N, K, lda, ldb, ldc, b_kmajor, a_tiled, s);
-  if (a_tiled) return hipErrorInvalidValue;
+    return poetx::launch_dense(A, B, C, M, N, K, lda, ldb, ldc, b_kmajor, a_tiled, b_tiled, s);
+  if (a_tiled || b_tiled) return hipErrorInvalidValue;
   GemmParams g;
   g.A = A; g.lda = lda;
   g.B = B; g.ldb = ldb;
@@ -378,7 +378,9 @@ hipError_t dense(DType t, const void* A, const void* B, void* C, int64_t M, int6
 // The forward's dense product Z = U W^T (W = W0, or the INT8 codes q), and
 // with R (256 x 256 blocks, fused) also Y = Z blockdiag(R)^T in the same
 // launches. With INT8 codes the output columns go in chunks (next_chunk):
-// each chunk's code rows widened into Wq, then its columns of Z (and Y).
+// each chunk's code rows widened into Wq, then its columns of Z (and Y);
+// Wq in the tiled layout when the dense kernel reads it and the chunk's
+// shape allows.
 hipError_t dense_forward(DType t, const poetx_linear_desc* d, const void* U, const void* W0,
                          void* Wq, void* Z, const void* R, void* Y, bool u_tiled, hipStream_t s) {
   const int64_t N = d->tokens, n = d->d_in, m = d->d_out;
@@ -388,9 +390,12 @@ hipError_t dense_forward(DType t, const poetx_linear_desc* d, const void* U, con
   for (int64_t c0 = 0, cn; c0 < m; c0 += cn) {
     cn = next_chunk(c0, m, cw);
     const void* Wc = static_cast<const char*>(W0) + c0 * n * es;
+    const bool w_tiled = q8 && dense_direct(t, N, cn, n, n, n, m) &&
+                         cn % poetx::kTileRows == 0 && n % poetx::kTileCols == 0;
     hipError_t e;
     if (q8) {
-      e = poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0) + c0 * n, cn, n, n, Wq, s);
+      e = poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0) + c0 * n, cn, n, n, Wq,
+                                    w_tiled, s);
       if (e != hipSuccess) return e;
       Wc = Wq;
     }
@@ -398,9 +403,9 @@ hipError_t dense_forward(DType t, const poetx_linear_desc* d, const void* U, con
     if (R)  // (c0 and cn are multiples of 256 here: m is, and so is the nominal chunk)
       e = poetx::launch_dense_fused_r(U, Wc, Zc, N, cn, n, n, n, m,
                                       static_cast<const char*>(R) + (c0 / 256) * 256 * 256 * es,
-                                      static_cast<char*>(Y) + c0 * es, m, u_tiled, s);
+                                      static_cast<char*>(Y) + c0 * es, m, u_tiled, w_tiled, s);
     else
-      e = dense(t, U, Wc, Zc, N, cn, n, n, n, m, true, s, u_tiled);
+      e = dense(t, U, Wc, Zc, N, cn, n, n, n, m, true, s, u_tiled, w_tiled);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -421,7 +426,8 @@ hipError_t dense_backward(DType t, const poetx_linear_desc* d, const void* gZ, c
     int64_t ldb = n;
     hipError_t e;
     if (q8) {
-      e = poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0) + c0, m, n, cn, Wq, s);
+      e = poetx::launch_widen_codes(t, static_cast<const int8_t*>(W0) + c0, m, n, cn, Wq, false,
+                                    s);
       if (e != hipSuccess) return e;
       B = Wq;
       ldb = cn;

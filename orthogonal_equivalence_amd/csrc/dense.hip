@@ -62,7 +62,8 @@
 // block and every copy reads 1 KB of consecutive bytes (eight whole 128-byte
 // lines), where the row-major layout gives each copy 16 half lines of 64
 // bytes; on the 8B MLP-up shapes the forward took 7 % less time and the
-// backward 4 % less.
+// backward 4 % less. A K-major B may be tiled the same way (the forward's
+// weight, where a caller widens INT8 codes into a buffer of its own).
 //
 // M and N must be at least 256 and K a multiple of 32: a tile that would
 // cross the end of M or N is shifted back to end there (it recomputes, and
@@ -123,6 +124,7 @@ struct Dense {
   const bf16_t* baseB;
   int64_t stepA, stepB; // elements between consecutive K tiles of A and of B
   bool a_tiled;         // A in the tiled layout (then M % 256 == 0 and lda == K)
+                        // (a tiled K-major B likewise: N % 256 == 0, ldb == K)
   uint32_t offA, offB;  // per-lane byte offsets of this wave's first piece at k = 0
   uint32_t strA, strB;  // bytes between this wave's consecutive pieces
   uint32_t lds0;        // LDS byte address of the ring, wave-uniform
@@ -131,7 +133,7 @@ struct Dense {
   floatx4 acc[FM][FN];
   bf16x8_t fa[2][FM], fb[2][FN];
 
-  __device__ __forceinline__ void init(int64_t lda, int64_t ldb, bool tiled) {
+  __device__ __forceinline__ void init(int64_t lda, int64_t ldb, bool tiled, bool b_tiled) {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     lane = threadIdx.x & 63;
     wm = wave & 1;
@@ -140,7 +142,7 @@ struct Dense {
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)g_dense_lds)));
     a_tiled = tiled;
     stepA = tiled ? (int64_t)BM * BK : BK;
-    stepB = B_KMAJ ? BK : (int64_t)BK * ldb;
+    stepB = B_KMAJ ? (b_tiled ? (int64_t)BN * BK : BK) : (int64_t)BK * ldb;
     const int r = lane & 15;
     rdA = (wm * 128 + r) * BK + (((lane >> 4) ^ kmaj_swz(r)) << 3);
     if (B_KMAJ) {
@@ -162,8 +164,9 @@ struct Dense {
     offA = (uint32_t)(row * rsa + 8 * c) * 2u;
     strA = (uint32_t)(16 * NW * rsa) * 2u;
     if (B_KMAJ) {
-      offB = (uint32_t)(row * ldb + 8 * c) * 2u;
-      strB = (uint32_t)(16 * NW * ldb) * 2u;
+      const int64_t rsb = b_tiled ? BK : ldb;
+      offB = (uint32_t)(row * rsb + 8 * c) * 2u;
+      strB = (uint32_t)(16 * NW * rsb) * 2u;
     } else {
       const int k = 2 * wave + (lane >> 5);
       const int cn = (lane & 31) ^ nmaj_swz(k);
@@ -435,7 +438,7 @@ __global__ void __launch_bounds__(NT)
 dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C,
              int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc,
              const bf16_t* __restrict__ R, bf16_t* __restrict__ Y, int64_t ldy, int nbatch,
-             int64_t sA, int64_t sB, int64_t sC, int a_tiled) {
+             int64_t sA, int64_t sB, int64_t sC, int a_tiled, int b_tiled) {
   const int num_mt = (M + BM - 1) / BM, num_nt = (N + BN - 1) / BN;
   const int total = num_mt * num_nt * nbatch;
   const int ntiles = K / BK;
@@ -443,7 +446,7 @@ dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
   if (tile >= total) return;
 
   Dense<B_KMAJ> d;
-  d.init(lda, ldb, a_tiled != 0);
+  d.init(lda, ldb, a_tiled != 0, B_KMAJ && b_tiled != 0);
   for (;;) {
     int mt, ntb;
     xcd_grouped_tile_at(tile, total, num_mt, num_nt * nbatch, mt, ntb);
@@ -497,8 +500,9 @@ hipError_t dense_grid(int64_t M, int64_t N, int* grid_out) {
 
 hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                         int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, bool a_tiled,
-                        hipStream_t s) {
+                        bool b_tiled, hipStream_t s) {
   if (a_tiled && (M % BM != 0 || lda != K)) return hipErrorInvalidValue;
+  if (b_tiled && (!b_kmajor || N % BN != 0 || ldb != K)) return hipErrorInvalidValue;
   int grid = 0;
   hipError_t e = dense_grid(M, N, &grid);
   if (e != hipSuccess) return e;
@@ -508,11 +512,11 @@ hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_
   if (b_kmajor)
     hipLaunchKernelGGL((dense_kernel<true, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, 1, (int64_t)0,
-                       (int64_t)0, (int64_t)0, (int)a_tiled);
+                       (int64_t)0, (int64_t)0, (int)a_tiled, (int)b_tiled);
   else
     hipLaunchKernelGGL((dense_kernel<false, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, 1, (int64_t)0,
-                       (int64_t)0, (int64_t)0, (int)a_tiled);
+                       (int64_t)0, (int64_t)0, (int)a_tiled, (int)b_tiled);
   return hipGetLastError();
 }
 
@@ -531,11 +535,11 @@ hipError_t launch_dense_batched(const void* A, const void* B, void* C, int64_t M
   if (b_kmajor)
     hipLaunchKernelGGL((dense_kernel<true, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, (int)nbatch,
-                       sA, sB, sC, 0);
+                       sA, sB, sC, 0, 0);
   else
     hipLaunchKernelGGL((dense_kernel<false, false>), dim3(grid), dim3(NT), 0, s, a, b, c, (int)M,
                        (int)N, (int)K, lda, ldb, ldc, nullptr, nullptr, (int64_t)0, (int)nbatch,
-                       sA, sB, sC, 0);
+                       sA, sB, sC, 0, 0);
   return hipGetLastError();
 }
 
@@ -546,8 +550,9 @@ bool dense_fused_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64
 
 hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M, int64_t N,
                                 int64_t K, int64_t lda, int64_t ldb, int64_t ldc, const void* R,
-                                void* Y, int64_t ldy, bool a_tiled, hipStream_t s) {
+                                void* Y, int64_t ldy, bool a_tiled, bool b_tiled, hipStream_t s) {
   if (a_tiled && (M % BM != 0 || lda != K)) return hipErrorInvalidValue;
+  if (b_tiled && (N % BN != 0 || ldb != K)) return hipErrorInvalidValue;
   int grid = 0;
   hipError_t e = dense_grid(M, N, &grid);
   if (e != hipSuccess) return e;
@@ -555,7 +560,7 @@ hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M
                      static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B),
                      static_cast<bf16_t*>(C), (int)M, (int)N, (int)K, lda, ldb, ldc,
                      static_cast<const bf16_t*>(R), static_cast<bf16_t*>(Y), ldy, 1, (int64_t)0,
-                     (int64_t)0, (int64_t)0, (int)a_tiled);
+                     (int64_t)0, (int64_t)0, (int)a_tiled, (int)b_tiled);
   return hipGetLastError();
 }
 

@@ -84,11 +84,12 @@ static_assert(kTileRows == 256 && kTileCols == 32, "tiled_offset's shifts");
 // ---- dense bf16 GEMM with direct-to-LDS loads (the W0 products) ----
 // C[M][N] = A[M][K] B(n, k), B(n, k) = B[n*ldb + k] (b_kmajor) or
 // B[k*ldb + n]; bf16 in and out, float32 accumulation. With a_tiled, A is in
-// the tiled layout (M % 256 == 0 and lda == K, else hipErrorInvalidValue).
+// the tiled layout (M % 256 == 0 and lda == K, else hipErrorInvalidValue);
+// with b_tiled, a K-major B is (an N x K matrix: N % 256 == 0, ldb == K).
 bool dense_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc);
 hipError_t launch_dense(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                         int64_t lda, int64_t ldb, int64_t ldc, bool b_kmajor, bool a_tiled,
-                        hipStream_t s);
+                        bool b_tiled, hipStream_t s);
 // nbatch products of that shape, product q at A + q sA, B + q sB, C + q sC
 // (elements), in one launch.
 hipError_t launch_dense_batched(const void* A, const void* B, void* C, int64_t M, int64_t N,
@@ -103,7 +104,7 @@ bool dense_fused_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64
                              int64_t ldc, int64_t ldy);
 hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M, int64_t N,
                                 int64_t K, int64_t lda, int64_t ldb, int64_t ldc, const void* R,
-                                void* Y, int64_t ldy, bool a_tiled, hipStream_t s);
+                                void* Y, int64_t ldy, bool a_tiled, bool b_tiled, hipStream_t s);
 
 // ---- streaming block-diagonal apply (bf16, b = 128 or 256, b | d) ----
 // Y[:, blk] = X[:, blk] M_blk^T (transpose) or X[:, blk] M_blk, token-major
@@ -193,9 +194,11 @@ hipError_t launch_quantize_rows(DType t, const void* W, int64_t rows, int d, int
                                 float* scale, hipStream_t s);
 // out[r][j] = q[r ldq + j] in the activation type (exact) for r < rows,
 // j < cols: a rows x cols slice of the codes (row stride ldq) into a
-// contiguous rows x cols matrix; cols and ldq multiples of 8, q 8-byte aligned.
+// contiguous rows x cols matrix; cols and ldq multiples of 8, q 8-byte
+// aligned. With out_tiled, out is in the tiled layout (rows % 256 == 0,
+// cols % 32 == 0).
 hipError_t launch_widen_codes(DType t, const int8_t* q, int64_t rows, int64_t ldq, int64_t cols,
-                              void* out, hipStream_t s);
+                              void* out, bool out_tiled, hipStream_t s);
 // out[k][i][j] = M[k][i][j] * scale[k b + j] (0 past d), activation type.
 hipError_t launch_scale_block_columns(DType t, const void* M, const float* scale, int64_t nblocks,
                                       int b, int64_t d, void* out, hipStream_t s);

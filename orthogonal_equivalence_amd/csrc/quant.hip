@@ -114,6 +114,26 @@ widen_codes_kernel(const int8_t* __restrict__ q, int64_t ldq, int64_t cols8, int
   }
 }
 
+// The same into the tiled layout (bf16; rows % 256 == 0, cols % 32 == 0),
+// walked in the output's order so that the stores are contiguous: group i
+// is the 8 codes at (r, k) of 256 x 32 block i / 1024, whose rows are 4
+// groups each.
+__global__ void __launch_bounds__(kNT)
+widen_codes_tiled_kernel(const int8_t* __restrict__ q, int64_t ldq, int64_t kblocks, int64_t n8,
+                         bf16_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kNT) {
+    const int64_t blk = i >> 10, rb = blk / kblocks;
+    const int64_t r = rb * 256 + ((i >> 2) & 255);
+    const int64_t k = (blk - rb * kblocks) * 32 + (i & 3) * 8;
+    union { uint2 u; int8_t b[8]; } in;
+    in.u = *reinterpret_cast<const uint2*>(q + r * ldq + k);
+    union { uint4 u; bf16_t h[8]; } o;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o.h[t] = f32_to_bf16((float)in.b[t]);
+    reinterpret_cast<uint4*>(out)[i] = o.u;
+  }
+}
+
 // out[k][i][j] = M[k][i][j] * s[k b + j] (0 for columns past d), in the
 // activation type. Flat over nblocks * b * b.
 template <typename T>
@@ -151,11 +171,16 @@ hipError_t launch_quantize_rows(DType t, const void* W, int64_t rows, int d, int
 }
 
 hipError_t launch_widen_codes(DType t, const int8_t* q, int64_t rows, int64_t ldq, int64_t cols,
-                              void* out, hipStream_t s) {
+                              void* out, bool out_tiled, hipStream_t s) {
   if (cols % 8 != 0 || ldq % 8 != 0 || cols > ldq || rows < 0) return hipErrorInvalidValue;
+  if (out_tiled && (t != DType::BF16 || rows % 256 != 0 || cols % 32 != 0))
+    return hipErrorInvalidValue;
   const int64_t n8 = rows * (cols / 8);
   if (n8 == 0) return hipSuccess;
-  if (t == DType::BF16)
+  if (out_tiled)
+    hipLaunchKernelGGL(widen_codes_tiled_kernel, dim3(flat_grid(n8)), dim3(kNT), 0, s, q, ldq,
+                       cols / 32, n8, static_cast<bf16_t*>(out));
+  else if (t == DType::BF16)
     hipLaunchKernelGGL(widen_codes_kernel<bf16_t>, dim3(flat_grid(n8)), dim3(kNT), 0, s, q, ldq,
                        cols / 8, n8, static_cast<bf16_t*>(out));
   else
