@@ -57,14 +57,15 @@ BWD_STAGES = ["grad_r", "gram_r", "dense_bwd", "gram_p", "grad_x", "vjp_r", "vjp
 BWD_PERM_STAGES = ["gather_gy_x", "scatter_gx"]
 
 
-def layer_work(s):
-    """Algorithmic flops and bytes of one layer's step (build + fwd + bwd)."""
+def layer_work(s, saved_y=False):
+    """Algorithmic flops and bytes of one layer's step (build + fwd + bwd).
+    The forward writes y and Z, or y alone when y is kept in Z's place."""
     N, n, m, b = s.tokens, s.d_in, s.d_out, s.b
     es = 2 if s.dtype == "bf16" else 4
     flops = 4 * N * m * n + 6 * N * b * (m + n) + 6 * b * b * (m + n)
     blocks = b * (m + n)          # elements of all R and P blocks
     theta = (m + n) * (b - 1) // 2
-    fwd = es * (N * n + m * n + blocks + 2 * N * m) + 4 * theta
+    fwd = es * (N * n + m * n + blocks + (1 if saved_y else 2) * N * m) + 4 * theta
     bwd = es * (2 * N * m + N * n + m * n + blocks + N * n) + 4 * blocks + 4 * theta
     build = 4 * theta + 4 * blocks + es * blocks
     return flops, fwd + bwd + build
@@ -206,6 +207,9 @@ def main():
                     help="skip the cold-cache steps (profiling runs)")
     ap.add_argument("--recompute-z", action="store_true",
                     help="POET-Xmem variant: the forward keeps no Z, the backward recomputes it")
+    ap.add_argument("--saved-y", action="store_true",
+                    help="the backward takes y in place of Z (POETX_SAVED_Y): the forward "
+                         "keeps no Z")
     ap.add_argument("--permute", action="store_true",
                     help="random block-mixing permutations of R and P (W0 folded once)")
     ap.add_argument("--int8", action="store_true",
@@ -244,12 +248,12 @@ def main():
         po, pi = make_permutations(s) if args.permute else (None, None)
         lay = PoetxLinear(torch.from_numpy(L.W0).to(tdt[s.dtype]), s.b, s.b, s.dtype, device=dev,
                           recompute_z=args.recompute_z, map=args.map, perm_out=po, perm_in=pi,
-                          int8=args.int8)
+                          int8=args.int8, saved_y=args.saved_y)
         lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
         x = torch.from_numpy(L.x).to(tdt[s.dtype]).to(dev)
         g_y = torch.from_numpy(L.g_y).to(tdt[s.dtype]).to(dev)
         out = dict(y=torch.empty(s.tokens, s.d_out, dtype=tdt[s.dtype], device=dev),
-                   z=None if args.recompute_z else
+                   z=None if args.recompute_z or args.saved_y else
                    torch.empty(s.tokens, s.d_out, dtype=tdt[s.dtype], device=dev),
                    g_x=torch.empty(s.tokens, s.d_in, dtype=tdt[s.dtype], device=dev),
                    gR=torch.empty_like(lay.theta_R), gP=torch.empty_like(lay.theta_P))
@@ -291,7 +295,8 @@ def main():
                 if e is not None and e["build"] is not None:
                     e["build"][1].record(stream)
             lay.forward(x, o["y"], o["z"], stream=stream, events=None if e is None else e["fwd"])
-            lay.backward(g_y, x, o["z"], o["g_x"], o["gR"], o["gP"], stream=stream,
+            lay.backward(g_y, x, o["y"] if args.saved_y else o["z"], o["g_x"], o["gR"], o["gP"],
+                         stream=stream,
                          events=None if e is None else e["bwd"])
 
     def make_events():
@@ -425,20 +430,23 @@ def main():
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                 "frac": achieved / peak,
                 "traffic": (measured_traffic(args.config) if args.map == "cayley" and not
-                            (args.permute or args.int8 or args.recompute_z) else None),
+                            (args.permute or args.int8 or args.recompute_z or args.saved_y)
+                            else None),
                 "traffic_kind": "L2-miss bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a "
                                 "plain copy): requests leaving the L2, answered by the Infinity "
                                 "Cache or HBM; null when the kernel changed since the passes "
                                 "or they were taken on another workload",
-                "kernel": ("dense_fwd: Z = U W0^T with Y = Z blockdiag(R)^T in its epilogue "
+                "kernel": ("dense_fwd: Y = (U W0^T) blockdiag(R)^T, Z not written "
+                           "(dense_kernel<true, true, false>" if fused_r and args.saved_y else
+                           "dense_fwd: Z = U W0^T with Y = Z blockdiag(R)^T in its epilogue "
                            "(dense_kernel<true, true>" if fused_r else
                            "dense_fwd: Z = U W0^T (dense_kernel<true, false>") +
                           ": bf16, K-major W0, persistent, direct-to-LDS, 4 waves of 128x128, "
                           "16x16x32 MFMA)",
                 "flops_per_launch": dense_flops, "avg_launch_ms": dense_ms}
 
-    F = sum(layer_work(s)[0] for s, *_ in layers)
-    B = sum(layer_work(s)[1] for s, *_ in layers)
+    F = sum(layer_work(s, args.saved_y)[0] for s, *_ in layers)
+    B = sum(layer_work(s, args.saved_y)[1] for s, *_ in layers)
     t_roof = max(F / PEAK_BF16, B / PEAK_HBM)
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
@@ -453,6 +461,8 @@ def main():
                    "layers": [f"{s.name} {s.d_out}x{s.d_in} b={s.b}" for s in specs],
                    "tokens": tokens, "block": specs[0].b,
                    "variant": ("POET-Xmem (Z recomputed in the backward)" if args.recompute_z
+                               else "POET-X (y kept for the backward in place of Z)"
+                               if args.saved_y
                                else "POET-X (Z kept for the backward)"),
                    "orthogonal_map": ("exact Cayley" if args.map == "cayley"
                                       else "Cayley-Neumann series to Q^4"),

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define POETX_ABI_VERSION 6
+#define POETX_ABI_VERSION 7
 
 typedef enum poetx_status {
   POETX_OK = 0,
@@ -89,6 +89,23 @@ typedef enum poetx_dtype { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
  * the skew blocks Q in place of the float32 orthogonal blocks and applies the
  * series' VJP (section 2 Methodik, Cayley-Neumann parameterisation item). */
 #define POETX_CAYLEY_NEUMANN 2
+/* Keep the layer's output Y for the backward in place of Z. R is orthogonal,
+ * so per block Z = Y R and the R gram g_Y^T Z equals (g_Y^T Y) R: the
+ * backward forms g_Y^T Y from y and takes the factor R into the first
+ * product of the Cayley VJP, M = 1/2 (R^T + I) (g_Y^T Y)(I + R), which costs
+ * what M = 1/2 (R^T + I) G (R^T + I) costs. A caller whose next operation
+ * keeps y anyway (an activation function, attention) then holds no
+ * [tokens, d_out] tensor for this layer. The forward takes z_save == NULL;
+ * with 256 x 256 bf16 R blocks (R-apply inside the dense product) it writes
+ * no Z at all, otherwise Z lives in its workspace. The backward takes the
+ * forward's y as z_saved. Agrees with the stored-Z path up to rounding: the
+ * identity is exact for orthogonal blocks, and the act-type blocks of bf16
+ * mode are orthogonal to about 2^-8. With an INT8 weight the R gram then
+ * needs no column scaling (Y already carries the scales). Not together with
+ * POETX_RECOMPUTE_Z, with POETX_CAYLEY_NEUMANN (the truncated series is not
+ * exactly orthogonal) or with permutations (y is in permuted column order):
+ * POETX_ERR_SHAPE. */
+#define POETX_SAVED_Y 4
 
 /* Shape of one POET-X linear layer. */
 typedef struct poetx_linear_desc {
@@ -99,7 +116,7 @@ typedef struct poetx_linear_desc {
   int32_t b_out;  /* block size of R */
   int32_t act;    /* poetx_dtype of the activations, W0 and the *_act blocks */
   int32_t n_events; /* number of entries in `events` (0 = no stage timing) */
-  int32_t flags;    /* 0 or POETX_RECOMPUTE_Z | POETX_CAYLEY_NEUMANN */
+  int32_t flags;    /* 0 or POETX_RECOMPUTE_Z | POETX_CAYLEY_NEUMANN | POETX_SAVED_Y */
   int32_t reserved; /* must be 0 */
   /* Optional stage timing: an array of hipEvent_t created by the caller (for
    * example with poetx_event_create). When n_events >= 2 s + 2, the call
@@ -257,7 +274,9 @@ int poetx_quantize_weight(const void* W0, int64_t d_out, int64_t d_in, int32_t a
                           float* scale, void* stream);
 
 /* Workspace bytes for poetx_linear_fwd / poetx_linear_bwd (0 if the
- * descriptor is invalid). With POETX_RECOMPUTE_Z the forward's includes Z. */
+ * descriptor is invalid). With POETX_RECOMPUTE_Z the forward's includes Z,
+ * and with POETX_SAVED_Y too unless the R-apply runs inside the dense
+ * product. */
 size_t poetx_fwd_workspace_size(const poetx_linear_desc* desc);
 size_t poetx_bwd_workspace_size(const poetx_linear_desc* desc);
 
@@ -273,7 +292,8 @@ size_t poetx_bwd_workspace_size(const poetx_linear_desc* desc);
  *   P_act  [nb_in,  b_in,  b_in ] act
  *   y      out [tokens, d_out] act
  *   z_save out [tokens, d_out] act: Z, kept for the backward; NULL (and
- *          only NULL) when desc->flags has POETX_RECOMPUTE_Z
+ *          only NULL) when desc->flags has POETX_RECOMPUTE_Z or
+ *          POETX_SAVED_Y
  *   ws     workspace of poetx_fwd_workspace_size(desc) bytes
  */
 int poetx_linear_fwd(const poetx_linear_desc* desc, const void* x, const void* W0,
@@ -333,8 +353,9 @@ int poetx_linear_fwd_noalloc(const poetx_linear_desc* desc, const void* x, const
  *              the orthogonal blocks, or with POETX_CAYLEY_NEUMANN the skew
  *              blocks q_f32 of poetx_build_cnp
  *   R_act, P_act  the act copies of the orthogonal blocks
- *   z_saved    [tokens, d_out] act, z_save of the matching forward; NULL
- *              (and only NULL) when desc->flags has POETX_RECOMPUTE_Z
+ *   z_saved    [tokens, d_out] act, z_save of the matching forward; with
+ *              POETX_SAVED_Y its y instead; NULL (and only NULL) when
+ *              desc->flags has POETX_RECOMPUTE_Z
  *   g_x        out [tokens, d_in] act
  *   g_theta_R  out [nb_out, b_out(b_out-1)/2] float32
  *   g_theta_P  out [nb_in,  b_in(b_in-1)/2]   float32

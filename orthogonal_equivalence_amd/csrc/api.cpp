@@ -47,9 +47,14 @@ int check_desc(const poetx_linear_desc* d) {
   if (d->b_in > d->d_in || d->b_out > d->d_out) return POETX_ERR_SHAPE;
   if (ceil_div(d->d_in, d->b_in) > kMaxBatch || ceil_div(d->d_out, d->b_out) > kMaxBatch) return POETX_ERR_SHAPE;
   if (d->n_events < 0 || (d->n_events > 0 && !d->events)) return POETX_ERR_NULL;
-  if ((d->flags & ~(POETX_RECOMPUTE_Z | POETX_CAYLEY_NEUMANN)) != 0 || d->reserved != 0)
+  if ((d->flags & ~(POETX_RECOMPUTE_Z | POETX_CAYLEY_NEUMANN | POETX_SAVED_Y)) != 0 ||
+      d->reserved != 0)
     return POETX_ERR_SHAPE;
   if ((d->perm_in == nullptr) != (d->perm_out == nullptr)) return POETX_ERR_NULL;
+  // Z = Y R needs exactly orthogonal blocks and y in block order
+  if ((d->flags & POETX_SAVED_Y) &&
+      ((d->flags & (POETX_RECOMPUTE_Z | POETX_CAYLEY_NEUMANN)) || d->perm_in != nullptr))
+    return POETX_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(d->perm_in) & 3) || (reinterpret_cast<uintptr_t>(d->perm_out) & 3))
     return POETX_ERR_ALIGN;
   // INT8 weight codes are widened 8 at a time
@@ -63,6 +68,7 @@ int check_desc(const poetx_linear_desc* d) {
 // ---------------------------------------------------------------- workspace
 bool recompute_z(const poetx_linear_desc* d) { return (d->flags & POETX_RECOMPUTE_Z) != 0; }
 bool neumann(const poetx_linear_desc* d) { return (d->flags & POETX_CAYLEY_NEUMANN) != 0; }
+bool saved_y(const poetx_linear_desc* d) { return (d->flags & POETX_SAVED_Y) != 0; }
 bool permuted(const poetx_linear_desc* d) { return d->perm_in != nullptr; }
 bool int8_weight(const poetx_linear_desc* d) { return d->w_scale != nullptr; }
 size_t weight_bytes(const poetx_linear_desc* d) {
@@ -106,6 +112,14 @@ struct FwdPlan {
   size_t u_off, z_off, xp_off, yp_off, inv_off, wq_off, rs_off, sb_off, total;
 };
 
+// Whether the forward runs the R-apply in the dense kernel's epilogue: bf16
+// with 256 x 256 R blocks, every 256-column output tile being one block.
+bool fwd_fuses_r(const poetx_linear_desc* d) {
+  const int64_t N = d->tokens, n = d->d_in, m = d->d_out;
+  return d->act == POETX_BF16 && d->b_out == 256 && m % 256 == 0 &&
+         poetx::dense_fused_r_supported(N, m, n, n, n, m, m);
+}
+
 // Bytes of the super-block buffer (block-diagonal 128 x 128 super blocks of
 // b = 32 or 64 blocks, for the b = 128 streaming kernels): one side at a
 // time, so the larger of the two.
@@ -121,8 +135,9 @@ FwdPlan plan_fwd(const poetx_linear_desc* d) {
   const size_t es = act_size(d->act);
   p.u_off = 0;
   size_t off = align_up((size_t)d->tokens * d->d_in * es);
-  p.z_off = off;  // Z lives here only when it is not kept
-  if (recompute_z(d)) off += align_up((size_t)d->tokens * d->d_out * es);
+  p.z_off = off;  // Z lives here only when it is not kept, and is formed
+  if (recompute_z(d) || (saved_y(d) && !fwd_fuses_r(d)))
+    off += align_up((size_t)d->tokens * d->d_out * es);
   // with permutations: the gathered x, Y before its scatter, the inverse map
   p.xp_off = p.yp_off = p.inv_off = off;
   if (permuted(d)) {
@@ -377,7 +392,7 @@ hipError_t dense(DType t, const void* A, const void* B, void* C, int64_t M, int6
 
 // The forward's dense product Z = U W^T (W = W0, or the INT8 codes q), and
 // with R (256 x 256 blocks, fused) also Y = Z blockdiag(R)^T in the same
-// launches. With INT8 codes the output columns go in chunks (next_chunk):
+// launches (then Z may be NULL: Y alone is written). With INT8 codes the output columns go in chunks (next_chunk):
 // each chunk's code rows widened into Wq, then its columns of Z (and Y);
 // Wq in the tiled layout when the dense kernel reads it and the chunk's
 // shape allows.
@@ -399,7 +414,7 @@ hipError_t dense_forward(DType t, const poetx_linear_desc* d, const void* U, con
       if (e != hipSuccess) return e;
       Wc = Wq;
     }
-    void* Zc = static_cast<char*>(Z) + c0 * es;
+    void* Zc = Z ? static_cast<char*>(Z) + c0 * es : nullptr;  // (no Z: fused only)
     if (R)  // (c0 and cn are multiples of 256 here: m is, and so is the nominal chunk)
       e = poetx::launch_dense_fused_r(U, Wc, Zc, N, cn, n, n, n, m,
                                       static_cast<const char*>(R) + (c0 / 256) * 256 * 256 * es,
@@ -442,8 +457,11 @@ hipError_t dense_backward(DType t, const poetx_linear_desc* d, const void* gZ, c
 // g_theta(i, j) = M[i][j] - M[j][i]. Computed as T = G R^T + G
 // (= G (R^T + I): both operands and the addend read in their stored order)
 // and M = 1/2 (R^T T + T), whose A operand R^T the GEMM reads column-wise
-// (its MN-major loader). When a second block set of the same size is given,
-// both run in the same launches.
+// (its MN-major loader). A set whose gram was formed from Y (POETX_SAVED_Y:
+// G = G' R with G' = g_Y^T Y) instead takes T = G' R + G' (= G (R^T + I),
+// since R R^T = I), the GEMM reading R row-wise; the second product is the
+// same. When a second block set of the same size is given, both run in the
+// same launches (the first product in two when their forms differ).
 //
 // float32 activations: float32 products throughout. bf16 activations: G and
 // T are rounded to bf16 and both products run on bf16 MFMA with float32
@@ -458,6 +476,7 @@ struct VjpSet {
   float* M;            // M (float32) or 1/2 R^T T (bf16 path)
   float* g_theta;
   int64_t d;
+  bool from_y;         // G holds G' = g_Y^T Y (POETX_SAVED_Y)
 };
 hipError_t cayley_vjp(DType t, const VjpSet& a, const VjpSet* b2, int b, hipStream_t s) {
   const int64_t nb1 = ceil_div(a.d, b);
@@ -465,23 +484,35 @@ hipError_t cayley_vjp(DType t, const VjpSet& a, const VjpSet* b2, int b, hipStre
   const int64_t bb = (int64_t)b * b;
   const bool lowp = t == DType::BF16;
   GemmParams g;
-  // T = G R^T + G: A = G (K-major), B(n, k) = R[n][k] (K-major), addend G
+  // T = G R^T + G: A = G (K-major), B(n, k) = R[n][k] (K-major), addend G;
+  // T = G' R + G': B(n, k) = R[k][n] (N-major)
   g.A = a.G; g.lda = b; g.sA = bb;
   g.B = lowp ? a.R_act : a.R; g.ldb = b; g.sB = bb;
   g.C = a.T; g.ldc = b; g.sC = bb;
   g.D = a.G; g.ldd = b; g.sD = bb;
   g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = b;
-  g.batch = (int)(nb1 + nb2);
+  g.batch = (int)nb1;
   g.kchunk = b;
   g.alpha = 1.0f; g.beta = 1.0f;
-  if (b2) {
+  hipError_t e;
+  if (b2 && b2->from_y == a.from_y) {
+    g.batch = (int)(nb1 + nb2);
     g.batch_split = (int)nb1;
     g.A2 = b2->G; g.B2 = lowp ? b2->R_act : b2->R; g.C2 = b2->T; g.D2 = b2->G;
+    if ((e = poetx::launch_gemm(t, t, true, !a.from_y, g, s)) != hipSuccess) return e;
+  } else {
+    if ((e = poetx::launch_gemm(t, t, true, !a.from_y, g, s)) != hipSuccess) return e;
+    if (b2) {
+      GemmParams g2 = g;
+      g2.A = b2->G; g2.B = lowp ? b2->R_act : b2->R; g2.C = b2->T; g2.D = b2->G;
+      g2.batch = (int)nb2;
+      if ((e = poetx::launch_gemm(t, t, true, !b2->from_y, g2, s)) != hipSuccess) return e;
+    }
   }
-  hipError_t e = poetx::launch_gemm(t, t, true, true, g, s);
-  if (e != hipSuccess) return e;
   // M = 1/2 (R^T T + T): A(m, k) = R[k][m] (MN-major), B(n, k) = T[k][n]; in
   // the bf16 path the GEMM writes 1/2 R^T T and the pack adds 1/2 T
+  g.batch = (int)(nb1 + nb2);
+  if (b2) g.batch_split = (int)nb1;
   g.A = lowp ? a.R_act : a.R; g.B = a.T; g.C = a.M;
   g.alpha = 0.5f;
   g.D = lowp ? nullptr : a.T; g.beta = lowp ? 0.0f : 0.5f;
@@ -558,7 +589,7 @@ int check_fwd_args(const poetx_linear_desc* d, const void* x, const void* W0, co
   int st = check_desc(d);
   if (st != POETX_OK) return st;
   if (!x || !W0 || !R_act || !P_act || !y) return POETX_ERR_NULL;
-  if (recompute_z(d) ? z_save != nullptr : z_save == nullptr) return POETX_ERR_NULL;
+  if ((recompute_z(d) || saved_y(d)) ? z_save != nullptr : z_save == nullptr) return POETX_ERR_NULL;
   const void* ptrs[] = {x, W0, R_act, P_act, y, z_save};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return POETX_ERR_ALIGN;
@@ -771,7 +802,9 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   const DType t = d->act == POETX_BF16 ? DType::BF16 : DType::F32;
   char* w = static_cast<char*>(ws);
   void* U = w + plan.u_off;
-  void* Z = z_save ? z_save : w + plan.z_off;
+  const bool fuse_r = fwd_fuses_r(d);
+  // (POETX_SAVED_Y with the fused R-apply: Z is never written)
+  void* Z = z_save ? z_save : (saved_y(d) && fuse_r) ? nullptr : w + plan.z_off;
   const bool perm = permuted(d);
   void* Xp = w + plan.xp_off;
   void* Yp = w + plan.yp_off;
@@ -820,8 +853,6 @@ int poetx_linear_fwd(const poetx_linear_desc* d, const void* x, const void* W0, 
   // multiplied by its block before it leaves (stage 1 then holds both and
   // stage 2 is empty).
   void* Yout = perm ? Yp : y;
-  const bool fuse_r = t == DType::BF16 && d->b_out == 256 && m % 256 == 0 &&
-                      poetx::dense_fused_r_supported(N, m, n, n, n, m, m);
   if ((e = sg.begin(1)) != hipSuccess) return hip_status(e);
   if ((e = dense_forward(t, d, U, W0, Wq, Z, fuse_r ? Rb : nullptr, Yout, u_tiled, s)) !=
       hipSuccess)
@@ -946,11 +977,13 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
 
   // INT8 weight: R blocks with scaled columns, g_Z' = g_Y R diag(s),
   // g_U = g_Z' q, G_R = (g_Y^T Z_q) diag(s) with Z_q = U q^T the forward's
-  // saved product. The codes are widened chunk by chunk inside stages 2 and
+  // saved product (with POETX_SAVED_Y, G_R = (g_Y^T Y) R unscaled: Y carries
+  // the scales). The codes are widened chunk by chunk inside stages 2 and
   // 7 into the region that holds the scaled R blocks (stage 10, made after
   // stage 7) while B1 reads them.
   void* Wq = w + plan.wq;
   const void* Rb = int8_weight(d) ? static_cast<const void*>(w + plan.rs) : R_act;
+  const float* gram_scale = saved_y(d) ? nullptr : d->w_scale;
   auto scale_r = [&]() -> hipError_t {
     if (!int8_weight(d)) return hipSuccess;
     hipError_t r;
@@ -987,7 +1020,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     if ((r = sg.begin(1)) != hipSuccess) return r;
     if ((r = block_gram(t, gY, Z, partR, N, m, bR, plan.sR, s)) != hipSuccess) return r;
     if ((r = poetx::launch_split_reduce(partR, plan.sR.nsplit, nbR, bR, lastR, GR, gt, s,
-                                        d->w_scale, plan.subR)) != hipSuccess)
+                                        gram_scale, plan.subR)) != hipSuccess)
       return r;
     return sg.end(1);
   };
@@ -1008,7 +1041,7 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
       return r;
     if ((r = sg.end(0)) != hipSuccess) return r;
     if ((r = sg.begin(1)) != hipSuccess) return r;
-    if ((r = poetx::launch_split_reduce(partR, ns, nbR, bR, lastR, GR, gt, s, d->w_scale,
+    if ((r = poetx::launch_split_reduce(partR, ns, nbR, bR, lastR, GR, gt, s, gram_scale,
                                         plan.subR)) != hipSuccess)
       return r;
     return sg.end(1);
@@ -1097,8 +1130,8 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
     if (!merged) POETX_TRY(cnp_vjp(cP, nullptr, bP, s));
     POETX_TRY(sg.end(6));
   } else {
-    const VjpSet vR{GR, R_f32, R_act, TR, MR, g_theta_R, m};
-    const VjpSet vP{GP, P_f32, P_act, TP, MP, g_theta_P, n};
+    const VjpSet vR{GR, R_f32, R_act, TR, MR, g_theta_R, m, saved_y(d)};
+    const VjpSet vP{GP, P_f32, P_act, TP, MP, g_theta_P, n, false};
     POETX_TRY(sg.begin(5));
     if (merged && bR > 1) {
       POETX_TRY(cayley_vjp(t, vR, &vP, bR, s));

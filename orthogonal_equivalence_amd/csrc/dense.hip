@@ -354,7 +354,9 @@ struct Dense {
   // Y tile = Z tile R_k^T for the output tile's R block R_k (its 256 columns
   // are one block): the bf16 Z tile staged in the ring is the A operand, R_k's
   // rows are the B fragments (loaded from global memory, the block stays in
-  // L2), K = 256 in 8 steps of 32, accumulated in the same AGPRs.
+  // L2), K = 256 in 8 steps of 32, accumulated in the same AGPRs. Without
+  // KEEP_Z only Y leaves the CU (a run-time test there made the compiler
+  // spill ~0.5 KB per lane).
   template <int S>
   __device__ __forceinline__ void load_r(const bf16_t* rrow) {
 #pragma unroll
@@ -400,6 +402,7 @@ struct Dense {
       *reinterpret_cast<uint4*>(C + (int64_t)(m0 + rl) * ldc + n0 + nl) = v;
     }
   }
+  template <bool KEEP_Z>
   __device__ __forceinline__ void epilogue_fused(bf16_t* __restrict__ C, int64_t ldc, int m0,
                                                  int n0, const bf16_t* __restrict__ Rk,
                                                  bf16_t* __restrict__ Y, int64_t ldy) {
@@ -417,7 +420,7 @@ struct Dense {
     // wait states before the VALU reads of the products' results
     asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    store_staged(C, ldc, m0, n0, tid);  // Z
+    if constexpr (KEEP_Z) store_staged(C, ldc, m0, n0, tid);  // Z
     wait_lds();
     barrier_nofence();  // every wave is done reading the staged Z
     stage_acc(ln);
@@ -433,7 +436,7 @@ struct Dense {
 // B + q sB, C + q sC (the block-diagonal products of b >= 512 blocks run as
 // one batched launch); their output tiles form one grid of num_mt x
 // (nbatch num_nt) tiles, products side by side along N.
-template <bool B_KMAJ, bool FUSE_R = false>
+template <bool B_KMAJ, bool FUSE_R = false, bool KEEP_Z = true>
 __global__ void __launch_bounds__(NT)
 dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t* __restrict__ C,
              int M, int N, int K, int64_t lda, int64_t ldb, int64_t ldc,
@@ -459,7 +462,8 @@ dense_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, bf16_t*
     wait_lds();
     barrier_nofence();  // every wave is done with the ring
     if constexpr (FUSE_R)
-      d.epilogue_fused(C, ldc, m0, n0, R + (int64_t)(n0 / 256) * 256 * 256, Y, ldy);
+      d.template epilogue_fused<KEEP_Z>(C, ldc, m0, n0, R + (int64_t)(n0 / 256) * 256 * 256, Y,
+                                        ldy);
     else
       d.epilogue(C + q * sC, ldc, m0, n0);
     tile += (int)gridDim.x;
@@ -556,11 +560,18 @@ hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M
   int grid = 0;
   hipError_t e = dense_grid(M, N, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dense_kernel<true, true>), dim3(grid), dim3(NT), 0, s,
-                     static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B),
-                     static_cast<bf16_t*>(C), (int)M, (int)N, (int)K, lda, ldb, ldc,
-                     static_cast<const bf16_t*>(R), static_cast<bf16_t*>(Y), ldy, 1, (int64_t)0,
-                     (int64_t)0, (int64_t)0, (int)a_tiled, (int)b_tiled);
+  if (C)
+    hipLaunchKernelGGL((dense_kernel<true, true>), dim3(grid), dim3(NT), 0, s,
+                       static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B),
+                       static_cast<bf16_t*>(C), (int)M, (int)N, (int)K, lda, ldb, ldc,
+                       static_cast<const bf16_t*>(R), static_cast<bf16_t*>(Y), ldy, 1, (int64_t)0,
+                       (int64_t)0, (int64_t)0, (int)a_tiled, (int)b_tiled);
+  else
+    hipLaunchKernelGGL((dense_kernel<true, true, false>), dim3(grid), dim3(NT), 0, s,
+                       static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B), nullptr,
+                       (int)M, (int)N, (int)K, lda, ldb, ldc, static_cast<const bf16_t*>(R),
+                       static_cast<bf16_t*>(Y), ldy, 1, (int64_t)0, (int64_t)0, (int64_t)0,
+                       (int)a_tiled, (int)b_tiled);
   return hipGetLastError();
 }
 

@@ -99,7 +99,8 @@ hipError_t launch_dense_batched(const void* A, const void* B, void* C, int64_t M
 // The forward's dense product with the R-apply fused into its epilogue
 // (256 x 256 R blocks, bf16): C = A B^T (B K-major) and Y = C blockdiag(R)^T
 // with C rounded to bf16 before the second product, as the separate R-apply
-// would read it. N must be a multiple of 256; R is [N / 256][256][256].
+// would read it. N must be a multiple of 256; R is [N / 256][256][256]. C
+// may be NULL: then only Y is written.
 bool dense_fused_r_supported(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                              int64_t ldc, int64_t ldy);
 hipError_t launch_dense_fused_r(const void* A, const void* B, void* C, int64_t M, int64_t N,

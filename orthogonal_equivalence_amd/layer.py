@@ -25,6 +25,10 @@ class PoetxLinear:
 
     recompute_z=True is the memory-saving variant: the forward keeps no
     Z = W0 P x for the backward, which recomputes it (POETX_RECOMPUTE_Z).
+    saved_y=True keeps nothing beside y: the backward takes y in place of Z
+    (POETX_SAVED_Y; per block Z = Y R for orthogonal R), for callers that
+    keep y anyway. forward() returns (y, saved), saved being what backward()
+    takes as z: Z, y itself with saved_y, None with recompute_z.
     map="cnp" builds the blocks by the truncated Cayley-Neumann series
     (poetx_build_cnp) and keeps the skew blocks Q for its VJP
     (POETX_CAYLEY_NEUMANN); map="cayley" (default) is the exact map.
@@ -37,13 +41,14 @@ class PoetxLinear:
 
     def __init__(self, W0: torch.Tensor, b_in: int, b_out: int, act: str, device="cuda",
                  recompute_z: bool = False, map: str = "cayley", perm_out=None, perm_in=None,
-                 int8: bool = False):
+                 int8: bool = False, saved_y: bool = False):
         if map not in ("cayley", "cnp"):
             raise ValueError(f"unknown orthogonal map {map!r}")
         self.torch_dtype, self.act = _DT[act]
         self.map = map
         self.flags = (P.POETX_RECOMPUTE_Z if recompute_z else 0) | \
-            (P.POETX_CAYLEY_NEUMANN if map == "cnp" else 0)
+            (P.POETX_CAYLEY_NEUMANN if map == "cnp" else 0) | \
+            (P.POETX_SAVED_Y if saved_y else 0)
         self.device = torch.device(device)
         self.W0 = W0.to(self.device, self.torch_dtype).contiguous()
         self.d_out, self.d_in = self.W0.shape
@@ -144,14 +149,14 @@ class PoetxLinear:
     def forward(self, x, y=None, z=None, stream=None, events=None):
         N = x.shape[0]
         y = torch.empty(N, self.d_out, device=self.device, dtype=self.torch_dtype) if y is None else y
-        if self.flags & P.POETX_RECOMPUTE_Z:
+        if self.flags & (P.POETX_RECOMPUTE_Z | P.POETX_SAVED_Y):
             z = None
         elif z is None:
             z = torch.empty(N, self.d_out, device=self.device, dtype=self.torch_dtype)
         R, Pb = self.blocks_for_act()
         ws = self._ws(self._fwd_ws, P.poetx_fwd_workspace_size, N)
         P.poetx_linear_fwd(self.desc(N, events), x, self.W0, R, Pb, y, z, ws, stream)
-        return y, z
+        return y, (y if self.flags & P.POETX_SAVED_Y else z)
 
     def backward(self, g_y, x, z=None, g_x=None, g_theta_R=None, g_theta_P=None, stream=None,
                  events=None):

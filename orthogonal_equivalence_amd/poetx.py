@@ -29,9 +29,10 @@ POETX_ERR_ALIAS = 7
 POETX_F32 = 0
 POETX_BF16 = 1
 
-POETX_ABI_VERSION = 6
+POETX_ABI_VERSION = 7
 POETX_RECOMPUTE_Z = 1
 POETX_CAYLEY_NEUMANN = 2
+POETX_SAVED_Y = 4
 
 EXPORTS = (
     "poetx_abi_version", "poetx_status_string", "poetx_num_blocks", "poetx_theta_count",

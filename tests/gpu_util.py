@@ -92,15 +92,17 @@ def check_blocks(name: str, got, ref, dtype: str) -> float:
     return whole
 
 
-def run_layer(L, stream=None, recompute_z=False, map="cayley", perms=None):
+def run_layer(L, stream=None, recompute_z=False, map="cayley", perms=None, saved_y=False,
+              int8=False):
     """Build, forward and backward one layer on the GPU (the bench's path).
     Returns the PoetxLinear and a dict of device results (z is None when the
-    layer recomputes Z in the backward). perms: (perm_out, perm_in) or None."""
+    layer keeps no Z: recomputed in the backward, or y kept in its place).
+    perms: (perm_out, perm_in) or None."""
     from orthogonal_equivalence_amd.layer import PoetxLinear
     s = L.spec
     po, pi = perms if perms is not None else (None, None)
     lay = PoetxLinear(dev(L.W0, s.dtype), s.b, s.b, s.dtype, recompute_z=recompute_z, map=map,
-                      perm_out=po, perm_in=pi)
+                      perm_out=po, perm_in=pi, saved_y=saved_y, int8=int8)
     lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
     x = dev(L.x, s.dtype)
     g_y = dev(L.g_y, s.dtype)
@@ -108,4 +110,5 @@ def run_layer(L, stream=None, recompute_z=False, map="cayley", perms=None):
     y, z = lay.forward(x, stream=stream)
     g_x, gR, gP = lay.backward(g_y, x, z, stream=stream)
     torch.cuda.synchronize()
-    return lay, dict(x=x, g_y=g_y, y=y, z=z, g_x=g_x, g_theta_R=gR, g_theta_P=gP)
+    return lay, dict(x=x, g_y=g_y, y=y, z=None if saved_y else z, g_x=g_x, g_theta_R=gR,
+                     g_theta_P=gP)

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strings():
-    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 6
+    assert P.poetx_abi_version() == P.POETX_ABI_VERSION == 7
     for s in range(8):
         assert P.status_string(s) and P.status_string(s) != "unknown status"
     assert P.status_string(99) == "unknown status"
@@ -220,8 +220,8 @@ def test_build_errors():
 
 def test_unknown_flags_and_reserved_rejected():
     for call in (_fwd, _bwd):
-        assert call(desc(flags=4)) == P.POETX_ERR_SHAPE
-        assert call(desc(flags=8 | P.POETX_CAYLEY_NEUMANN)) == P.POETX_ERR_SHAPE
+        assert call(desc(flags=8)) == P.POETX_ERR_SHAPE
+        assert call(desc(flags=16 | P.POETX_CAYLEY_NEUMANN)) == P.POETX_ERR_SHAPE
         assert call(desc(flags=-1)) == P.POETX_ERR_SHAPE
         d = desc()
         d.reserved = 1
@@ -281,6 +281,52 @@ def test_recompute_z_alias_checks_skip_null_z():
     d = desc(flags=P.POETX_RECOMPUTE_Z)
     assert _fwd(d, z=None, y=ALIGNED) == P.POETX_ERR_ALIAS
     assert _bwd(d, z=None, g_x=ALIGNED) == P.POETX_ERR_ALIAS
+
+
+# -- POETX_SAVED_Y (the backward takes y in place of Z) ----------------------
+
+def test_saved_y_takes_y_in_place_of_z():
+    d = desc(flags=P.POETX_SAVED_Y)
+    assert _fwd(d) == P.POETX_ERR_NULL            # the forward keeps no Z
+    assert _bwd(d, z=None) == P.POETX_ERR_NULL    # the backward needs y
+    # validation passes up to the workspace check with z_save NULL / y given
+    need = P.poetx_fwd_workspace_size(d)
+    assert need > 0 and _fwd(d, z=None, ws_bytes=need - 1) == P.POETX_ERR_WORKSPACE
+    need = P.poetx_bwd_workspace_size(d)
+    assert need > 0 and _bwd(d, ws_bytes=need - 1) == P.POETX_ERR_WORKSPACE
+    # y is an input of the backward: an output on top of it is refused
+    assert _bwd(d, z=ALIGNED * 64) == P.POETX_ERR_ALIAS
+
+
+def test_saved_y_refuses_what_breaks_z_equals_y_r():
+    """Z = Y R needs exactly orthogonal blocks (not the truncated series),
+    a kept product (not POET-Xmem) and y in block order (no permutations)."""
+    perm = ALIGNED * 512
+    for bad in (dict(flags=P.POETX_SAVED_Y | P.POETX_RECOMPUTE_Z),
+                dict(flags=P.POETX_SAVED_Y | P.POETX_CAYLEY_NEUMANN),
+                dict(flags=P.POETX_SAVED_Y, perm_in=perm, perm_out=perm + 4096)):
+        d = desc(**bad)
+        assert _fwd(d, z=None) == P.POETX_ERR_SHAPE
+        assert _bwd(d) == P.POETX_ERR_SHAPE
+        assert P.poetx_fwd_workspace_size(d) == 0 and P.poetx_bwd_workspace_size(d) == 0
+
+
+def test_saved_y_forward_workspace():
+    """With 256 x 256 bf16 R blocks the R-apply runs in the dense kernel and Z
+    is never formed: the workspace is that of the stored-Z forward. Otherwise
+    Z is formed in the workspace, as with POETX_RECOMPUTE_Z. The backward's
+    workspace is the same in every mode."""
+    big = dict(tokens=8192, d_in=4096, d_out=14336, b_in=256, b_out=256, act=P.POETX_BF16)
+    keep = P.poetx_fwd_workspace_size(desc(**big))
+    assert P.poetx_fwd_workspace_size(desc(flags=P.POETX_SAVED_Y, **big)) == keep
+    assert P.poetx_bwd_workspace_size(desc(flags=P.POETX_SAVED_Y, **big)) == \
+        P.poetx_bwd_workspace_size(desc(**big))
+    for other in (dict(big, b_out=128), dict(big, act=P.POETX_F32), dict(big, d_out=14208)):
+        keep = P.poetx_fwd_workspace_size(desc(**other))
+        saved = P.poetx_fwd_workspace_size(desc(flags=P.POETX_SAVED_Y, **other))
+        mem = P.poetx_fwd_workspace_size(desc(flags=P.POETX_RECOMPUTE_Z, **other))
+        es = 2 if other["act"] == P.POETX_BF16 else 4
+        assert saved == mem and saved - keep >= other["tokens"] * other["d_out"] * es
 
 
 # -- POETX_CAYLEY_NEUMANN and poetx_build_cnp (truncated series map) ---------

@@ -46,3 +46,15 @@ def test_layer_work_counts_every_product_of_the_step():
     # bytes: at least every activation tensor the step must read or write once
     es = 2
     assert nbytes >= es * (N * n + N * m + N * m + N * n)
+
+
+def test_layer_work_without_z_drops_one_activation_write():
+    """With y kept in Z's place the forward writes one [tokens, d_out] tensor
+    fewer; the flops are the same (the R gram's factor R moves into the VJP's
+    first product, which has the same size)."""
+    b_mod = _bench_module()
+    s = CONFIGS["mlp_up_8b"][0]
+    f0, b0 = b_mod.layer_work(s)
+    f1, b1 = b_mod.layer_work(s, saved_y=True)
+    assert f1 == f0
+    assert b0 - b1 == 2 * s.tokens * s.d_out

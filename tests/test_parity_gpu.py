@@ -359,6 +359,55 @@ def test_recompute_z_full_size_mlp_up_8b():
     torch.cuda.empty_cache()
 
 
+# ------------------------------- y kept in place of Z (POETX_SAVED_Y)
+SAVED_Y_CASES = [SMALL_BY_NAME[k] for k in (
+    "f32_tiles", "f32_padded_blocks", "bf16_tiles", "bf16_b256", "bf16_b64_one_token",
+    "bf16_padded_blocks", "bf16_b512", "bf16_b256_one_token", "bf16_b1024_dense",
+    "bf16_b32_super", "bf16_b256_splits", "bf16_b256_tiled", "bf16_b128_tiled")]
+
+
+@pytest.mark.parametrize("case", SAVED_Y_CASES, ids=lambda c: c[0])
+def test_saved_y_small(case):
+    """POETX_SAVED_Y: the backward takes y, forms g_Y^T Y per R block and
+    takes the factor R into the Cayley VJP (Z = Y R for orthogonal R). The
+    oracle's gradients (formed from Z) to the usual tolerance; y and g_x bit
+    for bit those of the stored-Z path (the same forward products, and g_Z =
+    g_Y R does not involve Z). With 256 x 256 bf16 R blocks the forward writes
+    no Z at all."""
+    name, n, m, b, N, dt, sigma = case
+    spec = LayerSpec(name, n, m, b, N, dt, sigma, seed=len(name) + 500)
+    U.log(f"[saved-y] {name}: d_in={n} d_out={m} b={b} tokens={N} {dt}")
+    L = make_layer(spec)
+    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, b, b)
+    y_ref = ora.forward(L.x)
+    gx_ref, gR_ref, gP_ref = ora.backward(L.g_y, L.x)
+    _, sy = U.run_layer(L, saved_y=True)
+    U.check("y", U.host(sy["y"]), y_ref, dt)
+    U.check("g_x", U.host(sy["g_x"]), gx_ref, dt)
+    U.check("g_theta_R", U.host(sy["g_theta_R"]), gR_ref, dt)
+    U.check("g_theta_P", U.host(sy["g_theta_P"]), gP_ref, dt)
+    _, keep = U.run_layer(L)
+    for k in ("y", "g_x"):
+        assert torch.equal(sy[k], keep[k]), k
+
+
+def test_saved_y_full_size_mlp_up_8b():
+    """The 8B MLP up-projection (14336 x 4096, b = 256, 8192 tokens) keeping
+    y in place of Z: every element against the oracle; y and g_x equal to the
+    stored-Z path."""
+    spec = CONFIGS["mlp_up_8b"][0]
+    U.log(f"[saved-y full] {spec.name}: {spec.d_out}x{spec.d_in} b={spec.b} tokens={spec.tokens}")
+    L = make_layer(spec)
+    lay, sy = U.run_layer(L, saved_y=True)
+    _, keep = U.run_layer(L)
+    for k in ("y", "g_x"):
+        assert torch.equal(sy[k], keep[k]), k
+    del keep
+    _full_check(L, lay, sy)
+    del lay, sy
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------- Cayley-Neumann series (CNP)
 def _build_cnp(theta: np.ndarray, d: int, b: int, act=P.POETX_BF16):
     nb = -(-d // b)
@@ -665,6 +714,26 @@ def test_int8_full_size_mlp_up_8b():
     _full_check(_int8_reference_inputs(L), lay, out, check_z=False)
     del lay, out, y, z, g_x
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("case", [c for c in INT8_CASES
+                                  if c[7] == "cayley" and not c[8] and not c[9]],
+                         ids=lambda c: c[0])
+def test_saved_y_int8(case):
+    """POETX_SAVED_Y with an INT8 weight: Y already carries the row scales,
+    so the R gram g_Y^T Y is taken without column scaling."""
+    name, n, m, b, N, dt, sigma, map_, _, _ = case
+    spec = LayerSpec(name, n, m, b, N, dt, sigma, seed=len(name) + 600)
+    U.log(f"[saved-y int8] {name}: d_in={n} d_out={m} b={b} tokens={N} {dt}")
+    L = make_layer(spec)
+    ora = O.LayerOracle(_int8_reference_inputs(L).W0, L.theta_R, L.theta_P, b, b)
+    y_ref = ora.forward(L.x)
+    gx_ref, gR_ref, gP_ref = ora.backward(L.g_y, L.x)
+    _, sy = U.run_layer(L, saved_y=True, int8=True)
+    U.check("y", U.host(sy["y"]), y_ref, dt)
+    U.check("g_x", U.host(sy["g_x"]), gx_ref, dt)
+    U.check("g_theta_R", U.host(sy["g_theta_R"]), gR_ref, dt)
+    U.check("g_theta_P", U.host(sy["g_theta_P"]), gP_ref, dt)
 
 
 # ------------------------------------------- the step captured in a HIP graph
