@@ -420,7 +420,7 @@ def main():
     sb = layers[big][0]
     dense_flops = 2.0 * sb.tokens * sb.d_in * sb.d_out
     # with bf16 and 256 x 256 R blocks the forward's R-apply runs in the dense
-    # kernel's epilogue (dense_kernel<true, true>), so that launch also does
+    # kernel's epilogue (dense_kernel<true, true, ...>), so that launch also does
     # the R-apply's 2 N d_out b flops
     fused_r = sb.dtype == "bf16" and sb.b == 256 and sb.d_out % 256 == 0
     if fused_r:
@@ -439,8 +439,8 @@ def main():
                 "kernel": ("dense_fwd: Y = (U W0^T) blockdiag(R)^T, Z not written "
                            "(dense_kernel<true, true, false>" if fused_r and args.saved_y else
                            "dense_fwd: Z = U W0^T with Y = Z blockdiag(R)^T in its epilogue "
-                           "(dense_kernel<true, true>" if fused_r else
-                           "dense_fwd: Z = U W0^T (dense_kernel<true, false>") +
+                           "(dense_kernel<true, true, true>" if fused_r else
+                           "dense_fwd: Z = U W0^T (dense_kernel<true, false, true>") +
                           ": bf16, K-major W0, persistent, direct-to-LDS, 4 waves of 128x128, "
                           "16x16x32 MFMA)",
                 "flops_per_launch": dense_flops, "avg_launch_ms": dense_ms}
