@@ -741,6 +741,7 @@ def test_saved_y_int8(case):
     (("bf16_b256_tiled", 768, 1280, 256, 1536), {}),
     (("bf16_b128_int8", 512, 768, 128, 1000), {"int8": True}),
     (("bf16_b256_mem", 512, 1024, 256, 300), {"recompute_z": True}),
+    (("bf16_b256_saved_y", 768, 1280, 256, 1536), {"saved_y": True}),
 ], ids=lambda c: c[0] if isinstance(c, tuple) else "-".join(c) or "plain")
 def test_step_in_hip_graph(case, kw):
     """Build, forward and backward captured in one HIP graph (the library
@@ -756,7 +757,8 @@ def test_step_in_hip_graph(case, kw):
     lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
     x, g_y = U.dev(L.x, "bf16"), U.dev(L.g_y, "bf16")
     y = torch.empty(N, m, dtype=torch.bfloat16, device="cuda")
-    z = None if kw.get("recompute_z") else torch.empty_like(y)
+    z = None if kw.get("recompute_z") or kw.get("saved_y") else torch.empty_like(y)
+    saved = y if kw.get("saved_y") else z  # what the backward takes
     g_x = torch.empty(N, n, dtype=torch.bfloat16, device="cuda")
     gR, gP = torch.empty_like(lay.theta_R), torch.empty_like(lay.theta_P)
     side = torch.cuda.Stream()
@@ -764,7 +766,7 @@ def test_step_in_hip_graph(case, kw):
     def step(stream):
         lay.build(stream)
         lay.forward(x, y, z, stream=stream)
-        lay.backward(g_y, x, z, g_x, gR, gP, stream=stream)
+        lay.backward(g_y, x, saved, g_x, gR, gP, stream=stream)
 
     def outputs():
         return [t.clone() for t in (y, g_x, gR, gP) + ((z,) if z is not None else ())]

@@ -27,9 +27,9 @@ CALLS = [
 ]
 
 
-def _layer(spec):
+def _layer(spec, **kw):
     L = make_layer(spec)
-    lay = PoetxLinear(U.dev(L.W0, spec.dtype), spec.b, spec.b, spec.dtype)
+    lay = PoetxLinear(U.dev(L.W0, spec.dtype), spec.b, spec.b, spec.dtype, **kw)
     lay.set_theta(torch.from_numpy(L.theta_R).float(), torch.from_numpy(L.theta_P).float())
     lay.build()
     return L, lay
@@ -60,6 +60,36 @@ def test_noalloc_forward_matches_workspace_forward():
         U.check("z", U.host(z_na), z_ref, spec.dtype)
         del lay, ws, x, y_ws, z_ws, y_na, z_na
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("spec", [
+    # 256 x 256 bf16 R blocks: the R-apply runs in the dense epilogue and no Z
+    # is formed; b = 128: Z is formed in the scratch area before the R-apply
+    LayerSpec("noalloc_saved_y_fused", 1024, 2048, 256, 4096, "bf16", 0.01, seed=24),
+    LayerSpec("noalloc_saved_y_b128", 512, 768, 128, 300, "bf16", 0.02, seed=25),
+], ids=lambda s: s.name)
+def test_noalloc_forward_keeping_y_for_z(spec):
+    """POETX_SAVED_Y (z_save NULL): the scratch forward's y bit for bit that
+    of the workspace forward, and the oracle's."""
+    U.log(f"[noalloc saved-y] {spec.name}: d_in={spec.d_in} d_out={spec.d_out} b={spec.b} "
+          f"tokens={spec.tokens}")
+    L, lay = _layer(spec, saved_y=True)
+    x = U.dev(L.x, spec.dtype)
+    d = lay.desc(spec.tokens)
+    assert d.flags & P.POETX_SAVED_Y
+    assert P.poetx_fwd_workspace_size(d) <= P.POETX_NOALLOC_SCRATCH_BYTES
+    shape = (spec.tokens, spec.d_out)
+    y_ws = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(P.poetx_fwd_workspace_size(d), dtype=torch.uint8, device="cuda")
+    P.poetx_linear_fwd(d, x, lay.W0, lay.R_act, lay.P_act, y_ws, None, ws)
+    y_na = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    P.poetx_linear_fwd_noalloc(d, x, lay.W0, lay.R_act, lay.P_act, y_na, None)
+    torch.cuda.synchronize()
+    assert torch.equal(y_na, y_ws)
+    ora = O.LayerOracle(L.W0, L.theta_R, L.theta_P, spec.b, spec.b)
+    U.check("y", U.host(y_na), ora.forward(L.x), spec.dtype)
+    del lay, ws, x, y_ws, y_na
+    torch.cuda.empty_cache()
 
 
 def test_noalloc_forward_rejects_oversize_workspace():
