@@ -342,7 +342,10 @@ int poetx_linear_fwd_noalloc(const poetx_linear_desc* desc, const void* x, const
  *   products, which accumulate in float32).
  *   With POETX_CAYLEY_NEUMANN, the series' VJP instead:
  *   D = 2 sum_{k=1..4} sum_{i+j=k-1} (Q^T)^i G (Q^T)^j,
- *   g_theta(i, j) = D[i][j] - D[j][i], all in float32.
+ *   g_theta(i, j) = D[i][j] - D[j][i], in float32; in bf16 mode with
+ *   b_in and b_out multiples of 8, its products take bf16 operands (G, Q
+ *   and the intermediate products rounded to bf16) and accumulate in
+ *   float32.
  * The token reductions are split over workgroups and summed in a fixed
  * order, so results are bitwise reproducible.
  *

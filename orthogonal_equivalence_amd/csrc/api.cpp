@@ -529,8 +529,8 @@ hipError_t cayley_vjp(DType t, const VjpSet& a, const VjpSet* b2, int b, hipStre
 }
 
 // VJP of the truncated Cayley-Neumann series R = I + 2 (Q + Q^2 + Q^3 + Q^4)
-// for every block, float32 throughout (the factored form is derived in
-// cnp.hip):
+// for every block, float32 throughout for float32 activations (bf16 mode:
+// cnp_vjp_bf16 below; the factored form is derived in cnp.hip):
 //   Q2 = Q Q -> w1;  Tt = Q2 - Q -> w2;  Tbar = 2 G Q2 + 2 G -> w3;
 //   Nbar = 2 Tt G -> w1;  Ws = (Tbar + Nbar) + (Tbar + Nbar)^T -> w2;
 //   X = Tbar - Ws Q -> w1;  g_theta(i, j) = X[i][j] - X[j][i].
@@ -579,6 +579,81 @@ hipError_t cnp_vjp(const CnpVjpSet& a, const CnpVjpSet* b2, int b, hipStream_t s
   if (!b2) return poetx::launch_pack_skew_grad(p1, nullptr, 0.0f, b, 1.0f, s);
   const poetx::PackSet p2{c.w1, nullptr, nb2, (int)(c.d - (nb2 - 1) * b), c.g_theta};
   return poetx::launch_pack_skew_grad(p1, &p2, 0.0f, b, 1.0f, s);
+}
+
+// The series VJP for bf16 activations: the same steps with bf16 operands
+// and float32 accumulation (as the exact map's VJP in bf16 mode), G the
+// bf16 reduced gram:
+//   Qb = bf16(Q);  Q2 = Qb Qb;  Tt = Q2 - Q;  Tbar = 2 G Q2 + 2 G;
+//   Nbar = 2 Tt G;  Ws = (Tbar + Nbar) + (Tbar + Nbar)^T;  X' = -Ws Qb,
+// all bf16 but X' (float32); the pack then forms (X' + Tbar) - (X' + Tbar)^T,
+// X' + Tbar being X. Buffers (each [nblocks][b][b], regions of the
+// backward's workspace that are free by then): Qb in the upper half of the
+// gram's region, Q2 and Tt in w1 (later X'), Tbar and Nbar in w2, Ws in w3.
+struct CnpVjpBf16Set {
+  const void* G;   // bf16 gram, in the lower half of its float32-sized region
+  const float* Q;  // float32 skew blocks
+  float* w1;
+  float* w2;
+  float* w3;
+  float* g_theta;
+  int64_t d;
+};
+hipError_t cnp_vjp_bf16(const CnpVjpBf16Set& a, const CnpVjpBf16Set* b2, int b, hipStream_t s) {
+  const int64_t nb1 = ceil_div(a.d, b);
+  const int64_t nb2 = b2 ? ceil_div(b2->d, b) : 0;
+  const int64_t bb = (int64_t)b * b;
+  const CnpVjpBf16Set z{};
+  const CnpVjpBf16Set& c = b2 ? *b2 : z;
+  // bf16 views: element offset e of a float32-sized region, in bf16 elements
+  auto half = [](const void* base, int64_t e) {
+    return static_cast<void*>(const_cast<char*>(static_cast<const char*>(base)) + 2 * e);
+  };
+  void* Qb1 = half(a.G, nb1 * bb);
+  void* Qb2 = b2 ? half(c.G, nb2 * bb) : nullptr;
+  void* Q2_1 = a.w1;
+  void* Q2_2 = c.w1;
+  void* Tt1 = half(a.w1, nb1 * bb);
+  void* Tt2 = b2 ? half(c.w1, nb2 * bb) : nullptr;
+  void* Tb1 = a.w2;
+  void* Tb2 = c.w2;
+  void* Nb1 = half(a.w2, nb1 * bb);
+  void* Nb2 = b2 ? half(c.w2, nb2 * bb) : nullptr;
+  GemmParams g;
+  g.lda = g.ldb = g.ldc = g.ldd = b;
+  g.sA = g.sB = g.sC = g.sD = bb;
+  g.M = g.N = g.K = g.M_last = g.N_last = g.K_last = b;
+  g.kchunk = b;
+  g.batch = (int)(nb1 + nb2);
+  if (b2) g.batch_split = (int)nb1;
+  // C = alpha A B + beta D per block (A, B row-major b x b, bf16)
+  auto mm = [&](DType out, const void* A1, const void* B1, void* C1, const void* D1, const void* A2,
+                const void* B2, void* C2, const void* D2, float alpha, float beta) {
+    g.A = A1; g.B = B1; g.C = C1; g.D = D1;
+    g.A2 = A2; g.B2 = B2; g.C2 = C2; g.D2 = D2;
+    g.alpha = alpha; g.beta = beta;
+    return poetx::launch_gemm(DType::BF16, out, true, false, g, s);
+  };
+  hipError_t e;
+  if ((e = poetx::launch_sub_to_bf16(DType::F32, a.Q, nullptr, Qb1, nb1 * bb, s)) != hipSuccess) return e;
+  if (b2 && (e = poetx::launch_sub_to_bf16(DType::F32, c.Q, nullptr, Qb2, nb2 * bb, s)) != hipSuccess)
+    return e;
+  if ((e = mm(DType::BF16, Qb1, Qb1, Q2_1, nullptr, Qb2, Qb2, Q2_2, nullptr, 1.0f, 0.0f)) != hipSuccess)
+    return e;
+  if ((e = poetx::launch_sub_to_bf16(DType::BF16, Q2_1, a.Q, Tt1, nb1 * bb, s)) != hipSuccess) return e;
+  if (b2 && (e = poetx::launch_sub_to_bf16(DType::BF16, Q2_2, c.Q, Tt2, nb2 * bb, s)) != hipSuccess)
+    return e;
+  if ((e = mm(DType::BF16, a.G, Q2_1, Tb1, a.G, c.G, Q2_2, Tb2, c.G, 2.0f, 2.0f)) != hipSuccess) return e;
+  if ((e = mm(DType::BF16, Tt1, a.G, Nb1, nullptr, Tt2, c.G, Nb2, nullptr, 2.0f, 0.0f)) != hipSuccess)
+    return e;
+  if ((e = poetx::launch_sym_sum_bf16(Tb1, Nb1, a.w3, nb1, b, s)) != hipSuccess) return e;
+  if (b2 && (e = poetx::launch_sym_sum_bf16(Tb2, Nb2, c.w3, nb2, b, s)) != hipSuccess) return e;
+  if ((e = mm(DType::F32, a.w3, Qb1, a.w1, nullptr, c.w3, Qb2, c.w1, nullptr, -1.0f, 0.0f)) != hipSuccess)
+    return e;
+  const poetx::PackSet p1{a.w1, Tb1, nb1, (int)(a.d - (nb1 - 1) * b), a.g_theta};
+  if (!b2) return poetx::launch_pack_skew_grad(p1, nullptr, 1.0f, b, 1.0f, s);
+  const poetx::PackSet p2{c.w1, Tb2, nb2, (int)(c.d - (nb2 - 1) * b), c.g_theta};
+  return poetx::launch_pack_skew_grad(p1, &p2, 1.0f, b, 1.0f, s);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? POETX_OK : POETX_ERR_HIP; }
@@ -946,8 +1021,10 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   float* MR = reinterpret_cast<float*>(w + plan.MR);
   float* MP = reinterpret_cast<float*>(w + plan.MP);
   const int lastR = (int)(m - (nbR - 1) * bR), lastP = (int)(n - (nbP - 1) * bP);
-  // the reduced grams: activation type for the Cayley VJP, float32 for the series
-  const DType gt = neumann(d) ? DType::F32 : t;
+  // the reduced grams: the activation type, except float32 for the series
+  // when its bf16 VJP does not apply (b not a multiple of 8 on either side)
+  const bool cnp_bf16 = neumann(d) && t == DType::BF16 && bR % 8 == 0 && bP % 8 == 0;
+  const DType gt = neumann(d) && !cnp_bf16 ? DType::F32 : t;
   Stages sg{d, s};
   hipError_t e;
 #define POETX_TRY(call)                            \
@@ -1121,14 +1198,25 @@ int poetx_linear_bwd(const poetx_linear_desc* d, const void* g_y, const void* x,
   if (neumann(d)) {
     // R_f32 / P_f32 hold the skew blocks Q; the partial-gram, T and M
     // buffers are free once the grams are reduced
-    const CnpVjpSet cR{GR, R_f32, partR, TR, MR, g_theta_R, m};
-    const CnpVjpSet cP{GP, P_f32, partP, TP, MP, g_theta_P, n};
-    POETX_TRY(sg.begin(5));
-    POETX_TRY(cnp_vjp(cR, merged ? &cP : nullptr, bR, s));
-    POETX_TRY(sg.end(5));
-    POETX_TRY(sg.begin(6));
-    if (!merged) POETX_TRY(cnp_vjp(cP, nullptr, bP, s));
-    POETX_TRY(sg.end(6));
+    if (cnp_bf16) {
+      const CnpVjpBf16Set cR{GR, R_f32, partR, TR, MR, g_theta_R, m};
+      const CnpVjpBf16Set cP{GP, P_f32, partP, TP, MP, g_theta_P, n};
+      POETX_TRY(sg.begin(5));
+      POETX_TRY(cnp_vjp_bf16(cR, merged ? &cP : nullptr, bR, s));
+      POETX_TRY(sg.end(5));
+      POETX_TRY(sg.begin(6));
+      if (!merged) POETX_TRY(cnp_vjp_bf16(cP, nullptr, bP, s));
+      POETX_TRY(sg.end(6));
+    } else {
+      const CnpVjpSet cR{GR, R_f32, partR, TR, MR, g_theta_R, m};
+      const CnpVjpSet cP{GP, P_f32, partP, TP, MP, g_theta_P, n};
+      POETX_TRY(sg.begin(5));
+      POETX_TRY(cnp_vjp(cR, merged ? &cP : nullptr, bR, s));
+      POETX_TRY(sg.end(5));
+      POETX_TRY(sg.begin(6));
+      if (!merged) POETX_TRY(cnp_vjp(cP, nullptr, bP, s));
+      POETX_TRY(sg.end(6));
+    }
   } else {
     const VjpSet vR{GR, R_f32, R_act, TR, MR, g_theta_R, m, saved_y(d)};
     const VjpSet vP{GP, P_f32, P_act, TP, MP, g_theta_P, n, false};

@@ -1,6 +1,7 @@
 // Cayley-Neumann series variant of the orthogonal map: the elementwise
 // steps of the build and of its VJP. The b x b products run on the batched
-// fp32 MFMA GEMM.
+// MFMA GEMM: float32 for the build, and for the VJP float32 or (bf16
+// activations) bf16 operands with float32 accumulation.
 //
 // Method (gist.science technical summary of "POET-X: Memory-efficient LLM
 // Training by Scaling Orthogonal Transformation", section 2 Methodik,
@@ -57,22 +58,48 @@ cnp_finish_kernel(const float* __restrict__ E, float* __restrict__ RF, bf16_t* _
   }
 }
 
-// C = A - B, flat float4 steps.
+// Four consecutive elements (4 q .. 4 q + 3) as floats, and back.
+__device__ __forceinline__ float4 ld4(const float* p, int64_t q) {
+  return reinterpret_cast<const float4*>(p)[q];
+}
+__device__ __forceinline__ float4 ld4(const bf16_t* p, int64_t q) {
+  union { uint2 u; bf16_t h[4]; } v;
+  v.u = reinterpret_cast<const uint2*>(p)[q];
+  return make_float4(bf16_to_f32(v.h[0]), bf16_to_f32(v.h[1]), bf16_to_f32(v.h[2]),
+                     bf16_to_f32(v.h[3]));
+}
+__device__ __forceinline__ void st4(float* p, int64_t q, float4 x) {
+  reinterpret_cast<float4*>(p)[q] = x;
+}
+__device__ __forceinline__ void st4(bf16_t* p, int64_t q, float4 x) {
+  union { uint2 u; bf16_t h[4]; } v;
+  v.h[0] = f32_to_bf16(x.x); v.h[1] = f32_to_bf16(x.y);
+  v.h[2] = f32_to_bf16(x.z); v.h[3] = f32_to_bf16(x.w);
+  reinterpret_cast<uint2*>(p)[q] = v.u;
+}
+
+// C = A - B (B NULL: C = A, a conversion), flat in steps of 4 elements; the
+// difference in float32, rounded once to C's type.
+template <typename TA, typename TB, typename TC>
 __global__ void __launch_bounds__(kNT)
-sub_kernel(const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C,
-           int64_t n4) {
+sub_kernel(const TA* __restrict__ A, const TB* __restrict__ B, TC* __restrict__ C, int64_t n4) {
   for (int64_t q = (int64_t)blockIdx.x * kNT + threadIdx.x; q < n4; q += (int64_t)gridDim.x * kNT) {
-    const float4 a = reinterpret_cast<const float4*>(A)[q];
-    const float4 c = reinterpret_cast<const float4*>(B)[q];
-    reinterpret_cast<float4*>(C)[q] = make_float4(a.x - c.x, a.y - c.y, a.z - c.z, a.w - c.w);
+    float4 a = ld4(A, q);
+    if (B) {
+      const float4 c = ld4(B, q);
+      a = make_float4(a.x - c.x, a.y - c.y, a.z - c.z, a.w - c.w);
+    }
+    st4(C, q, a);
   }
 }
 
-// W = S + S^T with S = A + B, per b x b block. grid (tiles of 32 x 32,
-// nblocks): each workgroup writes tile (TI, TJ) from tiles (TI, TJ) and
-// (TJ, TI) of S, the second transposed through LDS.
+// W = S + S^T with S = A + B, per b x b block, in float32, rounded once to
+// W's type. grid (tiles of 32 x 32, nblocks): each workgroup writes tile
+// (TI, TJ) from tiles (TI, TJ) and (TJ, TI) of S, the second transposed
+// through LDS.
+template <typename TIn, typename TOut>
 __global__ void __launch_bounds__(kNT)
-sym_sum_kernel(const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ W,
+sym_sum_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, TOut* __restrict__ W,
                int b) {
   __shared__ float s1[32][33], s2[32][33];
   const int ntile = (b + 31) / 32;
@@ -82,17 +109,21 @@ sym_sum_kernel(const float* __restrict__ A, const float* __restrict__ B, float* 
   for (int ty = ty0; ty < 32; ty += 8) {
     const int i = TI * 32 + ty, j = TJ * 32 + tx;
     float v = 0.0f;
-    if (i < b && j < b) v = A[base + (int64_t)i * b + j] + B[base + (int64_t)i * b + j];
+    if (i < b && j < b)
+      v = ElemTraits<TIn>::to_f32(A[base + (int64_t)i * b + j]) +
+          ElemTraits<TIn>::to_f32(B[base + (int64_t)i * b + j]);
     s1[ty][tx] = v;
     const int it = TJ * 32 + ty, jt = TI * 32 + tx;
     float w = 0.0f;
-    if (it < b && jt < b) w = A[base + (int64_t)it * b + jt] + B[base + (int64_t)it * b + jt];
+    if (it < b && jt < b)
+      w = ElemTraits<TIn>::to_f32(A[base + (int64_t)it * b + jt]) +
+          ElemTraits<TIn>::to_f32(B[base + (int64_t)it * b + jt]);
     s2[ty][tx] = w;
   }
   __syncthreads();
   for (int ty = ty0; ty < 32; ty += 8) {
     const int i = TI * 32 + ty, j = TJ * 32 + tx;
-    if (i < b && j < b) W[base + (int64_t)i * b + j] = s1[ty][tx] + s2[tx][ty];
+    if (i < b && j < b) store_as<TOut>(W + base + (int64_t)i * b + j, s1[ty][tx] + s2[tx][ty]);
   }
 }
 
@@ -115,7 +146,22 @@ hipError_t launch_cnp_finish(const float* E, float* RF, void* act_bf16, int64_t 
 hipError_t launch_sub(const float* A, const float* B, float* C, int64_t n, hipStream_t stream) {
   const int64_t n4 = n / 4;
   if (n4 == 0) return hipSuccess;
-  hipLaunchKernelGGL(sub_kernel, dim3(flat_grid(n4)), dim3(kNT), 0, stream, A, B, C, n4);
+  hipLaunchKernelGGL((sub_kernel<float, float, float>), dim3(flat_grid(n4)), dim3(kNT), 0, stream,
+                     A, B, C, n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_sub_to_bf16(DType ta, const void* A, const float* B, void* C, int64_t n,
+                              hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  if (n % 4 != 0) return hipErrorInvalidValue;
+  if (n4 == 0) return hipSuccess;
+  if (ta == DType::BF16)
+    hipLaunchKernelGGL((sub_kernel<bf16_t, float, bf16_t>), dim3(flat_grid(n4)), dim3(kNT), 0,
+                       stream, static_cast<const bf16_t*>(A), B, static_cast<bf16_t*>(C), n4);
+  else
+    hipLaunchKernelGGL((sub_kernel<float, float, bf16_t>), dim3(flat_grid(n4)), dim3(kNT), 0,
+                       stream, static_cast<const float*>(A), B, static_cast<bf16_t*>(C), n4);
   return hipGetLastError();
 }
 
@@ -123,7 +169,18 @@ hipError_t launch_sym_sum(const float* A, const float* B, float* W, int64_t nblo
                           hipStream_t stream) {
   if (nblocks == 0) return hipSuccess;
   const int nt = (b + 31) / 32;
-  hipLaunchKernelGGL(sym_sum_kernel, dim3(nt * nt, (int)nblocks), dim3(kNT), 0, stream, A, B, W, b);
+  hipLaunchKernelGGL((sym_sum_kernel<float, float>), dim3(nt * nt, (int)nblocks), dim3(kNT), 0,
+                     stream, A, B, W, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_sym_sum_bf16(const void* A, const void* B, void* W, int64_t nblocks, int b,
+                               hipStream_t stream) {
+  if (nblocks == 0) return hipSuccess;
+  const int nt = (b + 31) / 32;
+  hipLaunchKernelGGL((sym_sum_kernel<bf16_t, bf16_t>), dim3(nt * nt, (int)nblocks), dim3(kNT), 0,
+                     stream, static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B),
+                     static_cast<bf16_t*>(W), b);
   return hipGetLastError();
 }
 

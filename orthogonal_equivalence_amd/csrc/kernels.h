@@ -174,9 +174,17 @@ hipError_t launch_cnp_finish(const float* E, float* RF, void* act_bf16, int64_t 
                              hipStream_t stream);
 // C = A - B over n floats (n % 4 == 0, 16-byte aligned pointers).
 hipError_t launch_sub(const float* A, const float* B, float* C, int64_t n, hipStream_t stream);
+// C (bf16) = A - B with A of type ta and B float32, or C = A when B is NULL
+// (a conversion); the difference in float32, rounded once. n % 4 == 0, A and
+// C 8-byte aligned, B 16-byte aligned.
+hipError_t launch_sub_to_bf16(DType ta, const void* A, const float* B, void* C, int64_t n,
+                              hipStream_t stream);
 // W = S + S^T per b x b block, S = A + B.
 hipError_t launch_sym_sum(const float* A, const float* B, float* W, int64_t nblocks, int b,
                           hipStream_t stream);
+// The same for bf16 A, B and W (the sums in float32, W rounded once).
+hipError_t launch_sym_sum_bf16(const void* A, const void* B, void* W, int64_t nblocks, int b,
+                               hipStream_t stream);
 
 // ---- block-mixing permutations (permute.hip) ----
 // out[r][j] = in[src][perm[j]] for r < rows, j < d, src = rowmap ? rowmap[r] : r;
