@@ -22,7 +22,9 @@ Recipe (one layer):
   activation dtype: float32 (RNE) or bfloat16 (float64 -> float32 RNE ->
   bfloat16 RNE).
 The arrays returned are float64 arrays holding exactly the rounded values, so
-the oracle consumes the very numbers the GPU path is given.
+the oracle consumes the very numbers the GPU path is given. Where R and P have
+different block sizes (make_layer_blocks), theta_R has b_out(b_out-1)/2 entries
+per block and theta_P b_in(b_in-1)/2; the order and scaling are the same.
 
 Block-mixing permutations (when a test or the benchmark uses them) are drawn
 from their own generator, numpy.random.default_rng(seed + 7919):
@@ -39,7 +41,7 @@ import numpy as np
 __all__ = [
     "LayerSpec", "LayerInputs", "CONFIGS", "config_layers", "make_layer",
     "round_to_dtype", "bf16_bits", "num_blocks", "theta_count", "resized",
-    "make_permutations",
+    "make_permutations", "make_layer_blocks",
 ]
 
 
@@ -131,6 +133,22 @@ def make_layer(spec: LayerSpec) -> LayerInputs:
         x=round_to_dtype(x, act),
         g_y=round_to_dtype(g_y, act),
     )
+
+
+def make_layer_blocks(d_in: int, d_out: int, b_in: int, b_out: int, tokens: int, dtype: str,
+                      sigma_theta: float, seed: int) -> Dict[str, np.ndarray]:
+    """One layer whose R (on d_out) and P (on d_in) have their own block sizes,
+    drawn by the same recipe: a dict with W0, theta_R, theta_P, x and g_y."""
+    rng = np.random.default_rng(seed)
+    tri_out, tri_in = b_out * (b_out - 1) // 2, b_in * (b_in - 1) // 2
+    W0 = rng.standard_normal((d_out, d_in)) / math.sqrt(d_in)
+    thR = rng.standard_normal((num_blocks(d_out, b_out), tri_out)) * sigma_theta
+    thP = rng.standard_normal((num_blocks(d_in, b_in), tri_in)) * sigma_theta
+    x = rng.standard_normal((tokens, d_in))
+    g_y = rng.standard_normal((tokens, d_out))
+    return {"W0": round_to_dtype(W0, dtype), "theta_R": round_to_dtype(thR, "f32"),
+            "theta_P": round_to_dtype(thP, "f32"), "x": round_to_dtype(x, dtype),
+            "g_y": round_to_dtype(g_y, dtype)}
 
 
 def make_permutations(spec: LayerSpec):

@@ -408,6 +408,55 @@ def test_saved_y_full_size_mlp_up_8b():
     torch.cuda.empty_cache()
 
 
+# ------------------- block sizes off the fast paths, and b_in != b_out
+# R and P with different block sizes take separate builds and separate VJP
+# launches; block sizes the streaming and whole-block kernels do not take
+# run on the general GEMM and the panel build; ragged last blocks on either
+# side. Every flag that changes the backward's route appears at least once.
+ODD_BLOCK_CASES = [
+    # name, d_in, d_out, b_in, b_out, tokens, dtype, sigma, options
+    ("f32_b8_b16", 96, 128, 8, 16, 37, "f32", 0.05, {}),
+    ("f32_b24_b12_ragged", 120, 76, 24, 12, 65, "f32", 0.05, {}),
+    ("f32_b40_cnp", 200, 160, 40, 40, 50, "f32", 0.05, {"map": "cnp"}),
+    ("bf16_b16_b40", 160, 200, 16, 40, 300, "bf16", 0.05, {}),
+    ("bf16_b96_b80_ragged", 440, 328, 96, 80, 257, "bf16", 0.03, {}),
+    ("bf16_b96_b160", 480, 640, 96, 160, 513, "bf16", 0.03, {}),
+    ("bf16_b384", 768, 1152, 384, 384, 260, "bf16", 0.01, {}),
+    ("bf16_b128_b256", 512, 1024, 128, 256, 1024, "bf16", 0.02, {}),
+    ("bf16_b256_b128_saved_y", 768, 512, 256, 128, 700, "bf16", 0.02, {"saved_y": True}),
+    ("bf16_b64_b256_mem", 512, 768, 64, 256, 512, "bf16", 0.02, {"recompute_z": True}),
+    ("bf16_b256_b64_cnp", 512, 512, 256, 64, 300, "bf16", 0.02, {"map": "cnp"}),
+    ("bf16_b24_cnp", 240, 168, 24, 24, 100, "bf16", 0.03, {"map": "cnp"}),
+]
+
+
+@pytest.mark.parametrize("case", ODD_BLOCK_CASES, ids=lambda c: c[0])
+def test_layer_odd_and_unequal_blocks(case):
+    from orthogonal_equivalence_amd.inputs import make_layer_blocks
+    from orthogonal_equivalence_amd.layer import PoetxLinear
+    name, n, m, b_in, b_out, N, dt, sigma, opts = case
+    U.log(f"[odd blocks] {name}: d_in={n} d_out={m} b_in={b_in} b_out={b_out} tokens={N} {dt} "
+          f"{opts}")
+    L = make_layer_blocks(n, m, b_in, b_out, N, dt, sigma, seed=len(name) + 700)
+    map_ = opts.get("map", "cayley")
+    ora = O.LayerOracle(L["W0"], L["theta_R"], L["theta_P"], b_out, b_in, map=map_)
+    y_ref = ora.forward(L["x"])
+    gx_ref, gR_ref, gP_ref = ora.backward(L["g_y"], L["x"])
+    lay = PoetxLinear(U.dev(L["W0"], dt), b_in, b_out, dt, **opts)
+    lay.set_theta(torch.from_numpy(L["theta_R"]).float(), torch.from_numpy(L["theta_P"]).float())
+    x, g_y = U.dev(L["x"], dt), U.dev(L["g_y"], dt)
+    lay.build()
+    y, z = lay.forward(x)
+    g_x, gR, gP = lay.backward(g_y, x, z)
+    torch.cuda.synchronize()
+    U.check("R", U.host(lay.R_f32), ora.R, "f32")
+    U.check("P", U.host(lay.P_f32), ora.P, "f32")
+    U.check("y", U.host(y), y_ref, dt)
+    U.check("g_x", U.host(g_x), gx_ref, dt)
+    U.check("g_theta_R", U.host(gR), gR_ref, dt)
+    U.check("g_theta_P", U.host(gP), gP_ref, dt)
+
+
 # ----------------------------------------- Cayley-Neumann series (CNP)
 def _build_cnp(theta: np.ndarray, d: int, b: int, act=P.POETX_BF16):
     nb = -(-d // b)
