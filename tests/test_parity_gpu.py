@@ -418,6 +418,11 @@ ODD_BLOCK_CASES = [
     ("f32_b8_b16", 96, 128, 8, 16, 37, "f32", 0.05, {}),
     ("f32_b24_b12_ragged", 120, 76, 24, 12, 65, "f32", 0.05, {}),
     ("f32_b40_cnp", 200, 160, 40, 40, 50, "f32", 0.05, {"map": "cnp"}),
+    # float32 activations at the larger blocks (general GEMM applies, the
+    # whole-block and panel builds, the square float32 VJP products)
+    ("f32_b128_b256", 512, 768, 128, 256, 300, "f32", 0.02, {}),
+    ("f32_b256_saved_y", 512, 512, 256, 256, 257, "f32", 0.01, {"saved_y": True}),
+    ("f32_b512_mem", 1024, 512, 512, 512, 100, "f32", 0.01, {"recompute_z": True}),
     ("bf16_b16_b40", 160, 200, 16, 40, 300, "bf16", 0.05, {}),
     ("bf16_b96_b80_ragged", 440, 328, 96, 80, 257, "bf16", 0.03, {}),
     ("bf16_b96_b160", 480, 640, 96, 160, 513, "bf16", 0.03, {}),
