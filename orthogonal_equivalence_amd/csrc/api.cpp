@@ -635,19 +635,19 @@ hipError_t cnp_vjp_bf16(const CnpVjpBf16Set& a, const CnpVjpBf16Set* b2, int b, 
     return poetx::launch_gemm(DType::BF16, out, true, false, g, s);
   };
   hipError_t e;
-  if ((e = poetx::launch_sub_to_bf16(DType::F32, a.Q, nullptr, Qb1, nb1 * bb, s)) != hipSuccess) return e;
-  if (b2 && (e = poetx::launch_sub_to_bf16(DType::F32, c.Q, nullptr, Qb2, nb2 * bb, s)) != hipSuccess)
+  if ((e = poetx::launch_sub_to_bf16(DType::F32, a.Q, nullptr, Qb1, nb1 * bb, c.Q, nullptr, Qb2,
+                                     nb2 * bb, s)) != hipSuccess)
     return e;
   if ((e = mm(DType::BF16, Qb1, Qb1, Q2_1, nullptr, Qb2, Qb2, Q2_2, nullptr, 1.0f, 0.0f)) != hipSuccess)
     return e;
-  if ((e = poetx::launch_sub_to_bf16(DType::BF16, Q2_1, a.Q, Tt1, nb1 * bb, s)) != hipSuccess) return e;
-  if (b2 && (e = poetx::launch_sub_to_bf16(DType::BF16, Q2_2, c.Q, Tt2, nb2 * bb, s)) != hipSuccess)
+  if ((e = poetx::launch_sub_to_bf16(DType::BF16, Q2_1, a.Q, Tt1, nb1 * bb, Q2_2, c.Q, Tt2,
+                                     nb2 * bb, s)) != hipSuccess)
     return e;
   if ((e = mm(DType::BF16, a.G, Q2_1, Tb1, a.G, c.G, Q2_2, Tb2, c.G, 2.0f, 2.0f)) != hipSuccess) return e;
   if ((e = mm(DType::BF16, Tt1, a.G, Nb1, nullptr, Tt2, c.G, Nb2, nullptr, 2.0f, 0.0f)) != hipSuccess)
     return e;
-  if ((e = poetx::launch_sym_sum_bf16(Tb1, Nb1, a.w3, nb1, b, s)) != hipSuccess) return e;
-  if (b2 && (e = poetx::launch_sym_sum_bf16(Tb2, Nb2, c.w3, nb2, b, s)) != hipSuccess) return e;
+  if ((e = poetx::launch_sym_sum_bf16(Tb1, Nb1, a.w3, nb1, Tb2, Nb2, c.w3, nb2, b, s)) != hipSuccess)
+    return e;
   if ((e = mm(DType::F32, a.w3, Qb1, a.w1, nullptr, c.w3, Qb2, c.w1, nullptr, -1.0f, 0.0f)) != hipSuccess)
     return e;
   const poetx::PackSet p1{a.w1, Tb1, nb1, (int)(a.d - (nb1 - 1) * b), a.g_theta};

@@ -79,17 +79,26 @@ __device__ __forceinline__ void st4(bf16_t* p, int64_t q, float4 x) {
 }
 
 // C = A - B (B NULL: C = A, a conversion), flat in steps of 4 elements; the
-// difference in float32, rounded once to C's type.
+// difference in float32, rounded once to C's type. A second segment (A2,
+// B2, C2, m4 steps) may follow in the same launch: steps n4 .. n4 + m4 - 1.
 template <typename TA, typename TB, typename TC>
 __global__ void __launch_bounds__(kNT)
-sub_kernel(const TA* __restrict__ A, const TB* __restrict__ B, TC* __restrict__ C, int64_t n4) {
-  for (int64_t q = (int64_t)blockIdx.x * kNT + threadIdx.x; q < n4; q += (int64_t)gridDim.x * kNT) {
-    float4 a = ld4(A, q);
-    if (B) {
-      const float4 c = ld4(B, q);
+sub_kernel(const TA* __restrict__ A, const TB* __restrict__ B, TC* __restrict__ C, int64_t n4,
+           const TA* __restrict__ A2, const TB* __restrict__ B2, TC* __restrict__ C2,
+           int64_t m4) {
+  for (int64_t q = (int64_t)blockIdx.x * kNT + threadIdx.x; q < n4 + m4;
+       q += (int64_t)gridDim.x * kNT) {
+    const bool two = q >= n4;
+    const TA* a_ = two ? A2 : A;
+    const TB* b_ = two ? B2 : B;
+    TC* c_ = two ? C2 : C;
+    const int64_t r = two ? q - n4 : q;
+    float4 a = ld4(a_, r);
+    if (b_) {
+      const float4 c = ld4(b_, r);
       a = make_float4(a.x - c.x, a.y - c.y, a.z - c.z, a.w - c.w);
     }
-    st4(C, q, a);
+    st4(c_, r, a);
   }
 }
 
@@ -100,11 +109,19 @@ sub_kernel(const TA* __restrict__ A, const TB* __restrict__ B, TC* __restrict__ 
 template <typename TIn, typename TOut>
 __global__ void __launch_bounds__(kNT)
 sym_sum_kernel(const TIn* __restrict__ A, const TIn* __restrict__ B, TOut* __restrict__ W,
-               int b) {
+               int b, int nb1, const TIn* __restrict__ A2, const TIn* __restrict__ B2,
+               TOut* __restrict__ W2) {
+  // blocks y < nb1 of (A, B, W), then those of the second set
   __shared__ float s1[32][33], s2[32][33];
   const int ntile = (b + 31) / 32;
   const int TI = blockIdx.x / ntile, TJ = blockIdx.x - TI * ntile;
-  const int64_t base = (int64_t)blockIdx.y * b * b;
+  const bool two = (int)blockIdx.y >= nb1;
+  if (two) {
+    A = A2;
+    B = B2;
+    W = W2;
+  }
+  const int64_t base = (int64_t)(two ? (int)blockIdx.y - nb1 : (int)blockIdx.y) * b * b;
   const int tx = threadIdx.x & 31, ty0 = threadIdx.x >> 5;
   for (int ty = ty0; ty < 32; ty += 8) {
     const int i = TI * 32 + ty, j = TJ * 32 + tx;
@@ -147,21 +164,24 @@ hipError_t launch_sub(const float* A, const float* B, float* C, int64_t n, hipSt
   const int64_t n4 = n / 4;
   if (n4 == 0) return hipSuccess;
   hipLaunchKernelGGL((sub_kernel<float, float, float>), dim3(flat_grid(n4)), dim3(kNT), 0, stream,
-                     A, B, C, n4);
+                     A, B, C, n4, nullptr, nullptr, nullptr, (int64_t)0);
   return hipGetLastError();
 }
 
 hipError_t launch_sub_to_bf16(DType ta, const void* A, const float* B, void* C, int64_t n,
+                              const void* A2, const float* B2, void* C2, int64_t n2,
                               hipStream_t stream) {
-  const int64_t n4 = n / 4;
-  if (n % 4 != 0) return hipErrorInvalidValue;
-  if (n4 == 0) return hipSuccess;
+  if (n % 4 != 0 || n2 % 4 != 0 || n2 < 0) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4, m4 = n2 / 4;
+  if (n4 + m4 == 0) return hipSuccess;
   if (ta == DType::BF16)
-    hipLaunchKernelGGL((sub_kernel<bf16_t, float, bf16_t>), dim3(flat_grid(n4)), dim3(kNT), 0,
-                       stream, static_cast<const bf16_t*>(A), B, static_cast<bf16_t*>(C), n4);
+    hipLaunchKernelGGL((sub_kernel<bf16_t, float, bf16_t>), dim3(flat_grid(n4 + m4)), dim3(kNT), 0,
+                       stream, static_cast<const bf16_t*>(A), B, static_cast<bf16_t*>(C), n4,
+                       static_cast<const bf16_t*>(A2), B2, static_cast<bf16_t*>(C2), m4);
   else
-    hipLaunchKernelGGL((sub_kernel<float, float, bf16_t>), dim3(flat_grid(n4)), dim3(kNT), 0,
-                       stream, static_cast<const float*>(A), B, static_cast<bf16_t*>(C), n4);
+    hipLaunchKernelGGL((sub_kernel<float, float, bf16_t>), dim3(flat_grid(n4 + m4)), dim3(kNT), 0,
+                       stream, static_cast<const float*>(A), B, static_cast<bf16_t*>(C), n4,
+                       static_cast<const float*>(A2), B2, static_cast<bf16_t*>(C2), m4);
   return hipGetLastError();
 }
 
@@ -170,17 +190,20 @@ hipError_t launch_sym_sum(const float* A, const float* B, float* W, int64_t nblo
   if (nblocks == 0) return hipSuccess;
   const int nt = (b + 31) / 32;
   hipLaunchKernelGGL((sym_sum_kernel<float, float>), dim3(nt * nt, (int)nblocks), dim3(kNT), 0,
-                     stream, A, B, W, b);
+                     stream, A, B, W, b, (int)nblocks, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_sym_sum_bf16(const void* A, const void* B, void* W, int64_t nblocks, int b,
+hipError_t launch_sym_sum_bf16(const void* A, const void* B, void* W, int64_t nblocks,
+                               const void* A2, const void* B2, void* W2, int64_t nblocks2, int b,
                                hipStream_t stream) {
-  if (nblocks == 0) return hipSuccess;
+  if (nblocks + nblocks2 == 0) return hipSuccess;
   const int nt = (b + 31) / 32;
-  hipLaunchKernelGGL((sym_sum_kernel<bf16_t, bf16_t>), dim3(nt * nt, (int)nblocks), dim3(kNT), 0,
-                     stream, static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B),
-                     static_cast<bf16_t*>(W), b);
+  hipLaunchKernelGGL((sym_sum_kernel<bf16_t, bf16_t>), dim3(nt * nt, (int)(nblocks + nblocks2)),
+                     dim3(kNT), 0, stream, static_cast<const bf16_t*>(A),
+                     static_cast<const bf16_t*>(B), static_cast<bf16_t*>(W), b, (int)nblocks,
+                     static_cast<const bf16_t*>(A2), static_cast<const bf16_t*>(B2),
+                     static_cast<bf16_t*>(W2));
   return hipGetLastError();
 }
 

@@ -176,14 +176,18 @@ hipError_t launch_cnp_finish(const float* E, float* RF, void* act_bf16, int64_t 
 hipError_t launch_sub(const float* A, const float* B, float* C, int64_t n, hipStream_t stream);
 // C (bf16) = A - B with A of type ta and B float32, or C = A when B is NULL
 // (a conversion); the difference in float32, rounded once. n % 4 == 0, A and
-// C 8-byte aligned, B 16-byte aligned.
+// C 8-byte aligned, B 16-byte aligned. A second set (A2, B2, C2, n2
+// elements, the same rules; n2 = 0 for none) shares the launch.
 hipError_t launch_sub_to_bf16(DType ta, const void* A, const float* B, void* C, int64_t n,
+                              const void* A2, const float* B2, void* C2, int64_t n2,
                               hipStream_t stream);
 // W = S + S^T per b x b block, S = A + B.
 hipError_t launch_sym_sum(const float* A, const float* B, float* W, int64_t nblocks, int b,
                           hipStream_t stream);
-// The same for bf16 A, B and W (the sums in float32, W rounded once).
-hipError_t launch_sym_sum_bf16(const void* A, const void* B, void* W, int64_t nblocks, int b,
+// The same for bf16 A, B and W (the sums in float32, W rounded once), with
+// an optional second set of nblocks2 blocks in the same launch.
+hipError_t launch_sym_sum_bf16(const void* A, const void* B, void* W, int64_t nblocks,
+                               const void* A2, const void* B2, void* W2, int64_t nblocks2, int b,
                                hipStream_t stream);
 
 // ---- block-mixing permutations (permute.hip) ----
