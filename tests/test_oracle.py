@@ -37,3 +37,38 @@ def test_tiny_config_orthogonality_and_routes():
     y = ora.forward(L.x)
     y2, _, _ = O.forward_input_centric(L.x, L.W0, ora.R, ora.P, spec.b, spec.b)
     assert np.max(np.abs(y - y2)) <= 1e-12 * np.abs(y).max()
+
+
+@pytest.mark.parametrize("d_out,b", [(96, 32), (80, 32)], ids=["whole_blocks", "ragged_last"])
+def test_z_from_y_for_orthogonal_blocks(d_out, b):
+    """The identity the library's POETX_SAVED_Y route rests on, in float64:
+    per R block Y_k = Z_k R_k^T with R_k orthogonal, so Z_k = Y_k R_k and the
+    R gram g_Y^T Z equals (g_Y^T Y) R; the Cayley VJP's first factor
+    G (R^T + I) then equals G' (I + R) for G' = g_Y^T Y. A ragged last block
+    is the leading r x r part of an identity-padded orthogonal block, itself
+    orthogonal. A control with R^T in place of R must fail."""
+    rng = np.random.default_rng(11)
+    d_in, tokens = 64, 50
+    W0 = rng.standard_normal((d_out, d_in)) / 8.0
+    nbR, nbP = -(-d_out // b), -(-d_in // b)
+    tri = b * (b - 1) // 2
+    thR = rng.standard_normal((nbR, tri)) * 0.05
+    thP = rng.standard_normal((nbP, tri)) * 0.05
+    x = rng.standard_normal((tokens, d_in))
+    g_y = rng.standard_normal((tokens, d_out))
+    ora = O.LayerOracle(W0, thR, thP, b, b)
+    Y, Z, _ = O.forward_input_centric(x, W0, ora.R, ora.P, b, b)
+    for k in range(nbR):
+        c0, c1 = k * b, min(d_out, (k + 1) * b)
+        r = c1 - c0
+        Rk = ora.R[k][:r, :r]
+        Yk, Zk, gk = Y[:, c0:c1], Z[:, c0:c1], g_y[:, c0:c1]
+        assert np.abs(Zk - Yk @ Rk).max() <= 1e-12 * np.abs(Zk).max()
+        G = gk.T @ Zk
+        Gp = gk.T @ Yk
+        assert np.abs(G - Gp @ Rk).max() <= 1e-12 * np.abs(G).max()
+        I = np.eye(r)
+        lhs = G @ (Rk.T + I)
+        assert np.abs(lhs - Gp @ (I + Rk)).max() <= 1e-12 * np.abs(lhs).max()
+        # control: the transpose in the wrong place is far off
+        assert np.abs(G - Gp @ Rk.T).max() > 1e-3 * np.abs(G).max()
