@@ -153,6 +153,35 @@ scale_block_columns_kernel(const T* __restrict__ M, const float* __restrict__ s,
   }
 }
 
+// The same for b % 4 == 0, grid (ceil(b b / (4 kNT)), nblocks): each thread
+// scales four consecutive columns of one row (they never straddle a row), with
+// 32-bit index arithmetic inside the block.
+__device__ __forceinline__ void scale4(const float* in, float* out, const float sc[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(in);
+  *reinterpret_cast<float4*>(out) = make_float4(v.x * sc[0], v.y * sc[1], v.z * sc[2], v.w * sc[3]);
+}
+__device__ __forceinline__ void scale4(const bf16_t* in, bf16_t* out, const float sc[4]) {
+  union { uint2 u; bf16_t h[4]; } v;
+  v.u = *reinterpret_cast<const uint2*>(in);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v.h[t] = f32_to_bf16(bf16_to_f32(v.h[t]) * sc[t]);
+  *reinterpret_cast<uint2*>(out) = v.u;
+}
+template <typename T>
+__global__ void __launch_bounds__(kNT)
+scale_block_columns4_kernel(const T* __restrict__ M, const float* __restrict__ s, int b, int64_t d,
+                            T* __restrict__ out) {
+  const int q = (int)blockIdx.x * kNT + (int)threadIdx.x;
+  if (q >= b * b / 4) return;
+  const int e = 4 * q, j = e % b;
+  const int64_t base = (int64_t)blockIdx.y * b * b + e;
+  const int64_t col = (int64_t)blockIdx.y * b + j;
+  float sc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) sc[t] = col + t < d ? s[col + t] : 0.0f;
+  scale4(M + base, out + base, sc);
+}
+
 int flat_grid(int64_t n) { return (int)std::min<int64_t>((n + kNT - 1) / kNT, 8192); }
 
 }  // namespace
@@ -193,6 +222,16 @@ hipError_t launch_scale_block_columns(DType t, const void* M, const float* scale
                                       int b, int64_t d, void* out, hipStream_t s) {
   const int64_t total = nblocks * b * b;
   if (total == 0) return hipSuccess;
+  if (b % 4 == 0 && nblocks <= 65535) {
+    const dim3 grid((unsigned)((b * b / 4 + kNT - 1) / kNT), (unsigned)nblocks);
+    if (t == DType::BF16)
+      hipLaunchKernelGGL(scale_block_columns4_kernel<bf16_t>, grid, dim3(kNT), 0, s,
+                         static_cast<const bf16_t*>(M), scale, b, d, static_cast<bf16_t*>(out));
+    else
+      hipLaunchKernelGGL(scale_block_columns4_kernel<float>, grid, dim3(kNT), 0, s,
+                         static_cast<const float*>(M), scale, b, d, static_cast<float*>(out));
+    return hipGetLastError();
+  }
   if (t == DType::BF16)
     hipLaunchKernelGGL(scale_block_columns_kernel<bf16_t>, dim3(flat_grid(total)), dim3(kNT), 0, s,
                        static_cast<const bf16_t*>(M), scale, total, b, d, static_cast<bf16_t*>(out));
